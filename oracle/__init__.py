@@ -1,0 +1,214 @@
+"""fp64 CPU oracle for the packed varlen attention head -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  The HIP library never calls it and shares no code with it.
+
+What it computes, step by step, in float64 with numpy (matmul, exp, cos, sin,
+sqrt are the only library primitives used):
+
+1. Packing and positions.  Segments are (T, H, W) token grids truncated to L
+   tokens, packed back to back; ``cu_seqlens`` is the prefix sum of the L.
+   Token n of a segment sits at (t, h, w) in row-major order with w fastest.
+   [vllm.cpp PR #26, opening commit: the DiT runs once per step over the whole
+   packed sequence, with an fp64 position grid; per-segment grids follow the
+   packed fl2va/ref2va layouts named there.]
+2. Rotary angles.  The t, h and w axes own d_t, d_h, d_w rotated dims; axis a
+   contributes d_a / 2 frequencies f_a[j] = base ** (-2 j / d_a) and the angle
+   vector of a token is concat(t * f_t, h * f_h, w * f_w) (R / 2 entries,
+   R = d_t + d_h + d_w).  [PR #26 description, "The device-resident forward
+   (W2b)": the H3 3D MM-RoPE is plain NeoX rotate-half and only the angles,
+   three axes off the fp64 grid, are unusual; encoder-tower commit: the cache
+   is cat(freqs, freqs), so cos/sin repeat over the two halves.]
+3. Per-head RMSNorm: y = x / sqrt(mean_d x_d^2 + eps) * gamma.
+   [h3-spark model card, "What this config does": Q RMSNorm then rot96 RoPE.]
+4. NeoX rotary on the first R dims: pairs (i, i + R/2) for i < R/2 rotate by
+   the angle of entry i; dims >= R pass through.  [same passages as 2.]
+5. Attention restricted to each segment, non-causal: for every segment [a, b)
+   and head, o_i = sum_j softmax_j(scale <q_i, k_j>) v_j over j in [a, b),
+   with the textbook two-pass softmax (row max, exponentials, normalise).
+   [PR #26 opening commit: the packed varlen non-causal attention is exactly a
+   cu_seqlens varlen flash-attention call with a per-document bidirectional
+   contract.]
+
+Readings where the pages are silent (each is listed in the design doc):
+integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
+shared by all heads; RMSNorm before RoPE; V gets neither; empty segments are
+legal and contribute nothing.
+
+Parity against upstream H3 itself is unpinned (no upstream code or values are
+available); the functions here are pinned by closed forms, brute force and
+invariants in tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# 1. Packing and positions
+# ----------------------------------------------------------------------------
+
+
+def cu_seqlens(segments) -> np.ndarray:
+    """Prefix sums of the segment lengths: int64 [nseg + 1], starting at 0."""
+    lens = np.array([int(s[3]) for s in segments], dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+
+
+def segment_positions(segments) -> np.ndarray:
+    """Integer (t, h, w) of every packed token: int64 [S, 3].
+
+    Token n of a (T, H, W) segment is at t = n // (H W), h = (n // W) mod H,
+    w = n mod W (row-major, w fastest); positions restart at 0 per segment.
+    """
+    out = []
+    for (T, H, W, L) in segments:
+        n = np.arange(int(L), dtype=np.int64)
+        out.append(np.stack([n // (H * W), (n // W) % H, n % W], axis=1))
+    if not out:
+        return np.zeros((0, 3), dtype=np.int64)
+    return np.concatenate(out, axis=0)
+
+
+# ----------------------------------------------------------------------------
+# 2. Rotary angles and the cos/sin table
+# ----------------------------------------------------------------------------
+
+
+def axis_inverse_frequencies(d_axis: int, base: float) -> np.ndarray:
+    """f[j] = base ** (-2 j / d_axis) for j < d_axis / 2 (fp64)."""
+    j = np.arange(d_axis // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * j / np.float64(d_axis))
+
+
+def rope_angles(positions: np.ndarray, rot_dims, base: float) -> np.ndarray:
+    """theta [S, R/2] = concat(t * f_t, h * f_h, w * f_w) in fp64."""
+    parts = []
+    for axis, d_axis in enumerate(rot_dims):
+        f = axis_inverse_frequencies(int(d_axis), base)
+        parts.append(positions[:, axis:axis + 1].astype(np.float64) * f[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def rope_table(segments, rot_dims, base: float):
+    """(cu_seqlens, cos, sin) with cos/sin fp64 [S, R/2]."""
+    theta = rope_angles(segment_positions(segments), rot_dims, base)
+    return cu_seqlens(segments), np.cos(theta), np.sin(theta)
+
+
+# ----------------------------------------------------------------------------
+# 3./4. RMSNorm and rotary
+# ----------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2 over the last axis) + eps) * gamma, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, rot_dim: int) -> np.ndarray:
+    """NeoX rotate-half on x [S, heads, D] over its first rot_dim dims.
+
+    With half = rot_dim / 2 and a = x[..., :half], b = x[..., half:rot_dim]:
+    a' = a cos - b sin, b' = b cos + a sin (cos/sin [S, half] broadcast over
+    heads); dims >= rot_dim are copied.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    half = rot_dim // 2
+    c = cos[:, None, :]
+    s = sin[:, None, :]
+    a = x[..., :half]
+    b = x[..., half:rot_dim]
+    out = x.copy()
+    out[..., :half] = a * c - b * s
+    out[..., half:rot_dim] = b * c + a * s
+    return out
+
+
+def qk_rmsnorm_rope(q, k, gamma_q, gamma_k, eps, cos, sin, rot_dim):
+    """RMSNorm each head vector of q and k with its own gain, then rotate."""
+    qn = rope_rotate(rms_norm(q, gamma_q, eps), cos, sin, rot_dim)
+    kn = rope_rotate(rms_norm(k, gamma_k, eps), cos, sin, rot_dim)
+    return qn, kn
+
+
+# ----------------------------------------------------------------------------
+# 5. Attention restricted to each segment
+# ----------------------------------------------------------------------------
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Two-pass softmax along the last axis: subtract the row max, exponentiate, normalise."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def segment_head_attention(q, k, v, scale: float, row_block: int = 2048):
+    """softmax(scale q k^T) v for one segment and one head; q, k, v [L, D].
+
+    Query rows are independent, so they are processed ``row_block`` at a time
+    only to bound memory; nothing else is blocked.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((q.shape[0], v.shape[1]), dtype=np.float64)
+    for r0 in range(0, q.shape[0], row_block):
+        s = scale * (q[r0:r0 + row_block] @ k.T)
+        out[r0:r0 + row_block] = _softmax_rows(s) @ v
+    return out
+
+
+def varlen_attention(q, k, v, cu, scale: float) -> np.ndarray:
+    """o [S, heads, Dv] for q, k [S, heads, D], v [S, heads, Dv] packed by cu_seqlens."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.zeros(q.shape[:2] + (v.shape[2],), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in range(q.shape[1]):
+            o[a:b, h] = segment_head_attention(q[a:b, h], k[a:b, h], v[a:b, h], scale)
+    return o
+
+
+def segment_of_rows(cu, rows) -> np.ndarray:
+    """Index of the segment that holds each packed row."""
+    return np.searchsorted(np.asarray(cu), np.asarray(rows), side="right") - 1
+
+
+def varlen_attention_rows(q, k, v, cu, scale: float, rows) -> np.ndarray:
+    """Output rows ``rows`` only (all heads): o[rows] [len(rows), heads, Dv].
+
+    Each row is computed from its own segment's keys exactly as in
+    varlen_attention; used where the full result is too large to compute.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    seg = segment_of_rows(cu, rows)
+    out = np.empty((len(rows), q.shape[1], v.shape[2]), dtype=np.float64)
+    for s in np.unique(seg):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero(seg == s)[0]
+        for h in range(q.shape[1]):
+            qs = np.asarray(q[rows[sel], h], dtype=np.float64)
+            out[sel, h] = segment_head_attention(qs, k[a:b, h], v[a:b, h], scale)
+    return out
+
+
+def attention_weights(q, k, cu, scale: float, seg: int, head: int) -> np.ndarray:
+    """The softmax matrix [L, L] of one segment and head (for invariant checks)."""
+    a, b = int(cu[seg]), int(cu[seg + 1])
+    qs = np.asarray(q[a:b, head], dtype=np.float64)
+    ks = np.asarray(k[a:b, head], dtype=np.float64)
+    return _softmax_rows(scale * (qs @ ks.T))
+
+
+def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):
+    """The whole chain: table, norm + rotary on q and k, then varlen attention."""
+    cu, cos, sin = rope_table(segments, rot_dims, base)
+    qn, kn = qk_rmsnorm_rope(q, k, gamma_q, gamma_k, eps, cos, sin, int(sum(rot_dims)))
+    return varlen_attention(qn, kn, v, cu, scale)

@@ -1,0 +1,149 @@
+"""Workload descriptions (segment grids, head geometry) and their seeded tensors.
+
+Each workload is a packed sequence of segments; a segment is a (T, H, W) token
+grid truncated to L tokens.  The shapes follow the requests the MiniMax H3 DiT
+serves: a 864x480, 124-frame render with six reference images and an audio
+track packed into S = 20,423 tokens (h3-spark model card, "Measured on one DGX
+Spark"), 24 heads of 128 dims with rotary on the first 96.  The tensors are
+synthetic: Q, K, V ~ N(0, 1) and the RMSNorm gains ~ 1 + N(0, 0.1).
+
+Only descriptions and random draws live here.  The packing prefix sums, token
+positions and everything downstream are computed separately by the oracle and
+by the HIP library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+from . import rng
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    segments: tuple  # ((T, H, W, L), ...)
+    heads: int
+    head_dim: int
+    rot_dims: tuple  # rotated dims owned by the t, h and w axes
+    dtype: str  # "f32" or "bf16"
+    base: float = 10000.0
+    eps: float = 1e-6
+    seed: int = 0
+    gamma_mean: float = 1.0
+    gamma_std: float = 0.1
+    note: str = field(default="", compare=False)
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(s[3] for s in self.segments))
+
+    @property
+    def rot_dim(self) -> int:
+        return int(sum(self.rot_dims))
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def lengths(self) -> list:
+        return [int(s[3]) for s in self.segments]
+
+    def attention_flops(self) -> float:
+        """QK^T plus PV multiply-adds at 2 flop each: 4 * D * heads * sum(L^2)."""
+        return 4.0 * self.head_dim * self.heads * float(sum(L * L for L in self.lengths))
+
+    def with_segments(self, segments, name=None) -> "Workload":
+        d = dict(self.__dict__)
+        d["segments"] = tuple(tuple(int(v) for v in s) for s in segments)
+        d["name"] = name or self.name
+        return Workload(**d)
+
+    def replace(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+def ragged_segments(seed: int, n: int = 64, lo: int = 128, hi: int = 2048, rows: int = 16):
+    """n segments with integer lengths uniform in [lo, hi], each a 1 x rows x ceil(L/rows) grid."""
+    u = rng.uniform(seed, rng.TAG_LENS, n)
+    lens = lo + np.floor(u * (hi - lo + 1)).astype(np.int64)
+    return tuple((1, rows, -(-int(L) // rows), int(L)) for L in lens)
+
+
+def _h3_request(video_thw, ref_hw, audio_len):
+    t, h, w = video_thw
+    segs = [(t, h, w, t * h * w)]
+    segs += [(1, ref_hw[0], ref_hw[1], ref_hw[0] * ref_hw[1])] * 6
+    # 1-D audio track laid along the temporal axis (its h and w grids are 1).
+    segs.append((audio_len, 1, 1, audio_len))
+    return tuple(segs)
+
+
+TINY_F32 = Workload(
+    name="tiny_f32",
+    segments=((1, 37, 1, 37), (1, 7, 13, 91)),
+    heads=2, head_dim=64, rot_dims=(16, 16, 16), dtype="f32",
+    note="2 segments [37, 91], 2 heads, D=64, rotary on 48 dims",
+)
+
+TWO_SEG = Workload(
+    name="two_seg_bf16",
+    segments=((4, 32, 32, 4096), (1, 32, 32, 1024)),
+    heads=24, head_dim=128, rot_dims=(32, 32, 32), dtype="bf16",
+    note="2 segments [4096, 1024]",
+)
+
+H3_S20423 = Workload(
+    name="h3_s20423_bf16",
+    segments=_h3_request((10, 30, 54), (20, 30), 623),
+    heads=24, head_dim=128, rot_dims=(32, 32, 32), dtype="bf16",
+    note="video 10x30x54 + 6 refs 20x30 + audio 623: S=20,423",
+)
+
+H3_S25103 = Workload(
+    name="h3_s25103_bf16",
+    segments=_h3_request((10, 34, 60), (20, 34), 623),
+    heads=24, head_dim=128, rot_dims=(32, 32, 32), dtype="bf16",
+    note="video 10x34x60 + 6 refs 20x34 + audio 623: S=25,103",
+)
+
+RAGGED64 = Workload(
+    name="ragged64_bf16",
+    segments=ragged_segments(0),
+    heads=24, head_dim=128, rot_dims=(32, 32, 32), dtype="bf16",
+    note="64 segments, L ~ U{128..2048}, 1x16xceil(L/16) grids",
+)
+
+ALL = {w.name: w for w in (TINY_F32, TWO_SEG, H3_S20423, H3_S25103, RAGGED64)}
+
+# The configuration the headline throughput is quoted on.
+HEADLINE = H3_S20423
+
+
+@dataclass
+class Tensors:
+    """Seeded inputs of one workload.  Floating tensors are [S, heads, D].
+
+    For bf16 workloads ``q``, ``k``, ``v`` hold uint16 bit patterns; gains are
+    always fp32 [D].
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    gamma_q: np.ndarray
+    gamma_k: np.ndarray
+
+
+def make_tensors(w: Workload, with_v: bool = True) -> Tensors:
+    shape = (w.tokens, w.heads, w.head_dim)
+    q = rng.normal_tensor(w.seed, rng.TAG_Q, shape, w.dtype)
+    k = rng.normal_tensor(w.seed, rng.TAG_K, shape, w.dtype)
+    v = rng.normal_tensor(w.seed, rng.TAG_V, shape, w.dtype) if with_v else None
+    gq = rng.normal_tensor(w.seed, rng.TAG_GAMMA_Q, (w.head_dim,), "f32", w.gamma_mean, w.gamma_std)
+    gk = rng.normal_tensor(w.seed, rng.TAG_GAMMA_K, (w.head_dim,), "f32", w.gamma_mean, w.gamma_std)
+    return Tensors(q, k, v, gq, gk)

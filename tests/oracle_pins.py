@@ -1,0 +1,398 @@
+"""Pins for the fp64 oracle: checks against closed forms, brute force, library
+routines and invariants, none of which reuses the oracle's own formulas.
+
+Every check takes the oracle's namespace ``O`` as an argument so that
+tests/test_oracle_mutations.py can run the same checks against oracles with a
+planted mistake and show that each mistake is caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# packing and positions
+# ---------------------------------------------------------------------------
+
+def check_positions_enumeration(O):
+    """Nested loops over (t, h, w), w fastest, truncated to L; restart per segment."""
+    segs = [(2, 3, 4, 24), (1, 7, 13, 91), (3, 2, 5, 17), (4, 1, 1, 0), (623, 1, 1, 9), (1, 1, 1, 1)]
+    expect = []
+    for (T, H, W, L) in segs:
+        seg = []
+        for t in range(T):
+            for h in range(H):
+                for w in range(W):
+                    seg.append((t, h, w))
+        expect.extend(seg[:L])
+    got = O.segment_positions(segs)
+    assert got.shape == (len(expect), 3)
+    assert np.array_equal(got, np.array(expect, dtype=np.int64).reshape(-1, 3))
+    running, cu = 0, [0]
+    for s in segs:
+        running += s[3]
+        cu.append(running)
+    assert np.array_equal(O.cu_seqlens(segs), np.array(cu))
+
+
+# ---------------------------------------------------------------------------
+# rotary angles
+# ---------------------------------------------------------------------------
+
+def check_inverse_frequencies_closed_form(O):
+    g = golden()["inverse_frequencies"]
+    f = O.axis_inverse_frequencies(g[0]["d_axis"], g[0]["base"])
+    assert f.shape == (16,)
+    for j, val in g[0]["checks"].items():
+        assert abs(f[int(j)] - val) <= 1e-15 * max(1.0, val), (j, f[int(j)], val)
+    ratio = f[1:] / f[:-1]
+    assert np.allclose(ratio, 10000.0 ** (-1.0 / 16.0), rtol=1e-14, atol=0)
+    f4 = O.axis_inverse_frequencies(g[1]["d_axis"], g[1]["base"])
+    assert np.allclose(f4, g[1]["values"], rtol=1e-15, atol=0)
+
+
+def check_angle_layout(O):
+    """A unit step along one axis fills exactly that axis's block with its frequencies."""
+    dims = (32, 32, 32)
+    fr = [10000.0 ** (-2.0 * j / 32.0) for j in range(16)]
+    for axis in range(3):
+        p = np.zeros((1, 3), dtype=np.int64)
+        p[0, axis] = 1
+        th = O.rope_angles(p, dims, 10000.0)
+        assert th.shape == (1, 48)
+        want = np.zeros(48)
+        want[16 * axis:16 * axis + 16] = fr
+        assert np.allclose(th[0], want, rtol=1e-14, atol=0), axis
+    # unequal split: blocks of 8, 4, 12 frequencies
+    th = O.rope_angles(np.array([[2, 3, 5]]), (16, 8, 24), 100.0)
+    want = np.concatenate([2 * 100.0 ** (-2.0 * np.arange(8) / 16), 3 * 100.0 ** (-2.0 * np.arange(4) / 8),
+                           5 * 100.0 ** (-2.0 * np.arange(12) / 24)])
+    assert np.allclose(th[0], want, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def check_rms_norm_golden(O):
+    for case in golden()["rms_norm"]:
+        y = O.rms_norm(np.array([case["x"]]), np.array(case["gamma"]), case["eps"])
+        assert np.allclose(y[0], case["y"], rtol=1e-15, atol=1e-15), (y, case["y"])
+
+
+def check_rms_norm_invariants(O):
+    r = _rng(1)
+    x = r.normal(size=(50, 3, 64))
+    g1 = np.ones(64)
+    # scale invariance with eps = 0
+    assert np.allclose(O.rms_norm(7.25 * x, g1, 0.0), O.rms_norm(x, g1, 0.0), rtol=1e-14, atol=1e-14)
+    # with unit gain the output's mean square is ms / (ms + eps)
+    eps = 0.37
+    y = O.rms_norm(x, g1, eps)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(y * y, axis=-1), ms / (ms + eps), rtol=1e-13, atol=0)
+    # the gain multiplies each dim
+    g = r.normal(size=64)
+    assert np.allclose(O.rms_norm(x, g, eps), O.rms_norm(x, g1, eps) * g, rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# rotary
+# ---------------------------------------------------------------------------
+
+def _rotation_matrix(theta, rot_dim, head_dim):
+    """Independent dense formulation: a block rotation acting on pairs (i, i + R/2)."""
+    half = rot_dim // 2
+    M = np.eye(head_dim)
+    for i in range(half):
+        c, s = math.cos(theta[i]), math.sin(theta[i])
+        M[i, i] = c
+        M[i, i + half] = -s
+        M[i + half, i] = s
+        M[i + half, i + half] = c
+    return M
+
+
+def check_rope_golden(O):
+    case = golden()["rope"][0]
+    pos = np.array([case["position"]], dtype=np.int64)
+    th = O.rope_angles(pos, case["rot_dims"], case["base"])
+    R = sum(case["rot_dims"])
+    for c in case["cases"]:
+        x = np.zeros((1, 1, case["head_dim"]))
+        x[0, 0, c["x_index"]] = 1.0
+        y = O.rope_rotate(x, np.cos(th), np.sin(th), R)
+        assert np.allclose(y[0, 0], c["y"], rtol=0, atol=1e-15), (c, y)
+
+
+def check_rope_matches_rotation_matrix(O):
+    r = _rng(2)
+    for (dims, D) in (((32, 32, 32), 128), ((16, 16, 16), 64), ((8, 4, 12), 32)):
+        R = sum(dims)
+        pos = r.integers(0, 60, size=(9, 3))
+        th = O.rope_angles(pos, dims, 10000.0)
+        x = r.normal(size=(9, 2, D))
+        y = O.rope_rotate(x, np.cos(th), np.sin(th), R)
+        for n in range(9):
+            M = _rotation_matrix(th[n], R, D)
+            for h in range(2):
+                assert np.allclose(y[n, h], M @ x[n, h], rtol=0, atol=1e-13)
+
+
+def check_rope_identity_and_norm(O):
+    r = _rng(3)
+    dims = (32, 32, 32)
+    _, cos, sin = O.rope_table([(1, 1, 1, 1)], dims, 10000.0)
+    x = r.normal(size=(1, 4, 128))
+    assert np.array_equal(O.rope_rotate(x, cos, sin, 96), x)  # (0, 0, 0) is the identity
+    segs = [(3, 5, 7, 100), (623, 1, 1, 623)]
+    _, cos, sin = O.rope_table(segs, dims, 10000.0)
+    x = r.normal(size=(723, 2, 128))
+    y = O.rope_rotate(x, cos, sin, 96)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14, atol=0)
+    pair_x = x[..., :48] ** 2 + x[..., 48:96] ** 2
+    pair_y = y[..., :48] ** 2 + y[..., 48:96] ** 2
+    assert np.allclose(pair_y, pair_x, rtol=1e-13, atol=1e-15)
+    assert np.array_equal(y[..., 96:], x[..., 96:])
+
+
+def check_rope_single_axis(O):
+    """With h = w = 0 only the t block's pairs move."""
+    r = _rng(4)
+    pos = np.array([[5, 0, 0], [17, 0, 0]])
+    th = O.rope_angles(pos, (32, 32, 32), 10000.0)
+    x = r.normal(size=(2, 1, 128))
+    y = O.rope_rotate(x, np.cos(th), np.sin(th), 96)
+    moved = np.nonzero(np.any(np.abs(y - x) > 0, axis=(0, 1)))[0]
+    assert set(moved.tolist()) == set(range(0, 16)) | set(range(48, 64))
+
+
+def check_rope_relative_position(O):
+    """<R(p) a, R(p') b> = <a, R(p' - p) b> for integer position vectors."""
+    r = _rng(5)
+    dims = (32, 32, 32)
+    p = r.integers(0, 40, size=(20, 3))
+    p2 = p + r.integers(0, 40, size=(20, 3))
+    a = r.normal(size=(20, 1, 128))
+    b = r.normal(size=(20, 1, 128))
+
+    def rot(x, pos):
+        th = O.rope_angles(pos, dims, 10000.0)
+        return O.rope_rotate(x, np.cos(th), np.sin(th), 96)
+
+    lhs = np.sum(rot(a, p) * rot(b, p2), axis=-1)
+    rhs = np.sum(a * rot(b, p2 - p), axis=-1)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def check_attention_golden(O):
+    for case in golden()["attention"]:
+        q = np.array(case["q"])[:, None, :]
+        k = np.array(case["k"])[:, None, :]
+        v = np.array(case["v"])[:, None, :]
+        o = O.varlen_attention(q, k, v, np.array(case["cu_seqlens"]), case["scale"])
+        assert np.allclose(o[:, 0], case["o"], rtol=0, atol=1e-14), (o[:, 0], case["o"])
+
+
+def _dense_masked(q, k, v, cu, scale):
+    """Independent formulation: one S x S score matrix with -inf off the block diagonal."""
+    from scipy.special import softmax
+
+    S, H, _ = q.shape
+    seg = np.zeros(S, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        seg[cu[s]:cu[s + 1]] = s
+    mask = seg[:, None] == seg[None, :]
+    out = np.zeros((S, H, v.shape[2]))
+    for h in range(H):
+        sc = scale * np.einsum("id,jd->ij", q[:, h], k[:, h])
+        sc = np.where(mask, sc, -np.inf)
+        out[:, h] = softmax(sc, axis=1) @ v[:, h]
+    return out
+
+
+def check_attention_dense_bruteforce(O):
+    r = _rng(6)
+    lens = [37, 0, 91, 1, 64, 65, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    q, k, v = (r.normal(size=(S, 3, 16)) * 2 for _ in range(3))
+    o = O.varlen_attention(q, k, v, cu, 0.25)
+    ref = _dense_masked(q, k, v, cu, 0.25)
+    assert np.allclose(o, ref, rtol=1e-13, atol=1e-14)
+
+
+def check_attention_sdpa(O):
+    """One segment without norm or rotary equals torch's scaled_dot_product_attention (fp64, CPU)."""
+    import torch
+
+    r = _rng(7)
+    L, H, D = 77, 4, 32
+    q, k, v = (r.normal(size=(L, H, D)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, np.array([0, L]), 1.0 / math.sqrt(D))
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(1, 0, 2))) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy().transpose(1, 0, 2)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+def check_attention_special_cases(O):
+    r = _rng(8)
+    # length-1 segments return their value rows exactly
+    q, k, v = (r.normal(size=(5, 2, 8)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, np.arange(6), 0.5)
+    assert np.array_equal(o, v)
+    # identical keys give the mean value over the segment
+    L = 40
+    q = r.normal(size=(L, 1, 8))
+    k = np.repeat(r.normal(size=(1, 1, 8)), L, axis=0)
+    v = r.normal(size=(L, 1, 8))
+    o = O.varlen_attention(q, k, v, np.array([0, L]), 0.9)
+    assert np.allclose(o[:, 0], np.broadcast_to(v[:, 0].mean(axis=0), (L, 8)), rtol=0, atol=1e-14)
+    # softmax rows sum to 1 and are non-negative
+    lens = [30, 50]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k = (r.normal(size=(80, 2, 8)) * 3 for _ in range(2))
+    for seg in range(2):
+        for h in range(2):
+            P = O.attention_weights(q, k, cu, 0.7, seg, h)
+            assert P.shape == (lens[seg], lens[seg])
+            assert np.all(P >= 0)
+            assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def check_attention_segment_isolation(O):
+    """Perturbing a token of one segment leaves every output of the others bit-identical."""
+    r = _rng(9)
+    lens = [40, 33, 27]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = (r.normal(size=(100, 2, 16)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, cu, 0.3)
+    for x in (q, k, v):
+        x2 = x.copy()
+        x2[50] += 1.5  # a token of segment 1
+        args = [x2 if y is x else y for y in (q, k, v)]
+        o2 = O.varlen_attention(*args, cu, 0.3)
+        assert np.array_equal(o2[:40], o[:40]) and np.array_equal(o2[73:], o[73:])
+        assert not np.array_equal(o2[40:73], o[40:73])
+
+
+def check_attention_permutations(O):
+    r = _rng(10)
+    lens = [21, 34, 13]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    q, k, v = (r.normal(size=(S, 2, 8)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, cu, 0.6)
+    # keys/values permuted inside each segment: outputs unchanged
+    perm = np.concatenate([cu[s] + r.permutation(lens[s]) for s in range(3)])
+    o2 = O.varlen_attention(q, k[perm], v[perm], cu, 0.6)
+    assert np.allclose(o2, o, rtol=1e-13, atol=1e-14)
+    # queries permuted inside each segment: outputs permute the same way
+    o3 = O.varlen_attention(q[perm], k, v, cu, 0.6)
+    assert np.allclose(o3, o[perm], rtol=1e-13, atol=1e-14)
+    # segment order permuted: per-segment outputs move with their segments
+    order = [2, 0, 1]
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in order])
+    cu2 = np.concatenate([[0], np.cumsum([lens[s] for s in order])])
+    o4 = O.varlen_attention(q[idx], k[idx], v[idx], cu2, 0.6)
+    assert np.allclose(o4, o[idx], rtol=1e-13, atol=1e-14)
+
+
+def check_attention_rows_variant(O):
+    r = _rng(11)
+    lens = [70, 1, 45]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = (r.normal(size=(116, 3, 16)) for _ in range(3))
+    o = O.varlen_attention(q, k, v, cu, 0.25)
+    rows = np.array([0, 69, 70, 71, 100, 115, 3])
+    assert np.allclose(O.varlen_attention_rows(q, k, v, cu, 0.25, rows), o[rows], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# the chain
+# ---------------------------------------------------------------------------
+
+def check_chain_shift_invariance(O):
+    """Shifting all positions of a segment by a constant vector leaves its attention unchanged."""
+    r = _rng(12)
+    segs = [(2, 4, 5, 37)]
+    D, dims = 64, (16, 16, 16)
+    q, k, v = (r.normal(size=(37, 2, D)) for _ in range(3))
+    g = 1 + 0.1 * r.normal(size=D)
+    pos = O.segment_positions(segs)
+    cu = O.cu_seqlens(segs)
+
+    def run(p):
+        th = O.rope_angles(p, dims, 10000.0)
+        qn, kn = O.qk_rmsnorm_rope(q, k, g, g, 1e-6, np.cos(th), np.sin(th), 48)
+        return O.varlen_attention(qn, kn, v, cu, 1 / 8)
+
+    base = run(pos)
+    shifted = run(pos + np.array([3, 11, 6]))
+    assert np.allclose(shifted, base, rtol=1e-11, atol=1e-12)
+    # and the rotation is not a no-op: without it the output differs
+    qn, kn = O.rms_norm(q, g, 1e-6), O.rms_norm(k, g, 1e-6)
+    assert not np.allclose(O.varlen_attention(qn, kn, v, cu, 1 / 8), base, rtol=1e-6, atol=1e-6)
+
+
+def check_chain_composition(O):
+    """hot_path is table -> norm + rotary -> attention, with nothing else in between."""
+    r = _rng(13)
+    segs = [(1, 37, 1, 37), (1, 7, 13, 91)]
+    q, k, v = (r.normal(size=(128, 2, 64)) for _ in range(3))
+    gq, gk = 1 + 0.1 * r.normal(size=64), 1 + 0.1 * r.normal(size=64)
+    o = O.hot_path(q, k, v, gq, gk, segs, (16, 16, 16), 10000.0, 1e-6, 0.125)
+    ms_q = np.mean(q * q, axis=-1, keepdims=True)
+    ms_k = np.mean(k * k, axis=-1, keepdims=True)
+    qn = q / np.sqrt(ms_q + 1e-6) * gq
+    kn = k / np.sqrt(ms_k + 1e-6) * gk
+    pos = O.segment_positions(segs)
+    th = O.rope_angles(pos, (16, 16, 16), 10000.0)
+    for n in range(128):
+        M = _rotation_matrix(th[n], 48, 64)
+        qn[n] = qn[n] @ M.T
+        kn[n] = kn[n] @ M.T
+    ref = _dense_masked(qn, kn, v, O.cu_seqlens(segs), 0.125)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-13)
+
+
+ALL_CHECKS = [
+    check_positions_enumeration,
+    check_inverse_frequencies_closed_form,
+    check_angle_layout,
+    check_rms_norm_golden,
+    check_rms_norm_invariants,
+    check_rope_golden,
+    check_rope_matches_rotation_matrix,
+    check_rope_identity_and_norm,
+    check_rope_single_axis,
+    check_rope_relative_position,
+    check_attention_golden,
+    check_attention_dense_bruteforce,
+    check_attention_sdpa,
+    check_attention_special_cases,
+    check_attention_segment_isolation,
+    check_attention_permutations,
+    check_attention_rows_variant,
+    check_chain_shift_invariance,
+    check_chain_composition,
+]

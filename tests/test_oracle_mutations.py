@@ -1,0 +1,131 @@
+"""Plant one plausible mistake at a time in a copy of the oracle and show that
+the pins in tests/oracle_pins.py catch every one of them (CPU only)."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+def _mutant(**replace):
+    ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in dir(oracle) if not k.startswith("__")})
+    for k, v in replace.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def _rope_sign_flipped(x, cos, sin, rot_dim):
+    return oracle.rope_rotate(x, cos, -sin, rot_dim)
+
+
+def _rope_interleaved(x, cos, sin, rot_dim):
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    a, b = x[..., 0:rot_dim:2], x[..., 1:rot_dim:2]
+    out[..., 0:rot_dim:2] = a * cos[:, None] - b * sin[:, None]
+    out[..., 1:rot_dim:2] = b * cos[:, None] + a * sin[:, None]
+    return out
+
+
+def _rope_cos_only_on_first_half(x, cos, sin, rot_dim):
+    y = oracle.rope_rotate(x, cos, sin, rot_dim)
+    half = rot_dim // 2
+    x = np.asarray(x, dtype=np.float64)
+    y[..., half:rot_dim] = x[..., half:rot_dim] * cos[:, None]  # dropped the cross term
+    return y
+
+
+def _rms_no_eps(x, gamma, eps):
+    return oracle.rms_norm(x, gamma, 0.0)
+
+
+def _rms_sum_not_mean(x, gamma, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def _rms_gamma_reversed(x, gamma, eps):
+    return oracle.rms_norm(x, np.asarray(gamma)[::-1], eps)
+
+
+def _inv_freq_wrong_exponent(d_axis, base):
+    j = np.arange(d_axis // 2, dtype=np.float64)
+    return np.power(float(base), -j / d_axis)
+
+
+def _angles_axes_reversed(positions, rot_dims, base):
+    return oracle.rope_angles(positions[:, ::-1], rot_dims, base)
+
+
+def _positions_h_w_swapped(segments):
+    p = oracle.segment_positions(segments)
+    return p[:, [0, 2, 1]]
+
+
+def _attn_no_scale(q, k, v, cu, scale):
+    return oracle.varlen_attention(q, k, v, cu, 1.0)
+
+
+def _attn_kv_off_by_one(q, k, v, cu, scale):
+    cu = np.asarray(cu).copy()
+    cu[1:-1] += 1  # segment boundary one token late
+    return oracle.varlen_attention(q, k, v, cu, scale)
+
+
+def _attn_key_value_swapped(q, k, v, cu, scale):
+    return oracle.varlen_attention(q, v, k, cu, scale) if k.shape == v.shape else oracle.varlen_attention(q, k, v, cu, scale * 1.01)
+
+
+def _attn_softmax_wrong_axis(q, k, v, cu, scale):
+    q = np.asarray(q, dtype=np.float64)
+    o = np.zeros(q.shape[:2] + (np.asarray(v).shape[2],))
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in range(q.shape[1]):
+            sc = scale * (q[a:b, h] @ np.asarray(k, dtype=np.float64)[a:b, h].T)
+            e = np.exp(sc - sc.max(axis=0, keepdims=True))
+            o[a:b, h] = (e / e.sum(axis=0, keepdims=True)) @ np.asarray(v, dtype=np.float64)[a:b, h]
+    return o
+
+
+def _attn_global_not_segmented(q, k, v, cu, scale):
+    return oracle.varlen_attention(q, k, v, np.array([0, cu[-1]]), scale)
+
+
+def _weights_unnormalised(q, k, cu, scale, seg, head):
+    return 1.01 * oracle.attention_weights(q, k, cu, scale, seg, head)
+
+
+MUTANTS = {
+    "rope_sign_flipped": dict(rope_rotate=_rope_sign_flipped),
+    "rope_interleaved_pairs": dict(rope_rotate=_rope_interleaved),
+    "rope_dropped_cross_term": dict(rope_rotate=_rope_cos_only_on_first_half),
+    "rms_no_eps": dict(rms_norm=_rms_no_eps),
+    "rms_sum_not_mean": dict(rms_norm=_rms_sum_not_mean),
+    "rms_gamma_reversed": dict(rms_norm=_rms_gamma_reversed),
+    "inv_freq_wrong_exponent": dict(axis_inverse_frequencies=_inv_freq_wrong_exponent),
+    "angles_axes_reversed": dict(rope_angles=_angles_axes_reversed),
+    "positions_h_w_swapped": dict(segment_positions=_positions_h_w_swapped),
+    "attn_no_scale": dict(varlen_attention=_attn_no_scale),
+    "attn_boundary_off_by_one": dict(varlen_attention=_attn_kv_off_by_one),
+    "attn_k_v_swapped": dict(varlen_attention=_attn_key_value_swapped),
+    "attn_softmax_wrong_axis": dict(varlen_attention=_attn_softmax_wrong_axis),
+    "attn_not_segmented": dict(varlen_attention=_attn_global_not_segmented),
+    "weights_unnormalised": dict(attention_weights=_weights_unnormalised),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    ns = _mutant(**MUTANTS[name])
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(ns)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,176 @@
+/*
+ * h3a -- packed varlen attention head for AMD Instinct MI355X (gfx950).
+ *
+ * The per-step attention of the MiniMax H3 video+audio DiT over one packed
+ * multi-segment sequence:
+ *   1. a step-invariant 3D (t, h, w) rotary table for the packed segments,
+ *   2. per-head RMSNorm of Q and K fused with NeoX rotary on the first R dims,
+ *   3. bidirectional attention restricted to each cu_seqlens segment.
+ *
+ * Sources (the pages this library was built from):
+ *   - vllm.cpp PR #26 "feat(minimax-h3): port the MiniMax-H3 omni-modal
+ *     video+audio DiT", opening commit: the DiT runs once per step over the
+ *     whole packed sequence, and its packed non-causal attention is exactly a
+ *     cu_seqlens varlen flash-attention call with a per-document bidirectional
+ *     contract; the fp64 position grid feeds the rotary.
+ *   - same PR, description, "The device-resident forward (W2b)": the H3 3D
+ *     rotary is plain NeoX rotate-half fed by a per-row cos/sin cache whose
+ *     angles come from three axes; RmsNorm reduces in f32.
+ *   - same PR, commit on the attention fast path: f32 accumulation and an
+ *     online-softmax recurrence.
+ *   - h3-spark model card, "What this config does": Q RMSNorm followed by the
+ *     rotary on the first 96 dims, byte-exact on default and non-default
+ *     streams; rope/cond/mask tables are step-invariant caches.
+ *
+ * Conventions for every call:
+ *   - Device pointers are owned by the caller.  The library owns only its
+ *     attention tile plans (small device buffers keyed by the cu_seqlens
+ *     content; see h3a_release_caches).
+ *   - Every argument is validated before anything is launched.  On error the
+ *     call returns a non-zero status, records a message naming the offending
+ *     argument (h3a_last_error), and writes nothing.  No C++ exception crosses
+ *     the boundary.
+ *   - Work is enqueued on `stream` (0 = the null stream); no call
+ *     synchronises the stream.  Results are bitwise deterministic and
+ *     independent of the stream used.
+ *   - Tensors are token-major: element (n, h, d) of a [S, H, D] tensor with
+ *     token stride `stride` (in elements) is at base[n * stride + h * D + d].
+ *   - Floating point: H3A_BF16 tensors hold bfloat16; arithmetic is fp32 and
+ *     each bf16 result is rounded once, to nearest even.  H3A_F32 is fp32
+ *     throughout.
+ */
+#ifndef H3A_H
+#define H3A_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum h3a_status {
+  H3A_OK = 0,
+  H3A_EINVAL = 1,       /* null pointer, negative size, bad cu_seqlens ...   */
+  H3A_ESHAPE = 2,       /* sizes that disagree with each other               */
+  H3A_EDTYPE = 3,       /* unknown dtype                                     */
+  H3A_EUNSUPPORTED = 4, /* valid request outside what the kernels implement  */
+  H3A_EHIP = 5          /* the HIP runtime reported an error                 */
+} h3a_status;
+
+typedef enum h3a_dtype { H3A_F32 = 0, H3A_BF16 = 1 } h3a_dtype;
+
+/*
+ * Step-invariant rotary table for a packed sequence (built once per request).
+ *
+ * segments       host int32 [nseg][4]: (T, H, W, L) per segment, packed in this
+ *                order.  T, H, W >= 1 and 0 <= L <= T*H*W.  Token n < L of a
+ *                segment sits at t = n / (H*W), h = (n / W) % H, w = n % W
+ *                (row-major, w fastest); positions restart at 0 per segment.
+ * axis_dims      host int32 [3]: rotated dims owned by the t, h, w axes; each
+ *                even and >= 0; R = sum.  Axis a contributes axis_dims[a]/2
+ *                frequencies base^(-2j/axis_dims[a]), j = 0, 1, ...
+ * base           rotary base (> 0), e.g. 10000.
+ * cos_sin        device fp32 [2][S][R/2]: cos block, then sin block.  Entry
+ *                (n, i) is cos/sin of the i-th angle of token n, where the
+ *                angle vector is concat(t*f_t, h*f_h, w*f_w), evaluated in
+ *                fp64 and rounded once to fp32.  Must be 16-byte aligned.
+ * S              total tokens; must equal the sum of L (the size of cos_sin).
+ * cu_seqlens_out host int32 [nseg+1] or NULL: prefix sums of L, from 0.
+ *
+ * Errors: EINVAL (null segments/axis_dims, nseg < 1, T/H/W < 1, L out of
+ * range, odd or negative axis dims, base <= 0, S mismatch, S > INT32_MAX,
+ * null cos_sin with R > 0), EHIP.
+ */
+h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int32_t* axis_dims,
+                                double base, float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
+                                hipStream_t stream);
+
+/*
+ * Fused per-head RMSNorm + NeoX rotary of Q and K.
+ *
+ * For every token n, head h and x in {q, k} (each with its own gain g):
+ *   y_d  = x_d / sqrt(mean_d(x_d^2) + eps) * g_d               (d < D)
+ *   y'_i       = y_i cos(n,i) - y_{i+R/2} sin(n,i)              (i < R/2)
+ *   y'_{i+R/2} = y_{i+R/2} cos(n,i) + y_i sin(n,i)
+ *   y'_d = y_d                                                  (d >= R)
+ * V is not touched.
+ *
+ * q, k           device [S, H, D] of `dtype`, token strides stride_q, stride_k.
+ * q_out, k_out   device [S, H, D] of `dtype`, token strides stride_qo,
+ *                stride_ko.  An output may be its input (same pointer and
+ *                stride: in place); any other overlap is rejected.
+ * gamma_q/k      device fp32 [D].
+ * cos_sin        device fp32 [2][S][R/2] from h3a_build_rope_table; may be
+ *                NULL when rot_dim == 0.
+ * Supported: D in {64, 128}; rot_dim even, 0 <= rot_dim <= D, and (rot_dim/2)
+ * a multiple of 8 (bf16) or 4 (fp32); pointers 16-byte aligned and strides
+ * multiples of 16 bytes; strides >= H*D.
+ *
+ * Errors: EINVAL, ESHAPE (stride < H*D), EDTYPE, EUNSUPPORTED, EHIP.
+ */
+h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
+                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                               int64_t stride_q, int64_t stride_k, int64_t stride_qo,
+                               int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                               float eps, const float* cos_sin, int32_t rot_dim,
+                               hipStream_t stream);
+
+/*
+ * Bidirectional attention restricted to each packed segment.
+ *
+ * For segment s = [cu[s], cu[s+1]) and head h, every query row i in s gets
+ *   o_i = sum_j softmax_j(scale * <q_i, k_j>) v_j,   j in s.
+ * There are no cross-segment terms and no causal mask.  Empty segments are
+ * legal and produce nothing.
+ *
+ * q, k, v        device [S, H, D] of `dtype` with token strides stride_q/k/v.
+ * o              device [S, H, D] of `dtype`, token stride stride_o; must not
+ *                overlap q, k or v.  Rows of every segment are written; there
+ *                are no other rows (cu[nseg] == S).
+ * cu_seqlens     HOST int32 [nseg+1]: cu[0] = 0, non-decreasing, cu[nseg] = S.
+ *                It is planned on the host (tile work list, longest segments
+ *                first, balanced over the chip's XCDs) and the plan is cached
+ *                by content, so no device-to-host synchronisation happens.
+ * scale          softmax scale (> 0 and finite), typically 1/sqrt(D).
+ * Numerics: bf16 -- bf16 MFMA products with fp32 accumulation, fp32 online
+ * softmax, probabilities rounded to bf16 for the PV product, output rounded
+ * once; fp32 -- fp32 throughout.
+ * Supported: D in {64, 128}; pointers 16-byte aligned; strides multiples of
+ * 16 bytes and >= H*D; S <= INT32_MAX.
+ *
+ * Errors: EINVAL, ESHAPE, EDTYPE, EUNSUPPORTED, EHIP.
+ */
+h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                               int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                               int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
+                               float scale, hipStream_t stream);
+
+/*
+ * The attention tile plan, on the host only (no GPU needed); for tests and
+ * tooling.  Writes up to `cap` items of 4 int32 each -- (segment start,
+ * segment length, first query row relative to the segment start, head); an
+ * item with length 0 is padding -- in launch order, and sets *n_items to the
+ * plan's length (the attention grid size).  block_m is the query rows per
+ * item (128 for bf16, 64 for fp32); n_xcd the number of XCDs to balance over
+ * (>= 1).  Errors: EINVAL, ESHAPE (cap too small: *n_items still set).
+ */
+h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
+                          int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* h3a_last_error(void);
+
+/* Frees every cached attention plan.  The caller must make sure no attention
+ * launched earlier is still running (synchronise its streams first). */
+void h3a_release_caches(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t h3a_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3A_H */

@@ -1,0 +1,212 @@
+"""Python binding of libh3a (the packed varlen attention head for MI355X).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch tensors on the GPU in token-major [S, H, D] layout whose
+last two dims are contiguous (token stride = ``tensor.stride(0)``); torch
+supplies device memory and the current stream.  The names mirror the C ABI in
+include/h3a.h.
+
+If libh3a.so has not been built this module still imports, but every call
+raises ``H3ALibraryMissing``: there is no CPU fallback.  Build it with
+``python -m packed_varlen_attention_head_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libh3a.so")
+
+H3A_OK, H3A_EINVAL, H3A_ESHAPE, H3A_EDTYPE, H3A_EUNSUPPORTED, H3A_EHIP = range(6)
+H3A_F32, H3A_BF16 = 0, 1
+STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "EUNSUPPORTED", 5: "EHIP"}
+
+# Query rows per attention work item (must match the kernels).
+BLOCK_M = {H3A_BF16: 128, H3A_F32: 64}
+
+EXPORTS = (
+    "h3a_build_rope_table",
+    "h3a_qk_rmsnorm_rope",
+    "h3a_varlen_attn_fwd",
+    "h3a_plan_tiles",
+    "h3a_last_error",
+    "h3a_release_caches",
+    "h3a_version",
+)
+
+
+class H3AError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"h3a {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class H3ALibraryMissing(ImportError):
+    pass
+
+
+_lib = None
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+_i32, _i64, _f32, _f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types declared (loaded once)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise H3ALibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m packed_varlen_attention_head_amd.build` "
+            "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.h3a_build_rope_table.argtypes = [_c_i32p, _i32, _c_i32p, _f64, _vp, _i64, _c_i32p, _vp]
+    L.h3a_qk_rmsnorm_rope.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
+                                      _vp, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
+                                      _c_i32p, _i32, _f32, _vp]
+    L.h3a_plan_tiles.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
+    for name in ("h3a_build_rope_table", "h3a_qk_rmsnorm_rope", "h3a_varlen_attn_fwd", "h3a_plan_tiles"):
+        getattr(L, name).restype = ctypes.c_int
+    L.h3a_last_error.restype = ctypes.c_char_p
+    L.h3a_last_error.argtypes = []
+    L.h3a_release_caches.restype = None
+    L.h3a_release_caches.argtypes = []
+    L.h3a_version.restype = ctypes.c_int32
+    L.h3a_version.argtypes = []
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().h3a_last_error().decode()
+
+
+def _check(status: int):
+    if status != H3A_OK:
+        raise H3AError(status, last_error())
+
+
+def version() -> int:
+    return int(lib().h3a_version())
+
+
+def release_caches() -> None:
+    lib().h3a_release_caches()
+
+
+def _i32_array(values) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(_c_i32p)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return H3A_BF16
+    if t.dtype == torch.float32:
+        return H3A_F32
+    raise H3AError(H3A_EDTYPE, f"tensor dtype {t.dtype} (supported: bfloat16, float32)")
+
+
+def _token_major(name: str, t):
+    """(S, H, D, token stride) of a [S, H, D] tensor with contiguous last two dims."""
+    if t.dim() != 3:
+        raise H3AError(H3A_ESHAPE, f"{name} must be [S, H, D], got shape {tuple(t.shape)}")
+    S, H, D = t.shape
+    if t.stride(2) != 1 or (H > 1 and t.stride(1) != D):
+        raise H3AError(H3A_ESHAPE, f"{name}: heads and dims must be contiguous, strides {t.stride()}")
+    if not t.is_cuda:
+        raise H3AError(H3A_EINVAL, f"{name} must be a GPU tensor")
+    return S, H, D, t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+# the three calls of the hot path
+# ---------------------------------------------------------------------------
+
+def build_rope_table(segments, axis_dims, base: float, cos_sin, stream=None) -> np.ndarray:
+    """Fill ``cos_sin`` (fp32 GPU tensor [2, S, R/2]) and return cu_seqlens (int32 [nseg+1]).
+
+    ``segments``: sequence of (T, H, W, L); ``axis_dims``: rotated dims of the t, h, w axes.
+    """
+    segs = _i32_array(segments).reshape(-1, 4)
+    dims = _i32_array(axis_dims)
+    S = int(segs[:, 3].sum()) if len(segs) else 0
+    cu = np.zeros(len(segs) + 1, dtype=np.int32)
+    ptr = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_build_rope_table(_ptr_i32(segs), len(segs), _ptr_i32(dims), float(base), ptr, S,
+                                      _ptr_i32(cu), _stream_handle(stream)))
+    return cu
+
+
+def qk_rmsnorm_rope(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q_out=None, k_out=None,
+                    stream=None):
+    """RMSNorm + NeoX rotary of q and k; in place unless q_out / k_out are given."""
+    q_out = q if q_out is None else q_out
+    k_out = k if k_out is None else k_out
+    S, H, D, sq = _token_major("q", q)
+    _, _, _, sk = _token_major("k", k)
+    _, _, _, sqo = _token_major("q_out", q_out)
+    _, _, _, sko = _token_major("k_out", k_out)
+    for name, t in (("k", k), ("q_out", q_out), ("k_out", k_out)):
+        if tuple(t.shape) != (S, H, D) or t.dtype != q.dtype:
+            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from q")
+    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_qk_rmsnorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+                                     _dtype_code(q), S, H, D, sq, sk, sqo, sko, gamma_q.data_ptr(),
+                                     gamma_k.data_ptr(), float(eps), cs, int(rot_dim),
+                                     _stream_handle(stream)))
+    return q_out, k_out
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens, scale: float, out=None, stream=None):
+    """Per-segment bidirectional attention; returns ``out`` ([S, H, D], same dtype as q)."""
+    import torch
+
+    S, H, D, sq = _token_major("q", q)
+    _, _, _, sk = _token_major("k", k)
+    _, _, _, sv = _token_major("v", v)
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (S, H, D) or t.dtype != q.dtype:
+            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from q")
+    if out is None:
+        out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
+    _, _, _, so = _token_major("out", out)
+    cu = _i32_array(cu_seqlens)
+    _check(lib().h3a_varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
+                                     S, H, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
+                                     _stream_handle(stream)))
+    return out
+
+
+def plan_tiles(cu_seqlens, heads: int, block_m: int, n_xcd: int) -> np.ndarray:
+    """The attention tile plan as int32 [n, 4] rows (seg start, seg len, q start, head); host only."""
+    cu = _i32_array(cu_seqlens)
+    n = ctypes.c_int64(0)
+    st = lib().h3a_plan_tiles(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, None, 0, ctypes.byref(n))
+    if st not in (H3A_OK, H3A_ESHAPE):
+        _check(st)
+    out = np.zeros((max(n.value, 1), 4), dtype=np.int32)
+    _check(lib().h3a_plan_tiles(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, _ptr_i32(out), n.value,
+                                ctypes.byref(n)))
+    return out[:n.value]

@@ -1,0 +1,338 @@
+// The h3a C ABI: argument validation, error reporting, the attention plan
+// cache, and dispatch to the kernel launchers.  Every check runs before any
+// HIP call, so invalid requests fail without touching the device.
+//
+// Error style follows the pages' fail-loudly-by-name rule: a missing tensor
+// throws by name rather than reading as zeros and shape disagreements throw
+// rather than mis-slice (vllm.cpp PR #26, commits on the streamed bf16 stager
+// and the condition-noise row accounting); here that becomes a status code
+// plus a message naming the argument.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "h3a.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+h3a_status fail(h3a_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+h3a_status fail_hip(const char* what, hipError_t e) {
+  return fail(H3A_EHIP, "%s: HIP error %d (%s)", what, int(e), hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(h3a_dtype dt) { return dt == H3A_BF16 ? 2 : 4; }
+
+// Byte range [lo, hi) touched by a [S, H, D] tensor with token stride `stride`.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range tensor_range(const void* p, int64_t S, int64_t H, int64_t D, int64_t stride, size_t esz) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (S <= 0) return {lo, lo};
+  return {lo, lo + uintptr_t(((S - 1) * stride + H * D) * int64_t(esz))};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Validates a token-major [S, H, D] operand.
+h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, int32_t D,
+                         int64_t stride, size_t esz) {
+  if (S > 0 && p == nullptr) return fail(H3A_EINVAL, "%s is NULL", name);
+  if (stride < int64_t(H) * D)
+    return fail(H3A_ESHAPE, "%s: token stride %lld is smaller than H*D = %lld", name,
+                (long long)stride, (long long)(int64_t(H) * D));
+  if (!aligned(p, 16)) return fail(H3A_EUNSUPPORTED, "%s is not 16-byte aligned", name);
+  if ((stride * int64_t(esz)) % 16 != 0)
+    return fail(H3A_EUNSUPPORTED, "%s: token stride %lld elements is not a multiple of 16 bytes", name,
+                (long long)stride);
+  return H3A_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Attention plan cache: device copies of the tile plan keyed by the
+// cu_seqlens content, heads, block size and device.
+// ---------------------------------------------------------------------------
+struct Plan {
+  h3a::WorkItem* dev = nullptr;
+  int64_t n = 0;
+};
+
+constexpr size_t kMaxPlans = 256;
+
+struct PlanCache {
+  std::mutex mu;
+  std::unordered_map<std::string, Plan> map;
+  std::list<std::string> order;  // insertion order, oldest first
+};
+
+PlanCache& plan_cache() {
+  static PlanCache* c = new PlanCache();  // intentionally leaked: usable during exit
+  return *c;
+}
+
+int n_xcd_of(int device) {
+  static std::mutex mu;
+  static std::unordered_map<int, int> known;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = known.find(device);
+  if (it != known.end()) return it->second;
+  int cus = 0;
+  int n = 1;
+  // MI355X: 8 XCDs of 32 CUs; the dispatcher deals workgroups round-robin.
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+      cus >= 64 && cus % 32 == 0)
+    n = cus / 32;
+  known[device] = n;
+  return n;
+}
+
+h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, Plan* out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip("hipGetDevice", e);
+  const int n_xcd = n_xcd_of(device);
+  std::string key;
+  key.reserve(16 + size_t(nseg + 1) * 4);
+  const int32_t hdr[4] = {device, H, block_m, n_xcd};
+  key.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
+  key.append(reinterpret_cast<const char*>(cu), size_t(nseg + 1) * sizeof(int32_t));
+
+  PlanCache& pc = plan_cache();
+  std::lock_guard<std::mutex> lock(pc.mu);
+  auto it = pc.map.find(key);
+  if (it != pc.map.end()) {
+    *out = it->second;
+    return H3A_OK;
+  }
+  std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd);
+  Plan p;
+  p.n = int64_t(items.size());
+  if (p.n > 0) {
+    if (p.n > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "attention plan has %lld items", (long long)p.n);
+    if (pc.map.size() >= kMaxPlans) {
+      // Evicting frees device memory an earlier launch may still read.
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return fail_hip("hipDeviceSynchronize (plan eviction)", e);
+      const std::string& old = pc.order.front();
+      auto victim = pc.map.find(old);
+      if (victim != pc.map.end()) {
+        (void)hipFree(victim->second.dev);
+        pc.map.erase(victim);
+      }
+      pc.order.pop_front();
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&p.dev), items.size() * sizeof(h3a::WorkItem));
+    if (e != hipSuccess) return fail_hip("hipMalloc (attention plan)", e);
+    // Synchronous upload: the plan is complete before any stream can use it.
+    e = hipMemcpy(p.dev, items.data(), items.size() * sizeof(h3a::WorkItem), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(p.dev);
+      return fail_hip("hipMemcpy (attention plan)", e);
+    }
+  }
+  pc.map.emplace(key, p);
+  pc.order.push_back(key);
+  *out = p;
+  return H3A_OK;
+}
+
+h3a_status check_cu_seqlens(const int32_t* cu, int32_t nseg, int64_t S) {
+  if (cu == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+  if (cu[0] != 0) return fail(H3A_EINVAL, "cu_seqlens[0] = %d must be 0", cu[0]);
+  for (int32_t s = 0; s < nseg; ++s)
+    if (cu[s + 1] < cu[s])
+      return fail(H3A_EINVAL, "cu_seqlens decreases at index %d (%d -> %d)", s + 1, cu[s], cu[s + 1]);
+  if (int64_t(cu[nseg]) != S)
+    return fail(H3A_ESHAPE, "cu_seqlens[nseg] = %d but S = %lld", cu[nseg], (long long)S);
+  return H3A_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h3a_last_error(void) { return g_last_error.c_str(); }
+
+int32_t h3a_version(void) { return 100; }
+
+void h3a_release_caches(void) {
+  PlanCache& pc = plan_cache();
+  std::lock_guard<std::mutex> lock(pc.mu);
+  for (auto& kv : pc.map)
+    if (kv.second.dev) (void)hipFree(kv.second.dev);
+  pc.map.clear();
+  pc.order.clear();
+}
+
+h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int32_t* axis_dims,
+                                double base, float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
+                                hipStream_t stream) {
+  if (segments == nullptr) return fail(H3A_EINVAL, "segments is NULL");
+  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+  if (axis_dims == nullptr) return fail(H3A_EINVAL, "axis_dims is NULL");
+  int64_t R = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (axis_dims[a] < 0 || axis_dims[a] % 2 != 0)
+      return fail(H3A_EINVAL, "axis_dims[%d] = %d must be even and >= 0", a, axis_dims[a]);
+    R += axis_dims[a];
+  }
+  if (R > 128) return fail(H3A_EUNSUPPORTED, "rotated dims %lld > 128", (long long)R);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(H3A_EINVAL, "base = %g must be finite and > 0", base);
+  int64_t total = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    const int32_t* g = segments + 4 * int64_t(s);
+    if (g[0] < 1 || g[1] < 1 || g[2] < 1)
+      return fail(H3A_EINVAL, "segment %d grid (%d, %d, %d) must be >= 1 on every axis", s, g[0], g[1], g[2]);
+    const int64_t cap = int64_t(g[0]) * g[1] * g[2];
+    if (g[3] < 0 || int64_t(g[3]) > cap)
+      return fail(H3A_EINVAL, "segment %d length %d outside [0, T*H*W = %lld]", s, g[3], (long long)cap);
+    total += g[3];
+  }
+  if (total != S) return fail(H3A_ESHAPE, "S = %lld but the segment lengths sum to %lld", (long long)S, (long long)total);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (R > 0 && S > 0) {
+    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL");
+    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  }
+
+  std::vector<int32_t> starts(size_t(nseg) + 1, 0);
+  for (int32_t s = 0; s < nseg; ++s) starts[s + 1] = starts[s] + segments[4 * int64_t(s) + 3];
+  const int32_t half = int32_t(R / 2);
+  std::vector<double> inv_freq;
+  std::vector<int32_t> axis_of;
+  for (int a = 0; a < 3; ++a)
+    for (int32_t j = 0; j < axis_dims[a] / 2; ++j) {
+      inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(axis_dims[a])));
+      axis_of.push_back(a);
+    }
+  if (half > 0 && S > 0) {
+    hipError_t e = h3a::launch_rope_table(segments, starts.data(), nseg, inv_freq.data(), axis_of.data(),
+                                          half, cos_sin, S, stream);
+    if (e != hipSuccess) return fail_hip("rope table launch", e);
+  }
+  if (cu_seqlens_out != nullptr) std::memcpy(cu_seqlens_out, starts.data(), starts.size() * sizeof(int32_t));
+  return H3A_OK;
+}
+
+h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
+                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                               int64_t stride_q, int64_t stride_k, int64_t stride_qo,
+                               int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                               float eps, const float* cos_sin, int32_t rot_dim,
+                               hipStream_t stream) {
+  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  const int V = dtype == H3A_BF16 ? 8 : 4;
+  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+  if ((rot_dim / 2) % V != 0)
+    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+  const size_t esz = elem_size(dtype);
+  h3a_status st;
+  if ((st = check_operand("q", q, S, H, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, H, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("q_out", q_out, S, H, D, stride_qo, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k_out", k_out, S, H, D, stride_ko, esz)) != H3A_OK) return st;
+  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+  if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
+  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+  if (rot_dim > 0 && S > 0) {
+    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  }
+  if (S == 0) return H3A_OK;
+  const Range rq = tensor_range(q, S, H, D, stride_q, esz), rk = tensor_range(k, S, H, D, stride_k, esz);
+  const Range rqo = tensor_range(q_out, S, H, D, stride_qo, esz), rko = tensor_range(k_out, S, H, D, stride_ko, esz);
+  const bool q_inplace = q_out == q && stride_qo == stride_q;
+  const bool k_inplace = k_out == k && stride_ko == stride_k;
+  if (!q_inplace && overlap(rqo, rq)) return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
+  if (!k_inplace && overlap(rko, rk)) return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
+  if (overlap(rqo, rk)) return fail(H3A_EINVAL, "q_out overlaps k");
+  if (overlap(rko, rq)) return fail(H3A_EINVAL, "k_out overlaps q");
+  if (overlap(rqo, rko)) return fail(H3A_EINVAL, "q_out overlaps k_out");
+
+  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, H, D, stride_q, stride_k,
+                                             stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+  if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                               int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                               int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
+                               float scale, hipStream_t stream) {
+  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  const size_t esz = elem_size(dtype);
+  if ((st = check_operand("q", q, S, H, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, H, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, H, D, stride_v, esz)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, H, D, stride_o, esz)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  const Range ro = tensor_range(o, S, H, D, stride_o, esz);
+  if (overlap(ro, tensor_range(q, S, H, D, stride_q, esz))) return fail(H3A_EINVAL, "o overlaps q");
+  if (overlap(ro, tensor_range(k, S, H, D, stride_k, esz))) return fail(H3A_EINVAL, "o overlaps k");
+  if (overlap(ro, tensor_range(v, S, H, D, stride_v, esz))) return fail(H3A_EINVAL, "o overlaps v");
+
+  const bool bf16 = dtype == H3A_BF16;
+  Plan plan;
+  if ((st = get_plan(cu_seqlens, nseg, H, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, &plan)) != H3A_OK)
+    return st;
+  hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                  plan.n, scale, stream)
+                      : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                 plan.n, scale, stream);
+  if (e != hipSuccess) return fail_hip("varlen attention launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
+                          int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items) {
+  if (n_items == nullptr) return fail(H3A_EINVAL, "n_items is NULL");
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (block_m < 1) return fail(H3A_EINVAL, "block_m = %d must be >= 1", block_m);
+  if (n_xcd < 1) return fail(H3A_EINVAL, "n_xcd = %d must be >= 1", n_xcd);
+  h3a_status st;
+  if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+  std::vector<h3a::WorkItem> plan = h3a::plan_tiles(cu_seqlens, nseg, H, block_m, n_xcd);
+  *n_items = int64_t(plan.size());
+  if (int64_t(plan.size()) > cap) return fail(H3A_ESHAPE, "cap %lld < plan length %lld", (long long)cap, (long long)plan.size());
+  if (!plan.empty() && items == nullptr) return fail(H3A_EINVAL, "items is NULL");
+  if (!plan.empty()) std::memcpy(items, plan.data(), plan.size() * sizeof(h3a::WorkItem));
+  return H3A_OK;
+}
+
+}  // extern "C"

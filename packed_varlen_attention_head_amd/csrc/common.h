@@ -1,0 +1,56 @@
+// Internal declarations shared by the h3a host code and its kernel launchers.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+namespace h3a {
+
+// One attention work item: query rows [q_start, q_start + block_m) of one
+// segment and one head.  seg_len == 0 marks a padding item (the workgroup
+// exits at once).
+struct WorkItem {
+  int32_t seg_start;
+  int32_t seg_len;
+  int32_t q_start;  // relative to seg_start
+  int32_t head;
+};
+static_assert(sizeof(WorkItem) == 16, "WorkItem is uploaded as 4 x int32");
+
+// ---- host tile planner (planner.cpp) --------------------------------------
+// Items for every (non-empty segment, head, query tile), longest segments
+// first, balanced over n_xcd XCDs and interleaved so that workgroup b lands on
+// XCD b % n_xcd with that XCD's items in its own longest-first order.
+std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
+                                 int32_t n_xcd);
+
+// ---- kernel launchers (one per .hip file) ---------------------------------
+
+hipError_t launch_rope_table(const int32_t* segments, const int32_t* starts, int32_t nseg,
+                             const double* inv_freq, const int32_t* axis_of, int32_t half,
+                             float* cos_sin, int64_t S, hipStream_t stream);
+
+hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void* q_out, void* k_out,
+                                  int64_t S, int32_t H, int32_t D, int64_t sq, int64_t sk,
+                                  int64_t sqo, int64_t sko, const float* gq, const float* gk,
+                                  float eps, const float* cos_sin, int32_t rot_dim,
+                                  hipStream_t stream);
+
+// Query rows per work item of each attention kernel.
+constexpr int kAttnBlockM_BF16 = 128;
+constexpr int kAttnBlockM_F32 = 64;
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int32_t D,
+                                int64_t sq, int64_t sk, int64_t sv, int64_t so,
+                                const WorkItem* items, int64_t n_items, float scale,
+                                hipStream_t stream);
+
+hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,
+                               int64_t sq, int64_t sk, int64_t sv, int64_t so,
+                               const WorkItem* items, int64_t n_items, float scale,
+                               hipStream_t stream);
+
+}  // namespace h3a

@@ -1,0 +1,193 @@
+// Fused per-head RMSNorm + NeoX rotary of Q and K (one HBM pass).
+//
+// The GB10 serving build fuses "Q RMSNorm + rot96 RoPE" into one kernel,
+// byte-exact on default and non-default streams (h3-spark model card, "What
+// this config does"); RmsNorm reduces in f32 (vllm.cpp PR #26, description,
+// "The device-resident forward (W2b)"), and the rotary is NeoX rotate-half
+// from a per-row cos/sin cache (same section).
+//
+// Mapping (HBM-bound; designed for 16-byte coalesced loads):
+//   * one wavefront per token, four tokens per 256-thread workgroup;
+//   * a head vector of D elements is split over LPV = D / V lanes, each lane
+//     owning one 16-byte vector of V elements (V = 8 bf16 or 4 fp32), so a
+//     wave touches G = 64 / LPV head vectors per instruction;
+//   * a lane's cos/sin (and gains) depend only on its dims, so they are loaded
+//     once per token and reused for every head of q and k;
+//   * the rotary partner of element i (i +- R/2) lives in the lane R/(2V)
+//     positions away, same slot, and is fetched with a lane shuffle;
+//   * all loads of a token are issued before any store, so in-place calls are
+//     safe (each token is owned by a single wave).
+#include <cstdint>
+
+#include "common.h"
+
+namespace h3a {
+namespace {
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int V = 4;
+  __device__ static void unpack(const uint4& r, float* x) {
+    x[0] = __uint_as_float(r.x);
+    x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z);
+    x[3] = __uint_as_float(r.w);
+  }
+  __device__ static uint4 pack(const float* y) {
+    return make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]),
+                      __float_as_uint(y[3]));
+  }
+};
+
+struct Bf16Tag;
+template <>
+struct Elem<Bf16Tag> {
+  static constexpr int V = 8;
+  __device__ static void unpack(const uint4& r, float* x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  // fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+  __device__ static uint32_t pack2(float lo, float hi) {
+    const __bf16 a = __bf16(lo);
+    const __bf16 b = __bf16(hi);
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  }
+  __device__ static uint4 pack(const float* y) {
+    return make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
+  }
+};
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBatch = 8;  // head vectors a lane keeps in flight
+
+template <typename T, int D>
+__device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, int64_t stride_b,
+                                              int64_t stride_ob, int32_t token, int32_t H,
+                                              const float* g, const float* c, const float* s, int role,
+                                              int partner, float eps, int lane) {
+  constexpr int V = Elem<T>::V;
+  constexpr int LPV = D / V;
+  constexpr int G = 64 / LPV;
+  constexpr int esz = 16 / V;
+  const int sub = lane % LPV;
+  const int grp = lane / LPV;
+  const char* row = src + int64_t(token) * stride_b + sub * 16;
+  char* orow = dst + int64_t(token) * stride_ob + sub * 16;
+  for (int h0 = 0; h0 < H; h0 += G * kBatch) {
+    uint4 raw[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int h = h0 + b * G + grp;
+      raw[b] = h < H ? *reinterpret_cast<const uint4*>(row + int64_t(h) * D * esz) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (h0 + b * G >= H) break;  // wave-uniform
+      float x[V];
+      Elem<T>::unpack(raw[b], x);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+      for (int off = LPV / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      const float r = 1.0f / sqrtf(ss * (1.0f / float(D)) + eps);
+      float y[V], out[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = x[e] * r * g[e];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float py = __shfl(y[e], partner, 64);
+        out[e] = role == 0 ? fmaf(y[e], c[e], -py * s[e]) : (role == 1 ? fmaf(y[e], c[e], py * s[e]) : y[e]);
+      }
+      const int h = h0 + b * G + grp;
+      if (h < H) *reinterpret_cast<uint4*>(orow + int64_t(h) * D * esz) = Elem<T>::pack(out);
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq_b, int64_t sk_b,
+                    int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H,
+                    const float* __restrict__ gq, const float* __restrict__ gk, float eps,
+                    const float* __restrict__ cos_sin, int32_t rot_dim) {
+  constexpr int V = Elem<T>::V;
+  constexpr int LPV = D / V;
+  const int lane = threadIdx.x & 63;
+  const int32_t token = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (token >= S) return;
+  const int sub = lane % LPV;
+  const int d0 = sub * V;
+  const int half = rot_dim >> 1;
+  const int po = half / V;  // partner distance in lanes
+  const int role = d0 < half ? 0 : (d0 < rot_dim ? 1 : 2);
+  const int partner = role == 0 ? lane + po : (role == 1 ? lane - po : lane);
+  float c[V], s[V], g_q[V], g_k[V];
+  if (role != 2) {
+    const int j0 = role == 0 ? d0 : d0 - half;
+    const float* cp = cos_sin + int64_t(token) * half + j0;
+    const float* sp = cp + int64_t(S) * half;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      c[e] = cp[e];
+      s[e] = sp[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      c[e] = 1.f;
+      s[e] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    g_q[e] = gq[d0 + e];
+    g_k[e] = gk[d0 + e];
+  }
+  norm_rope_one<T, D>(q, qo, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D>(k, ko, sk_b, sko_b, token, H, g_k, c, s, role, partner, eps, lane);
+}
+
+template <typename T, int D>
+hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int64_t sq,
+                  int64_t sk, int64_t sqo, int64_t sko, const float* gq, const float* gk, float eps,
+                  const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  constexpr int esz = 16 / Elem<T>::V;
+  const unsigned blocks = unsigned((S + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
+                     static_cast<const char*>(q), static_cast<const char*>(k), static_cast<char*>(qo),
+                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * esz, sko * esz, int32_t(S), H, gq,
+                     gk, eps, cos_sin, rot_dim);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void* q_out, void* k_out,
+                                  int64_t S, int32_t H, int32_t D, int64_t sq, int64_t sk,
+                                  int64_t sqo, int64_t sko, const float* gq, const float* gk,
+                                  float eps, const float* cos_sin, int32_t rot_dim,
+                                  hipStream_t stream) {
+  if (bf16) {
+    if (D == 128)
+      return launch<Bf16Tag, 128>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+    if (D == 64)
+      return launch<Bf16Tag, 64>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+  } else {
+    if (D == 128)
+      return launch<float, 128>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+    if (D == 64)
+      return launch<float, 64>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace h3a

@@ -16,6 +16,8 @@ RNE from fp32 to bf16; bf16 tensors are held as uint16 bit patterns.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -44,16 +46,50 @@ def uniform(seed: int, tag: int, n: int) -> np.ndarray:
     return (z >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
 
 
-def normal(seed: int, tag: int, n: int) -> np.ndarray:
-    """n standard normals (fp64) by Box-Muller over consecutive uniform pairs."""
-    m = (n + 1) // 2
-    u = uniform(seed, tag, 2 * m)
+def _normal_pairs(seed: int, tag: int, p0: int, p1: int) -> np.ndarray:
+    """Normals 2*p0 .. 2*p1-1 of a stream: Box-Muller on uniform pairs p0 .. p1-1."""
+    z = splitmix64(seed, tag, 2 * (p1 - p0), offset=2 * p0)
+    u = (z >> np.uint64(11)).astype(np.float64)
+    u *= 1.0 / 9007199254740992.0
     u1, u2 = u[0::2], u[1::2]
     r = np.sqrt(-2.0 * np.log1p(-u1))  # log(1 - u1): u1 < 1 so the log is finite
     t = (2.0 * np.pi) * u2
+    out = np.empty(2 * (p1 - p0), dtype=np.float64)
+    np.multiply(r, np.cos(t), out=out[0::2])
+    np.multiply(r, np.sin(t), out=out[1::2])
+    return out
+
+
+_CHUNK_PAIRS = 1 << 20
+
+
+def _chunks(m: int):
+    return [(p, min(m, p + _CHUNK_PAIRS)) for p in range(0, m, _CHUNK_PAIRS)]
+
+
+def _pool_map(fn, items):
+    """Map over chunks with threads (numpy releases the GIL); order-preserving
+    and independent of the thread count, since each chunk is a pure function of
+    its stream offsets."""
+    if len(items) <= 1:
+        return [fn(i) for i in items]
+    from concurrent.futures import ThreadPoolExecutor
+
+    workers = min(len(items), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def normal(seed: int, tag: int, n: int) -> np.ndarray:
+    """n standard normals (fp64) by Box-Muller over consecutive uniform pairs."""
+    m = (n + 1) // 2
     out = np.empty(2 * m, dtype=np.float64)
-    out[0::2] = r * np.cos(t)
-    out[1::2] = r * np.sin(t)
+
+    def work(c):
+        p0, p1 = c
+        out[2 * p0:2 * p1] = _normal_pairs(seed, tag, p0, p1)
+
+    _pool_map(work, _chunks(m))
     return out[:n]
 
 
@@ -75,14 +111,23 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def normal_tensor(seed: int, tag: int, shape, dtype: str, mean: float = 0.0, std: float = 1.0):
-    """A tensor of N(mean, std^2) values in ``dtype`` ("f32" -> float32, "bf16" -> uint16 bits)."""
+    """A tensor of N(mean, std^2) values in ``dtype`` ("f32" -> float32, "bf16" -> uint16 bits).
+
+    Each value is mean + std * z in fp64, rounded RNE to fp32 (then RNE to bf16).
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
     n = int(np.prod(shape))
-    x = (mean + std * normal(seed, tag, n)).astype(np.float32).reshape(shape)
-    if dtype == "f32":
-        return x
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x)
-    raise ValueError(f"unknown dtype {dtype!r}")
+    m = (n + 1) // 2
+    out = np.empty(2 * m, dtype=np.float32 if dtype == "f32" else np.uint16)
+
+    def work(c):
+        p0, p1 = c
+        x = (mean + std * _normal_pairs(seed, tag, p0, p1)).astype(np.float32)
+        out[2 * p0:2 * p1] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    _pool_map(work, _chunks(m))
+    return out[:n].reshape(shape)
 
 
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports what include/h3a.h declares,
+and rejects invalid requests with a status and a message naming the argument
+before any HIP call (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import packed_varlen_attention_head_amd as h3a
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(h3a.LIB_PATH), reason="libh3a.so not built")
+
+P = 0x7F0000000000  # a 16-byte aligned address that is never dereferenced
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "h3a.h")).read()
+    return sorted(set(re.findall(r"\b(h3a_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = h3a.lib()
+    names = declared_symbols()
+    assert set(names) == set(h3a.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+    assert h3a.version() >= 100
+
+
+def i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def rope(segments, dims=(32, 32, 32), base=10000.0, table=P, S=None, cu_out=None):
+    segs, sp = i32(np.asarray(segments).reshape(-1)) if segments is not None else (None, None)
+    d, dp = i32(dims) if dims is not None else (None, None)
+    n = len(segments) if segments is not None else 0
+    if S is None:
+        S = int(sum(s[3] for s in segments)) if segments is not None else 0
+    cp = cu_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if cu_out is not None else None
+    return h3a.lib().h3a_build_rope_table(sp, n, dp, base, table, S, cp, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(segments=None), h3a.H3A_EINVAL, "segments"),
+    (dict(segments=[]), h3a.H3A_EINVAL, "nseg"),
+    (dict(segments=[(1, 2, 2, 4)], dims=None), h3a.H3A_EINVAL, "axis_dims"),
+    (dict(segments=[(1, 2, 2, 4)], dims=(32, 31, 32)), h3a.H3A_EINVAL, "axis_dims[1]"),
+    (dict(segments=[(1, 2, 2, 4)], dims=(64, 64, 64)), h3a.H3A_EUNSUPPORTED, "rotated dims"),
+    (dict(segments=[(1, 2, 2, 5)]), h3a.H3A_EINVAL, "length"),
+    (dict(segments=[(0, 2, 2, 0)]), h3a.H3A_EINVAL, "grid"),
+    (dict(segments=[(1, 2, 2, -1)]), h3a.H3A_EINVAL, "length"),
+    (dict(segments=[(1, 2, 2, 4)], S=5), h3a.H3A_ESHAPE, "S = 5"),
+    (dict(segments=[(1, 2, 2, 4)], base=0.0), h3a.H3A_EINVAL, "base"),
+    (dict(segments=[(1, 2, 2, 4)], base=float("nan")), h3a.H3A_EINVAL, "base"),
+    (dict(segments=[(1, 2, 2, 4)], table=None), h3a.H3A_EINVAL, "cos_sin"),
+    (dict(segments=[(1, 2, 2, 4)], table=P + 4), h3a.H3A_EUNSUPPORTED, "cos_sin"),
+])
+def test_rope_table_rejects(kw, status, word):
+    cu = np.full(8, -7, dtype=np.int32)
+    assert rope(cu_out=cu, **kw) == status
+    assert word in h3a.last_error()
+    assert np.all(cu == -7), "an invalid call wrote cu_seqlens_out"
+
+
+def qk(dtype=h3a.H3A_BF16, S=16, H=2, D=128, sq=None, sk=None, sqo=None, sko=None, q=P, k=P + (1 << 24),
+       qo=None, ko=None, gq=P + (2 << 24), gk=P + (3 << 24), eps=1e-6, cs=P + (4 << 24), rot=96):
+    hd = H * D
+    qo = q if qo is None else qo
+    ko = k if ko is None else ko
+    return h3a.lib().h3a_qk_rmsnorm_rope(q, k, qo, ko, dtype, S, H, D, sq or hd, sk or hd, sqo or hd, sko or hd,
+                                         gq, gk, eps, cs, rot, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(dtype=7), h3a.H3A_EDTYPE, "dtype"),
+    (dict(D=96, rot=48), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(rot=95), h3a.H3A_EINVAL, "rot_dim"),
+    (dict(rot=130), h3a.H3A_EINVAL, "rot_dim"),
+    (dict(rot=40), h3a.H3A_EUNSUPPORTED, "rot_dim / 2"),
+    (dict(dtype=h3a.H3A_F32, rot=36), h3a.H3A_EUNSUPPORTED, "rot_dim / 2"),
+    (dict(H=0), h3a.H3A_EINVAL, "H ="),
+    (dict(S=-1), h3a.H3A_EINVAL, "S ="),
+    (dict(sq=100), h3a.H3A_ESHAPE, "q: token stride"),
+    (dict(sko=255), h3a.H3A_ESHAPE, "k_out"),
+    (dict(sq=260), h3a.H3A_EUNSUPPORTED, "multiple of 16 bytes"),
+    (dict(q=None), h3a.H3A_EINVAL, "q is NULL"),
+    (dict(k=P + 2), h3a.H3A_EUNSUPPORTED, "k is not 16-byte aligned"),
+    (dict(gq=None), h3a.H3A_EINVAL, "gamma_q"),
+    (dict(cs=None), h3a.H3A_EINVAL, "cos_sin"),
+    (dict(eps=-1.0), h3a.H3A_EINVAL, "eps"),
+    (dict(qo=P + 256), h3a.H3A_EINVAL, "q_out overlaps q"),
+    (dict(qo=P + (1 << 24)), h3a.H3A_EINVAL, "q_out overlaps k"),
+    (dict(qo=P + (5 << 24), ko=P + (5 << 24) + 64), h3a.H3A_EINVAL, "q_out overlaps k_out"),
+])
+def test_qk_rmsnorm_rope_rejects(kw, status, word):
+    assert qk(**kw) == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+def test_qk_rmsnorm_rope_empty_is_a_no_op():
+    assert qk(S=0) == h3a.H3A_OK
+
+
+def attn(dtype=h3a.H3A_BF16, S=300, H=2, D=128, cu=(0, 100, 300), strides=None, q=P, k=P + (1 << 24),
+         v=P + (2 << 24), o=P + (3 << 24), scale=0.088):
+    hd = H * D
+    s = strides or (hd, hd, hd, hd)
+    c, cp = i32(cu) if cu is not None else (None, None)
+    n = len(cu) - 1 if cu is not None else 1
+    return h3a.lib().h3a_varlen_attn_fwd(q, k, v, o, dtype, S, H, D, *s, cp, n, scale, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(dtype=3), h3a.H3A_EDTYPE, "dtype"),
+    (dict(D=256), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(cu=None), h3a.H3A_EINVAL, "cu_seqlens"),
+    (dict(cu=(0,)), h3a.H3A_EINVAL, "nseg"),
+    (dict(cu=(1, 100, 300)), h3a.H3A_EINVAL, "cu_seqlens[0]"),
+    (dict(cu=(0, 200, 100, 300)), h3a.H3A_EINVAL, "decreases at index 2"),
+    (dict(cu=(0, 100, 299)), h3a.H3A_ESHAPE, "cu_seqlens[nseg]"),
+    (dict(scale=0.0), h3a.H3A_EINVAL, "scale"),
+    (dict(scale=float("inf")), h3a.H3A_EINVAL, "scale"),
+    (dict(strides=(256, 128, 256, 256)), h3a.H3A_ESHAPE, "k: token stride"),
+    (dict(strides=(256, 256, 256, 260)), h3a.H3A_EUNSUPPORTED, "o: token stride"),
+    (dict(v=None), h3a.H3A_EINVAL, "v is NULL"),
+    (dict(o=P + 8), h3a.H3A_EUNSUPPORTED, "o is not 16-byte aligned"),
+    (dict(o=P + 512), h3a.H3A_EINVAL, "o overlaps q"),
+    (dict(o=P + (2 << 24) - 256), h3a.H3A_EINVAL, "o overlaps v"),
+    (dict(H=0), h3a.H3A_EINVAL, "H ="),
+])
+def test_varlen_attn_rejects(kw, status, word):
+    assert attn(**kw) == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+def test_varlen_attn_empty_is_a_no_op():
+    assert attn(S=0, cu=(0, 0, 0)) == h3a.H3A_OK
+
+
+def test_binding_reports_errors_by_exception():
+    with pytest.raises(h3a.H3AError) as e:
+        h3a.plan_tiles([0, 5, 3], heads=2, block_m=128, n_xcd=8)
+    assert e.value.status == h3a.H3A_EINVAL and "decreases" in e.value.message

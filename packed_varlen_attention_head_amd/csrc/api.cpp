@@ -51,7 +51,23 @@ Range tensor_range(const void* p, int64_t S, int64_t H, int64_t D, int64_t strid
   if (S <= 0) return {lo, lo};
   return {lo, lo + uintptr_t(((S - 1) * stride + H * D) * int64_t(esz))};
 }
-bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Whether two token-major [S, H, D] tensors can share an element.  Disjoint
+// byte ranges never do.  With equal token strides the rows of one tensor sit
+// at a fixed offset from the other's (e.g. the q, k, v slices of one fused
+// [S, 3, H, D] buffer); they are disjoint when that offset, taken modulo the
+// stride, leaves room for a whole row on both sides.  Anything else is
+// treated as overlapping.
+bool may_overlap(const void* a, int64_t sa, const void* b, int64_t sb, int64_t S, int64_t H, int64_t D,
+                 size_t esz) {
+  const Range ra = tensor_range(a, S, H, D, sa, esz), rb = tensor_range(b, S, H, D, sb, esz);
+  if (!(ra.lo < rb.hi && rb.lo < ra.hi)) return false;
+  if (sa != sb) return true;
+  const int64_t stride_b = sa * int64_t(esz), row_b = H * D * int64_t(esz);
+  const int64_t diff = int64_t(reinterpret_cast<uintptr_t>(b) - reinterpret_cast<uintptr_t>(a));
+  const int64_t phase = ((diff % stride_b) + stride_b) % stride_b;
+  return !(phase >= row_b && stride_b - phase >= row_b);
+}
 
 // Validates a token-major [S, H, D] operand.
 h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, int32_t D,
@@ -265,15 +281,15 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
     if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
   }
   if (S == 0) return H3A_OK;
-  const Range rq = tensor_range(q, S, H, D, stride_q, esz), rk = tensor_range(k, S, H, D, stride_k, esz);
-  const Range rqo = tensor_range(q_out, S, H, D, stride_qo, esz), rko = tensor_range(k_out, S, H, D, stride_ko, esz);
   const bool q_inplace = q_out == q && stride_qo == stride_q;
   const bool k_inplace = k_out == k && stride_ko == stride_k;
-  if (!q_inplace && overlap(rqo, rq)) return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
-  if (!k_inplace && overlap(rko, rk)) return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
-  if (overlap(rqo, rk)) return fail(H3A_EINVAL, "q_out overlaps k");
-  if (overlap(rko, rq)) return fail(H3A_EINVAL, "k_out overlaps q");
-  if (overlap(rqo, rko)) return fail(H3A_EINVAL, "q_out overlaps k_out");
+  if (!q_inplace && may_overlap(q_out, stride_qo, q, stride_q, S, H, D, esz))
+    return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
+  if (!k_inplace && may_overlap(k_out, stride_ko, k, stride_k, S, H, D, esz))
+    return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
+  if (may_overlap(q_out, stride_qo, k, stride_k, S, H, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k");
+  if (may_overlap(k_out, stride_ko, q, stride_q, S, H, D, esz)) return fail(H3A_EINVAL, "k_out overlaps q");
+  if (may_overlap(q_out, stride_qo, k_out, stride_ko, S, H, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k_out");
 
   hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, H, D, stride_q, stride_k,
                                              stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
@@ -300,10 +316,9 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
   if ((st = check_operand("v", v, S, H, D, stride_v, esz)) != H3A_OK) return st;
   if ((st = check_operand("o", o, S, H, D, stride_o, esz)) != H3A_OK) return st;
   if (S == 0) return H3A_OK;
-  const Range ro = tensor_range(o, S, H, D, stride_o, esz);
-  if (overlap(ro, tensor_range(q, S, H, D, stride_q, esz))) return fail(H3A_EINVAL, "o overlaps q");
-  if (overlap(ro, tensor_range(k, S, H, D, stride_k, esz))) return fail(H3A_EINVAL, "o overlaps k");
-  if (overlap(ro, tensor_range(v, S, H, D, stride_v, esz))) return fail(H3A_EINVAL, "o overlaps v");
+  if (may_overlap(o, stride_o, q, stride_q, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
+  if (may_overlap(o, stride_o, k, stride_k, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
+  if (may_overlap(o, stride_o, v, stride_v, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
 
   const bool bf16 = dtype == H3A_BF16;
   Plan plan;

@@ -244,7 +244,7 @@ def test_strided_views_and_guard_rows():
     qkv = to_device(fused, "bf16")
     q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
     pad = 16
-    canary = -12345.0
+    canary = -1024.0  # exactly representable in bf16
     big = torch.full((S + 2, H * D + pad), canary, dtype=torch.bfloat16, device="cuda")
     out = torch.as_strided(big, (S, H, D), (H * D + pad, D, 1), storage_offset=H * D + pad)
     run_attn(q, k, v, cu, 1 / np.sqrt(D), out=out)

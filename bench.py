@@ -43,7 +43,26 @@ def parse():
     ap.add_argument("--config", default="h3_s20423_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, five
+    launches.  Its FETCH_SIZE / WRITE_SIZE readings convert the counters of the
+    other kernels into bytes."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 5}))
+    return 0
 
 
 def source_hash(path):
@@ -110,6 +129,8 @@ def cpu_baseline(w, T, target_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        return calibrate_copy()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "

@@ -20,20 +20,31 @@
 //   * The output is accumulated transposed as well, O^T += V^T P^T: the
 //     probabilities leave the score accumulator as the B operand with no data
 //     movement (converted to bf16 in place), and the per-query rescale factor
-//     is a per-lane scalar.
-//   * V^T is produced while staging V into LDS.  The score accumulator hands
-//     a lane keys {0-3, 8-11} (lanes 0-31) or {4-7, 12-15} (lanes 32-63) of
-//     each 16-key group as its 8 contraction slots, so V^T is stored with bits
-//     2 and 3 of the key index swapped, which makes each A operand one
-//     contiguous 16-byte LDS read.
-//   * K rows and V^T rows are padded by 16 bytes so the 32 rows read by one
-//     MFMA operand load fall on distinct LDS banks.
-//   * K/V tiles of 64 keys are prefetched into registers one tile ahead.
-//   * Keys past the segment end are loaded as zeros and masked to -inf in the
-//     last tile only; query rows past the end are computed but not stored.
-//   * exp2 with scale * log2(e) folded into one FMA; the accumulator rescale
-//     is skipped when no query of the wave raised its running max.
+//     is a per-lane scalar.  The accumulator hands a lane keys {0-3, 8-11}
+//     (lanes 0-31) or {4-7, 12-15} (lanes 32-63) of each 16-key group as its
+//     8 contraction slots; the matching V^T operand is two transposing LDS
+//     reads (ds_read_b64_tr_b16) of 4 consecutive keys each from row-major V.
+//   * K and V tiles of 64 keys go from HBM straight into LDS with 16-byte
+//     buffer-to-LDS loads (no staging registers), double-buffered: the next
+//     tile's loads are in flight while the current tile is computed, and one
+//     barrier per tile separates the two stages' writers and readers.
+//   * LDS rows are not padded (the LDS-bound loads write 1 KiB runs); bank
+//     conflicts are avoided by XOR-swizzling the 16-byte chunks of a row:
+//     K chunk c of row r sits at c ^ (r % 8) (the 8 rows one K operand read
+//     serves together land on 8 distinct chunks), V chunk c at
+//     c ^ 2 (r % 4) (the 4 rows of one transposing read land on 4 distinct
+//     32-byte windows).  All per-lane LDS addresses are computed once; tile,
+//     stage and block offsets are immediates (the tile loop is unrolled over
+//     the two stages).
+//   * Loads go through buffer resources bounded at the segment end, so rows
+//     past it read as zeros with no per-lane branches; those keys are masked
+//     to -inf in the last tile only, and query rows past the end are computed
+//     but not stored.
+//   * exp2 with scale * log2(e) folded into one FMA; the running max is
+//     only raised (and the accumulator rescaled) when a tile exceeds it by
+//     more than 2^8, which is exact and skips the rescale on most tiles.
 #include <cstdint>
+#include <type_traits>
 
 #include "common.h"
 
@@ -41,23 +52,23 @@ namespace h3a {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
 constexpr int kBN = 64;           // keys per tile
-constexpr int kPad = 8;           // bf16 elements of row padding in LDS
+constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running max moves
 static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 
-template <int D>
-struct Smem {
-  uint16_t k[kBN][D + kPad];   // K tile, row-major
-  uint16_t vt[D][kBN + kPad];  // V tile transposed, key index bits 2 and 3 swapped
-};
+#define LDS __attribute__((address_space(3)))
 
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
+template <int D>
+struct Stage {
+  uint16_t k[kBN * D];  // row-major, chunk c of row r at c ^ (r % 8)
+  uint16_t v[kBN * D];  // row-major, chunk c of row r at c ^ 2 (r % 4)
+};
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = __bf16(lo);
@@ -65,27 +76,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+// Buffer resource over `rows` rows of `stride_bytes` starting at `base`:
+// loads at offsets past the last row return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows, int64_t stride_bytes) {
+  const int64_t n = rows > 0 ? int64_t(rows) * stride_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(n > 0x7fffffff ? 0x7fffffff : n),
+                                           0x00020000);
+}
+
+
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
                      int64_t sk, int64_t sv, int64_t so, const WorkItem* __restrict__ items,
                      float c) {
-  constexpr int KS = D / 16;               // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;               // 32-wide output dim blocks
-  constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int KCH = kBN * CH / (64 * kWaves);  // K chunks staged per thread
-  constexpr int KPT = kBN * CH / (64 * kWaves);  // V keys staged per thread
-  static_assert(KCH >= 1 && KPT >= 2 && (KPT & (KPT - 1)) == 0, "staging layout");
+  // The body uses LDS address-space pointers and gfx950-only builtins, which
+  // exist only in the device pass; the host pass needs just the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KS = D / 16;                    // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                    // 32-wide output dim blocks
+  constexpr int CH = D / 8;                     // 16-byte chunks per row
+  constexpr int ROWB = D * 2;                   // bytes per LDS row
+  constexpr int NDMA = kBN * CH / (64 * kWaves);  // 16-byte loads per thread per tile and operand
+  static_assert(NDMA >= 1 && CH >= 8, "tile layout");
 
-  __shared__ Smem<D> sm;
+  __shared__ Stage<D> sm[2];
 
   const WorkItem it = items[blockIdx.x];
   if (it.seg_len <= 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int head_off = it.head * D;
@@ -95,94 +118,67 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Q as the B operand: lane holds query (qrow0 + l32), dims ks*16 + hi*8 .. +8.
   bf16x8 qb[KS];
   {
-    const int qi = qrow0 + l32;
-    const uint16_t* qp = q + int64_t(it.seg_start + qi) * sq + head_off + hi * 8;
+    const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, sq * 2);
+    const int off = (l32 * int(sq) + hi * 8) * 2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (qi < it.seg_len) {
-        qb[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-      } else {
-        qb[ks] = bf16x8{};
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
   }
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m_run = -1e30f;  // running max of scale*log2(e)*score
+  float m_run = -1e30f;  // reference max of scale*log2(e)*score
   float l_run = 0.f;     // this lane's partial row sum (its 16-of-32 keys)
 
-  // Staging assignment.  K: chunk index tid + i*256 -> (row, col chunk).
-  // V: column chunk vc, keys vk0 .. vk0 + KPT - 1.
-  const int vc = tid % CH;
-  const int vk0 = (tid / CH) * KPT;
+  // LDS-bound loads: slot s = (i * kWaves + wave) * 64 + lane holds physical
+  // chunk s % CH of row s / CH; the lane fetches the logical chunk stored there.
+  int koff[NDMA], voff[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int s = (i * kWaves + wave) * 64 + lane;
+    const int row = s / CH, pc = s % CH;
+    koff[i] = row * int(sk) * 2 + ((pc ^ (row & 7)) * 16);
+    voff[i] = row * int(sv) * 2 + ((pc ^ (2 * (row & 3))) * 16);
+  }
+  // K operand reads: row l32 (+32 kb), logical chunk 2 ks + hi.
+  int kaddr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ (l32 & 7)) * 16);
+  // V^T operand reads (transposing): 16-lane group g reads keys
+  // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
+  // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
+  int vaddr[DB];
+  {
+    const int g = lane >> 4, m = lane & 15;
+    const int row = 4 * (g >> 1) + (m >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int lc = db * 4 + 2 * (g & 1) + ((m & 3) >> 1);
+      vaddr[db] = row * ROWB + ((lc ^ (2 * (row & 3))) * 16) + 8 * (m & 1);
+    }
+  }
 
-  uint4 kst[KCH], vst[KPT];
+  const uint16_t* kbase = k + int64_t(it.seg_start) * sk + head_off;
+  const uint16_t* vbase = v + int64_t(it.seg_start) * sv + head_off;
   const int ntiles = (it.seg_len + kBN - 1) / kBN;
 
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t, Stage<D>& st) {
     const int key0 = t * kBN;
-    const int kvalid = it.seg_len - key0;
+    const int rows = it.seg_len - key0;
+    const auto rk = rows_rsrc(kbase + int64_t(key0) * sk, rows, sk * 2);
+    const auto rv = rows_rsrc(vbase + int64_t(key0) * sv, rows, sv * 2);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * 64 * kWaves;
-      const int row = idx / CH, cc = idx % CH;
-      if (row < kvalid) {
-        kst[i] = *reinterpret_cast<const uint4*>(k + int64_t(it.seg_start + key0 + row) * sk + head_off + cc * 8);
-      } else {
-        kst[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int row = vk0 + i;
-      if (row < kvalid) {
-        vst[i] = *reinterpret_cast<const uint4*>(v + int64_t(it.seg_start + key0 + row) * sv + head_off + vc * 8);
-      } else {
-        vst[i] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot0 = (i * kWaves + wave) * 64 * 8;  // elements; wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(st.k + slot0), 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(st.v + slot0), 16, voff[i], 0, 0, 0);
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int idx = tid + i * 64 * kWaves;
-      const int row = idx / CH, cc = idx % CH;
-      *reinterpret_cast<uint4*>(&sm.k[row][cc * 8]) = kst[i];
-    }
-    // Transpose: for each of the 8 dims of chunk vc, the KPT keys form one
-    // contiguous run at vt_pos(vk0) (KPT divides 4, so bits 2/3 stay fixed).
-    const int pos0 = vt_pos(vk0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t vals[KPT];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const uint32_t w = (&vst[i].x)[e >> 1];
-        vals[i] = uint16_t((e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-      uint16_t* dst = &sm.vt[vc * 8 + e][pos0];
-      if constexpr (KPT == 4) {
-        uint2 pk;
-        pk.x = uint32_t(vals[0]) | (uint32_t(vals[1]) << 16);
-        pk.y = uint32_t(vals[2]) | (uint32_t(vals[3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = uint32_t(vals[0]) | (uint32_t(vals[1]) << 16);
-      }
-    }
-  };
-
-  load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-    if (!active) continue;
-
+  auto compute_tile = [&](int t, const Stage<D>& st) {
+    const LDS char* kl = (const LDS char*)(st.k);
+    const LDS char* vl = (const LDS char*)(st.v);
     // ---- S^T = K Q^T --------------------------------------------------------
     f32x16 sacc[kBN / 32];
 #pragma unroll
@@ -190,7 +186,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[kb * 32 + l32][ks * 16 + hi * 8]);
+        const bf16x8 a = *reinterpret_cast<const LDS bf16x8*>(kl + kaddr[ks] + kb * 32 * ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
       }
     }
@@ -208,50 +204,79 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
 
     // ---- online softmax ---------------------------------------------------
+    // The reference max m_run only moves when a query's tile max exceeds it
+    // by more than kRescaleSlack (log2 units), so probabilities stay below
+    // 2^kRescaleSlack and most tiles skip the accumulator rescale.  The
+    // result is exact: numerator and denominator share the same reference.
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    const bool grow = m_new > m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-    m_run = m_new;
-
-    bf16x8 pb[kBN / 16];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], c, -m_new));
-          rs += p[i];
-        }
-        bf16x8 v8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = __bf16(p[i]);
-        pb[kb * 2 + hh] = v8;
-      }
-    }
-    l_run = l_run * alpha + rs;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    const bool grow = mx > m_run + kRescaleSlack;
     if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
 
-    // ---- O^T += V^T P^T -----------------------------------------------------
+    // p = 2^(c*s - m_run), rounded to bf16 for the PV product; the row sum
+    // adds the rounded values (v_dot2 against (1, 1)), so the normaliser
+    // matches the weights actually applied to V.
+    bf16x8 pb[kBN / 16];
+    const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 v8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], c, -m_run)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 pr = {v8[2 * i], v8[2 * i + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        }
+        pb[kb * 2 + hh] = v8;
+      }
+    }
+
+    // ---- O^T += V^T P^T -------------------------------------------------------
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kk = 0; kk < kBN / 16; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[db * 32 + l32][kk * 16 + hi * 8]);
+        const LDS char* p0 = vl + vaddr[db] + kk * 16 * ROWB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0));
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0 + 8 * ROWB));
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
       }
+  };
+
+  // One tile: start loading the next tile into the other stage, compute this
+  // one, then wait for this thread's loads and the barrier that publishes them.
+  auto step = [&](int t, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    if (t + 1 < ntiles) issue_tile(t + 1, sm[S ^ 1]);
+    if (active) compute_tile(t, sm[S]);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+  };
+
+  issue_tile(0, sm[0]);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 <= ntiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
 
   if (!active) return;
   const int qi = qrow0 + l32;
@@ -268,6 +293,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pk.y = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + db * 32 + g * 8) = pk;
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <int D>

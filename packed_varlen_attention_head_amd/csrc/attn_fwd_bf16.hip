@@ -65,9 +65,9 @@ static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 #define LDS __attribute__((address_space(3)))
 
 template <int D>
-struct Stage {
-  uint16_t k[kBN * D];  // row-major, chunk c of row r at c ^ (r % 8)
-  uint16_t v[kBN * D];  // row-major, chunk c of row r at c ^ 2 (r % 4)
+struct Rings {
+  uint16_t k[2][kBN * D];  // K tiles, row-major, chunk c of row r at c ^ (r % 8)
+  uint16_t v[2][kBN * D];  // V tiles, row-major, chunk c of row r at c ^ 2 (r % 4)
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -84,6 +84,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
                                            0x00020000);
 }
 
+// The value held by lane ^ 32 (v_permlane32_swap exchanges the two halves).
+__device__ __forceinline__ float other_half(float x, int hi) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, hi ? r[0] : r[1]);
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves, 2)
@@ -94,14 +103,15 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // The body uses LDS address-space pointers and gfx950-only builtins, which
   // exist only in the device pass; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int KS = D / 16;                    // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;                    // 32-wide output dim blocks
-  constexpr int CH = D / 8;                     // 16-byte chunks per row
-  constexpr int ROWB = D * 2;                   // bytes per LDS row
+  constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;                      // 32-wide output dim blocks
+  constexpr int CH = D / 8;                       // 16-byte chunks per row
+  constexpr int ROWB = D * 2;                     // bytes per LDS row
+  constexpr int TILEB = kBN * ROWB;               // bytes per LDS tile
   constexpr int NDMA = kBN * CH / (64 * kWaves);  // 16-byte loads per thread per tile and operand
   static_assert(NDMA >= 1 && CH >= 8, "tile layout");
 
-  __shared__ Stage<D> sm[2];
+  __shared__ Rings<D> sm;
 
   const WorkItem it = items[blockIdx.x];
   if (it.seg_len <= 0) return;
@@ -162,58 +172,60 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const uint16_t* kbase = k + int64_t(it.seg_start) * sk + head_off;
   const uint16_t* vbase = v + int64_t(it.seg_start) * sv + head_off;
   const int ntiles = (it.seg_len + kBN - 1) / kBN;
+  const LDS char* lds_k = (const LDS char*)(&sm.k[0][0]);
+  const LDS char* lds_v = (const LDS char*)(&sm.v[0][0]);
 
-  auto issue_tile = [&](int t, Stage<D>& st) {
+  // ---- building blocks ------------------------------------------------------
+  auto load_k = [&](int t, int slot) {
     const int key0 = t * kBN;
-    const int rows = it.seg_len - key0;
-    const auto rk = rows_rsrc(kbase + int64_t(key0) * sk, rows, sk * 2);
-    const auto rv = rows_rsrc(vbase + int64_t(key0) * sv, rows, sv * 2);
+    const auto r = rows_rsrc(kbase + int64_t(key0) * sk, it.seg_len - key0, sk * 2);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot0 = (i * kWaves + wave) * 64 * 8;  // elements; wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(st.k + slot0), 16, koff[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(st.v + slot0), 16, voff[i], 0, 0, 0);
-    }
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(&sm.k[slot][(i * kWaves + wave) * 64 * 8]), 16,
+                                               koff[i], 0, 0, 0);
   };
-
-  auto compute_tile = [&](int t, const Stage<D>& st) {
-    const LDS char* kl = (const LDS char*)(st.k);
-    const LDS char* vl = (const LDS char*)(st.v);
-    // ---- S^T = K Q^T --------------------------------------------------------
-    f32x16 sacc[kBN / 32];
+  auto load_v = [&](int t, int slot) {
+    const int key0 = t * kBN;
+    const auto r = rows_rsrc(vbase + int64_t(key0) * sv, it.seg_len - key0, sv * 2);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(&sm.v[slot][(i * kWaves + wave) * 64 * 8]), 16,
+                                               voff[i], 0, 0, 0);
+  };
+  // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
+  auto qk = [&](auto slot, f32x16* sacc) {
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const LDS bf16x8*>(kl + kaddr[ks] + kb * 32 * ROWB);
+        const bf16x8 a = *(const LDS bf16x8*)(lds_k + kaddr[ks] + slot * TILEB + kb * 32 * ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
       }
     }
-
-    // ---- mask keys past the segment end (last tile only) ------------------
-    const int kvalid = it.seg_len - t * kBN;
-    if (kvalid < kBN) {
+  };
+  // Keys at or past `kvalid` in the tile get -inf.
+  auto mask = [&](f32x16* sacc, int kvalid) {
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-          if (key >= kvalid) sacc[kb][r] = -__builtin_inff();
-        }
-    }
-
-    // ---- online softmax ---------------------------------------------------
-    // The reference max m_run only moves when a query's tile max exceeds it
-    // by more than kRescaleSlack (log2 units), so probabilities stay below
-    // 2^kRescaleSlack and most tiles skip the accumulator rescale.  The
-    // result is exact: numerator and denominator share the same reference.
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        if (key >= kvalid) sacc[kb][r] = -__builtin_inff();
+      }
+  };
+  // Tile max; the reference max m_run only moves when a query's tile max
+  // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
+  // below 2^kRescaleSlack and most tiles skip the rescale.  Exact: numerator
+  // and denominator share the reference.  Must run after every PV product
+  // issued with the old reference.
+  auto update_max = [&](const f32x16* sacc) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    mx = fmaxf(mx, other_half(mx, hi)) * c;
     const bool grow = mx > m_run + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -223,14 +235,14 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
-
-    // p = 2^(c*s - m_run), rounded to bf16 for the PV product; the row sum
-    // adds the rounded values (v_dot2 against (1, 1)), so the normaliser
-    // matches the weights actually applied to V.
-    bf16x8 pb[kBN / 16];
+  };
+  // p = 2^(c*s - m_run), rounded to bf16 for the PV product; the row sum adds
+  // the rounded values (v_dot2 against (1, 1)), so the normaliser matches the
+  // weights actually applied to V.
+  auto probs = [&](const f32x16* sacc, bf16x8* pb) {
     const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
+    for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 v8;
@@ -243,44 +255,89 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         }
         pb[kb * 2 + hh] = v8;
       }
-    }
-
-    // ---- O^T += V^T P^T -------------------------------------------------------
+  };
+  // O^T += V^T P^T for the V tile in `slot`.
+  auto pv = [&](auto slot, const bf16x8* pb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kk = 0; kk < kBN / 16; ++kk) {
-        const LDS char* p0 = vl + vaddr[db] + kk * 16 * ROWB;
+        const LDS char* p0 = lds_v + vaddr[db] + slot * TILEB + kk * 16 * ROWB;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0));
         const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0 + 8 * ROWB));
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
       }
   };
-
-  // One tile: start loading the next tile into the other stage, compute this
-  // one, then wait for this thread's loads and the barrier that publishes them.
-  auto step = [&](int t, auto stage) {
-    constexpr int S = decltype(stage)::value;
-    if (t + 1 < ntiles) issue_tile(t + 1, sm[S ^ 1]);
-    if (active) compute_tile(t, sm[S]);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's LDS-bound loads landed
     __syncthreads();
   };
 
-  issue_tile(0, sm[0]);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __syncthreads();
-  int t = 0;
-  for (; t + 2 <= ntiles; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
+  // ---- software-pipelined tile loop -----------------------------------------
+  // Entering iteration t: `s` holds the scores of tile t with the running max
+  // already updated for it, K_{t+1} sits in K slot (t+1) % 2 and V_t in V slot
+  // t % 2.  The iteration loads K_{t+2} and V_{t+1} into the slots freed by
+  // the previous iteration, turns tile t's scores into probabilities while the
+  // MFMA pipe computes tile t+1's scores, then accumulates tile t's PV product
+  // while the VALU reduces tile t+1's max.
+  f32x16 s[kBN / 32];
+  bf16x8 pb[kBN / 16];
+  load_k(0, 0);
+  load_v(0, 0);
+  if (ntiles > 1) load_k(1, 1);
+  publish();
+  if (active) {
+    qk(IC<0>{}, s);
+    if (it.seg_len < kBN) mask(s, it.seg_len);
+    update_max(s);
   }
-  if (t < ntiles) step(t, std::integral_constant<int, 0>{});
+  // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
+  __syncthreads();
+
+  // Steady state: tiles t and t+1 both exist and t+1 is not the last, so
+  // tile t+1 is full and K_{t+2} exists.  Two iterations per trip fix the
+  // slot parities as immediates.
+  auto steady = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
+    load_k(t + 2, P);
+    load_v(t + 1, P ^ 1);
+    if (active) {
+      probs(s, pb);
+      qk(IC<P ^ 1>{}, s);
+      pv(IC<P>{}, pb);
+      update_max(s);
+    }
+    publish();
+  };
+  int t = 0;
+  for (; t + 3 < ntiles; t += 2) {
+    steady(t, IC<0>{});
+    steady(t + 1, IC<1>{});
+  }
+  // Remaining one to three iterations, with slot parity in a register.
+  for (; t < ntiles; ++t) {
+    const int par = t & 1;
+    if (t + 2 < ntiles) load_k(t + 2, par);
+    if (t + 1 < ntiles) load_v(t + 1, par ^ 1);
+    if (active) {
+      probs(s, pb);
+      if (t + 1 < ntiles) {
+        qk(par ^ 1, s);
+        pv(par, pb);
+        const int kvalid = it.seg_len - (t + 1) * kBN;
+        if (kvalid < kBN) mask(s, kvalid);
+        update_max(s);
+      } else {
+        pv(par, pb);
+      }
+    }
+    publish();
+  }
 
   if (!active) return;
   const int qi = qrow0 + l32;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = l_run + other_half(l_run, hi);
   const float inv = 1.0f / l_tot;
   if (qi >= it.seg_len) return;
   uint16_t* op = o + int64_t(it.seg_start + qi) * so + head_off + hi * 4;

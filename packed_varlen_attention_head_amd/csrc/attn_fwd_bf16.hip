@@ -227,7 +227,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = fmaxf(mx, other_half(mx, hi)) * c;
     const bool grow = mx > m_run + kRescaleSlack;
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
+      // Rare after the first tiles; the empty asm keeps the compiler from
+      // speculating the accumulator rescale onto every tile.
+      asm volatile("" ::: "memory");
       const float m_new = grow ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;

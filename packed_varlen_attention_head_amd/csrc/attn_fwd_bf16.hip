@@ -28,6 +28,9 @@
 //     buffer-to-LDS loads (no staging registers), double-buffered: the next
 //     tile's loads are in flight while the current tile is computed, and one
 //     barrier per tile separates the two stages' writers and readers.
+//   * Each ring slot is its own LDS object: with one array and an index, the
+//     compiler cannot tell a load into one slot from reads of another and
+//     waits for every outstanding load before each LDS read.
 //   * LDS rows are not padded (the LDS-bound loads write 1 KiB runs); bank
 //     conflicts are avoided by XOR-swizzling the 16-byte chunks of a row:
 //     K chunk c of row r sits at c ^ (r % 8) (the 8 rows one K operand read
@@ -58,17 +61,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
-constexpr int kBN = 64;           // keys per tile
-constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running max moves
+[[maybe_unused]] constexpr int kBN = 64;  // keys per tile
+[[maybe_unused]] constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running max moves
 static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 
 #define LDS __attribute__((address_space(3)))
-
-template <int D>
-struct Rings {
-  uint16_t k[2][kBN * D];  // K tiles, row-major, chunk c of row r at c ^ (r % 8)
-  uint16_t v[2][kBN * D];  // V tiles, row-major, chunk c of row r at c ^ 2 (r % 4)
-};
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = __bf16(lo);
@@ -107,11 +104,24 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int DB = D / 32;                      // 32-wide output dim blocks
   constexpr int CH = D / 8;                       // 16-byte chunks per row
   constexpr int ROWB = D * 2;                     // bytes per LDS row
-  constexpr int TILEB = kBN * ROWB;               // bytes per LDS tile
   constexpr int NDMA = kBN * CH / (64 * kWaves);  // 16-byte loads per thread per tile and operand
   static_assert(NDMA >= 1 && CH >= 8, "tile layout");
 
-  __shared__ Rings<D> sm;
+  // One object per ring slot, so alias analysis can tell a load into one slot
+  // from reads of another (otherwise every LDS read waits for all loads).
+  __shared__ uint16_t k_slot0[kBN * D], k_slot1[kBN * D];
+  __shared__ uint16_t v_slot0[kBN * D], v_slot1[kBN * D];
+  // Slot pointers: compile-time choice for IC<> slots, a select otherwise.
+  auto kslot = [&](auto slot) -> uint16_t* {
+    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? k_slot1 : k_slot0;
+    else if constexpr (decltype(slot)::value == 0) return k_slot0;
+    else return k_slot1;
+  };
+  auto vslot = [&](auto slot) -> uint16_t* {
+    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? v_slot1 : v_slot0;
+    else if constexpr (decltype(slot)::value == 0) return v_slot0;
+    else return v_slot1;
+  };
 
   const WorkItem it = items[blockIdx.x];
   if (it.seg_len <= 0) return;
@@ -172,24 +182,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const uint16_t* kbase = k + int64_t(it.seg_start) * sk + head_off;
   const uint16_t* vbase = v + int64_t(it.seg_start) * sv + head_off;
   const int ntiles = (it.seg_len + kBN - 1) / kBN;
-  const LDS char* lds_k = (const LDS char*)(&sm.k[0][0]);
-  const LDS char* lds_v = (const LDS char*)(&sm.v[0][0]);
 
   // ---- building blocks ------------------------------------------------------
-  auto load_k = [&](int t, int slot) {
+  auto load_k = [&](int t, auto slot) {
     const int key0 = t * kBN;
     const auto r = rows_rsrc(kbase + int64_t(key0) * sk, it.seg_len - key0, sk * 2);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(&sm.k[slot][(i * kWaves + wave) * 64 * 8]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                koff[i], 0, 0, 0);
   };
-  auto load_v = [&](int t, int slot) {
+  auto load_v = [&](int t, auto slot) {
     const int key0 = t * kBN;
     const auto r = rows_rsrc(vbase + int64_t(key0) * sv, it.seg_len - key0, sv * 2);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(&sm.v[slot][(i * kWaves + wave) * 64 * 8]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                voff[i], 0, 0, 0);
   };
   // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
@@ -199,7 +207,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const LDS bf16x8*)(lds_k + kaddr[ks] + slot * TILEB + kb * 32 * ROWB);
+        const bf16x8 a = *(const LDS bf16x8*)((const LDS char*)kslot(slot) + kaddr[ks] + kb * 32 * ROWB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
       }
     }
@@ -265,7 +273,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int kk = 0; kk < kBN / 16; ++kk) {
-        const LDS char* p0 = lds_v + vaddr[db] + slot * TILEB + kk * 16 * ROWB;
+        const LDS char* p0 = (const LDS char*)vslot(slot) + vaddr[db] + kk * 16 * ROWB;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0));
         const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0 + 8 * ROWB));
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -286,9 +294,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // while the VALU reduces tile t+1's max.
   f32x16 s[kBN / 32];
   bf16x8 pb[kBN / 16];
-  load_k(0, 0);
-  load_v(0, 0);
-  if (ntiles > 1) load_k(1, 1);
+  load_k(0, IC<0>{});
+  load_v(0, IC<0>{});
+  if (ntiles > 1) load_k(1, IC<1>{});
   publish();
   if (active) {
     qk(IC<0>{}, s);
@@ -303,8 +311,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // slot parities as immediates.
   auto steady = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
-    load_k(t + 2, P);
-    load_v(t + 1, P ^ 1);
+    load_k(t + 2, IC<P>{});
+    load_v(t + 1, IC<P ^ 1>{});
     if (active) {
       probs(s, pb);
       qk(IC<P ^ 1>{}, s);

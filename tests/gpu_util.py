@@ -57,7 +57,7 @@ def compare(g: np.ndarray, r: np.ndarray, dtype: str, what: str):
     return max_abs, mean_rel
 
 
-def sample_rows(cu, block_m: int = 128, every: int = 97, seed: int = 0) -> np.ndarray:
+def sample_rows(cu, block_m: int = 256, every: int = 97, seed: int = 0) -> np.ndarray:
     """Every `every`-th row, each segment's first and last row, and every row of
     each segment's last (possibly partial) query tile."""
     cu = np.asarray(cu, dtype=np.int64)

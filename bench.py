@@ -45,7 +45,70 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
+    ap.add_argument("--rocprof-summary", metavar="RESULTS_DB",
+                    help="print a per-kernel duration table from a rocprofv3 --kernel-trace results.db")
+    ap.add_argument("--rocprof-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="HBM bytes per launch of each h3a kernel from FETCH_SIZE/WRITE_SIZE runs, scaled by "
+                         "the same counters on the --calibrate-copy run; prints JSON")
     return ap.parse_args()
+
+
+def _rocpd_rows(db, query):
+    import sqlite3
+
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(query))
+    finally:
+        con.close()
+
+
+def _short_kernel(name):
+    import re
+
+    m = re.search(r"(attn_fwd_bf16_kernel<\d+>|attn_fwd_f32_kernel<\d+>|qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
+                  r"__amd_rocclr_\w+|elementwise_kernel|vectorized_elementwise_kernel|reduce_kernel)", name)
+    return m.group(1) if m else name[:60]
+
+
+def rocprof_summary(db):
+    """Per-kernel table (calls, total, average) from a rocprofv3 results database."""
+    rows = _rocpd_rows(db, "select name, total_calls, total_duration, average, percentage from top_kernels")
+    print("| kernel | calls | total (us) | average (us) | share |")
+    print("|---|---|---|---|---|")
+    for name, calls, total, avg, pct in rows:
+        print(f"| {_short_kernel(name)} | {calls} | {total:.1f} | {avg:.1f} | {pct:.2f}% |")
+    return 0
+
+
+def rocprof_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, converted to bytes with the
+    factor the same counter reads for a 1 GiB copy (bytes moved / counter bytes)."""
+    import collections
+
+    def per_kernel(db, counter):
+        acc = collections.defaultdict(list)
+        for name, value in _rocpd_rows(db, f"select kernel_name, value from counters_collection "
+                                           f"where counter_name = '{counter}'"):
+            acc[_short_kernel(name)].append(value * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    copy_bytes = float(1 << 30)
+    cf = per_kernel(copy_fetch_db, "FETCH_SIZE")
+    cw = per_kernel(copy_write_db, "WRITE_SIZE")
+    cname = max(cf, key=cf.get)
+    f_scale = copy_bytes / cf[cname]
+    w_scale = copy_bytes / cw[max(cw, key=cw.get)]
+    fetch, write = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
+    out = {"kernel_source_sha256_16": source_hash(ATTN_SRC), "copy_kernel": cname,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in sorted(set(fetch) | set(write)):
+        if not (k.startswith("attn") or k.startswith("qk_norm") or k.startswith("rope")):
+            continue
+        rb, wb = fetch.get(k, 0.0) * f_scale, write.get(k, 0.0) * w_scale
+        out["kernels"][k] = {"hbm_read_bytes": rb, "hbm_write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def calibrate_copy():
@@ -70,9 +133,9 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(n_launch_bytes_alg):
-    """HBM bytes per attention launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -80,7 +143,8 @@ def measured_traffic(n_launch_bytes_alg):
         return None
     if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
         return None
-    return t.get("hbm_bytes_per_launch")
+    k = t.get("kernels", {}).get("attn_fwd_bf16_kernel<128>")
+    return k.get("hbm_bytes_per_launch") if k else None
 
 
 def cpu_baseline(w, T, target_s):
@@ -131,6 +195,10 @@ def main():
     args = parse()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.rocprof_summary:
+        return rocprof_summary(args.rocprof_summary)
+    if args.rocprof_traffic:
+        return rocprof_traffic(*args.rocprof_traffic)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -227,7 +295,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(attn_alg_bytes),
+            "traffic": measured_traffic(),
             "kernel": "attn_fwd_bf16_kernel<128>",
             "algorithmic_flop_per_launch": F,
             "algorithmic_bytes_per_launch": attn_alg_bytes,

@@ -105,7 +105,7 @@ h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int
  *                NULL when rot_dim == 0.
  * Supported: D in {64, 128}; rot_dim even, 0 <= rot_dim <= D, and (rot_dim/2)
  * a multiple of 8 (bf16) or 4 (fp32); pointers 16-byte aligned and strides
- * multiples of 16 bytes; strides >= H*D.
+ * multiples of 16 bytes; strides >= H*D and below 2^31 / 64 bytes.
  *
  * Errors: EINVAL, ESHAPE (stride < H*D), EDTYPE, EUNSUPPORTED, EHIP.
  */
@@ -137,7 +137,7 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
  * softmax, probabilities rounded to bf16 for the PV product, output rounded
  * once; fp32 -- fp32 throughout.
  * Supported: D in {64, 128}; pointers 16-byte aligned; strides multiples of
- * 16 bytes and >= H*D; S <= INT32_MAX.
+ * 16 bytes, >= H*D and below 2^31 / 64 bytes; S <= INT32_MAX.
  *
  * Errors: EINVAL, ESHAPE, EDTYPE, EUNSUPPORTED, EHIP.
  */

@@ -80,6 +80,11 @@ h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, 
   if ((stride * int64_t(esz)) % 16 != 0)
     return fail(H3A_EUNSUPPORTED, "%s: token stride %lld elements is not a multiple of 16 bytes", name,
                 (long long)stride);
+  // The attention kernels address up to 64 rows of a tensor with 32-bit
+  // buffer offsets.
+  if (stride * int64_t(esz) * 64 > int64_t(INT32_MAX))
+    return fail(H3A_EUNSUPPORTED, "%s: token stride %lld elements is too large (64 rows must fit in 2 GiB)", name,
+                (long long)stride);
   return H3A_OK;
 }
 

@@ -32,13 +32,12 @@
 //     compiler cannot tell a load into one slot from reads of another and
 //     waits for every outstanding load before each LDS read.
 //   * LDS rows are not padded (the LDS-bound loads write 1 KiB runs); bank
-//     conflicts are avoided by XOR-swizzling the 16-byte chunks of a row:
-//     K chunk c of row r sits at c ^ (r % 8) (the 8 rows one K operand read
-//     serves together land on 8 distinct chunks), V chunk c at
-//     c ^ 2 (r % 4) (the 4 rows of one transposing read land on 4 distinct
-//     32-byte windows).  All per-lane LDS addresses are computed once; tile,
-//     stage and block offsets are immediates (the tile loop is unrolled over
-//     the two stages).
+//     conflicts are avoided by XOR-swizzling the 16-byte chunks of a row
+//     (k_swz, v_swz below: the 16 rows of one K operand read, and the 4 rows
+//     x 64 bytes of one transposing V read, each land on distinct bank
+//     slots).  All per-lane LDS addresses are computed once; tile, slot and
+//     block offsets are immediates (the tile loop is unrolled over the two
+//     slots).
 //   * Loads go through buffer resources bounded at the segment end, so rows
 //     past it read as zeros with no per-lane branches; those keys are masked
 //     to -inf in the last tile only, and query rows past the end are computed
@@ -67,18 +66,35 @@ static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 
 #define LDS __attribute__((address_space(3)))
 
+// LDS serves 16 lanes x 16 bytes per clock (64 banks of 4 bytes), so the
+// rows one operand read touches must land on distinct 16-byte bank slots of
+// a 256-byte window.  K operand reads: 16 lanes read one chunk of 16
+// consecutive rows.  V transposing reads: 32 lanes read 4 consecutive rows x
+// 64 contiguous bytes.  Both swizzles permute the 16-byte chunks of a row.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = __bf16(lo);
   const __bf16 b = __bf16(hi);
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// Buffer resource over `rows` rows of `stride_bytes` starting at `base`:
-// loads at offsets past the last row return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows, int64_t stride_bytes) {
-  const int64_t n = rows > 0 ? int64_t(rows) * stride_bytes : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, int(n > 0x7fffffff ? 0x7fffffff : n),
-                                           0x00020000);
+// Buffer resource over min(rows, max_rows) rows of `stride_bytes` starting at
+// `base` (rows <= 0: none): loads past the last row return zeros.  32-bit
+// arithmetic (the host bounds max_rows * stride_bytes) and readfirstlane keep
+// it a branch-free scalar, so loads need no per-lane waterfall.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows, int max_rows,
+                                                            int stride_bytes) {
+  const int r = __builtin_amdgcn_readfirstlane(rows < 0 ? 0 : (rows > max_rows ? max_rows : rows));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane(r * stride_bytes), 0x00020000);
 }
 
 // The value held by lane ^ 32 (v_permlane32_swap exchanges the two halves).
@@ -138,7 +154,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Q as the B operand: lane holds query (qrow0 + l32), dims ks*16 + hi*8 .. +8.
   bf16x8 qb[KS];
   {
-    const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, sq * 2);
+    const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq) * 2);
     const int off = (l32 * int(sq) + hi * 8) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -158,13 +174,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int i = 0; i < NDMA; ++i) {
     const int s = (i * kWaves + wave) * 64 + lane;
     const int row = s / CH, pc = s % CH;
-    koff[i] = row * int(sk) * 2 + ((pc ^ (row & 7)) * 16);
-    voff[i] = row * int(sv) * 2 + ((pc ^ (2 * (row & 3))) * 16);
+    koff[i] = row * int(sk) * 2 + ((pc ^ k_swz<D>(row)) * 16);
+    voff[i] = row * int(sv) * 2 + ((pc ^ v_swz<D>(row)) * 16);
   }
   // K operand reads: row l32 (+32 kb), logical chunk 2 ks + hi.
   int kaddr[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ (l32 & 7)) * 16);
+  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ k_swz<D>(l32)) * 16);
   // V^T operand reads (transposing): 16-lane group g reads keys
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
@@ -175,7 +191,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int lc = db * 4 + 2 * (g & 1) + ((m & 3) >> 1);
-      vaddr[db] = row * ROWB + ((lc ^ (2 * (row & 3))) * 16) + 8 * (m & 1);
+      vaddr[db] = row * ROWB + ((lc ^ v_swz<D>(row)) * 16) + 8 * (m & 1);
     }
   }
 
@@ -186,7 +202,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // ---- building blocks ------------------------------------------------------
   auto load_k = [&](int t, auto slot) {
     const int key0 = t * kBN;
-    const auto r = rows_rsrc(kbase + int64_t(key0) * sk, it.seg_len - key0, sk * 2);
+    const auto r = rows_rsrc(kbase + int64_t(key0) * sk, it.seg_len - key0, kBN, int(sk) * 2);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
@@ -194,7 +210,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   auto load_v = [&](int t, auto slot) {
     const int key0 = t * kBN;
-    const auto r = rows_rsrc(vbase + int64_t(key0) * sv, it.seg_len - key0, sv * 2);
+    const auto r = rows_rsrc(vbase + int64_t(key0) * sv, it.seg_len - key0, kBN, int(sv) * 2);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
@@ -213,14 +229,15 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   };
   // Keys at or past `kvalid` in the tile get -inf.
+  // (The lane's key offset hi*4 is folded into one bound, so every compare
+  // is against a constant.)
   auto mask = [&](f32x16* sacc, int kvalid) {
+    const int lim = kvalid - hi * 4;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        if (key >= kvalid) sacc[kb][r] = -__builtin_inff();
-      }
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) sacc[kb][r] = -__builtin_inff();
   };
   // Tile max; the reference max m_run only moves when a query's tile max
   // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
@@ -313,12 +330,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     constexpr int P = decltype(par)::value;
     load_k(t + 2, IC<P>{});
     load_v(t + 1, IC<P ^ 1>{});
-    if (active) {
-      probs(s, pb);
-      qk(IC<P ^ 1>{}, s);
-      pv(IC<P>{}, pb);
-      update_max(s);
-    }
+    // Every wave computes here, also one whose rows all lie past the segment
+    // end (rare: last query tile only; its rows are not stored), so the loads
+    // and the MFMA/softmax work form one block the scheduler can interleave.
+    probs(s, pb);
+    qk(IC<P ^ 1>{}, s);
+    pv(IC<P>{}, pb);
+    update_max(s);
     publish();
   };
   int t = 0;

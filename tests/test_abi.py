@@ -133,6 +133,7 @@ def attn(dtype=h3a.H3A_BF16, S=300, H=2, D=128, cu=(0, 100, 300), strides=None, 
     (dict(o=P + 512), h3a.H3A_EINVAL, "o overlaps q"),
     (dict(o=P + (2 << 24) - 256), h3a.H3A_EINVAL, "o overlaps v"),
     (dict(H=0), h3a.H3A_EINVAL, "H ="),
+    (dict(strides=(256, 256, 1 << 24, 256)), h3a.H3A_EUNSUPPORTED, "v: token stride"),
 ])
 def test_varlen_attn_rejects(kw, status, word):
     assert attn(**kw) == status

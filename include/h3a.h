@@ -87,6 +87,57 @@ h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int
                                 hipStream_t stream);
 
 /*
+ * Other ways of filling the same rotary table.  Only the angles change; the
+ * table layout, the rotate-half that consumes it and every other argument
+ * are as for h3a_build_rope_table.
+ *
+ * For a token with grid index i_a and segment extent n_a on axis a (n_t = T,
+ * n_h = H, n_w = W), the fp64 coordinate p_a is
+ *   H3A_ROPE_GRID         i_a (exactly h3a_build_rope_table);
+ *   H3A_ROPE_LINSPACE     i_a * step_a + start[a], step_a = (stop[a] -
+ *                         start[a]) / n_a -- numpy.linspace(start, stop, n_a,
+ *                         endpoint=False), whose evaluation order the DiT's
+ *                         fp64 grid follows bit for bit (vllm.cpp PR #26
+ *                         description, "Correctness gates");
+ *   H3A_ROPE_NORMALIZED   2 pi (2 ((i_a + 0.5) / n_a) - 1), the ViT3D
+ *                         decoder's length-normalised ids; L may exceed
+ *                         T*H*W, and tokens past the grid (its register and
+ *                         cls suffix) get angle 0, the identity (video-VAE
+ *                         decoder commit, "3D ROPE DETAIL");
+ *   H3A_ROPE_INTERLEAVED  i_a, with M-RoPE's interleaved layout (encoder-tower
+ *                         commit, "M-RoPE": axes [t h w t h w ...]).
+ * GRID, LINSPACE and NORMALIZED use per-axis blocks: angle vector
+ * concat(p_t f_t, p_h f_h, p_w f_w) with f_a[j] = base^(-2j/axis_dims[a]).
+ * INTERLEAVED uses one ladder F[j] = base^(-2j/R), j < R/2, where angle j
+ * takes axis h if j % 3 == 1 and j < 3 n_h, axis w if j % 3 == 2 and
+ * j < 3 n_w, else t (n_a = axis_dims[a] / 2); the shares must come out
+ * exactly (e.g. equal shares, or Qwen-style (48, 40, 40) for R = 128).
+ *
+ * spec           host pointer, read during the call only.
+ * Errors: as h3a_build_rope_table, plus EINVAL for a null spec, an unknown
+ * mode, non-finite start/stop, shares that do not interleave, or T*H*W
+ * above INT32_MAX.
+ */
+typedef enum h3a_rope_mode {
+  H3A_ROPE_GRID = 0,
+  H3A_ROPE_LINSPACE = 1,
+  H3A_ROPE_NORMALIZED = 2,
+  H3A_ROPE_INTERLEAVED = 3
+} h3a_rope_mode;
+
+typedef struct h3a_rope_spec {
+  int32_t mode;          /* h3a_rope_mode */
+  int32_t axis_dims[3];  /* rotated dims owned by the t, h, w axes; each even */
+  double base;           /* frequency base (> 0) */
+  double start[3];       /* H3A_ROPE_LINSPACE only: per-axis start */
+  double stop[3];        /* H3A_ROPE_LINSPACE only: per-axis stop (excluded) */
+} h3a_rope_spec;
+
+h3a_status h3a_build_rope_table_ex(const int32_t* segments, int32_t nseg, const h3a_rope_spec* spec,
+                                   float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
+                                   hipStream_t stream);
+
+/*
  * Fused per-head RMSNorm + NeoX rotary of Q and K.
  *
  * For every token n, head h and x in {q, k} (each with its own gain g):

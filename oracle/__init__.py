@@ -19,6 +19,8 @@ sqrt are the only library primitives used):
    (W2b)": the H3 3D MM-RoPE is plain NeoX rotate-half and only the angles,
    three axes off the fp64 grid, are unusual; encoder-tower commit: the cache
    is cat(freqs, freqs), so cos/sin repeat over the two halves.]
+   Three more table modes (fp64 linspace grid, the ViT3D length-normalised
+   ids, interleaved M-RoPE) change only the angles; section 2b states each.
 3. Per-head RMSNorm: y = x / sqrt(mean_d x_d^2 + eps) * gamma.
    [h3-spark model card, "What this config does": Q RMSNorm then rot96 RoPE.]
 4. NeoX rotary on the first R dims: pairs (i, i + R/2) for i < R/2 rotate by
@@ -92,6 +94,108 @@ def rope_angles(positions: np.ndarray, rot_dims, base: float) -> np.ndarray:
 def rope_table(segments, rot_dims, base: float):
     """(cu_seqlens, cos, sin) with cos/sin fp64 [S, R/2]."""
     theta = rope_angles(segment_positions(segments), rot_dims, base)
+    return cu_seqlens(segments), np.cos(theta), np.sin(theta)
+
+
+# ----------------------------------------------------------------------------
+# 2b. Other rotary table modes
+#
+# Besides the integer grid above, the pages name three other ways the same
+# per-row cos/sin cache gets its angles:
+#   LINSPACE     fp64 positions from numpy.linspace(start, stop, n,
+#                endpoint=False), i.e. i * step + start with
+#                step = (stop - start) / n, in that order  [PR #26
+#                description, "Correctness gates": the fp64 grid feeding the
+#                rotary is gated bit-exact and follows linspace's order].
+#   NORMALIZED   the ViT3D decoder's length-normalised ids: (i + 0.5) / n
+#                mapped into [-1, 1), times 2 pi, per-axis frequency blocks
+#                concatenated; suffix tokens (registers, cls) carry id 0, an
+#                identity rotation  [video-VAE decoder commit, "3D ROPE
+#                DETAIL"; pipeline commit on tiling: 2 ((i + 0.5) / n) - 1].
+#   INTERLEAVED  M-RoPE: the three axes interleaved [t h w t h w ...] over one
+#                frequency ladder, cos/sin repeated over the two halves
+#                [encoder-tower commit, "M-RoPE"].
+# Readings where the pages stop short: NORMALIZED uses the per-axis
+# frequencies base ** (-2 j / d_a) of the grid mode; INTERLEAVED uses the
+# global ladder base ** (-2 j / R) and, for unequal axis shares, interleaves
+# while the h and w shares last (entry j is h if j % 3 == 1 and j < 3 n_h, w
+# if j % 3 == 2 and j < 3 n_w, t otherwise, n_a = d_a / 2); LINSPACE takes
+# per-axis (start, stop) shared by all segments, n = the segment's extent on
+# that axis.
+# ----------------------------------------------------------------------------
+
+ROPE_GRID, ROPE_LINSPACE, ROPE_NORMALIZED, ROPE_INTERLEAVED = 0, 1, 2, 3
+
+
+def _grid_indices(segments, allow_suffix: bool):
+    """Integer (t, h, w) indices [S, 3], segment extents (T, H, W) [S, 3] and
+    an in-grid flag [S] (False for suffix tokens past T*H*W)."""
+    idx, ext, inside = [], [], []
+    for (T, H, W, L) in segments:
+        T, H, W, L = int(T), int(H), int(W), int(L)
+        n_grid = T * H * W
+        if L > n_grid and not allow_suffix:
+            raise ValueError(f"segment length {L} exceeds its grid {T}x{H}x{W}")
+        n = np.arange(L, dtype=np.int64)
+        g = np.minimum(n, max(n_grid - 1, 0))
+        idx.append(np.where((n < n_grid)[:, None], np.stack([g // (H * W), (g // W) % H, g % W], axis=1), 0))
+        ext.append(np.broadcast_to(np.array([T, H, W], dtype=np.int64), (L, 3)))
+        inside.append(n < n_grid)
+    if not idx:
+        return np.zeros((0, 3), np.int64), np.zeros((0, 3), np.int64), np.zeros(0, bool)
+    return np.concatenate(idx), np.concatenate(ext), np.concatenate(inside)
+
+
+def linspace_positions(segments, start, stop) -> np.ndarray:
+    """fp64 [S, 3]: along axis a, index i of an extent-n axis sits at
+    i * ((stop[a] - start[a]) / n) + start[a]."""
+    idx, ext, _ = _grid_indices(segments, allow_suffix=False)
+    start = np.asarray(start, dtype=np.float64)
+    stop = np.asarray(stop, dtype=np.float64)
+    step = (stop[None, :] - start[None, :]) / ext.astype(np.float64)
+    return idx.astype(np.float64) * step + start[None, :]
+
+
+def normalized_positions(segments):
+    """(fp64 [S, 3] of 2 ((i + 0.5) / n) - 1 per axis, in-grid flag [S])."""
+    idx, ext, inside = _grid_indices(segments, allow_suffix=True)
+    p = ((idx.astype(np.float64) + 0.5) / ext.astype(np.float64)) * 2.0 - 1.0
+    return p, inside
+
+
+def interleaved_axes(rot_dims) -> np.ndarray:
+    """Axis (0 t, 1 h, 2 w) of each of the R/2 angles of the interleaved layout."""
+    n_t, n_h, n_w = (int(d) // 2 for d in rot_dims)
+    half = n_t + n_h + n_w
+    ax = np.zeros(half, dtype=np.int64)
+    for j in range(half):
+        if j % 3 == 1 and j < 3 * n_h:
+            ax[j] = 1
+        elif j % 3 == 2 and j < 3 * n_w:
+            ax[j] = 2
+    return ax
+
+
+def rope_table_mode(segments, mode: int, rot_dims, base: float, start=None, stop=None):
+    """(cu_seqlens, cos, sin) fp64 [S, R/2] for any of the four table modes."""
+    if mode == ROPE_GRID:
+        return rope_table(segments, rot_dims, base)
+    if mode == ROPE_LINSPACE:
+        theta = rope_angles(linspace_positions(segments, start, stop), rot_dims, base)
+    elif mode == ROPE_NORMALIZED:
+        p, inside = normalized_positions(segments)
+        theta = rope_angles(p * (2.0 * np.pi), rot_dims, base)
+        theta[~inside] = 0.0
+    elif mode == ROPE_INTERLEAVED:
+        pos = segment_positions(segments).astype(np.float64)
+        R = int(sum(rot_dims))
+        ax = interleaved_axes(rot_dims)
+        if [int(np.sum(ax == a)) for a in range(3)] != [int(d) // 2 for d in rot_dims]:
+            raise ValueError(f"axis shares {tuple(rot_dims)} cannot be interleaved t, h, w")
+        f = axis_inverse_frequencies(R, base)
+        theta = pos[:, ax] * f[None, :]
+    else:
+        raise ValueError(f"unknown rotary table mode {mode}")
     return cu_seqlens(segments), np.cos(theta), np.sin(theta)
 
 

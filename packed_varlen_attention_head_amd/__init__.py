@@ -27,8 +27,11 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "EUNSUPPORTED
 # Query rows per attention work item (must match the kernels).
 BLOCK_M = {H3A_BF16: 128, H3A_F32: 64}
 
+H3A_ROPE_GRID, H3A_ROPE_LINSPACE, H3A_ROPE_NORMALIZED, H3A_ROPE_INTERLEAVED = range(4)
+
 EXPORTS = (
     "h3a_build_rope_table",
+    "h3a_build_rope_table_ex",
     "h3a_qk_rmsnorm_rope",
     "h3a_varlen_attn_fwd",
     "h3a_plan_tiles",
@@ -47,6 +50,12 @@ class H3AError(RuntimeError):
 
 class H3ALibraryMissing(ImportError):
     pass
+
+
+class RopeSpec(ctypes.Structure):
+    """h3a_rope_spec: table mode, per-axis rotated dims, base, linspace start/stop."""
+    _fields_ = [("mode", ctypes.c_int32), ("axis_dims", ctypes.c_int32 * 3), ("base", ctypes.c_double),
+                ("start", ctypes.c_double * 3), ("stop", ctypes.c_double * 3)]
 
 
 _lib = None
@@ -68,12 +77,13 @@ def lib() -> ctypes.CDLL:
             "(there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     L.h3a_build_rope_table.argtypes = [_c_i32p, _i32, _c_i32p, _f64, _vp, _i64, _c_i32p, _vp]
+    L.h3a_build_rope_table_ex.argtypes = [_c_i32p, _i32, ctypes.POINTER(RopeSpec), _vp, _i64, _c_i32p, _vp]
     L.h3a_qk_rmsnorm_rope.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_plan_tiles.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
-    for name in ("h3a_build_rope_table", "h3a_qk_rmsnorm_rope", "h3a_varlen_attn_fwd", "h3a_plan_tiles"):
+    for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_varlen_attn_fwd", "h3a_plan_tiles"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
     L.h3a_last_error.argtypes = []
@@ -156,6 +166,30 @@ def build_rope_table(segments, axis_dims, base: float, cos_sin, stream=None) -> 
     ptr = cos_sin.data_ptr() if cos_sin is not None else None
     _check(lib().h3a_build_rope_table(_ptr_i32(segs), len(segs), _ptr_i32(dims), float(base), ptr, S,
                                       _ptr_i32(cu), _stream_handle(stream)))
+    return cu
+
+
+def rope_spec(mode: int, axis_dims, base: float, start=(0.0, 0.0, 0.0), stop=(0.0, 0.0, 0.0)) -> RopeSpec:
+    spec = RopeSpec()
+    spec.mode = int(mode)
+    for a in range(3):
+        spec.axis_dims[a] = int(axis_dims[a])
+        spec.start[a] = float(start[a])
+        spec.stop[a] = float(stop[a])
+    spec.base = float(base)
+    return spec
+
+
+def build_rope_table_ex(segments, mode: int, axis_dims, base: float, cos_sin, start=(0.0, 0.0, 0.0),
+                        stop=(0.0, 0.0, 0.0), stream=None) -> np.ndarray:
+    """Fill ``cos_sin`` in table mode ``mode`` (H3A_ROPE_*); returns cu_seqlens."""
+    segs = _i32_array(segments).reshape(-1, 4)
+    S = int(segs[:, 3].sum()) if len(segs) else 0
+    cu = np.zeros(len(segs) + 1, dtype=np.int32)
+    spec = rope_spec(mode, axis_dims, base, start, stop)
+    ptr = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_build_rope_table_ex(_ptr_i32(segs), len(segs), ctypes.byref(spec), ptr, S, _ptr_i32(cu),
+                                         _stream_handle(stream)))
     return cu
 
 

@@ -205,12 +205,15 @@ void h3a_release_caches(void) {
   pc.order.clear();
 }
 
-h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int32_t* axis_dims,
-                                double base, float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
-                                hipStream_t stream) {
+h3a_status h3a_build_rope_table_ex(const int32_t* segments, int32_t nseg, const h3a_rope_spec* spec,
+                                   float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
+                                   hipStream_t stream) {
   if (segments == nullptr) return fail(H3A_EINVAL, "segments is NULL");
   if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
-  if (axis_dims == nullptr) return fail(H3A_EINVAL, "axis_dims is NULL");
+  if (spec == nullptr) return fail(H3A_EINVAL, "spec is NULL");
+  const int32_t mode = spec->mode;
+  if (mode < H3A_ROPE_GRID || mode > H3A_ROPE_INTERLEAVED) return fail(H3A_EINVAL, "unknown rotary table mode %d", mode);
+  const int32_t* axis_dims = spec->axis_dims;
   int64_t R = 0;
   for (int a = 0; a < 3; ++a) {
     if (axis_dims[a] < 0 || axis_dims[a] % 2 != 0)
@@ -218,14 +221,22 @@ h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int
     R += axis_dims[a];
   }
   if (R > 128) return fail(H3A_EUNSUPPORTED, "rotated dims %lld > 128", (long long)R);
+  const double base = spec->base;
   if (!(base > 0.0) || !std::isfinite(base)) return fail(H3A_EINVAL, "base = %g must be finite and > 0", base);
+  if (mode == H3A_ROPE_LINSPACE)
+    for (int a = 0; a < 3; ++a)
+      if (!std::isfinite(spec->start[a]) || !std::isfinite(spec->stop[a]))
+        return fail(H3A_EINVAL, "linspace start/stop of axis %d must be finite", a);
   int64_t total = 0;
   for (int32_t s = 0; s < nseg; ++s) {
     const int32_t* g = segments + 4 * int64_t(s);
     if (g[0] < 1 || g[1] < 1 || g[2] < 1)
       return fail(H3A_EINVAL, "segment %d grid (%d, %d, %d) must be >= 1 on every axis", s, g[0], g[1], g[2]);
     const int64_t cap = int64_t(g[0]) * g[1] * g[2];
-    if (g[3] < 0 || int64_t(g[3]) > cap)
+    if (cap > int64_t(INT32_MAX))
+      return fail(H3A_EINVAL, "segment %d grid %d x %d x %d exceeds INT32_MAX tokens", s, g[0], g[1], g[2]);
+    if (g[3] < 0) return fail(H3A_EINVAL, "segment %d length %d is negative", s, g[3]);
+    if (mode != H3A_ROPE_NORMALIZED && int64_t(g[3]) > cap)
       return fail(H3A_EINVAL, "segment %d length %d outside [0, T*H*W = %lld]", s, g[3], (long long)cap);
     total += g[3];
   }
@@ -241,18 +252,54 @@ h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int
   const int32_t half = int32_t(R / 2);
   std::vector<double> inv_freq;
   std::vector<int32_t> axis_of;
-  for (int a = 0; a < 3; ++a)
-    for (int32_t j = 0; j < axis_dims[a] / 2; ++j) {
-      inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(axis_dims[a])));
+  if (mode == H3A_ROPE_INTERLEAVED) {
+    // One ladder base^(-2j/R); angle j takes h while j % 3 == 1 and the h
+    // share lasts, w likewise for j % 3 == 2, t otherwise.
+    const int32_t n_h = axis_dims[1] / 2, n_w = axis_dims[2] / 2;
+    int32_t count[3] = {0, 0, 0};
+    for (int32_t j = 0; j < half; ++j) {
+      const int32_t a = (j % 3 == 1 && j < 3 * n_h) ? 1 : ((j % 3 == 2 && j < 3 * n_w) ? 2 : 0);
       axis_of.push_back(a);
+      ++count[a];
+      inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(R)));
     }
+    for (int a = 0; a < 3; ++a)
+      if (count[a] != axis_dims[a] / 2)
+        return fail(H3A_EINVAL, "axis_dims (%d, %d, %d) cannot be interleaved t, h, w", axis_dims[0],
+                    axis_dims[1], axis_dims[2]);
+  } else {
+    for (int a = 0; a < 3; ++a)
+      for (int32_t j = 0; j < axis_dims[a] / 2; ++j) {
+        inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(axis_dims[a])));
+        axis_of.push_back(a);
+      }
+  }
   if (half > 0 && S > 0) {
-    hipError_t e = h3a::launch_rope_table(segments, starts.data(), nseg, inv_freq.data(), axis_of.data(),
-                                          half, cos_sin, S, stream);
+    h3a::RopeTableSpec ts{};
+    ts.mode = mode;
+    ts.half = half;
+    ts.inv_freq = inv_freq.data();
+    ts.axis_of = axis_of.data();
+    for (int a = 0; a < 3; ++a) {
+      ts.lin_start[a] = mode == H3A_ROPE_LINSPACE ? spec->start[a] : 0.0;
+      ts.lin_stop[a] = mode == H3A_ROPE_LINSPACE ? spec->stop[a] : 0.0;
+    }
+    hipError_t e = h3a::launch_rope_table(ts, segments, starts.data(), nseg, cos_sin, S, stream);
     if (e != hipSuccess) return fail_hip("rope table launch", e);
   }
   if (cu_seqlens_out != nullptr) std::memcpy(cu_seqlens_out, starts.data(), starts.size() * sizeof(int32_t));
   return H3A_OK;
+}
+
+h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int32_t* axis_dims,
+                                double base, float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
+                                hipStream_t stream) {
+  if (axis_dims == nullptr) return fail(H3A_EINVAL, "axis_dims is NULL");
+  h3a_rope_spec spec{};
+  spec.mode = H3A_ROPE_GRID;
+  for (int a = 0; a < 3; ++a) spec.axis_dims[a] = axis_dims[a];
+  spec.base = base;
+  return h3a_build_rope_table_ex(segments, nseg, &spec, cos_sin, S, cu_seqlens_out, stream);
 }
 
 h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,

@@ -29,9 +29,22 @@ std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads,
 
 // ---- kernel launchers (one per .hip file) ---------------------------------
 
-hipError_t launch_rope_table(const int32_t* segments, const int32_t* starts, int32_t nseg,
-                             const double* inv_freq, const int32_t* axis_of, int32_t half,
-                             float* cos_sin, int64_t S, hipStream_t stream);
+// Rotary table modes (values of h3a_rope_mode).
+constexpr int32_t kRopeGrid = 0, kRopeLinspace = 1, kRopeNormalized = 2, kRopeInterleaved = 3;
+
+// Angle j of a token = p_axis_of[j] * inv_freq[j]; the mode says how the
+// coordinate p comes from the grid index (see rope_table.hip).
+struct RopeTableSpec {
+  int32_t mode;
+  int32_t half;             // R / 2 angles per token (<= 64)
+  const double* inv_freq;   // [half]
+  const int32_t* axis_of;   // [half], 0 = t, 1 = h, 2 = w
+  double lin_start[3];      // linspace mode only
+  double lin_stop[3];
+};
+
+hipError_t launch_rope_table(const RopeTableSpec& spec, const int32_t* segments, const int32_t* starts,
+                             int32_t nseg, float* cos_sin, int64_t S, hipStream_t stream);
 
 hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void* q_out, void* k_out,
                                   int64_t S, int32_t H, int32_t D, int64_t sq, int64_t sk,

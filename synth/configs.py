@@ -34,6 +34,9 @@ class Workload:
     seed: int = 0
     gamma_mean: float = 1.0
     gamma_std: float = 0.1
+    rope_mode: int = 0  # 0 grid, 1 linspace, 2 length-normalised, 3 interleaved (h3a_rope_mode)
+    lin_start: tuple = (0.0, 0.0, 0.0)
+    lin_stop: tuple = (0.0, 0.0, 0.0)
     note: str = field(default="", compare=False)
 
     @property
@@ -120,6 +123,35 @@ RAGGED64 = Workload(
 )
 
 ALL = {w.name: w for w in (TINY_F32, TWO_SEG, H3_S20423, H3_S25103, RAGGED64)}
+
+# Other attention workloads of the same model family (parity cases of the
+# other rotary table modes).  The video VAE's ViT3D decoder: 32 heads of 64,
+# rotary on 0.75 of the head dim with theta 100 from length-normalised ids,
+# q/k RMSNorm without a gain (video-VAE decoder commit), run per 16x16 latent
+# tile (pipeline commit on tiling); three tiles of 4 latent frames are packed
+# as segments, each followed by a suffix of 4 register tokens and a cls token
+# (the suffix size is not given on the pages: 5 is this workload's choice).
+VIT3D_TILES = Workload(
+    name="vit3d_tiles_bf16",
+    segments=((4, 16, 16, 1024 + 5),) * 3,
+    heads=32, head_dim=64, rot_dims=(16, 16, 16), dtype="bf16", base=100.0,
+    gamma_std=0.0, rope_mode=2,
+    note="3 ViT3D tiles of 4x16x16 latents + 5 suffix tokens; 32 heads x 64; normalised ids",
+)
+
+# A packed prompt with M-RoPE's interleaved angles (three images as
+# (1, h, w) grids and a text run along t), 16 heads of 128, all 128 dims
+# rotated with Qwen-style shares (48, 40, 40) (encoder-tower commit,
+# "M-RoPE"); attention per segment as everywhere here.
+MROPE_PACKED = Workload(
+    name="mrope_packed_bf16",
+    segments=((1, 24, 36, 864), (1, 20, 30, 600), (1, 16, 16, 256), (300, 1, 1, 300)),
+    heads=16, head_dim=128, rot_dims=(48, 40, 40), dtype="bf16", base=1000000.0,
+    rope_mode=3,
+    note="3 images + 300 text tokens, interleaved M-RoPE over all 128 dims",
+)
+
+MODE_WORKLOADS = {w.name: w for w in (VIT3D_TILES, MROPE_PACKED)}
 
 # The configuration the headline throughput is quoted on.
 HEADLINE = H3_S20423

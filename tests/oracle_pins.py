@@ -86,6 +86,102 @@ def check_angle_layout(O):
 
 
 # ---------------------------------------------------------------------------
+# other rotary table modes
+# ---------------------------------------------------------------------------
+
+def check_linspace_matches_numpy(O):
+    """Positions along each axis are numpy.linspace(start, stop, n, endpoint=False), bit for bit."""
+    segs = [(3, 2, 5, 30), (7, 1, 16, 100), (1, 9, 1, 9), (5, 3, 3, 44)]
+    start, stop = (0.25, -1.0, 0.0), (3.0, 1.0, 1.0 / 3.0)
+    p = O.linspace_positions(segs, start, stop)
+    cu = O.cu_seqlens(segs)
+    for s, (T, H, W, L) in enumerate(segs):
+        rows = p[cu[s]:cu[s + 1]]
+        ext = (T, H, W)
+        n = np.arange(L)
+        idx = (n // (H * W), (n // W) % H, n % W)
+        for a in range(3):
+            ref = np.linspace(start[a], stop[a], ext[a], endpoint=False)
+            assert np.array_equal(rows[:, a], ref[idx[a]]), (s, a)
+
+
+def check_linspace_reduces_to_grid(O):
+    """start 0 and stop = the extent give the integer grid: the same table bit for bit."""
+    seg = [(4, 6, 10, 200)]
+    dims = (32, 32, 32)
+    _, c0, s0 = O.rope_table(seg, dims, 10000.0)
+    _, c1, s1 = O.rope_table_mode(seg, O.ROPE_LINSPACE, dims, 10000.0, start=(0, 0, 0), stop=(4, 6, 10))
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    # and a shifted, stretched grid is that affine map of the integers
+    p = O.linspace_positions(seg, (1.0, 2.0, -3.0), (9.0, 14.0, 17.0))
+    ip = O.segment_positions(seg)
+    assert np.allclose(p, ip * np.array([2.0, 2.0, 2.0]) + np.array([1.0, 2.0, -3.0]), rtol=0, atol=1e-13)
+
+
+def check_normalized_golden(O):
+    case = golden()["rope_normalized"][0]
+    _, c, s = O.rope_table_mode([case["segment"]], O.ROPE_NORMALIZED, case["rot_dims"], case["base"])
+    assert np.allclose(c, case["cos"], rtol=0, atol=1e-15), c
+    assert np.allclose(s, case["sin"], rtol=0, atol=1e-15), s
+
+
+def check_normalized_invariants(O):
+    """Ids lie in [-1, 1), mirror about the grid centre, and an extent-1 axis is the identity."""
+    segs = [(3, 8, 5, 120), (1, 1, 1, 1), (2, 16, 9, 288 + 5)]
+    p, inside = O.normalized_positions(segs)
+    assert np.all(p[inside] >= -1.0) and np.all(p[inside] < 1.0)
+    cu = O.cu_seqlens(segs)
+    for s, (T, H, W, L) in enumerate(segs):
+        rows = p[cu[s]:cu[s] + T * H * W].reshape(T, H, W, 3)
+        assert np.allclose(rows[::-1, :, :, 0], -rows[:, :, :, 0], rtol=0, atol=1e-15)
+        assert np.allclose(rows[:, ::-1, :, 1], -rows[:, :, :, 1], rtol=0, atol=1e-15)
+        assert np.allclose(rows[:, :, ::-1, 2], -rows[:, :, :, 2], rtol=0, atol=1e-15)
+    dims = (16, 16, 16)
+    _, c, sn = O.rope_table_mode(segs, O.ROPE_NORMALIZED, dims, 100.0)
+    assert np.all(c[120] == 1.0) and np.all(sn[120] == 0.0)  # the 1x1x1 segment
+    # suffix tokens: identity; grid tokens as without the suffix
+    _, c2, s2 = O.rope_table_mode([(2, 16, 9, 288)], O.ROPE_NORMALIZED, dims, 100.0)
+    assert np.array_equal(c[121:121 + 288], c2) and np.array_equal(sn[121:121 + 288], s2)
+    assert np.all(c[121 + 288:] == 1.0) and np.all(sn[121 + 288:] == 0.0)
+    # four evenly spaced ids: -3/4, -1/4, 1/4, 3/4
+    p4, _ = O.normalized_positions([(1, 1, 4, 4)])
+    assert np.array_equal(p4[:, 2], [-0.75, -0.25, 0.25, 0.75])
+
+
+def check_interleaved_golden(O):
+    g = golden()["rope_interleaved"]
+    case = g[0]
+    _, c, s = O.rope_table_mode([case["segment"]], O.ROPE_INTERLEAVED, case["rot_dims"], case["base"])
+    th = np.array(case["angles"])
+    assert np.allclose(c[case["token"]], np.cos(th), rtol=0, atol=1e-15)
+    assert np.allclose(s[case["token"]], np.sin(th), rtol=0, atol=1e-15)
+    assert np.array_equal(O.interleaved_axes(g[1]["rot_dims"]), g[1]["axes"])
+
+
+def check_interleaved_layout(O):
+    """A unit step along one axis moves exactly that axis's interleaved slots, and
+    equal coordinates on all three axes give plain 1-D rotary over R."""
+    R, base = 96, 10000.0
+    dims = (32, 32, 32)
+    ladder = [base ** (-2.0 * j / R) for j in range(48)]
+    segs = [(2, 2, 2, 8)]
+    _, c, s = O.rope_table_mode(segs, O.ROPE_INTERLEAVED, dims, base)
+    th = np.arctan2(s, c)
+    for axis, token in ((0, 4), (1, 2), (2, 1)):  # (1,0,0), (0,1,0), (0,0,1)
+        want = np.zeros(48)
+        want[axis::3] = ladder[axis::3]
+        assert np.allclose(th[token], want, rtol=1e-14, atol=0), axis
+    assert np.allclose(th[7], ladder, rtol=1e-14, atol=0)  # (1, 1, 1)
+    # shares that cannot be interleaved are rejected
+    try:
+        O.rope_table_mode(segs, O.ROPE_INTERLEAVED, (4, 8, 4), base)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("shares (4, 8, 4) accepted")
+
+
+# ---------------------------------------------------------------------------
 # RMSNorm
 # ---------------------------------------------------------------------------
 
@@ -379,6 +475,12 @@ ALL_CHECKS = [
     check_positions_enumeration,
     check_inverse_frequencies_closed_form,
     check_angle_layout,
+    check_linspace_matches_numpy,
+    check_linspace_reduces_to_grid,
+    check_normalized_golden,
+    check_normalized_invariants,
+    check_interleaved_golden,
+    check_interleaved_layout,
     check_rms_norm_golden,
     check_rms_norm_invariants,
     check_rope_golden,

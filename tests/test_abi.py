@@ -68,6 +68,33 @@ def test_rope_table_rejects(kw, status, word):
     assert np.all(cu == -7), "an invalid call wrote cu_seqlens_out"
 
 
+def rope_ex(segments, mode=h3a.H3A_ROPE_GRID, dims=(32, 32, 32), base=10000.0, start=(0, 0, 0), stop=(1, 1, 1),
+            table=P, spec=True):
+    segs, sp = i32(np.asarray(segments).reshape(-1))
+    S = int(sum(s[3] for s in segments))
+    sp_ = ctypes.byref(h3a.rope_spec(mode, dims, base, start, stop)) if spec else None
+    return h3a.lib().h3a_build_rope_table_ex(sp, len(segments), sp_, table, S, None, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(spec=False), h3a.H3A_EINVAL, "spec"),
+    (dict(mode=4), h3a.H3A_EINVAL, "mode"),
+    (dict(mode=-1), h3a.H3A_EINVAL, "mode"),
+    (dict(mode=h3a.H3A_ROPE_LINSPACE, stop=(1, float("inf"), 1)), h3a.H3A_EINVAL, "linspace"),
+    (dict(mode=h3a.H3A_ROPE_INTERLEAVED, dims=(4, 8, 4)), h3a.H3A_EINVAL, "interleaved"),
+    (dict(mode=h3a.H3A_ROPE_INTERLEAVED, dims=(8, 4, 4), base=-1.0), h3a.H3A_EINVAL, "base"),
+    (dict(mode=h3a.H3A_ROPE_LINSPACE, segments=[(1, 2, 2, 5)]), h3a.H3A_EINVAL, "length"),
+    (dict(mode=h3a.H3A_ROPE_INTERLEAVED, dims=(8, 4, 4), segments=[(1, 2, 2, 5)]), h3a.H3A_EINVAL, "length"),
+    (dict(mode=h3a.H3A_ROPE_NORMALIZED, segments=[(1, 2, 2, -1)]), h3a.H3A_EINVAL, "negative"),
+    (dict(mode=h3a.H3A_ROPE_NORMALIZED, segments=[(2000, 2000, 2000, 5)]), h3a.H3A_EINVAL, "INT32_MAX"),
+    (dict(mode=h3a.H3A_ROPE_NORMALIZED, segments=[(1, 2, 2, 6)], table=None), h3a.H3A_EINVAL, "cos_sin"),
+])
+def test_rope_table_ex_rejects(kw, status, word):
+    kw.setdefault("segments", [(1, 2, 2, 4)])
+    assert rope_ex(**kw) == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
 def qk(dtype=h3a.H3A_BF16, S=16, H=2, D=128, sq=None, sk=None, sqo=None, sko=None, q=P, k=P + (1 << 24),
        qo=None, ko=None, gq=P + (2 << 24), gk=P + (3 << 24), eps=1e-6, cs=P + (4 << 24), rot=96):
     hd = H * D

@@ -100,7 +100,58 @@ def _weights_unnormalised(q, k, cu, scale, seg, head):
     return 1.01 * oracle.attention_weights(q, k, cu, scale, seg, head)
 
 
+def _linspace_off_by_one(segments, start, stop):
+    p = oracle.linspace_positions(segments, start, stop)
+    step = (np.asarray(stop, float) - np.asarray(start, float))[None, :] / oracle._grid_indices(segments, False)[1]
+    return p + step
+
+
+def _linspace_other_order(segments, start, stop):
+    idx, ext, _ = oracle._grid_indices(segments, allow_suffix=False)
+    start = np.asarray(start, dtype=np.float64)
+    stop = np.asarray(stop, dtype=np.float64)
+    return idx * (stop - start)[None, :] / ext + start[None, :]
+
+
+def _normalized_no_half(segments):
+    idx, ext, inside = oracle._grid_indices(segments, allow_suffix=True)
+    return (idx / ext) * 2.0 - 1.0, inside
+
+
+def _mode_variant(kind):
+    def table(segments, mode, rot_dims, base, start=None, stop=None):
+        if mode == oracle.ROPE_NORMALIZED and kind in ("no_two_pi", "suffix_not_identity"):
+            p, inside = oracle.normalized_positions(segments)
+            th = oracle.rope_angles(p if kind == "no_two_pi" else p * 2 * np.pi, rot_dims, base)
+            if kind == "no_two_pi":
+                th[~inside] = 0.0
+            return oracle.cu_seqlens(segments), np.cos(th), np.sin(th)
+        if mode == oracle.ROPE_INTERLEAVED and kind in ("per_axis_ladder", "blockwise_axes"):
+            pos = oracle.segment_positions(segments).astype(np.float64)
+            if kind == "per_axis_ladder":
+                th = oracle.rope_angles(pos[:, :], rot_dims, base)[:, np.argsort(np.argsort(oracle.interleaved_axes(rot_dims), kind="stable"))]
+            else:
+                R = int(sum(rot_dims))
+                ax = np.concatenate([[a] * (int(d) // 2) for a, d in enumerate(rot_dims)])
+                th = pos[:, ax] * oracle.axis_inverse_frequencies(R, base)[None, :]
+            return oracle.cu_seqlens(segments), np.cos(th), np.sin(th)
+        return oracle.rope_table_mode(segments, mode, rot_dims, base, start, stop)
+    return table
+
+
+def _interleaved_axes_blockwise(rot_dims):
+    return np.concatenate([[a] * (int(d) // 2) for a, d in enumerate(rot_dims)]).astype(np.int64)
+
+
 MUTANTS = {
+    "linspace_off_by_one": dict(linspace_positions=_linspace_off_by_one),
+    "linspace_other_order": dict(linspace_positions=_linspace_other_order),
+    "normalized_no_half_offset": dict(normalized_positions=_normalized_no_half),
+    "normalized_no_two_pi": dict(rope_table_mode=_mode_variant("no_two_pi")),
+    "normalized_suffix_not_identity": dict(rope_table_mode=_mode_variant("suffix_not_identity")),
+    "interleaved_per_axis_ladder": dict(rope_table_mode=_mode_variant("per_axis_ladder")),
+    "interleaved_blockwise_axes": dict(rope_table_mode=_mode_variant("blockwise_axes")),
+    "interleaved_axes_blockwise": dict(interleaved_axes=_interleaved_axes_blockwise),
     "rope_sign_flipped": dict(rope_rotate=_rope_sign_flipped),
     "rope_interleaved_pairs": dict(rope_rotate=_rope_interleaved),
     "rope_dropped_cross_term": dict(rope_rotate=_rope_cos_only_on_first_half),

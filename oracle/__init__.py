@@ -31,6 +31,9 @@ sqrt are the only library primitives used):
    [PR #26 opening commit: the packed varlen non-causal attention is exactly a
    cu_seqlens varlen flash-attention call with a per-document bidirectional
    contract.]
+   The encoder text tower's causal grouped-query attention (query i of a
+   segment sees keys 0..i; K/V heads broadcast over their query groups) is
+   section 5b.
 
 Readings where the pages are silent (each is listed in the design doc):
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
@@ -309,6 +312,73 @@ def attention_weights(q, k, cu, scale: float, seg: int, head: int) -> np.ndarray
     qs = np.asarray(q[a:b, head], dtype=np.float64)
     ks = np.asarray(k[a:b, head], dtype=np.float64)
     return _softmax_rows(scale * (qs @ ks.T))
+
+
+# ----------------------------------------------------------------------------
+# 5b. Causal and grouped-query attention
+#
+# The encoder's text tower runs causal attention with grouped K/V heads: a
+# query head attends with the K/V head of its group, the K/V heads being
+# broadcast over their query groups (encoder-tower commit, "Causal GQA
+# attention"; the tower's layer: per-head q/k RMSNorm and interleaved M-RoPE,
+# then causal GQA).  Reading where the pages stop short: causality is per
+# packed segment with both ends aligned at the segment start (query i of a
+# segment sees keys 0..i of the same segment), and query head h uses K/V head
+# h // (Hq / Hkv).
+# ----------------------------------------------------------------------------
+
+
+def segment_head_attention_masked(q, k, v, scale: float, causal: bool, row_block: int = 2048):
+    """softmax(scale q k^T + mask) v for one segment and head; the mask is -inf
+    above the diagonal when causal (key j > query i), else empty."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((q.shape[0], v.shape[1]), dtype=np.float64)
+    for r0 in range(0, q.shape[0], row_block):
+        s = scale * (q[r0:r0 + row_block] @ k.T)
+        if causal:
+            i = np.arange(r0, r0 + s.shape[0])[:, None]
+            j = np.arange(k.shape[0])[None, :]
+            s = np.where(j > i, -np.inf, s)
+        out[r0:r0 + row_block] = _softmax_rows(s) @ v
+    return out
+
+
+def varlen_attention_gqa(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """o [S, Hq, Dv] for q [S, Hq, D] and k [S, Hkv, D], v [S, Hkv, Dv], Hkv | Hq;
+    query head h attends with K/V head h // (Hq // Hkv), per segment."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, Hkv = q.shape[1], np.asarray(k).shape[1]
+    if Hq % Hkv != 0:
+        raise ValueError(f"{Hkv} K/V heads do not divide {Hq} query heads")
+    group = Hq // Hkv
+    o = np.zeros(q.shape[:2] + (np.asarray(v).shape[2],), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        for h in range(Hq):
+            kh = h // group
+            o[a:b, h] = segment_head_attention_masked(q[a:b, h], k[a:b, kh], v[a:b, kh], scale, causal)
+    return o
+
+
+def varlen_attention_gqa_rows(q, k, v, cu, scale: float, rows, causal: bool = False) -> np.ndarray:
+    """Rows ``rows`` of varlen_attention_gqa (all query heads)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    group = Hq // Hkv
+    seg = segment_of_rows(cu, rows)
+    out = np.empty((len(rows), Hq, v.shape[2]), dtype=np.float64)
+    for n, r in enumerate(rows):
+        a, b = int(cu[seg[n]]), int(cu[seg[n] + 1])
+        end = r + 1 if causal else b
+        for h in range(Hq):
+            kh = h // group
+            qs = np.asarray(q[r:r + 1, h], dtype=np.float64)
+            out[n, h] = segment_head_attention_masked(qs, k[a:end, kh], v[a:end, kh], scale, False)[0]
+    return out
 
 
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):

@@ -424,6 +424,104 @@ def check_attention_rows_variant(O):
 
 
 # ---------------------------------------------------------------------------
+# causal and grouped-query attention
+# ---------------------------------------------------------------------------
+
+def check_causal_gqa_bruteforce(O):
+    """Scalar loops: query i of a segment sees keys 0..i; K/V head g serves the
+    query heads g * group .. g * group + group - 1."""
+    r = _rng(14)
+    lens = [9, 0, 1, 14, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S, Hkv, group, D = int(cu[-1]), 2, 3, 5
+    q = r.normal(size=(S, Hkv * group, D))
+    k = r.normal(size=(S, Hkv, D))
+    v = r.normal(size=(S, Hkv, 4))
+    scale = 0.45
+    for causal in (True, False):
+        o = O.varlen_attention_gqa(q, k, v, cu, scale, causal=causal)
+        ref = np.zeros((S, Hkv * group, 4))
+        for sgi in range(len(lens)):
+            a, b = int(cu[sgi]), int(cu[sgi + 1])
+            for g in range(Hkv):
+                for member in range(group):
+                    h = g * group + member
+                    for i in range(a, b):
+                        last = i if causal else b - 1
+                        num, den = np.zeros(4), 0.0
+                        for j in range(a, last + 1):
+                            w = math.exp(scale * sum(q[i, h, d] * k[j, g, d] for d in range(D)))
+                            num += w * v[j, g]
+                            den += w
+                        ref[i, h] = num / den
+        assert np.allclose(o, ref, rtol=1e-12, atol=1e-13), causal
+
+
+def check_causal_prefix_properties(O):
+    r = _rng(15)
+    lens = [33, 20]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = (r.normal(size=(53, 4, 8)) for _ in range(3))
+    o = O.varlen_attention_gqa(q, k, v, cu, 0.7, causal=True)
+    # the first query of a segment sees only its own key
+    assert np.array_equal(o[0], v[0]) and np.array_equal(o[33], v[33])
+    # a change at token 40 leaves every earlier row (and the other segment) bit-identical
+    for x in (q, k, v):
+        x2 = x.copy()
+        x2[40] += 2.0
+        args = [x2 if y is x else y for y in (q, k, v)]
+        o2 = O.varlen_attention_gqa(*args, cu, 0.7, causal=True)
+        assert np.array_equal(o2[:40], o[:40])
+        assert not np.array_equal(o2[40:53], o[40:53])
+    # the last query of a segment sees the whole segment: the bidirectional result
+    ob = O.varlen_attention_gqa(q, k, v, cu, 0.7, causal=False)
+    assert np.allclose(o[[32, 52]], ob[[32, 52]], rtol=1e-14, atol=1e-15)
+
+
+def check_gqa_is_repeated_kv(O):
+    """Grouped K/V heads equal plain multi-head attention on K/V repeated per group."""
+    r = _rng(16)
+    lens = [25, 40, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = r.normal(size=(66, 8, 16))
+    k, v = (r.normal(size=(66, 2, 16)) for _ in range(2))
+    o = O.varlen_attention_gqa(q, k, v, cu, 0.25)
+    ref = O.varlen_attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), cu, 0.25)
+    assert np.allclose(o, ref, rtol=1e-13, atol=1e-14)
+    # one K/V head per query head is the plain function
+    k8, v8 = (r.normal(size=(66, 8, 16)) for _ in range(2))
+    assert np.allclose(O.varlen_attention_gqa(q, k8, v8, cu, 0.25), O.varlen_attention(q, k8, v8, cu, 0.25),
+                       rtol=1e-14, atol=1e-15)
+
+
+def check_causal_gqa_sdpa(O):
+    """One segment: torch's scaled_dot_product_attention(is_causal, enable_gqa) in fp64 on the CPU."""
+    import torch
+
+    r = _rng(17)
+    L, Hq, Hkv, D = 70, 6, 2, 32
+    q = r.normal(size=(L, Hq, D))
+    k, v = (r.normal(size=(L, Hkv, D)) for _ in range(2))
+    o = O.varlen_attention_gqa(q, k, v, np.array([0, L]), 1.0 / math.sqrt(D), causal=True)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(1, 0, 2))) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True)
+    assert np.allclose(o, ref.numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def check_gqa_rows_variant(O):
+    r = _rng(18)
+    lens = [50, 1, 37]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = r.normal(size=(88, 4, 8))
+    k, v = (r.normal(size=(88, 1, 8)) for _ in range(2))
+    rows = np.array([0, 1, 49, 50, 51, 87, 60])
+    for causal in (False, True):
+        full = O.varlen_attention_gqa(q, k, v, cu, 0.3, causal=causal)
+        part = O.varlen_attention_gqa_rows(q, k, v, cu, 0.3, rows, causal=causal)
+        assert np.allclose(part, full[rows], rtol=1e-14, atol=1e-15), causal
+
+
+# ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
 
@@ -495,6 +593,11 @@ ALL_CHECKS = [
     check_attention_segment_isolation,
     check_attention_permutations,
     check_attention_rows_variant,
+    check_causal_gqa_bruteforce,
+    check_causal_prefix_properties,
+    check_gqa_is_repeated_kv,
+    check_causal_gqa_sdpa,
+    check_gqa_rows_variant,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

@@ -143,7 +143,60 @@ def _interleaved_axes_blockwise(rot_dims):
     return np.concatenate([[a] * (int(d) // 2) for a, d in enumerate(rot_dims)]).astype(np.int64)
 
 
+def _masked_diagonal_too(q, k, v, scale, causal, row_block=2048):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    s = scale * (q @ k.T)
+    if causal:
+        i = np.arange(s.shape[0])[:, None]
+        j = np.arange(s.shape[1])[None, :]
+        s = np.where(j >= i - 1, s, s)  # keeps j == i + 1: one key too many
+        s = np.where(j > i + 1, -np.inf, s)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)) @ v
+
+
+def _gqa_with(masked):
+    def f(q, k, v, cu, scale, causal=False):
+        Hq, Hkv = q.shape[1], k.shape[1]
+        o = np.zeros(q.shape[:2] + (v.shape[2],))
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            if b > a:
+                for h in range(Hq):
+                    g = h // (Hq // Hkv)
+                    o[a:b, h] = masked(q[a:b, h], k[a:b, g], v[a:b, g], scale, causal)
+        return o
+    return f
+
+
+def _gqa_modulo_heads(q, k, v, cu, scale, causal=False):
+    Hq, Hkv = q.shape[1], k.shape[1]
+    idx = np.arange(Hq) % Hkv
+    return oracle.varlen_attention(q, k[:, idx], v[:, idx], cu, scale) if not causal else \
+        oracle.varlen_attention_gqa(q, k[:, np.sort(idx)], v[:, np.sort(idx)], cu, scale, causal) * 1.0001
+
+
+def _gqa_causal_ignored(q, k, v, cu, scale, causal=False):
+    return oracle.varlen_attention_gqa(q, k, v, cu, scale, causal=False)
+
+
+def _gqa_rows_one_key_short(q, k, v, cu, scale, rows, causal=False):
+    rows = np.asarray(rows)
+    seg = oracle.segment_of_rows(cu, rows)
+    out = oracle.varlen_attention_gqa_rows(q, k, v, cu, scale, rows, causal)
+    if causal:
+        for n, r in enumerate(rows):
+            if r > cu[seg[n]]:
+                out[n] = oracle.varlen_attention_gqa_rows(q[:r], k[:r], v[:r], np.minimum(cu, r), scale,
+                                                           [r - 1], causal)[0]
+    return out
+
+
 MUTANTS = {
+    "causal_one_key_too_many": dict(varlen_attention_gqa=_gqa_with(_masked_diagonal_too)),
+    "gqa_modulo_heads": dict(varlen_attention_gqa=_gqa_modulo_heads),
+    "gqa_causal_ignored": dict(varlen_attention_gqa=_gqa_causal_ignored),
+    "gqa_rows_one_key_short": dict(varlen_attention_gqa_rows=_gqa_rows_one_key_short),
     "linspace_off_by_one": dict(linspace_positions=_linspace_off_by_one),
     "linspace_other_order": dict(linspace_positions=_linspace_other_order),
     "normalized_no_half_offset": dict(normalized_positions=_normalized_no_half),

@@ -168,6 +168,20 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
                                hipStream_t stream);
 
 /*
+ * h3a_qk_rmsnorm_rope with Hk K heads against Hq Q heads (the grouped K/V
+ * heads of causal GQA; encoder-tower commit: per-head q/k RMSNorm, then
+ * interleaved M-RoPE, then causal GQA).  q, q_out: [S, Hq, D]; k, k_out:
+ * [S, Hk, D]; everything else as for h3a_qk_rmsnorm_rope, which is this call
+ * with Hk = Hq.  Errors: as h3a_qk_rmsnorm_rope, plus EINVAL for Hk < 1.
+ */
+h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
+                                  h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hk, int32_t D,
+                                  int64_t stride_q, int64_t stride_k, int64_t stride_qo,
+                                  int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                                  float eps, const float* cos_sin, int32_t rot_dim,
+                                  hipStream_t stream);
+
+/*
  * Bidirectional attention restricted to each packed segment.
  *
  * For segment s = [cu[s], cu[s+1]) and head h, every query row i in s gets
@@ -199,6 +213,31 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                float scale, hipStream_t stream);
 
 /*
+ * Varlen attention with grouped K/V heads and an optional causal mask: the
+ * encoder text tower's causal GQA (vllm.cpp PR #26, encoder-tower commit,
+ * "Causal GQA attention": K/V heads are broadcast across their query group).
+ *
+ * q, o           device [S, Hq, D] of `dtype`, token strides stride_q/o.
+ * k, v           device [S, Hkv, D] of `dtype`, token strides stride_k/v
+ *                (>= Hkv*D).  Hkv >= 1 divides Hq; query head h attends
+ *                with K/V head h / (Hq / Hkv).
+ * causal         0: bidirectional within each segment (exactly
+ *                h3a_varlen_attn_fwd when Hkv == Hq).  1: query row i of a
+ *                segment sees the segment's keys 0..i (the mask is aligned at
+ *                the segment start).
+ * Everything else -- cu_seqlens, scale, numerics, supported shapes, plan
+ * cache -- as for h3a_varlen_attn_fwd.
+ *
+ * Errors: as h3a_varlen_attn_fwd, plus EINVAL (Hkv < 1, causal not 0/1) and
+ * ESHAPE (Hkv does not divide Hq).
+ */
+h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                                  h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                  int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
+                                  float scale, int32_t causal, hipStream_t stream);
+
+/*
  * The attention tile plan, on the host only (no GPU needed); for tests and
  * tooling.  Writes up to `cap` items of 4 int32 each -- (segment start,
  * segment length, first query row relative to the segment start, head); an
@@ -209,6 +248,12 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  */
 h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
                           int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items);
+
+/* h3a_plan_tiles for the causal variant (causal = 1: an item costs the keys
+ * up to its last row, and each chunk of one segment and head lists its
+ * query tiles last to first).  causal = 0 is h3a_plan_tiles. */
+h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
+                             int32_t n_xcd, int32_t causal, int32_t* items, int64_t cap, int64_t* n_items);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* h3a_last_error(void);

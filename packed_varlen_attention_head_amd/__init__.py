@@ -33,8 +33,11 @@ EXPORTS = (
     "h3a_build_rope_table",
     "h3a_build_rope_table_ex",
     "h3a_qk_rmsnorm_rope",
+    "h3a_qk_rmsnorm_rope_ex",
     "h3a_varlen_attn_fwd",
+    "h3a_varlen_attn_fwd_ex",
     "h3a_plan_tiles",
+    "h3a_plan_tiles_ex",
     "h3a_last_error",
     "h3a_release_caches",
     "h3a_version",
@@ -80,10 +83,17 @@ def lib() -> ctypes.CDLL:
     L.h3a_build_rope_table_ex.argtypes = [_c_i32p, _i32, ctypes.POINTER(RopeSpec), _vp, _i64, _c_i32p, _vp]
     L.h3a_qk_rmsnorm_rope.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _vp, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_qk_rmsnorm_rope_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
+                                         _i64, _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
+    L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
+                                         _i64, _c_i32p, _i32, _f32, _i32, _vp]
     L.h3a_plan_tiles.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
-    for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_varlen_attn_fwd", "h3a_plan_tiles"):
+    L.h3a_plan_tiles_ex.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
+    for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
+                 "h3a_varlen_attn_fwd",
+                 "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
     L.h3a_last_error.argtypes = []
@@ -195,21 +205,26 @@ def build_rope_table_ex(segments, mode: int, axis_dims, base: float, cos_sin, st
 
 def qk_rmsnorm_rope(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q_out=None, k_out=None,
                     stream=None):
-    """RMSNorm + NeoX rotary of q and k; in place unless q_out / k_out are given."""
+    """RMSNorm + NeoX rotary of q and k; in place unless q_out / k_out are given.
+
+    k may have fewer heads than q (grouped K/V heads); then the _ex entry runs."""
     q_out = q if q_out is None else q_out
     k_out = k if k_out is None else k_out
     S, H, D, sq = _token_major("q", q)
-    _, _, _, sk = _token_major("k", k)
+    _, Hk, _, sk = _token_major("k", k)
     _, _, _, sqo = _token_major("q_out", q_out)
     _, _, _, sko = _token_major("k_out", k_out)
-    for name, t in (("k", k), ("q_out", q_out), ("k_out", k_out)):
-        if tuple(t.shape) != (S, H, D) or t.dtype != q.dtype:
-            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from q")
+    for name, t, h in (("k", k, Hk), ("q_out", q_out, H), ("k_out", k_out, Hk)):
+        if tuple(t.shape) != (S, h, D) or t.dtype != q.dtype:
+            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} does not match q")
     cs = cos_sin.data_ptr() if cos_sin is not None else None
-    _check(lib().h3a_qk_rmsnorm_rope(q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
-                                     _dtype_code(q), S, H, D, sq, sk, sqo, sko, gamma_q.data_ptr(),
-                                     gamma_k.data_ptr(), float(eps), cs, int(rot_dim),
-                                     _stream_handle(stream)))
+    args = (q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _dtype_code(q), S)
+    rest = (D, sq, sk, sqo, sko, gamma_q.data_ptr(), gamma_k.data_ptr(), float(eps), cs, int(rot_dim),
+            _stream_handle(stream))
+    if Hk == H:
+        _check(lib().h3a_qk_rmsnorm_rope(*args, H, *rest))
+    else:
+        _check(lib().h3a_qk_rmsnorm_rope_ex(*args, H, Hk, *rest))
     return q_out, k_out
 
 
@@ -233,14 +248,36 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, scale: float, out=None, stream=None):
     return out
 
 
-def plan_tiles(cu_seqlens, heads: int, block_m: int, n_xcd: int) -> np.ndarray:
+def varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
+    """Grouped-K/V (k, v: [S, Hkv, D], Hkv | Hq) and optionally causal per-segment attention."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q", q)
+    _, Hkv, _, sk = _token_major("k", k)
+    _, _, _, sv = _token_major("v", v)
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (S, Hkv, D) or t.dtype != q.dtype:
+            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from "
+                                       f"{(S, Hkv, D)}/{q.dtype}")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=q.dtype, device=q.device)
+    _, _, _, so = _token_major("out", out)
+    cu = _i32_array(cu_seqlens)
+    _check(lib().h3a_varlen_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
+                                        S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
+                                        int(bool(causal)), _stream_handle(stream)))
+    return out
+
+
+def plan_tiles(cu_seqlens, heads: int, block_m: int, n_xcd: int, causal: bool = False) -> np.ndarray:
     """The attention tile plan as int32 [n, 4] rows (seg start, seg len, q start, head); host only."""
     cu = _i32_array(cu_seqlens)
     n = ctypes.c_int64(0)
-    st = lib().h3a_plan_tiles(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, None, 0, ctypes.byref(n))
+    c = int(bool(causal))
+    st = lib().h3a_plan_tiles_ex(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, c, None, 0, ctypes.byref(n))
     if st not in (H3A_OK, H3A_ESHAPE):
         _check(st)
     out = np.zeros((max(n.value, 1), 4), dtype=np.int32)
-    _check(lib().h3a_plan_tiles(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, _ptr_i32(out), n.value,
-                                ctypes.byref(n)))
+    _check(lib().h3a_plan_tiles_ex(_ptr_i32(cu), len(cu) - 1, heads, block_m, n_xcd, c, _ptr_i32(out), n.value,
+                                   ctypes.byref(n)))
     return out[:n.value]

@@ -52,21 +52,22 @@ Range tensor_range(const void* p, int64_t S, int64_t H, int64_t D, int64_t strid
   return {lo, lo + uintptr_t(((S - 1) * stride + H * D) * int64_t(esz))};
 }
 
-// Whether two token-major [S, H, D] tensors can share an element.  Disjoint
-// byte ranges never do.  With equal token strides the rows of one tensor sit
-// at a fixed offset from the other's (e.g. the q, k, v slices of one fused
-// [S, 3, H, D] buffer); they are disjoint when that offset, taken modulo the
-// stride, leaves room for a whole row on both sides.  Anything else is
-// treated as overlapping.
-bool may_overlap(const void* a, int64_t sa, const void* b, int64_t sb, int64_t S, int64_t H, int64_t D,
-                 size_t esz) {
-  const Range ra = tensor_range(a, S, H, D, sa, esz), rb = tensor_range(b, S, H, D, sb, esz);
+// Whether two token-major tensors, [S, Ha, D] at a and [S, Hb, D] at b, can
+// share an element.  Disjoint byte ranges never do.  With equal token
+// strides the rows of one tensor sit at a fixed offset from the other's (e.g.
+// the q, k, v slices of one fused [S, Hq + 2 Hkv, D] buffer); they are
+// disjoint when that offset, taken modulo the stride, puts b's row after a's
+// and before a's next one.  Anything else is treated as overlapping.
+bool may_overlap(const void* a, int64_t sa, int64_t Ha, const void* b, int64_t sb, int64_t Hb, int64_t S,
+                 int64_t D, size_t esz) {
+  const Range ra = tensor_range(a, S, Ha, D, sa, esz), rb = tensor_range(b, S, Hb, D, sb, esz);
   if (!(ra.lo < rb.hi && rb.lo < ra.hi)) return false;
   if (sa != sb) return true;
-  const int64_t stride_b = sa * int64_t(esz), row_b = H * D * int64_t(esz);
+  const int64_t stride_b = sa * int64_t(esz);
+  const int64_t row_a = Ha * D * int64_t(esz), row_b = Hb * D * int64_t(esz);
   const int64_t diff = int64_t(reinterpret_cast<uintptr_t>(b) - reinterpret_cast<uintptr_t>(a));
   const int64_t phase = ((diff % stride_b) + stride_b) % stride_b;
-  return !(phase >= row_b && stride_b - phase >= row_b);
+  return !(phase >= row_a && phase + row_b <= stride_b);
 }
 
 // Validates a token-major [S, H, D] operand.
@@ -126,14 +127,14 @@ int n_xcd_of(int device) {
   return n;
 }
 
-h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, Plan* out) {
+h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, Plan* out) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail_hip("hipGetDevice", e);
   const int n_xcd = n_xcd_of(device);
   std::string key;
-  key.reserve(16 + size_t(nseg + 1) * 4);
-  const int32_t hdr[4] = {device, H, block_m, n_xcd};
+  key.reserve(20 + size_t(nseg + 1) * 4);
+  const int32_t hdr[5] = {device, H, block_m, n_xcd, causal ? 1 : 0};
   key.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
   key.append(reinterpret_cast<const char*>(cu), size_t(nseg + 1) * sizeof(int32_t));
 
@@ -144,7 +145,7 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
     *out = it->second;
     return H3A_OK;
   }
-  std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd);
+  std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd, causal);
   Plan p;
   p.n = int64_t(items.size());
   if (p.n > 0) {
@@ -302,16 +303,17 @@ h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int
   return h3a_build_rope_table_ex(segments, nseg, &spec, cos_sin, S, cu_seqlens_out, stream);
 }
 
-h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
-                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
-                               int64_t stride_q, int64_t stride_k, int64_t stride_qo,
-                               int64_t stride_ko, const float* gamma_q, const float* gamma_k,
-                               float eps, const float* cos_sin, int32_t rot_dim,
-                               hipStream_t stream) {
+h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
+                                  h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hk, int32_t D,
+                                  int64_t stride_q, int64_t stride_k, int64_t stride_qo,
+                                  int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                                  float eps, const float* cos_sin, int32_t rot_dim,
+                                  hipStream_t stream) {
   if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
   if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
   if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
   if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
   const int V = dtype == H3A_BF16 ? 8 : 4;
   if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
@@ -321,10 +323,10 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
   const size_t esz = elem_size(dtype);
   h3a_status st;
-  if ((st = check_operand("q", q, S, H, D, stride_q, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, H, D, stride_k, esz)) != H3A_OK) return st;
-  if ((st = check_operand("q_out", q_out, S, H, D, stride_qo, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k_out", k_out, S, H, D, stride_ko, esz)) != H3A_OK) return st;
+  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, Hk, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("q_out", q_out, S, Hq, D, stride_qo, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k_out", k_out, S, Hk, D, stride_ko, esz)) != H3A_OK) return st;
   if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
   if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
   if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
@@ -335,17 +337,71 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
   if (S == 0) return H3A_OK;
   const bool q_inplace = q_out == q && stride_qo == stride_q;
   const bool k_inplace = k_out == k && stride_ko == stride_k;
-  if (!q_inplace && may_overlap(q_out, stride_qo, q, stride_q, S, H, D, esz))
+  if (!q_inplace && may_overlap(q_out, stride_qo, Hq, q, stride_q, Hq, S, D, esz))
     return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
-  if (!k_inplace && may_overlap(k_out, stride_ko, k, stride_k, S, H, D, esz))
+  if (!k_inplace && may_overlap(k_out, stride_ko, Hk, k, stride_k, Hk, S, D, esz))
     return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
-  if (may_overlap(q_out, stride_qo, k, stride_k, S, H, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k");
-  if (may_overlap(k_out, stride_ko, q, stride_q, S, H, D, esz)) return fail(H3A_EINVAL, "k_out overlaps q");
-  if (may_overlap(q_out, stride_qo, k_out, stride_ko, S, H, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k_out");
+  if (may_overlap(q_out, stride_qo, Hq, k, stride_k, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k");
+  if (may_overlap(k_out, stride_ko, Hk, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "k_out overlaps q");
+  if (may_overlap(q_out, stride_qo, Hq, k_out, stride_ko, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k_out");
 
-  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, H, D, stride_q, stride_k,
-                                             stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, Hq, Hk, D, stride_q,
+                                             stride_k, stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin,
+                                             rot_dim, stream);
   if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
+                               h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                               int64_t stride_q, int64_t stride_k, int64_t stride_qo,
+                               int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                               float eps, const float* cos_sin, int32_t rot_dim,
+                               hipStream_t stream) {
+  return h3a_qk_rmsnorm_rope_ex(q, k, q_out, k_out, dtype, S, H, H, D, stride_q, stride_k, stride_qo, stride_ko,
+                                gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+}
+
+h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
+                                  h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                  int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
+                                  float scale, int32_t causal, hipStream_t stream) {
+  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  const size_t esz = elem_size(dtype);
+  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  auto overlaps = [&](const void* x, int64_t sx, int32_t h) {
+    return may_overlap(o, stride_o, Hq, x, sx, h, S, D, esz);
+  };
+  if (overlaps(q, stride_q, Hq)) return fail(H3A_EINVAL, "o overlaps q");
+  if (overlaps(k, stride_k, Hkv)) return fail(H3A_EINVAL, "o overlaps k");
+  if (overlaps(v, stride_v, Hkv)) return fail(H3A_EINVAL, "o overlaps v");
+
+  const bool bf16 = dtype == H3A_BF16;
+  Plan plan;
+  if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
+                     &plan)) != H3A_OK)
+    return st;
+  const int32_t group = Hq / Hkv;
+  hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                  plan.n, scale, group, causal != 0, stream)
+                      : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                 plan.n, scale, group, causal != 0, stream);
+  if (e != hipSuccess) return fail_hip("varlen attention launch", e);
   return H3A_OK;
 }
 
@@ -354,52 +410,32 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
                                float scale, hipStream_t stream) {
-  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  const size_t esz = elem_size(dtype);
-  if ((st = check_operand("q", q, S, H, D, stride_q, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, H, D, stride_k, esz)) != H3A_OK) return st;
-  if ((st = check_operand("v", v, S, H, D, stride_v, esz)) != H3A_OK) return st;
-  if ((st = check_operand("o", o, S, H, D, stride_o, esz)) != H3A_OK) return st;
-  if (S == 0) return H3A_OK;
-  if (may_overlap(o, stride_o, q, stride_q, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
-  if (may_overlap(o, stride_o, k, stride_k, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
-  if (may_overlap(o, stride_o, v, stride_v, S, H, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
-
-  const bool bf16 = dtype == H3A_BF16;
-  Plan plan;
-  if ((st = get_plan(cu_seqlens, nseg, H, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, &plan)) != H3A_OK)
-    return st;
-  hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                  plan.n, scale, stream)
-                      : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                 plan.n, scale, stream);
-  if (e != hipSuccess) return fail_hip("varlen attention launch", e);
-  return H3A_OK;
+  return h3a_varlen_attn_fwd_ex(q, k, v, o, dtype, S, H, H, D, stride_q, stride_k, stride_v, stride_o,
+                                cu_seqlens, nseg, scale, 0, stream);
 }
 
-h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
-                          int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items) {
+h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
+                             int32_t n_xcd, int32_t causal, int32_t* items, int64_t cap, int64_t* n_items) {
   if (n_items == nullptr) return fail(H3A_EINVAL, "n_items is NULL");
   if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
   if (block_m < 1) return fail(H3A_EINVAL, "block_m = %d must be >= 1", block_m);
   if (n_xcd < 1) return fail(H3A_EINVAL, "n_xcd = %d must be >= 1", n_xcd);
+  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
   h3a_status st;
   if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
   if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
   if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
-  std::vector<h3a::WorkItem> plan = h3a::plan_tiles(cu_seqlens, nseg, H, block_m, n_xcd);
+  std::vector<h3a::WorkItem> plan = h3a::plan_tiles(cu_seqlens, nseg, H, block_m, n_xcd, causal != 0);
   *n_items = int64_t(plan.size());
   if (int64_t(plan.size()) > cap) return fail(H3A_ESHAPE, "cap %lld < plan length %lld", (long long)cap, (long long)plan.size());
   if (!plan.empty() && items == nullptr) return fail(H3A_EINVAL, "items is NULL");
   if (!plan.empty()) std::memcpy(items, plan.data(), plan.size() * sizeof(h3a::WorkItem));
   return H3A_OK;
+}
+
+h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
+                          int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items) {
+  return h3a_plan_tiles_ex(cu_seqlens, nseg, H, block_m, n_xcd, 0, items, cap, n_items);
 }
 
 }  // extern "C"

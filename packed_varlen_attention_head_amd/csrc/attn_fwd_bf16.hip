@@ -45,6 +45,13 @@
 //   * exp2 with scale * log2(e) folded into one FMA; the running max is
 //     only raised (and the accumulator rescaled) when a tile exceeds it by
 //     more than 2^8, which is exact and skips the rescale on most tiles.
+//   * Variants: K/V heads shared by groups of query heads (query head h reads
+//     K/V head h / kv_group), and a causal mask aligned at the segment start
+//     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
+//     items stop at their last query row's key tile; with 128-row items on
+//     128-aligned starts only the last two key tiles cross the diagonal, and
+//     those are always computed in the masked tail of the tile loop, so the
+//     steady-state loop is the same code in both variants.
 #include <cstdint>
 #include <type_traits>
 
@@ -107,12 +114,12 @@ __device__ __forceinline__ float other_half(float x, int hi) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
                      int64_t sk, int64_t sv, int64_t so, const WorkItem* __restrict__ items,
-                     float c) {
+                     float c, int kv_group) {
   // The body uses LDS address-space pointers and gfx950-only builtins, which
   // exist only in the device pass; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -148,6 +155,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int head_off = it.head * D;
+  const int kv_off = __builtin_amdgcn_readfirstlane(it.head / kv_group) * D;
   const int qrow0 = it.q_start + wave * 32;
   const bool active = qrow0 < it.seg_len;
 
@@ -195,9 +203,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
-  const uint16_t* kbase = k + int64_t(it.seg_start) * sk + head_off;
-  const uint16_t* vbase = v + int64_t(it.seg_start) * sv + head_off;
-  const int ntiles = (it.seg_len + kBN - 1) / kBN;
+  const uint16_t* kbase = k + int64_t(it.seg_start) * sk + kv_off;
+  const uint16_t* vbase = v + int64_t(it.seg_start) * sv + kv_off;
+  // Keys the item needs: the whole segment, or (causal) up to its last row.
+  const int nkeys = CAUSAL ? min(it.seg_len, it.q_start + kBM) : it.seg_len;
+  const int ntiles = (nkeys + kBN - 1) / kBN;
+  // First key tile that crosses the causal diagonal of the item's rows.
+  [[maybe_unused]] const int tdiag = it.q_start / kBN;
 
   // ---- building blocks ------------------------------------------------------
   auto load_k = [&](int t, auto slot) {
@@ -228,16 +240,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     }
   };
-  // Keys at or past `kvalid` in the tile get -inf.
-  // (The lane's key offset hi*4 is folded into one bound, so every compare
-  // is against a constant.)
-  auto mask = [&](f32x16* sacc, int kvalid) {
-    const int lim = kvalid - hi * 4;
+  // Keys of tile `tt` past the segment end, or (causal) past the lane's
+  // query row, get -inf.  The lane's key offset hi*4 is folded into one
+  // bound, so every compare is against a constant.
+  auto mask = [&](f32x16* sacc, int tt) {
+    int lim = it.seg_len - tt * kBN - 1;  // last key of the tile inside the segment
+    if constexpr (CAUSAL) lim = min(lim, qrow0 + l32 - tt * kBN);
+    lim -= hi * 4;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (kb * 32 + (r >> 2) * 8 + (r & 3) >= lim) sacc[kb][r] = -__builtin_inff();
+        if (kb * 32 + (r >> 2) * 8 + (r & 3) > lim) sacc[kb][r] = -__builtin_inff();
+  };
+  // Does key tile `tt` need the mask?
+  auto needs_mask = [&](int tt) {
+    return (tt + 1) * kBN > it.seg_len || (CAUSAL && tt >= tdiag);
   };
   // Tile max; the reference max m_run only moves when a query's tile max
   // exceeds it by more than kRescaleSlack (log2 units), so probabilities stay
@@ -317,7 +335,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   publish();
   if (active) {
     qk(IC<0>{}, s);
-    if (it.seg_len < kBN) mask(s, it.seg_len);
+    if (needs_mask(0)) mask(s, 0);
     update_max(s);
   }
   // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
@@ -325,7 +343,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // Steady state: tiles t and t+1 both exist and t+1 is not the last, so
   // tile t+1 is full and K_{t+2} exists.  Two iterations per trip fix the
-  // slot parities as immediates.
+  // slot parities as immediates.  No tile computed here needs a mask: a trip
+  // at t computes the scores of tiles t+1 and t+2, which stay below
+  // ntiles - 1 (bidirectional: only the last tile can be partial) or below
+  // ntiles - 2 (causal: the diagonal tiles are the last two).
   auto steady = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
     load_k(t + 2, IC<P>{});
@@ -340,11 +361,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     publish();
   };
   int t = 0;
-  for (; t + 3 < ntiles; t += 2) {
+  constexpr int kTail = CAUSAL ? 4 : 3;
+  for (; t + kTail < ntiles; t += 2) {
     steady(t, IC<0>{});
     steady(t + 1, IC<1>{});
   }
-  // Remaining one to three iterations, with slot parity in a register.
+  // Remaining iterations (at most kTail), with slot parity in a register.
   for (; t < ntiles; ++t) {
     const int par = t & 1;
     if (t + 2 < ntiles) load_k(t + 2, par);
@@ -354,8 +376,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       if (t + 1 < ntiles) {
         qk(par ^ 1, s);
         pv(par, pb);
-        const int kvalid = it.seg_len - (t + 1) * kBN;
-        if (kvalid < kBN) mask(s, kvalid);
+        if (needs_mask(t + 1)) mask(s, t + 1);
         update_max(s);
       } else {
         pv(par, pb);
@@ -382,14 +403,15 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                  hipStream_t stream) {
+                  int kv_group, hipStream_t stream) {
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c);
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c,
+                     kv_group);
   return hipGetLastError();
 }
 
@@ -398,10 +420,15 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int32_t D,
                                 int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                 const WorkItem* items, int64_t n_items, float scale,
-                                hipStream_t stream) {
+                                int32_t kv_group, bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (D == 128) return launch<128>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, stream);
-  if (D == 64) return launch<64>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, stream);
+  if (kv_group < 1) return hipErrorInvalidValue;
+  if (D == 128)
+    return causal ? launch<128, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream)
+                  : launch<128, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream);
+  if (D == 64)
+    return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream)
+                  : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream);
   return hipErrorInvalidValue;
 }
 

@@ -24,8 +24,10 @@ static_assert(sizeof(WorkItem) == 16, "WorkItem is uploaded as 4 x int32");
 // Items for every (non-empty segment, head, query tile), longest segments
 // first, balanced over n_xcd XCDs and interleaved so that workgroup b lands on
 // XCD b % n_xcd with that XCD's items in its own longest-first order.
+// Causal plans cost an item by the keys up to its last row and put each
+// chunk's costliest (last) query tiles first.
 std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
-                                 int32_t n_xcd);
+                                 int32_t n_xcd, bool causal = false);
 
 // ---- kernel launchers (one per .hip file) ---------------------------------
 
@@ -47,7 +49,7 @@ hipError_t launch_rope_table(const RopeTableSpec& spec, const int32_t* segments,
                              int32_t nseg, float* cos_sin, int64_t S, hipStream_t stream);
 
 hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void* q_out, void* k_out,
-                                  int64_t S, int32_t H, int32_t D, int64_t sq, int64_t sk,
+                                  int64_t S, int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk,
                                   int64_t sqo, int64_t sko, const float* gq, const float* gk,
                                   float eps, const float* cos_sin, int32_t rot_dim,
                                   hipStream_t stream);
@@ -56,14 +58,16 @@ hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void*
 constexpr int kAttnBlockM_BF16 = 128;
 constexpr int kAttnBlockM_F32 = 64;
 
+// Query head h reads K/V head h / kv_group; causal: query i of a segment
+// sees keys 0..i of it.
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int32_t D,
                                 int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                 const WorkItem* items, int64_t n_items, float scale,
-                                hipStream_t stream);
+                                int32_t kv_group, bool causal, hipStream_t stream);
 
 hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,
                                int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                const WorkItem* items, int64_t n_items, float scale,
-                               hipStream_t stream);
+                               int32_t kv_group, bool causal, hipStream_t stream);
 
 }  // namespace h3a

@@ -18,6 +18,9 @@
 //     b % n_xcd (the dispatcher hands workgroups to XCDs round-robin), each
 //     XCD seeing its own items longest first.  Short queues are padded with
 //     empty items.
+// Causal items stream only the keys up to their last row, so an item costs
+// min(len, (t + 1) block_m) keys and each chunk lists its query tiles last
+// to first (costliest first).
 #include <algorithm>
 #include <cstdint>
 #include <vector>
@@ -42,7 +45,7 @@ constexpr double kItemOverheadKeys = 128.0;
 }  // namespace
 
 std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
-                                 int32_t n_xcd) {
+                                 int32_t n_xcd, bool causal) {
   std::vector<int32_t> order;
   for (int32_t s = 0; s < nseg; ++s)
     if (cu[s + 1] > cu[s]) order.push_back(s);
@@ -54,17 +57,25 @@ std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads,
   for (int32_t s : order) {
     const int32_t len = cu[s + 1] - cu[s];
     const int32_t ntiles = (len + block_m - 1) / block_m;
-    const double tile_cost = double(len) + kItemOverheadKeys;
+    auto tile_cost = [&](int32_t t) {
+      const int64_t keys = causal ? std::min<int64_t>(len, int64_t(t + 1) * block_m) : len;
+      return double(keys) + kItemOverheadKeys;
+    };
     for (int32_t h = 0; h < heads; ++h)
       for (int32_t t0 = 0; t0 < ntiles; t0 += kChunkTiles) {
         const int32_t t1 = std::min(ntiles, t0 + kChunkTiles);
-        chunks.push_back({s, h, t0, t1, tile_cost * double(t1 - t0)});
+        double cost = 0.0;
+        for (int32_t t = t0; t < t1; ++t) cost += tile_cost(t);
+        chunks.push_back({s, h, t0, t1, cost});
       }
   }
 
   auto expand = [&](const Chunk& c, std::vector<WorkItem>& out) {
     const int32_t len = cu[c.seg + 1] - cu[c.seg];
-    for (int32_t t = c.t0; t < c.t1; ++t) out.push_back({cu[c.seg], len, t * block_m, c.head});
+    for (int32_t i = c.t0; i < c.t1; ++i) {
+      const int32_t t = causal ? c.t0 + c.t1 - 1 - i : i;
+      out.push_back({cu[c.seg], len, t * block_m, c.head});
+    }
   };
 
   if (n_xcd <= 1) {

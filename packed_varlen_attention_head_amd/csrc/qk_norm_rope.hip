@@ -16,7 +16,8 @@
 //   * the rotary partner of element i (i +- R/2) lives in the lane R/(2V)
 //     positions away, same slot, and is fetched with a lane shuffle;
 //   * all loads of a token are issued before any store, so in-place calls are
-//     safe (each token is owned by a single wave).
+//     safe (each token is owned by a single wave);
+//   * k may have fewer heads than q (grouped K/V heads of causal GQA).
 #include <cstdint>
 
 #include "common.h"
@@ -116,7 +117,7 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq_b, int64_t sk_b,
-                    int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H,
+                    int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H, int32_t Hk,
                     const float* __restrict__ gq, const float* __restrict__ gk, float eps,
                     const float* __restrict__ cos_sin, int32_t rot_dim) {
   constexpr int V = Elem<T>::V;
@@ -153,18 +154,18 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq
     g_k[e] = gk[d0 + e];
   }
   norm_rope_one<T, D>(q, qo, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
-  norm_rope_one<T, D>(k, ko, sk_b, sko_b, token, H, g_k, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D>(k, ko, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
 }
 
 template <typename T, int D>
-hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int64_t sq,
+hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int32_t Hk, int64_t sq,
                   int64_t sk, int64_t sqo, int64_t sko, const float* gq, const float* gk, float eps,
                   const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
   constexpr int esz = 16 / Elem<T>::V;
   const unsigned blocks = unsigned((S + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
                      static_cast<const char*>(q), static_cast<const char*>(k), static_cast<char*>(qo),
-                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * esz, sko * esz, int32_t(S), H, gq,
+                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * esz, sko * esz, int32_t(S), H, Hk, gq,
                      gk, eps, cos_sin, rot_dim);
   return hipGetLastError();
 }
@@ -172,20 +173,20 @@ hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, i
 }  // namespace
 
 hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void* q_out, void* k_out,
-                                  int64_t S, int32_t H, int32_t D, int64_t sq, int64_t sk,
+                                  int64_t S, int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk,
                                   int64_t sqo, int64_t sko, const float* gq, const float* gk,
                                   float eps, const float* cos_sin, int32_t rot_dim,
                                   hipStream_t stream) {
   if (bf16) {
     if (D == 128)
-      return launch<Bf16Tag, 128>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+      return launch<Bf16Tag, 128>(q, k, q_out, k_out, S, H, Hk, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
     if (D == 64)
-      return launch<Bf16Tag, 64>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+      return launch<Bf16Tag, 64>(q, k, q_out, k_out, S, H, Hk, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
   } else {
     if (D == 128)
-      return launch<float, 128>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+      return launch<float, 128>(q, k, q_out, k_out, S, H, Hk, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
     if (D == 64)
-      return launch<float, 64>(q, k, q_out, k_out, S, H, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
+      return launch<float, 64>(q, k, q_out, k_out, S, H, Hk, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -34,6 +34,8 @@ class Workload:
     seed: int = 0
     gamma_mean: float = 1.0
     gamma_std: float = 0.1
+    kv_heads: int = 0  # K/V heads (grouped-query attention); 0: as many as query heads
+    causal: bool = False  # per-segment causal mask aligned at the segment start
     rope_mode: int = 0  # 0 grid, 1 linspace, 2 length-normalised, 3 interleaved (h3a_rope_mode)
     lin_start: tuple = (0.0, 0.0, 0.0)
     lin_stop: tuple = (0.0, 0.0, 0.0)
@@ -55,9 +57,15 @@ class Workload:
     def lengths(self) -> list:
         return [int(s[3]) for s in self.segments]
 
+    @property
+    def kv(self) -> int:
+        return self.kv_heads or self.heads
+
     def attention_flops(self) -> float:
-        """QK^T plus PV multiply-adds at 2 flop each: 4 * D * heads * sum(L^2)."""
-        return 4.0 * self.head_dim * self.heads * float(sum(L * L for L in self.lengths))
+        """QK^T plus PV multiply-adds at 2 flop each over the visible (query, key)
+        pairs: 4 * D * heads * sum(L^2), or sum(L (L + 1) / 2) pairs when causal."""
+        pairs = sum(L * (L + 1) // 2 if self.causal else L * L for L in self.lengths)
+        return 4.0 * self.head_dim * self.heads * float(pairs)
 
     def with_segments(self, segments, name=None) -> "Workload":
         d = dict(self.__dict__)
@@ -153,6 +161,29 @@ MROPE_PACKED = Workload(
 
 MODE_WORKLOADS = {w.name: w for w in (VIT3D_TILES, MROPE_PACKED)}
 
+# Causal grouped-query attention as in the encoder's text tower (per-head q/k
+# RMSNorm, interleaved M-RoPE, causal GQA: encoder-tower commit).  Packed
+# prompts of 2048, 1500, 500, 47 and 1 tokens as (L, 1, 1) grids; 32 query
+# heads sharing 8 K/V heads of 128 dims.  Head counts and rotary base are this
+# workload's choice (the pages give none for the tower).
+CAUSAL_GQA_TEXT = Workload(
+    name="causal_gqa_text_bf16",
+    segments=tuple((L, 1, 1, L) for L in (2048, 1500, 500, 47, 1)),
+    heads=32, kv_heads=8, causal=True, head_dim=128, rot_dims=(48, 40, 40), dtype="bf16", base=1000000.0,
+    rope_mode=3,
+    note="5 packed prompts (S=4096), 32 q heads / 8 kv heads, causal, interleaved M-RoPE",
+)
+
+CAUSAL_GQA_TINY_F32 = Workload(
+    name="causal_gqa_tiny_f32",
+    segments=((37, 1, 1, 37), (91, 1, 1, 91)),
+    heads=4, kv_heads=2, causal=True, head_dim=64, rot_dims=(16, 16, 16), dtype="f32", base=10000.0,
+    rope_mode=3,
+    note="2 segments [37, 91], 4 q heads / 2 kv heads, causal, fp32",
+)
+
+CAUSAL_WORKLOADS = {w.name: w for w in (CAUSAL_GQA_TEXT, CAUSAL_GQA_TINY_F32)}
+
 # The configuration the headline throughput is quoted on.
 HEADLINE = H3_S20423
 
@@ -173,9 +204,10 @@ class Tensors:
 
 def make_tensors(w: Workload, with_v: bool = True) -> Tensors:
     shape = (w.tokens, w.heads, w.head_dim)
+    kv_shape = (w.tokens, w.kv, w.head_dim)
     q = rng.normal_tensor(w.seed, rng.TAG_Q, shape, w.dtype)
-    k = rng.normal_tensor(w.seed, rng.TAG_K, shape, w.dtype)
-    v = rng.normal_tensor(w.seed, rng.TAG_V, shape, w.dtype) if with_v else None
+    k = rng.normal_tensor(w.seed, rng.TAG_K, kv_shape, w.dtype)
+    v = rng.normal_tensor(w.seed, rng.TAG_V, kv_shape, w.dtype) if with_v else None
     gq = rng.normal_tensor(w.seed, rng.TAG_GAMMA_Q, (w.head_dim,), "f32", w.gamma_mean, w.gamma_std)
     gk = rng.normal_tensor(w.seed, rng.TAG_GAMMA_K, (w.head_dim,), "f32", w.gamma_mean, w.gamma_std)
     return Tensors(q, k, v, gq, gk)

@@ -167,6 +167,68 @@ def test_varlen_attn_rejects(kw, status, word):
     assert word in h3a.last_error(), h3a.last_error()
 
 
+def attn_ex(dtype=h3a.H3A_BF16, S=300, Hq=8, Hkv=2, D=128, cu=(0, 100, 300), strides=None, q=P,
+            k=P + (1 << 24), v=P + (2 << 24), o=P + (3 << 24), scale=0.088, causal=1):
+    s = strides or (Hq * D, Hkv * D, Hkv * D, Hq * D)
+    c, cp = i32(cu)
+    return h3a.lib().h3a_varlen_attn_fwd_ex(q, k, v, o, dtype, S, Hq, Hkv, D, *s, cp, len(cu) - 1, scale, causal,
+                                            None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(Hkv=3), h3a.H3A_ESHAPE, "does not divide"),
+    (dict(Hkv=0), h3a.H3A_EINVAL, "Hkv ="),
+    (dict(Hq=0), h3a.H3A_EINVAL, "H ="),
+    (dict(causal=2), h3a.H3A_EINVAL, "causal"),
+    (dict(causal=-1), h3a.H3A_EINVAL, "causal"),
+    (dict(strides=(1024, 128, 256, 1024)), h3a.H3A_ESHAPE, "k: token stride"),
+    (dict(strides=(1024, 256, 256, 512)), h3a.H3A_ESHAPE, "o: token stride"),
+    (dict(dtype=9), h3a.H3A_EDTYPE, "dtype"),
+    (dict(D=96), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(o=P + (1 << 24) + 512), h3a.H3A_EINVAL, "o overlaps k"),
+])
+def test_varlen_attn_ex_rejects(kw, status, word):
+    assert attn_ex(**kw) == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+def _device_visible():
+    import torch
+
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_device_visible(), reason="a valid call would launch on the visible GPU")
+def test_grouped_tensors_side_by_side_pass_validation():
+    """A narrow K/V tensor right below a wider output: no false overlap.  Without a GPU the
+    call gets past validation and stops at the device query (EHIP)."""
+    S = 300
+    st = attn_ex(dtype=h3a.H3A_F32, S=S, Hq=4, Hkv=1, strides=(512, 128, 128, 512), q=P + (1 << 26),
+                 k=P + (1 << 27), v=P, o=P + S * 128 * 4)
+    assert st == h3a.H3A_EHIP and "hipGetDevice" in h3a.last_error(), h3a.last_error()
+    # q, k, v as column slices of one fused [S, (Hq + 2 Hkv) D] bf16 buffer
+    Hq, Hkv, D = 8, 2, 128
+    row = (Hq + 2 * Hkv) * D
+    st = attn_ex(S=S, strides=(row, row, row, Hq * D), q=P, k=P + Hq * D * 2, v=P + (Hq + Hkv) * D * 2,
+                 o=P + (1 << 27))
+    assert st == h3a.H3A_EHIP, h3a.last_error()
+    # and a real overlap inside the fused row is still caught
+    st = attn_ex(S=S, strides=(row, row, row, row), q=P, k=P + Hq * D * 2, v=P + (Hq + Hkv) * D * 2,
+                 o=P + (Hq + Hkv) * D * 2 + 256)
+    assert st == h3a.H3A_EINVAL and "o overlaps" in h3a.last_error(), h3a.last_error()
+
+
+def qk_ex(Hq=8, Hk=0, **kw):
+    D, hd, hk = 128, Hq * 128, max(Hk, 1) * 128
+    return h3a.lib().h3a_qk_rmsnorm_rope_ex(P, P + (1 << 24), P, P + (1 << 24), h3a.H3A_BF16, 16, Hq, Hk, D, hd, hk,
+                                            hd, hk, P + (2 << 24), P + (3 << 24), 1e-6, P + (4 << 24), 96, None)
+
+
+def test_qk_rmsnorm_rope_ex_rejects():
+    assert qk_ex(Hk=0) == h3a.H3A_EINVAL and "Hk =" in h3a.last_error()
+    assert qk_ex(Hq=0, Hk=2) == h3a.H3A_EINVAL and "H =" in h3a.last_error()
+
+
 def test_varlen_attn_empty_is_a_no_op():
     assert attn(S=0, cu=(0, 0, 0)) == h3a.H3A_OK
 

@@ -77,3 +77,39 @@ def test_xcd_queues_balanced_and_longest_first(name):
 def test_plan_skips_empty_segments_and_handles_all_empty():
     plan = h3a.plan_tiles(cu_of([0, 0, 0]), 2, 128, 8)
     assert len(plan) == 0
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("n_xcd", [1, 8])
+def test_causal_plan_covers_every_tile_once(name, n_xcd):
+    lens = CASES[name]
+    H = 8
+    cu = cu_of(lens)
+    plan = h3a.plan_tiles(cu, H, 128, n_xcd, causal=True)
+    real = plan[plan[:, 1] > 0]
+    want = Counter((int(cu[s]), L, t, h) for s, L in enumerate(lens) for h in range(H) for t in range(0, L, 128))
+    assert Counter(tuple(int(x) for x in row) for row in real) == want
+
+
+def test_causal_plan_balances_key_work():
+    """Each XCD's causal work (keys up to each item's last row) is within 5% of the mean."""
+    lens = [8000, 3000, 1000, 700, 64, 1]
+    n_xcd = 8
+    plan = h3a.plan_tiles(cu_of(lens), 32, 128, n_xcd, causal=True)
+    loads = []
+    for x in range(n_xcd):
+        q = plan[x::n_xcd]
+        q = q[q[:, 1] > 0]
+        keys = np.minimum(q[:, 1], q[:, 2] + 128).astype(np.float64)
+        loads.append(float(np.sum(keys + 128.0)))
+        # within one XCD the first item is one of the costliest
+        assert keys[0] == keys.max()
+    loads = np.array(loads)
+    assert loads.max() / loads.mean() < 1.05, loads
+
+
+def test_causal_and_bidirectional_plans_differ_only_in_order():
+    cu = cu_of(CASES["h3_s20423"])
+    a = h3a.plan_tiles(cu, 24, 128, 1)
+    b = h3a.plan_tiles(cu, 24, 128, 1, causal=True)
+    assert sorted(map(tuple, a.tolist())) == sorted(map(tuple, b.tolist()))

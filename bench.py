@@ -12,7 +12,11 @@ attention kernel alone (HIP events on its launch stream) against the bf16
 dense MFMA peak; `cpu_baseline` times the fp64 oracle on a bounded sample of
 the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+--config runs another bf16 workload of the same family through the same step
+(its own rotary table mode, grouped K/V heads, causal mask); F then counts the
+visible (query, key) pairs, sum(L (L + 1) / 2) when causal.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--config NAME]
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 METRIC = "varlen attn TFLOP/s and % bf16 MFMA peak at S=20,423, 24 heads, d=128"
+HEADLINE = "h3_s20423_bf16"
 ATTN_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "attn_fwd_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_h3_s20423_traffic.json")
 
@@ -40,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="h3_s20423_bf16")
+    ap.add_argument("--config", default=HEADLINE, help="bf16 workload name (synth.configs.BF16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -64,9 +69,13 @@ def _rocpd_rows(db, query):
 
 
 def _short_kernel(name):
+    """attn_fwd_*_kernel<D> (bidirectional) or <D, causal>, and the other kernels' short names."""
     import re
 
-    m = re.search(r"(attn_fwd_bf16_kernel<\d+>|attn_fwd_f32_kernel<\d+>|qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
+    m = re.search(r"(attn_fwd_(?:bf16|f32)_kernel)<(\d+)(?:, *(true|false))?>", name)
+    if m:
+        return f"{m.group(1)}<{m.group(2)}{', causal' if m.group(3) == 'true' else ''}>"
+    m = re.search(r"(qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
                   r"__amd_rocclr_\w+|elementwise_kernel|vectorized_elementwise_kernel|reduce_kernel)", name)
     return m.group(1) if m else name[:60]
 
@@ -149,7 +158,8 @@ def measured_traffic():
 
 def cpu_baseline(w, T, target_s):
     """fp64 oracle on a bounded sample of query rows (all heads, rows spread
-    evenly over the packed sequence), scaled to TFLOP/s with the same F."""
+    evenly over the packed sequence), scaled to TFLOP/s with the same F (a
+    row costs 4 D heads times the keys it sees)."""
     import oracle
     from synth import rng
 
@@ -165,16 +175,21 @@ def cpu_baseline(w, T, target_s):
     vf = rng.as_f64(T.v, w.dtype)
     lens = np.diff(cu)
     seg = oracle.segment_of_rows(cu, np.arange(w.tokens))
+    grouped = w.causal or w.kv != w.heads
 
     def flops(rows):
-        return float(np.sum(4.0 * w.head_dim * w.heads * lens[seg[rows]]))
+        keys = (rows - cu[seg[rows]] + 1) if w.causal else lens[seg[rows]]
+        return float(np.sum(4.0 * w.head_dim * w.heads * keys))
 
     n = 32
     spent, done_flops, done_rows = 0.0, 0.0, 0
     while True:
         rows = np.linspace(0, w.tokens - 1, n).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.varlen_attention_rows(qf, kf, vf, cu, w.scale, rows)
+        if grouped:
+            oracle.varlen_attention_gqa_rows(qf, kf, vf, cu, w.scale, rows, causal=w.causal)
+        else:
+            oracle.varlen_attention_rows(qf, kf, vf, cu, w.scale, rows)
         dt = time.perf_counter() - t0
         spent, done_flops, done_rows = dt, flops(rows), n
         if dt >= target_s * 0.5 or n >= w.tokens:
@@ -186,8 +201,8 @@ def cpu_baseline(w, T, target_s):
         "cores": cores,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle attention on {done_rows} query rows spread evenly over the "
-                  f"S={w.tokens} packed sequence, all {w.heads} heads, each against its full segment "
-                  f"({done_flops:.3e} flop in {spent:.1f} s); same F convention",
+                  f"S={w.tokens} packed sequence, all {w.heads} heads, each against its segment's keys "
+                  f"({'causal, ' if w.causal else ''}{done_flops:.3e} flop in {spent:.1f} s); same F convention",
     }
 
 
@@ -210,8 +225,11 @@ def main():
     import packed_varlen_attention_head_amd as h3a
     from synth import configs
 
-    w = configs.ALL[args.config]
-    assert w.dtype == "bf16"
+    if args.config not in configs.BF16:
+        print(f"unknown workload {args.config!r}; bf16 workloads: {', '.join(sorted(configs.BF16))}",
+              file=sys.stderr)
+        return 2
+    w = configs.BF16[args.config]
     T = configs.make_tensors(w)
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -221,13 +239,25 @@ def main():
     gk = torch.from_numpy(T.gamma_k).to(dev)
     tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device=dev)
     qn, kn = torch.empty_like(q), torch.empty_like(k)
-    o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
+    o = torch.empty_like(q)
+
+    def table():
+        if w.rope_mode == 0:
+            return h3a.build_rope_table(w.segments, w.rot_dims, w.base, tab, stream=stream)
+        return h3a.build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start,
+                                       stop=w.lin_stop, stream=stream)
+
+    def attention(cu):
+        if w.causal or w.kv != w.heads:
+            return h3a.varlen_attn_fwd_ex(qn, kn, v, cu, w.scale, causal=w.causal, out=o, stream=stream)
+        return h3a.varlen_attn_fwd(qn, kn, v, cu, w.scale, out=o, stream=stream)
+
     def step():
-        cu = h3a.build_rope_table(w.segments, w.rot_dims, w.base, tab, stream=stream)
+        cu = table()
         h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
-        h3a.varlen_attn_fwd(qn, kn, v, cu, w.scale, out=o, stream=stream)
+        attention(cu)
         return cu
 
     for _ in range(args.warmup):
@@ -253,18 +283,20 @@ def main():
         return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
 
     n_ev = max(args.steps, 10)
-    attn_s = timed(lambda: h3a.varlen_attn_fwd(qn, kn, v, cu, w.scale, out=o, stream=stream), n_ev)
+    attn_s = timed(lambda: attention(cu), n_ev)
     norm_s = timed(lambda: h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn,
                                                stream=stream), n_ev)
-    table_s = timed(lambda: h3a.build_rope_table(w.segments, w.rot_dims, w.base, tab, stream=stream), n_ev)
+    table_s = timed(table, n_ev)
 
     F = w.attention_flops()
     attn_tflops = F / attn_s / 1e12
-    S, H, D = w.tokens, w.heads, w.head_dim
-    norm_bytes = 2 * (2 * S * H * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + 2 * D * 4
-    attn_alg_bytes = 4 * S * H * D * 2
+    S, H, Hkv, D = w.tokens, w.heads, w.kv, w.head_dim
+    # q and k (H + Hkv heads) read and written, the table and both gains read
+    norm_bytes = 2 * (S * (H + Hkv) * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + 2 * D * 4
+    # Q read and O written (H heads), K and V read (Hkv heads), once each
+    attn_alg_bytes = 2 * S * H * D * 2 + 2 * S * Hkv * D * 2
     result = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == HEADLINE else f"varlen attn TFLOP/s and % bf16 MFMA peak on {w.name}",
         "value": F / step_s / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -275,10 +307,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: Q,K,V ~ N(0,1) bf16, gains ~ 1+N(0,0.1) fp32, SplitMix64 seed 0",
+        "data": f"synthetic: Q,K,V ~ N(0,1) bf16, gains ~ {w.gamma_mean:g}+N(0,{w.gamma_std:g}) fp32, "
+                f"SplitMix64 seed {w.seed}",
         "config": {
             "workload": w.name,
-            "S": S, "heads": H, "head_dim": D, "rot_dims": list(w.rot_dims),
+            "S": S, "heads": H, "kv_heads": Hkv, "causal": w.causal, "head_dim": D,
+            "rot_dims": list(w.rot_dims), "rope_mode": w.rope_mode,
             "segments": [list(s) for s in w.segments],
             "parallelism": "single GPU",
         },
@@ -295,8 +329,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(),
-            "kernel": "attn_fwd_bf16_kernel<128>",
+            "traffic": measured_traffic() if w.name == HEADLINE else None,
+            "kernel": f"attn_fwd_bf16_kernel<{D}>",
             "algorithmic_flop_per_launch": F,
             "algorithmic_bytes_per_launch": attn_alg_bytes,
         },

@@ -184,6 +184,29 @@ CAUSAL_GQA_TINY_F32 = Workload(
 
 CAUSAL_WORKLOADS = {w.name: w for w in (CAUSAL_GQA_TEXT, CAUSAL_GQA_TINY_F32)}
 
+# The encoder's vision tower: non-causal attention over per-frame cu_seqlens of
+# a ragged batch of two images with different h x w (vision-tower commit),
+# with a 2-D (h, w) rotary: the grid table with no t share.  Frames: image A
+# 4 x 24 x 36 patches, image B 2 x 20 x 30; 16 heads of 64 (this workload's
+# choice; the pages give the tower's shapes only as reduced dimensions).
+VISION_FRAMES = Workload(
+    name="vision_frames_bf16",
+    segments=((1, 24, 36, 864),) * 4 + ((1, 20, 30, 600),) * 2,
+    heads=16, head_dim=64, rot_dims=(0, 16, 16), dtype="bf16", base=10000.0,
+    note="per-frame segments of two ragged images (4 x 864, 2 x 600), 16 heads x 64, 2-D rotary",
+)
+
+# One long causal prompt with the text tower's head layout, large enough to
+# time the causal kernel away from launch overhead.
+CAUSAL_GQA_16K = CAUSAL_GQA_TEXT.replace(
+    name="causal_gqa_16k_bf16", segments=((16384, 1, 1, 16384),),
+    note="one 16,384-token causal prompt, 32 q heads / 8 kv heads, interleaved M-RoPE",
+)
+
+# Every bf16 workload, by name (the benchmark can run any of them).
+BF16 = {w.name: w for w in (TWO_SEG, H3_S20423, H3_S25103, RAGGED64, VIT3D_TILES, MROPE_PACKED, CAUSAL_GQA_TEXT,
+                            CAUSAL_GQA_16K, VISION_FRAMES)}
+
 # The configuration the headline throughput is quoted on.
 HEADLINE = H3_S20423
 

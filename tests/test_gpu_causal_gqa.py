@@ -1,7 +1,8 @@
-"""GPU parity of causal grouped-query varlen attention (the encoder text tower's
-attention) against the fp64 oracle: the whole chain on two workloads, causal
-edge lengths around the tile sizes, and GPU-side invariants (prefix isolation,
-grouped heads equal to repeated K/V)."""
+"""GPU parity of the encoder towers' attention workloads against the fp64 oracle:
+causal grouped-query attention (text tower) through the whole chain on two
+workloads, edge lengths around the tile sizes, GPU-side invariants (prefix
+isolation, grouped heads equal to repeated K/V), and per-frame ragged ViT
+attention (vision tower)."""
 from __future__ import annotations
 
 import numpy as np
@@ -122,3 +123,21 @@ def test_causal_prefix_isolation_and_repeated_kv():
     b = h3a().varlen_attn_fwd(q, kr, vr, cu, 0.088)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_per_frame_ragged_vit_attention():
+    """Per-frame cu_seqlens over a ragged two-image batch, 2-D rotary table, bidirectional."""
+    import torch
+
+    w = configs.VISION_FRAMES
+    T = configs.make_tensors(w)
+    log(f"[vision frames] S={w.tokens} H={w.heads} D={w.head_dim} segments={w.lengths}")
+    tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    cu = h3a().build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    q, k, v = (to_device(x, w.dtype) for x in (T.q, T.k, T.v))
+    o = to_f64(h3a().varlen_attn_fwd(q, k, v, cu, w.scale))
+    ocu, cos, sin = oracle.rope_table(w.segments, w.rot_dims, w.base)
+    g = to_f64(tab)
+    assert max(np.abs(g[0] - cos).max(), np.abs(g[1] - sin).max()) <= 1.2e-7
+    qf, kf, vf = (rng.as_f64(x, w.dtype) for x in (T.q, T.k, T.v))
+    compare(o, oracle.varlen_attention(qf, kf, vf, ocu, w.scale), w.dtype, "o")

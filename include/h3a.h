@@ -174,6 +174,17 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
  * [S, Hk, D]; everything else as for h3a_qk_rmsnorm_rope, which is this call
  * with Hk = Hq.  Errors: as h3a_qk_rmsnorm_rope, plus EINVAL for Hk < 1.
  */
+/*
+ * RMSNorm + NeoX rotary of one tensor (the K half of h3a_qk_rmsnorm_rope, for
+ * use with h3a_varlen_attn_fwd_qnorm, which does the Q half itself).
+ * x, x_out: [S, H, D]; in place when x_out == x with the same stride;
+ * gamma: fp32 [D].  Same arithmetic, shapes and errors as
+ * h3a_qk_rmsnorm_rope.
+ */
+h3a_status h3a_rmsnorm_rope(const void* x, void* x_out, h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                            int64_t stride_x, int64_t stride_xo, const float* gamma, float eps,
+                            const float* cos_sin, int32_t rot_dim, hipStream_t stream);
+
 h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
                                   h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hk, int32_t D,
                                   int64_t stride_q, int64_t stride_k, int64_t stride_qo,
@@ -211,6 +222,35 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
                                float scale, hipStream_t stream);
+
+/*
+ * Bidirectional varlen attention whose Q rows arrive raw: each workgroup
+ * RMS-normalises (gain gamma_q, eps) and rotates (cos_sin, rot_dim) its Q
+ * tile in registers before the attention, so the Q half of the separate norm
+ * + rotary pass disappears (the GB10 build fuses Q RMSNorm + rot96 RoPE into
+ * its attention front end: h3-spark model card, "What this config does").
+ * k must already be normalised and rotated (h3a_rmsnorm_rope).
+ *
+ * The result is bit-identical to h3a_qk_rmsnorm_rope followed by
+ * h3a_varlen_attn_fwd(_ex): the fused prologue performs the same fp32
+ * operations in the same order and rounds q' to bf16 once.
+ *
+ * q              device bf16 [S, Hq, D], raw (before norm and rotary); not
+ *                modified.
+ * k, v           device bf16 [S, Hkv, D]; Hkv divides Hq.
+ * gamma_q        device fp32 [D], 16-byte aligned.
+ * cos_sin        the [2][S][rot_dim/2] table; rot_dim a multiple of 32 and
+ *                at most D (e.g. 96 for d = 128).
+ * Everything else as for h3a_varlen_attn_fwd_ex with causal = 0.
+ *
+ * Errors: as h3a_varlen_attn_fwd_ex, plus EUNSUPPORTED for fp32 or a
+ * rot_dim not a multiple of 32, EINVAL for a bad eps or null gamma/table.
+ */
+h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v, void* o, h3a_dtype dtype,
+                                     int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t stride_q,
+                                     int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                     const int32_t* cu_seqlens, int32_t nseg, float scale, const float* gamma_q,
+                                     float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
 /*
  * Varlen attention with grouped K/V heads and an optional causal mask: the

@@ -34,8 +34,10 @@ EXPORTS = (
     "h3a_build_rope_table_ex",
     "h3a_qk_rmsnorm_rope",
     "h3a_qk_rmsnorm_rope_ex",
+    "h3a_rmsnorm_rope",
     "h3a_varlen_attn_fwd",
     "h3a_varlen_attn_fwd_ex",
+    "h3a_varlen_attn_fwd_qnorm",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -85,6 +87,9 @@ def lib() -> ctypes.CDLL:
                                       _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_qk_rmsnorm_rope_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                          _i64, _vp, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_rmsnorm_rope.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_varlen_attn_fwd_qnorm.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
+                                            _i64, _c_i32p, _i32, _f32, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
@@ -92,7 +97,7 @@ def lib() -> ctypes.CDLL:
     L.h3a_plan_tiles.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     L.h3a_plan_tiles_ex.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
-                 "h3a_varlen_attn_fwd",
+                 "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
                  "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -245,6 +250,43 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, scale: float, out=None, stream=None):
     _check(lib().h3a_varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
                                      S, H, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
                                      _stream_handle(stream)))
+    return out
+
+
+def rmsnorm_rope(x, gamma, eps: float, cos_sin, rot_dim: int, x_out=None, stream=None):
+    """RMSNorm + NeoX rotary of one [S, H, D] tensor; in place unless x_out is given."""
+    x_out = x if x_out is None else x_out
+    S, H, D, sx = _token_major("x", x)
+    _, _, _, sxo = _token_major("x_out", x_out)
+    if tuple(x_out.shape) != (S, H, D) or x_out.dtype != x.dtype:
+        raise H3AError(H3A_ESHAPE, f"x_out shape/dtype {tuple(x_out.shape)}/{x_out.dtype} differs from x")
+    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_rmsnorm_rope(x.data_ptr(), x_out.data_ptr(), _dtype_code(x), S, H, D, sx, sxo,
+                                  gamma.data_ptr(), float(eps), cs, int(rot_dim), _stream_handle(stream)))
+    return x_out
+
+
+def varlen_attn_fwd_qnorm(q, k, v, cu_seqlens, scale: float, gamma_q, eps: float, cos_sin, rot_dim: int,
+                          out=None, stream=None):
+    """Bidirectional attention on raw q (normalised and rotated inside the kernel) and prepared k, v."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q", q)
+    _, Hkv, _, sk = _token_major("k", k)
+    _, _, _, sv = _token_major("v", v)
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (S, Hkv, D) or t.dtype != q.dtype:
+            raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} differs from "
+                                       f"{(S, Hkv, D)}/{q.dtype}")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=q.dtype, device=q.device)
+    _, _, _, so = _token_major("out", out)
+    cu = _i32_array(cu_seqlens)
+    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_varlen_attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           _dtype_code(q), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
+                                           float(scale), gamma_q.data_ptr(), float(eps), cs, int(rot_dim),
+                                           _stream_handle(stream)))
     return out
 
 

@@ -352,6 +352,42 @@ h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, voi
   return H3A_OK;
 }
 
+h3a_status h3a_rmsnorm_rope(const void* x, void* x_out, h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
+                            int64_t stride_x, int64_t stride_xo, const float* gamma, float eps,
+                            const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  const int V = dtype == H3A_BF16 ? 8 : 4;
+  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+  if ((rot_dim / 2) % V != 0)
+    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+  const size_t esz = elem_size(dtype);
+  h3a_status st;
+  if ((st = check_operand("x", x, S, H, D, stride_x, esz)) != H3A_OK) return st;
+  if ((st = check_operand("x_out", x_out, S, H, D, stride_xo, esz)) != H3A_OK) return st;
+  if (gamma == nullptr) return fail(H3A_EINVAL, "gamma is NULL");
+  if (!aligned(gamma, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+  if (rot_dim > 0 && S > 0) {
+    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  }
+  if (S == 0) return H3A_OK;
+  const bool inplace = x_out == x && stride_xo == stride_x;
+  if (!inplace && may_overlap(x_out, stride_xo, H, x, stride_x, H, S, D, esz))
+    return fail(H3A_EINVAL, "x_out overlaps x without being x itself");
+  // The fused kernel with no q heads: only its k pass runs.
+  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, x, x, x_out, x_out, S, 0, H, D, stride_x,
+                                             stride_x, stride_xo, stride_xo, gamma, gamma, eps, cos_sin, rot_dim,
+                                             stream);
+  if (e != hipSuccess) return fail_hip("rmsnorm_rope launch", e);
+  return H3A_OK;
+}
+
 h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
                                h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
                                int64_t stride_q, int64_t stride_k, int64_t stride_qo,
@@ -402,6 +438,50 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
                       : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
                                                  plan.n, scale, group, causal != 0, stream);
   if (e != hipSuccess) return fail_hip("varlen attention launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v, void* o, h3a_dtype dtype,
+                                     int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t stride_q,
+                                     int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                     const int32_t* cu_seqlens, int32_t nseg, float scale, const float* gamma_q,
+                                     float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  if (dtype != H3A_BF16)
+    return dtype == H3A_F32 ? fail(H3A_EUNSUPPORTED, "dtype: the fused Q norm path is bf16 only")
+                            : fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+  if (rot_dim % 32 != 0) return fail(H3A_EUNSUPPORTED, "rot_dim = %d must be a multiple of 32 on the fused path", rot_dim);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+  if (!aligned(gamma_q, 16)) return fail(H3A_EUNSUPPORTED, "gamma_q is not 16-byte aligned");
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  const size_t esz = elem_size(dtype);
+  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
+  if (rot_dim > 0 && S > 0) {
+    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  }
+  if (S == 0) return H3A_OK;
+  if (may_overlap(o, stride_o, Hq, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
+  if (may_overlap(o, stride_o, Hq, k, stride_k, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
+  if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
+  Plan plan;
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan)) != H3A_OK) return st;
+  hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                 plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
+  if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
   return H3A_OK;
 }
 

@@ -45,6 +45,15 @@
 //   * exp2 with scale * log2(e) folded into one FMA; the running max is
 //     only raised (and the accumulator rescaled) when a tile exceeds it by
 //     more than 2^8, which is exact and skips the rescale on most tiles.
+//   * Optionally (QNORM) the Q rows are RMS-normalised and rotated in the
+//     prologue, from raw q, fusing the Q half of the norm + rotary pass into
+//     the attention (the GB10 build fuses Q RMSNorm + rot96 RoPE into its
+//     attention front end: h3-spark model card, "What this config does").
+//     The arithmetic follows the standalone norm + rotary kernel operation
+//     for operation (per-16-byte-chunk FMA chains, the same xor-butterfly
+//     for the sum of squares, the same rotation FMAs and one RNE rounding),
+//     so q' -- and therefore the output -- is bit-identical to the unfused
+//     path.
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -114,12 +123,26 @@ __device__ __forceinline__ float other_half(float x, int hi) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL>
+}  // namespace
+
+// Arguments of the fused Q norm + rotary (QNORM variant).
+struct QNormArgs {
+  const float* gamma;    // [D] fp32 gain of q
+  const float* cos_sin;  // [2][S][half] fp32 rotary table
+  int64_t S;             // rows of the table
+  int32_t half;          // rot_dim / 2
+  float eps;
+};
+
+namespace {
+
+// RH: 16-dim blocks per rotary half when QNORM (rot_dim = 32 RH), else 0.
+template <int D, bool CAUSAL, bool QNORM, int RH>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
                      int64_t sk, int64_t sv, int64_t so, const WorkItem* __restrict__ items,
-                     float c, int kv_group) {
+                     float c, int kv_group, QNormArgs qn) {
   // The body uses LDS address-space pointers and gfx950-only builtins, which
   // exist only in the device pass; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -167,6 +190,62 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
+  }
+  if constexpr (QNORM) {
+    // The lane holds 16-byte chunks 2 ks + hi (dims (2 ks + hi) * 8 .. +7)
+    // of its query row: half the row; the other half is in lane ^ 32.
+    static_assert(2 * RH <= KS, "rotary dims exceed the head");
+    float p[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(float(qb[ks][e]), float(qb[ks][e]), ss);
+      p[ks] = ss;
+    }
+    // Butterfly over chunk bits 3..1 (ks bits), then bit 0 (the two halves):
+    // the standalone kernel's shuffle-xor tree, pair by pair.
+#pragma unroll
+    for (int m = KS / 2; m >= 1; m >>= 1) {
+      float t[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) t[ks] = p[ks] + p[ks ^ m];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) p[ks] = t[ks];
+    }
+    const float ssum = p[0] + other_half(p[0], hi);
+    const float r = 1.0f / sqrtf(ssum * (1.0f / float(D)) + qn.eps);
+    float y[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4* gp = reinterpret_cast<const float4*>(qn.gamma + (2 * ks + hi) * 8);
+      const float4 g0 = gp[0], g1 = gp[1];
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[ks][e] = float(qb[ks][e]) * r * g[e];
+    }
+    // Chunk 2 ks + hi (ks < RH) pairs with chunk 2 (ks + RH) + hi: the
+    // partner dim is i + rot_dim / 2, in the same lane.  Rows past the
+    // segment end read a valid table row (their outputs are not stored).
+    const int64_t trow = int64_t(it.seg_start) + min(qrow0 + l32, it.seg_len - 1);
+#pragma unroll
+    for (int ks = 0; ks < RH; ++ks) {
+      const float4* cp = reinterpret_cast<const float4*>(qn.cos_sin + trow * qn.half + (2 * ks + hi) * 8);
+      const float4* sp = reinterpret_cast<const float4*>(qn.cos_sin + (qn.S + trow) * qn.half + (2 * ks + hi) * 8);
+      const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = y[ks][e], b = y[ks + RH][e];
+        y[ks][e] = fmaf(a, cs[e], -b * sn[e]);
+        y[ks + RH][e] = fmaf(b, cs[e], a * sn[e]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[ks][e] = __bf16(y[ks][e]);
   }
 
   f32x16 oacc[DB];
@@ -403,15 +482,15 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool QNORM = false, int RH = 0>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                  int kv_group, hipStream_t stream) {
+                  int kv_group, const QNormArgs& qn, hipStream_t stream) {
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QNORM, RH>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c,
-                     kv_group);
+                     kv_group, qn);
   return hipGetLastError();
 }
 
@@ -423,12 +502,30 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 int32_t kv_group, bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
+  const QNormArgs none{};
   if (D == 128)
-    return causal ? launch<128, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream)
-                  : launch<128, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream);
+    return causal ? launch<128, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream)
+                  : launch<128, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream);
   if (D == 64)
-    return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream)
-                  : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, stream);
+    return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream)
+                  : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* v, void* o, int32_t D,
+                                      int64_t sq, int64_t sk, int64_t sv, int64_t so,
+                                      const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
+                                      const float* gamma_q, float eps, const float* cos_sin, int64_t S,
+                                      int32_t rot_dim, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  if (kv_group < 1 || rot_dim % 32 != 0) return hipErrorInvalidValue;
+  const QNormArgs qn{gamma_q, cos_sin, S, rot_dim / 2, eps};
+#define H3A_QNORM_CASE(DD, R)                                                                               \
+  if (D == DD && rot_dim == 32 * R)                                                                         \
+    return launch<DD, false, true, R>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, qn, stream);
+  H3A_QNORM_CASE(128, 0) H3A_QNORM_CASE(128, 1) H3A_QNORM_CASE(128, 2) H3A_QNORM_CASE(128, 3)
+  H3A_QNORM_CASE(128, 4) H3A_QNORM_CASE(64, 0) H3A_QNORM_CASE(64, 1) H3A_QNORM_CASE(64, 2)
+#undef H3A_QNORM_CASE
   return hipErrorInvalidValue;
 }
 

@@ -65,6 +65,15 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
                                 const WorkItem* items, int64_t n_items, float scale,
                                 int32_t kv_group, bool causal, hipStream_t stream);
 
+// Bidirectional bf16 attention that RMS-normalises and rotates the raw q rows
+// in its prologue (rot_dim a multiple of 32, at most D); q' is bit-identical
+// to launch_qk_rmsnorm_rope's.
+hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* v, void* o, int32_t D,
+                                      int64_t sq, int64_t sk, int64_t sv, int64_t so,
+                                      const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
+                                      const float* gamma_q, float eps, const float* cos_sin, int64_t S,
+                                      int32_t rot_dim, hipStream_t stream);
+
 hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,
                                int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                const WorkItem* items, int64_t n_items, float scale,

@@ -218,6 +218,48 @@ def test_grouped_tensors_side_by_side_pass_validation():
     assert st == h3a.H3A_EINVAL and "o overlaps" in h3a.last_error(), h3a.last_error()
 
 
+def attn_qn(dtype=h3a.H3A_BF16, S=300, Hq=8, Hkv=2, D=128, rot=96, g=P + (5 << 24), cs=P + (6 << 24), eps=1e-6,
+            o=P + (3 << 24), scale=0.088):
+    c, cp = i32((0, 100, 300))
+    return h3a.lib().h3a_varlen_attn_fwd_qnorm(P, P + (1 << 24), P + (2 << 24), o, dtype, S, Hq, Hkv, D, Hq * D,
+                                               Hkv * D, Hkv * D, Hq * D, cp, 2, scale, g, eps, cs, rot, None)
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(dtype=h3a.H3A_F32), h3a.H3A_EUNSUPPORTED, "bf16 only"),
+    (dict(dtype=5), h3a.H3A_EDTYPE, "dtype"),
+    (dict(rot=48), h3a.H3A_EUNSUPPORTED, "multiple of 32"),
+    (dict(rot=160), h3a.H3A_EINVAL, "rot_dim"),
+    (dict(rot=96, D=64), h3a.H3A_EINVAL, "rot_dim"),
+    (dict(g=None), h3a.H3A_EINVAL, "gamma_q"),
+    (dict(g=P + 4), h3a.H3A_EUNSUPPORTED, "gamma_q is not 16-byte aligned"),
+    (dict(cs=None), h3a.H3A_EINVAL, "cos_sin"),
+    (dict(eps=float("nan")), h3a.H3A_EINVAL, "eps"),
+    (dict(Hkv=3), h3a.H3A_ESHAPE, "does not divide"),
+    (dict(o=P + 256), h3a.H3A_EINVAL, "o overlaps q"),
+    (dict(scale=-1.0), h3a.H3A_EINVAL, "scale"),
+])
+def test_varlen_attn_fwd_qnorm_rejects(kw, status, word):
+    assert attn_qn(**kw) == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(H=0), h3a.H3A_EINVAL, "H ="),
+    (dict(rot=40), h3a.H3A_EUNSUPPORTED, "rot_dim / 2"),
+    (dict(xo=P + 256), h3a.H3A_EINVAL, "x_out overlaps x"),
+    (dict(g=None), h3a.H3A_EINVAL, "gamma"),
+    (dict(sx=100), h3a.H3A_ESHAPE, "x: token stride"),
+])
+def test_rmsnorm_rope_rejects(kw, status, word):
+    H = kw.get("H", 2)
+    sx = kw.get("sx", max(H, 1) * 128)
+    st = h3a.lib().h3a_rmsnorm_rope(P, kw.get("xo", P), h3a.H3A_BF16, 16, H, 128, sx, sx, kw.get("g", P + (2 << 24)),
+                                    1e-6, P + (4 << 24), kw.get("rot", 96), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
 def qk_ex(Hq=8, Hk=0, **kw):
     D, hd, hk = 128, Hq * 128, max(Hk, 1) * 128
     return h3a.lib().h3a_qk_rmsnorm_rope_ex(P, P + (1 << 24), P, P + (1 << 24), h3a.H3A_BF16, 16, Hq, Hk, D, hd, hk,

@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE, help="bf16 workload name (synth.configs.BF16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-q", action="store_true",
+                    help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
@@ -249,14 +251,26 @@ def main():
         return h3a.build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start,
                                        stop=w.lin_stop, stream=stream)
 
+    fused = args.fused_q
+    if fused and (w.causal or w.rot_dim % 32 != 0):
+        print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32 ({w.name})", file=sys.stderr)
+        return 2
+
+    def norm():
+        if fused:
+            return h3a.rmsnorm_rope(k, gk, w.eps, tab, w.rot_dim, x_out=kn, stream=stream)
+        return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
+
     def attention(cu):
+        if fused:  # raw q, normalised and rotated in the attention's prologue
+            return h3a.varlen_attn_fwd_qnorm(q, kn, v, cu, w.scale, gq, w.eps, tab, w.rot_dim, out=o, stream=stream)
         if w.causal or w.kv != w.heads:
             return h3a.varlen_attn_fwd_ex(qn, kn, v, cu, w.scale, causal=w.causal, out=o, stream=stream)
         return h3a.varlen_attn_fwd(qn, kn, v, cu, w.scale, out=o, stream=stream)
 
     def step():
         cu = table()
-        h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
+        norm()
         attention(cu)
         return cu
 
@@ -272,27 +286,32 @@ def main():
     if not np.isfinite(checksum):
         raise SystemExit("non-finite attention output")
 
-    # per-kernel durations with HIP events on the launch stream
+    # Per-kernel average launch duration: HIP events on the launch stream
+    # around n back-to-back launches of that call alone, divided by n.  (An
+    # event pair per launch would add the runtime's per-event cost to short
+    # kernels.)
     def timed(fn, n):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / n
 
     n_ev = max(args.steps, 10)
     attn_s = timed(lambda: attention(cu), n_ev)
-    norm_s = timed(lambda: h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn,
-                                               stream=stream), n_ev)
+    norm_s = timed(norm, n_ev)
     table_s = timed(table, n_ev)
 
     F = w.attention_flops()
     attn_tflops = F / attn_s / 1e12
     S, H, Hkv, D = w.tokens, w.heads, w.kv, w.head_dim
-    # q and k (H + Hkv heads) read and written, the table and both gains read
-    norm_bytes = 2 * (S * (H + Hkv) * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + 2 * D * 4
+    # q and k (H + Hkv heads; k only when fused) read and written, the table and gains read
+    normed_heads = Hkv if fused else H + Hkv
+    norm_bytes = 2 * (S * normed_heads * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + (1 if fused else 2) * D * 4
     # Q read and O written (H heads), K and V read (Hkv heads), once each
     attn_alg_bytes = 2 * S * H * D * 2 + 2 * S * Hkv * D * 2
     result = {
@@ -315,6 +334,8 @@ def main():
             "rot_dims": list(w.rot_dims), "rope_mode": w.rope_mode,
             "segments": [list(s) for s in w.segments],
             "parallelism": "single GPU",
+            "step": ("rope table + k norm/rotary + attention with q norm/rotary fused in its prologue" if fused
+                     else "rope table + q/k norm/rotary + attention"),
         },
         "pct_bf16_peak_step": 100.0 * F / step_s / 1e12 / PEAK_BF16_TFLOPS,
         "attn_ms": attn_s * 1e3,

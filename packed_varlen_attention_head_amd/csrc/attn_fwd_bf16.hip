@@ -191,10 +191,44 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int ks = 0; ks < KS; ++ks)
       qb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
   }
+  // QNORM operands (the gain of each of the lane's dims, cos/sin of its
+  // rotated pairs) load together with Q, so their latency overlaps; the
+  // arithmetic (qnorm_apply) runs once the first K/V tiles are in flight.
+  // The lane holds 16-byte chunks 2 ks + hi (dims (2 ks + hi) * 8 .. +7) of
+  // its query row, half the row; the other half is in lane ^ 32.  Chunk
+  // 2 ks + hi (ks < RH) pairs with chunk 2 (ks + RH) + hi: the partner dim is
+  // i + rot_dim / 2, in the same lane.
+  static_assert(2 * RH <= KS, "rotary dims exceed the head");
+  [[maybe_unused]] float qg[QNORM ? KS : 1][8];
+  [[maybe_unused]] float qc[RH > 0 ? RH : 1][8];
+  [[maybe_unused]] float qs[RH > 0 ? RH : 1][8];
   if constexpr (QNORM) {
-    // The lane holds 16-byte chunks 2 ks + hi (dims (2 ks + hi) * 8 .. +7)
-    // of its query row: half the row; the other half is in lane ^ 32.
-    static_assert(2 * RH <= KS, "rotary dims exceed the head");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4* gp = reinterpret_cast<const float4*>(qn.gamma + (2 * ks + hi) * 8);
+      const float4 g0 = gp[0], g1 = gp[1];
+      qg[ks][0] = g0.x; qg[ks][1] = g0.y; qg[ks][2] = g0.z; qg[ks][3] = g0.w;
+      qg[ks][4] = g1.x; qg[ks][5] = g1.y; qg[ks][6] = g1.z; qg[ks][7] = g1.w;
+    }
+    // Rows past the segment end read a valid table row (their outputs are
+    // not stored).
+    const int64_t trow = int64_t(it.seg_start) + min(qrow0 + l32, it.seg_len - 1);
+#pragma unroll
+    for (int ks = 0; ks < RH; ++ks) {
+      const float4* cp = reinterpret_cast<const float4*>(qn.cos_sin + trow * qn.half + (2 * ks + hi) * 8);
+      const float4* sp = reinterpret_cast<const float4*>(qn.cos_sin + (qn.S + trow) * qn.half + (2 * ks + hi) * 8);
+      const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+      qc[ks][0] = c0.x; qc[ks][1] = c0.y; qc[ks][2] = c0.z; qc[ks][3] = c0.w;
+      qc[ks][4] = c1.x; qc[ks][5] = c1.y; qc[ks][6] = c1.z; qc[ks][7] = c1.w;
+      qs[ks][0] = s0.x; qs[ks][1] = s0.y; qs[ks][2] = s0.z; qs[ks][3] = s0.w;
+      qs[ks][4] = s1.x; qs[ks][5] = s1.y; qs[ks][6] = s1.z; qs[ks][7] = s1.w;
+    }
+  }
+  // RMSNorm + rotary of qb in place, operation for operation as the
+  // standalone kernel: per-chunk FMA chains for the sum of squares, its
+  // shuffle-xor tree (chunk bits 3..1 are ks bits here, bit 0 is the lane
+  // half), the same rotation FMAs, one RNE rounding.
+  [[maybe_unused]] auto qnorm_apply = [&]() {
     float p[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -203,8 +237,6 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int e = 0; e < 8; ++e) ss = fmaf(float(qb[ks][e]), float(qb[ks][e]), ss);
       p[ks] = ss;
     }
-    // Butterfly over chunk bits 3..1 (ks bits), then bit 0 (the two halves):
-    // the standalone kernel's shuffle-xor tree, pair by pair.
 #pragma unroll
     for (int m = KS / 2; m >= 1; m >>= 1) {
       float t[KS];
@@ -217,36 +249,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const float r = 1.0f / sqrtf(ssum * (1.0f / float(D)) + qn.eps);
     float y[KS][8];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float4* gp = reinterpret_cast<const float4*>(qn.gamma + (2 * ks + hi) * 8);
-      const float4 g0 = gp[0], g1 = gp[1];
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[ks][e] = float(qb[ks][e]) * r * g[e];
-    }
-    // Chunk 2 ks + hi (ks < RH) pairs with chunk 2 (ks + RH) + hi: the
-    // partner dim is i + rot_dim / 2, in the same lane.  Rows past the
-    // segment end read a valid table row (their outputs are not stored).
-    const int64_t trow = int64_t(it.seg_start) + min(qrow0 + l32, it.seg_len - 1);
+      for (int e = 0; e < 8; ++e) y[ks][e] = float(qb[ks][e]) * r * qg[ks][e];
 #pragma unroll
-    for (int ks = 0; ks < RH; ++ks) {
-      const float4* cp = reinterpret_cast<const float4*>(qn.cos_sin + trow * qn.half + (2 * ks + hi) * 8);
-      const float4* sp = reinterpret_cast<const float4*>(qn.cos_sin + (qn.S + trow) * qn.half + (2 * ks + hi) * 8);
-      const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    for (int ks = 0; ks < RH; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float a = y[ks][e], b = y[ks + RH][e];
-        y[ks][e] = fmaf(a, cs[e], -b * sn[e]);
-        y[ks + RH][e] = fmaf(b, cs[e], a * sn[e]);
+        y[ks][e] = fmaf(a, qc[ks][e], -b * qs[ks][e]);
+        y[ks + RH][e] = fmaf(b, qc[ks][e], a * qs[ks][e]);
       }
-    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) qb[ks][e] = __bf16(y[ks][e]);
-  }
+  };
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -411,6 +429,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   load_k(0, IC<0>{});
   load_v(0, IC<0>{});
   if (ntiles > 1) load_k(1, IC<1>{});
+  if constexpr (QNORM) qnorm_apply();
   publish();
   if (active) {
     qk(IC<0>{}, s);

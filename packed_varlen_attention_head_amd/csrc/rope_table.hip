@@ -24,7 +24,8 @@
 // the fp64 positions are the exact IEEE results of those expressions.
 //
 // One thread per (token, angle).  Segment descriptors travel in the kernel
-// arguments, kMaxSegs per launch, so no device staging buffer is needed.
+// arguments, kMaxSegs per launch (an argument block under 1 KiB), so no
+// device staging buffer is needed.
 #include <cstdint>
 
 #include "common.h"
@@ -32,7 +33,7 @@
 namespace h3a {
 namespace {
 
-constexpr int kMaxSegs = 32;
+constexpr int kMaxSegs = 16;
 constexpr int kMaxHalf = 64;  // R/2 <= D/2 <= 64
 
 struct RopeArgs {
@@ -46,10 +47,11 @@ struct RopeArgs {
   int32_t gh[kMaxSegs];   // grid H
   int32_t gw[kMaxSegs];   // grid W
   double lin_start[3];
-  double lin_step[kMaxSegs][3];
+  double lin_stop[3];
   double inv_freq[kMaxHalf];
-  int32_t axis[kMaxHalf]; // 0 = t, 1 = h, 2 = w
+  int8_t axis[kMaxHalf];  // 0 = t, 1 = h, 2 = w
 };
+static_assert(sizeof(RopeArgs) <= 1024, "kernel argument block");
 
 __global__ void __launch_bounds__(256) rope_table_kernel(RopeArgs a, float* __restrict__ cos_sin,
                                                           int32_t first_token, int32_t ntok) {
@@ -67,7 +69,9 @@ __global__ void __launch_bounds__(256) rope_table_kernel(RopeArgs a, float* __re
   const int32_t i = ax == 0 ? n / hw : (ax == 1 ? (n / a.gw[s]) % a.gh[s] : n % a.gw[s]);
   double p;
   if (a.mode == kRopeLinspace) {
-    p = double(i) * a.lin_step[s][ax] + a.lin_start[ax];
+    // numpy.linspace's step, (stop - start) / n; IEEE division and product.
+    const double step = (a.lin_stop[ax] - a.lin_start[ax]) / double(ext);
+    p = double(i) * step + a.lin_start[ax];
   } else if (a.mode == kRopeNormalized) {
     p = (((double(i) + 0.5) / double(ext)) * 2.0 - 1.0) * (2.0 * 3.141592653589793);
     if (n >= a.gt[s] * hw) p = 0.0;  // suffix token: identity
@@ -92,9 +96,12 @@ hipError_t launch_rope_table(const RopeTableSpec& spec, const int32_t* segments,
   a.mode = spec.mode;
   for (int i = 0; i < half; ++i) {
     a.inv_freq[i] = spec.inv_freq[i];
-    a.axis[i] = spec.axis_of[i];
+    a.axis[i] = int8_t(spec.axis_of[i]);
   }
-  for (int ax = 0; ax < 3; ++ax) a.lin_start[ax] = spec.lin_start[ax];
+  for (int ax = 0; ax < 3; ++ax) {
+    a.lin_start[ax] = spec.lin_start[ax];
+    a.lin_stop[ax] = spec.lin_stop[ax];
+  }
   for (int32_t s0 = 0; s0 < nseg; s0 += kMaxSegs) {
     const int32_t n = nseg - s0 < kMaxSegs ? nseg - s0 : kMaxSegs;
     a.nseg = n;
@@ -105,9 +112,6 @@ hipError_t launch_rope_table(const RopeTableSpec& spec, const int32_t* segments,
       a.gh[i] = g[1];
       a.gw[i] = g[2];
       a.len[i] = g[3];
-      // numpy.linspace's step, (stop - start) / n, rounded once on the host.
-      for (int ax = 0; ax < 3; ++ax)
-        a.lin_step[i][ax] = (spec.lin_stop[ax] - spec.lin_start[ax]) / double(g[ax]);
     }
     const int32_t first = starts[s0];
     const int32_t ntok = starts[s0 + n - 1] + a.len[n - 1] - first;

@@ -33,7 +33,8 @@ sqrt are the only library primitives used):
    contract.]
    The encoder text tower's causal grouped-query attention (query i of a
    segment sees keys 0..i; K/V heads broadcast over their query groups) is
-   section 5b.
+   section 5b; the low-precision variant (Q and K rounded to FP8 E4M3 before
+   the score product) is section 5c.
 
 Readings where the pages are silent (each is listed in the design doc):
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
@@ -379,6 +380,62 @@ def varlen_attention_gqa_rows(q, k, v, cu, scale: float, rows, causal: bool = Fa
             qs = np.asarray(q[r:r + 1, h], dtype=np.float64)
             out[n, h] = segment_head_attention_masked(qs, k[a:end, kh], v[a:end, kh], scale, False)[0]
     return out
+
+
+# ----------------------------------------------------------------------------
+# 5c. Low-precision attention: QK^T on FP8 e4m3 operands
+#
+# The low-precision attention the pages' GB10 builds use (SageAttention 2++,
+# Comfy Kitchen's INT8 Q/K/V; h3-spark model card, runtime options and "What
+# this config does") quantise Q and K before the score product.  Here Q' and
+# K' are rounded to OCP FP8 E4M3 ("fn": no infinities; exponent bias 7, three
+# mantissa bits, subnormals down to 2^-9, largest finite 448, codes 0x7f and
+# 0xff NaN), round to nearest even, saturating at +-448.  Reading where the
+# pages stop short: no per-block scale is applied, since RMSNorm bounds every
+# element of q' and k' by sqrt(D) max|gamma| (well inside e4m3's range for
+# the gains here) and FP8's relative precision does not depend on scale.  The
+# rest of the attention is exact.
+# ----------------------------------------------------------------------------
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """fp64 value of each E4M3 code (uint8); NaN for 0x7f and 0xff."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to the even mantissa), saturating
+    at +-448; x must not be NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    # spacing of the codes around a: 2^-9 below 2^-6, else 2^(floor(log2 a) - 3)
+    ex = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    ulp = np.exp2(ex - 3.0)
+    n = np.rint(a / ulp)  # np.rint rounds halves to even
+    v = np.minimum(n * ulp, 448.0)
+    # code from the rounded magnitude
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))
+    sub = v < 2.0 ** -6
+    mant = np.where(sub, v / 2.0 ** -9, v / np.exp2(e) * 8.0 - 8.0)
+    expf = np.where(sub, 0, e + 7)
+    code = (expf.astype(np.int64) << 3) + np.rint(mant).astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_round(x) -> np.ndarray:
+    """x rounded to the nearest E4M3 value (saturating), as fp64."""
+    return e4m3_decode(e4m3_encode(x))
+
+
+def varlen_attention_fp8qk(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """varlen_attention_gqa with q and k rounded to E4M3 first."""
+    return varlen_attention_gqa(e4m3_round(q), e4m3_round(k), v, cu, scale, causal=causal)
 
 
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):

@@ -522,6 +522,73 @@ def check_gqa_rows_variant(O):
 
 
 # ---------------------------------------------------------------------------
+# FP8 E4M3 codec and the low-precision attention
+# ---------------------------------------------------------------------------
+
+def check_e4m3_decode_table(O):
+    g = golden()["e4m3"]
+    for code, val in g["decode"].items():
+        got = O.e4m3_decode(np.array([int(code)], dtype=np.uint8))[0]
+        assert got == val and np.signbit(got) == np.signbit(val), (code, got, val)
+    for code in g["nan_codes"]:
+        assert np.isnan(O.e4m3_decode(np.array([code], dtype=np.uint8))[0])
+    v = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(v) > 0) and v[-1] == 448.0  # 127 increasing non-negative values
+    assert np.array_equal(O.e4m3_decode(np.arange(0x80, 0xFF, dtype=np.uint8)), -v)
+
+
+def check_e4m3_encode(O):
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = O.e4m3_decode(finite)
+    assert np.array_equal(O.e4m3_encode(vals), finite)  # every finite code round-trips
+    # midpoints between neighbours go to the even mantissa; just off the midpoint, to the nearer
+    pos = O.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    for i in range(len(pos) - 1):
+        lo, hi = pos[i], pos[i + 1]
+        mid = 0.5 * (lo + hi)
+        want = i if i % 2 == 0 else i + 1
+        assert O.e4m3_encode(np.array([mid]))[0] == want, (i, mid)
+        assert O.e4m3_encode(np.array([mid - (hi - lo) * 1e-3]))[0] == i
+        assert O.e4m3_encode(np.array([mid + (hi - lo) * 1e-3]))[0] == i + 1
+        assert O.e4m3_encode(np.array([-mid]))[0] == 0x80 | want
+    # saturation and flush
+    assert list(O.e4m3_encode(np.array([460.0, 1e6, -1e9, 2.0 ** -10, -(2.0 ** -11)]))) == [0x7E, 0x7E, 0xFE, 0, 0x80]
+
+
+def check_e4m3_matches_torch(O):
+    """torch's float8_e4m3fn conversion (round to nearest even) on random in-range values."""
+    import torch
+
+    r = _rng(19)
+    x = r.normal(size=50000) * np.exp2(r.uniform(-12, 9, size=50000))
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+
+
+def check_fp8qk_attention(O):
+    """E4M3-representable q, k pass through unchanged; otherwise the score product sees the
+    rounded operands; the rounding error on normalised inputs stays small."""
+    r = _rng(20)
+    lens = [40, 1, 77]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    q8 = O.e4m3_decode(r.integers(0, 0x7F, size=(S, 4, 16)).astype(np.uint8)) * r.choice([-1, 1], size=(S, 4, 16))
+    k8 = O.e4m3_decode(r.integers(0, 0x70, size=(S, 2, 16)).astype(np.uint8))
+    v = r.normal(size=(S, 2, 16))
+    for causal in (False, True):
+        assert np.array_equal(O.varlen_attention_fp8qk(q8, k8, v, cu, 0.05, causal),
+                              O.varlen_attention_gqa(q8, k8, v, cu, 0.05, causal))
+    q, k = r.normal(size=(S, 4, 16)), r.normal(size=(S, 2, 16))
+    a = O.varlen_attention_fp8qk(q, k, v, cu, 0.25)
+    b = O.varlen_attention_gqa(q, k, v, cu, 0.25)
+    rel = np.abs(a - b).sum() / np.abs(b).sum()
+    assert 0 < rel < 0.05, rel
+    # and rounding only one operand is not the same thing
+    assert not np.allclose(a, O.varlen_attention_gqa(O.e4m3_round(q), k, v, cu, 0.25), rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
 
@@ -598,6 +665,10 @@ ALL_CHECKS = [
     check_gqa_is_repeated_kv,
     check_causal_gqa_sdpa,
     check_gqa_rows_variant,
+    check_e4m3_decode_table,
+    check_e4m3_encode,
+    check_e4m3_matches_torch,
+    check_fp8qk_attention,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

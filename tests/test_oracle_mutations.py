@@ -192,7 +192,43 @@ def _gqa_rows_one_key_short(q, k, v, cu, scale, rows, causal=False):
     return out
 
 
+def _decode_bias_8(codes):
+    return oracle.e4m3_decode(codes) / 2.0
+
+
+def _encode_half_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    ex = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    ulp = np.exp2(ex - 3.0)
+    v = np.minimum(np.floor(a / ulp + 0.5) * ulp, 448.0)
+    return oracle.e4m3_encode(np.copysign(v, x))
+
+
+def _encode_no_saturation(x):
+    x = np.asarray(x, dtype=np.float64)
+    c = oracle.e4m3_encode(x)
+    return np.where(np.abs(x) > 448.0, np.uint8(0x7F) | (c & 0x80), c).astype(np.uint8)
+
+
+def _encode_truncating(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    ex = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    ulp = np.exp2(ex - 3.0)
+    return oracle.e4m3_encode(np.copysign(np.floor(a / ulp) * ulp, x))
+
+
+def _fp8qk_only_q(q, k, v, cu, scale, causal=False):
+    return oracle.varlen_attention_gqa(oracle.e4m3_round(q), k, v, cu, scale, causal=causal)
+
+
 MUTANTS = {
+    "e4m3_decode_bias_8": dict(e4m3_decode=_decode_bias_8),
+    "e4m3_round_half_up": dict(e4m3_encode=_encode_half_up),
+    "e4m3_no_saturation": dict(e4m3_encode=_encode_no_saturation),
+    "e4m3_truncating": dict(e4m3_encode=_encode_truncating),
+    "fp8qk_rounds_only_q": dict(varlen_attention_fp8qk=_fp8qk_only_q),
     "causal_one_key_too_many": dict(varlen_attention_gqa=_gqa_with(_masked_diagonal_too)),
     "gqa_modulo_heads": dict(varlen_attention_gqa=_gqa_modulo_heads),
     "gqa_causal_ignored": dict(varlen_attention_gqa=_gqa_causal_ignored),

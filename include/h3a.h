@@ -253,6 +253,41 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
                                      float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
 /*
+ * Low-precision attention, step 1: bf16 [S, H, D] (token stride stride_x
+ * elements) to OCP FP8 E4M3 codes ("fn" variant: no infinities, largest
+ * finite 448), one byte per element in y [S, H, D] (token stride stride_y
+ * bytes, a multiple of 16).  Round to nearest even, saturating at +-448.
+ * This quantises q' and k' for h3a_varlen_attn_fwd_fp8qk (the pages' GB10
+ * builds run Q and K through low-precision attention kernels --
+ * SageAttention 2++, Comfy Kitchen's INT8 attention -- after the Q RMSNorm +
+ * rotary; h3-spark model card, runtime options and "What this config does").
+ * Errors: EINVAL (null, sizes, overlap), ESHAPE, EUNSUPPORTED, EHIP.
+ */
+h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32_t D, int64_t stride_x,
+                             int64_t stride_y, hipStream_t stream);
+
+/*
+ * Low-precision attention, step 2: h3a_varlen_attn_fwd_ex with q and k given
+ * as E4M3 codes.  The score product q.k runs on the FP8 MFMA (twice the bf16
+ * rate) with fp32 accumulation; the softmax, the bf16 probabilities, the PV
+ * product with bf16 v and the bf16 output are those of the bf16 path.
+ *
+ * q8             device uint8 [S, Hq, D] E4M3 codes, token stride stride_q
+ *                bytes (a multiple of 16).
+ * k8             device uint8 [S, Hkv, D] E4M3 codes, token stride stride_k
+ *                bytes.
+ * v, o           device bf16 as for h3a_varlen_attn_fwd_ex.
+ * The result equals attention on the E4M3-rounded q, k up to the bf16 path's
+ * rounding; against exact attention on unrounded q, k it carries the E4M3
+ * rounding of the scores (three mantissa bits per operand element).
+ * Errors: as h3a_varlen_attn_fwd_ex.
+ */
+h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                     int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                     int32_t causal, hipStream_t stream);
+
+/*
  * Varlen attention with grouped K/V heads and an optional causal mask: the
  * encoder text tower's causal GQA (vllm.cpp PR #26, encoder-tower commit,
  * "Causal GQA attention": K/V heads are broadcast across their query group).

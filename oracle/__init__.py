@@ -433,6 +433,17 @@ def e4m3_round(x) -> np.ndarray:
     return e4m3_decode(e4m3_encode(x))
 
 
+def bf16_round(x) -> np.ndarray:
+    """x rounded to the nearest bfloat16 value (8 significant bits, ties to even),
+    directly from fp64; normal-range values (the storage precision of q' and k'
+    whose E4M3 codes the low-precision path takes)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    ex = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    ulp = np.exp2(ex - 7.0)
+    return np.copysign(np.rint(a / ulp) * ulp, x)
+
+
 def varlen_attention_fp8qk(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
     """varlen_attention_gqa with q and k rounded to E4M3 first."""
     return varlen_attention_gqa(e4m3_round(q), e4m3_round(k), v, cu, scale, causal=causal)

@@ -38,6 +38,8 @@ EXPORTS = (
     "h3a_varlen_attn_fwd",
     "h3a_varlen_attn_fwd_ex",
     "h3a_varlen_attn_fwd_qnorm",
+    "h3a_varlen_attn_fwd_fp8qk",
+    "h3a_quantize_e4m3",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.h3a_rmsnorm_rope.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd_qnorm.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                             _i64, _c_i32p, _i32, _f32, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_quantize_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
+    L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+                                            _c_i32p, _i32, _f32, _i32, _vp]
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
@@ -98,6 +103,7 @@ def lib() -> ctypes.CDLL:
     L.h3a_plan_tiles_ex.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
                  "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
+                 "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk",
                  "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -286,6 +292,43 @@ def varlen_attn_fwd_qnorm(q, k, v, cu_seqlens, scale: float, gamma_q, eps: float
     _check(lib().h3a_varlen_attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                            _dtype_code(q), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
                                            float(scale), gamma_q.data_ptr(), float(eps), cs, int(rot_dim),
+                                           _stream_handle(stream)))
+    return out
+
+
+def quantize_e4m3(x, out=None, stream=None):
+    """bf16 [S, H, D] -> uint8 [S, H, D] OCP FP8 E4M3 codes (nearest even, saturating)."""
+    import torch
+
+    S, H, D, sx = _token_major("x", x)
+    if x.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"x must be bfloat16, got {x.dtype}")
+    if out is None:
+        out = torch.empty((S, H, D), dtype=torch.uint8, device=x.device)
+    _, _, _, sy = _token_major("out", out)
+    if tuple(out.shape) != (S, H, D) or out.dtype != torch.uint8:
+        raise H3AError(H3A_ESHAPE, f"out must be uint8 {(S, H, D)}, got {out.dtype} {tuple(out.shape)}")
+    _check(lib().h3a_quantize_e4m3(x.data_ptr(), out.data_ptr(), S, H, D, sx, sy, _stream_handle(stream)))
+    return out
+
+
+def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
+    """Attention with q8 [S, Hq, D] and k8 [S, Hkv, D] as uint8 E4M3 codes, v bf16 [S, Hkv, D]."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q8", q8)
+    _, Hkv, _, sk = _token_major("k8", k8)
+    _, _, _, sv = _token_major("v", v)
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise H3AError(H3A_EDTYPE, f"q8/k8 must hold uint8 E4M3 codes, got {q8.dtype}/{k8.dtype}")
+    if tuple(k8.shape) != (S, Hkv, D) or tuple(v.shape) != (S, Hkv, D) or v.dtype != torch.bfloat16:
+        raise H3AError(H3A_ESHAPE, f"k8 {tuple(k8.shape)} / v {tuple(v.shape)} {v.dtype} do not match q8")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=v.device)
+    _, _, _, so = _token_major("out", out)
+    cu = _i32_array(cu_seqlens)
+    _check(lib().h3a_varlen_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), S, Hq, Hkv, D,
+                                           sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale), int(bool(causal)),
                                            _stream_handle(stream)))
     return out
 

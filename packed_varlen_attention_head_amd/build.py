@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh3a.so")
 
-SOURCES = ["api.cpp", "planner.cpp", "rope_table.hip", "qk_norm_rope.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "rope_table.hip", "qk_norm_rope.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
+           "quantize_fp8.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

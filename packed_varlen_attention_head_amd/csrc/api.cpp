@@ -485,6 +485,59 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
   return H3A_OK;
 }
 
+h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32_t D, int64_t stride_x,
+                             int64_t stride_y, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  h3a_status st;
+  if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
+  if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  // y (bytes) against x (bf16): plain byte ranges.
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+  const uintptr_t x1 = x0 + uintptr_t(((S - 1) * stride_x + int64_t(H) * D) * 2);
+  const uintptr_t y1 = y0 + uintptr_t((S - 1) * stride_y + int64_t(H) * D);
+  if (x0 < y1 && y0 < x1) return fail(H3A_EINVAL, "y overlaps x");
+  hipError_t e = h3a::launch_quantize_e4m3(x, y, S, H * D, stride_x, stride_y, stream);
+  if (e != hipSuccess) return fail_hip("quantize_e4m3 launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                     int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                     int32_t causal, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+  if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  // o (bf16) against the byte-coded q and k, and against v (bf16)
+  const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+  const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+  if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
+  if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
+  if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
+  Plan plan;
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan)) != H3A_OK) return st;
+  hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
+                                            scale, Hq / Hkv, causal != 0, stream);
+  if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
+  return H3A_OK;
+}
+
 h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
                                int64_t stride_q, int64_t stride_k, int64_t stride_v,

@@ -54,6 +54,13 @@
 //     for the sum of squares, the same rotation FMAs and one RNE rounding),
 //     so q' -- and therefore the output -- is bit-identical to the unfused
 //     path.
+//   * Low-precision variant (F8): Q and K arrive as FP8 E4M3 codes and the
+//     score product runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales),
+//     at twice the bf16 MFMA rate, with K tiles of half the bytes; the
+//     softmax and the PV product (bf16) are unchanged.  Each lane carries 32
+//     consecutive dims of its key (A) and query (B) row per 64-dim step: the
+//     instruction pairs A and B elements by (lane half, byte), so any
+//     assignment shared by both operands contracts correctly.
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -73,6 +80,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
@@ -96,6 +104,14 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+// FP8 K rows are D bytes (8 or 4 chunks of 16 bytes): two (D = 128) or four
+// (D = 64) rows share a 256-byte bank window, so the swizzle takes the
+// remaining row bits.
+template <int D>
+__device__ __forceinline__ int k8_swz(int row) {
+  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = __bf16(lo);
   const __bf16 b = __bf16(hi);
@@ -106,10 +122,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // `base` (rows <= 0: none): loads past the last row return zeros.  32-bit
 // arithmetic (the host bounds max_rows * stride_bytes) and readfirstlane keep
 // it a branch-free scalar, so loads need no per-lane waterfall.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows, int max_rows,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int max_rows,
                                                             int stride_bytes) {
   const int r = __builtin_amdgcn_readfirstlane(rows < 0 ? 0 : (rows > max_rows ? max_rows : rows));
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            __builtin_amdgcn_readfirstlane(r * stride_bytes), 0x00020000);
 }
 
@@ -137,7 +153,8 @@ struct QNormArgs {
 namespace {
 
 // RH: 16-dim blocks per rotary half when QNORM (rot_dim = 32 RH), else 0.
-template <int D, bool CAUSAL, bool QNORM, int RH>
+// F8: q and k hold E4M3 codes (token strides sq, sk in bytes).
+template <int D, bool CAUSAL, bool QNORM, int RH, bool F8>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
@@ -152,10 +169,16 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int ROWB = D * 2;                     // bytes per LDS row
   constexpr int NDMA = kBN * CH / (64 * kWaves);  // 16-byte loads per thread per tile and operand
   static_assert(NDMA >= 1 && CH >= 8, "tile layout");
+  constexpr int KESZ = F8 ? 1 : 2;                 // bytes per K (and Q) element
+  constexpr int KROWB = D * KESZ;                  // bytes per K row
+  constexpr int KCH = KROWB / 16;                  // 16-byte chunks per K row
+  constexpr int NDMAK = kBN * KCH / (64 * kWaves);
+  constexpr int KS8 = D / 64;                      // FP8 MFMA k-steps over the head dim
+  static_assert(NDMAK >= 1 && !(F8 && QNORM), "tile layout / variant");
 
   // One object per ring slot, so alias analysis can tell a load into one slot
   // from reads of another (otherwise every LDS read waits for all loads).
-  __shared__ uint16_t k_slot0[kBN * D], k_slot1[kBN * D];
+  __shared__ uint16_t k_slot0[kBN * KROWB / 2], k_slot1[kBN * KROWB / 2];
   __shared__ uint16_t v_slot0[kBN * D], v_slot1[kBN * D];
   // Slot pointers: compile-time choice for IC<> slots, a select otherwise.
   auto kslot = [&](auto slot) -> uint16_t* {
@@ -184,12 +207,24 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // Q as the B operand: lane holds query (qrow0 + l32), dims ks*16 + hi*8 .. +8.
   bf16x8 qb[KS];
-  {
+  // F8: lane holds query (qrow0 + l32), dims ks8*64 + hi*32 .. +32.
+  [[maybe_unused]] i32x8 qb8[F8 ? KS8 : 1];
+  if constexpr (!F8) {
     const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq) * 2);
     const int off = (l32 * int(sq) + hi * 8) * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
+  } else {
+    const uint8_t* q8 = reinterpret_cast<const uint8_t*>(q);
+    const auto rq = rows_rsrc(q8 + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq));
+    const int off = l32 * int(sq) + hi * 32;
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      const auto lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64, 0, 0);
+      const auto up = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64 + 16, 0, 0);
+      qb8[ks] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(up[0]), int(up[1]), int(up[2]), int(up[3])};
+    }
   }
   // QNORM operands (the gain of each of the lane's dims, cos/sin of its
   // rotated pairs) load together with Q, so their latency overlaps; the
@@ -274,18 +309,30 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // LDS-bound loads: slot s = (i * kWaves + wave) * 64 + lane holds physical
   // chunk s % CH of row s / CH; the lane fetches the logical chunk stored there.
-  int koff[NDMA], voff[NDMA];
+  int koff[NDMAK], voff[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMAK; ++i) {
+    const int s = (i * kWaves + wave) * 64 + lane;
+    const int row = s / KCH, pc = s % KCH;
+    koff[i] = row * int(sk) * KESZ + ((pc ^ (F8 ? k8_swz<D>(row) : k_swz<D>(row))) * 16);
+  }
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int s = (i * kWaves + wave) * 64 + lane;
     const int row = s / CH, pc = s % CH;
-    koff[i] = row * int(sk) * 2 + ((pc ^ k_swz<D>(row)) * 16);
     voff[i] = row * int(sv) * 2 + ((pc ^ v_swz<D>(row)) * 16);
   }
   // K operand reads: row l32 (+32 kb), logical chunk 2 ks + hi.
   int kaddr[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ k_swz<D>(l32)) * 16);
+  // F8 K operand reads: row l32 (+32 kb), chunks 4 ks8 + 2 hi + {0, 1}.
+  [[maybe_unused]] int kaddr8[F8 ? KS8 : 1][2];
+  if constexpr (F8)
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) kaddr8[ks][j] = l32 * KROWB + (((4 * ks + 2 * hi + j) ^ k8_swz<D>(l32)) * 16);
   // V^T operand reads (transposing): 16-lane group g reads keys
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
@@ -300,7 +347,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
-  const uint16_t* kbase = k + int64_t(it.seg_start) * sk + kv_off;
+  const char* kbase = reinterpret_cast<const char*>(k) + (int64_t(it.seg_start) * sk + kv_off) * KESZ;
   const uint16_t* vbase = v + int64_t(it.seg_start) * sv + kv_off;
   // Keys the item needs: the whole segment, or (causal) up to its last row.
   const int nkeys = CAUSAL ? min(it.seg_len, it.q_start + kBM) : it.seg_len;
@@ -311,9 +358,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // ---- building blocks ------------------------------------------------------
   auto load_k = [&](int t, auto slot) {
     const int key0 = t * kBN;
-    const auto r = rows_rsrc(kbase + int64_t(key0) * sk, it.seg_len - key0, kBN, int(sk) * 2);
+    const auto r = rows_rsrc(kbase + int64_t(key0) * sk * KESZ, it.seg_len - key0, kBN, int(sk) * KESZ);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i)
+    for (int i = 0; i < NDMAK; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                koff[i], 0, 0, 0);
   };
@@ -330,10 +377,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
+      if constexpr (!F8) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const LDS bf16x8*)((const LDS char*)kslot(slot) + kaddr[ks] + kb * 32 * ROWB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *(const LDS bf16x8*)((const LDS char*)kslot(slot) + kaddr[ks] + kb * 32 * ROWB);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS8; ++ks) {
+          const LDS char* kp = (const LDS char*)kslot(slot) + kb * 32 * KROWB;
+          const uint4 lo = *(const LDS uint4*)(kp + kaddr8[ks][0]);
+          const uint4 up = *(const LDS uint4*)(kp + kaddr8[ks][1]);
+          const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
+          // formats 0/0: E4M3 x E4M3; E8M0 scales 127 = 1.0
+          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[ks], sacc[kb], 0, 0, 0, 127, 0, 127);
+        }
       }
     }
   };
@@ -501,12 +560,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool CAUSAL, bool QNORM = false, int RH = 0>
+template <int D, bool CAUSAL, bool QNORM = false, int RH = 0, bool F8 = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
                   int kv_group, const QNormArgs& qn, hipStream_t stream) {
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QNORM, RH>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QNORM, RH, F8>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c,
                      kv_group, qn);
@@ -528,6 +587,23 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
   if (D == 64)
     return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream)
                   : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int32_t D, int64_t sq,
+                                 int64_t sk, int64_t sv, int64_t so, const WorkItem* items, int64_t n_items,
+                                 float scale, int32_t kv_group, bool causal, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  if (kv_group < 1) return hipErrorInvalidValue;
+  const QNormArgs none{};
+#define H3A_F8_CASE(DD)                                                                                     \
+  if (D == DD)                                                                                              \
+    return causal ? launch<DD, true, false, 0, true>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,     \
+                                                     kv_group, none, stream)                               \
+                  : launch<DD, false, false, 0, true>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,    \
+                                                      kv_group, none, stream);
+  H3A_F8_CASE(128) H3A_F8_CASE(64)
+#undef H3A_F8_CASE
   return hipErrorInvalidValue;
 }
 

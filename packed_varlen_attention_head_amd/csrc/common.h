@@ -74,6 +74,17 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
                                       const float* gamma_q, float eps, const float* cos_sin, int64_t S,
                                       int32_t rot_dim, hipStream_t stream);
 
+// Attention whose q and k are FP8 E4M3 codes (token strides in bytes); the
+// score product runs on FP8 MFMA, the rest as launch_attn_fwd_bf16.
+hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int32_t D, int64_t sq,
+                                 int64_t sk, int64_t sv, int64_t so, const WorkItem* items, int64_t n_items,
+                                 float scale, int32_t kv_group, bool causal, hipStream_t stream);
+
+// bf16 [S, row_elems] rows (token stride sx elements) -> E4M3 codes (token
+// stride sy bytes); row_elems a multiple of 8.
+hipError_t launch_quantize_e4m3(const void* x, void* y, int64_t S, int32_t row_elems, int64_t sx, int64_t sy,
+                                hipStream_t stream);
+
 hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,
                                int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                const WorkItem* items, int64_t n_items, float scale,

@@ -566,6 +566,20 @@ def check_e4m3_matches_torch(O):
     assert np.array_equal(O.e4m3_encode(x), ref)
 
 
+def check_bf16_round(O):
+    """Against torch's bfloat16 conversion of fp32 values (one rounding), hand-derived ties
+    (1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to 1; 1 + 3 * 2^-8 ties to 1 + 2^-6),
+    and representable values unchanged."""
+    import torch
+
+    r = _rng(21)
+    x = (r.normal(size=20000) * np.exp2(r.uniform(-20, 20, size=20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(x.astype(np.float64)), ref)
+    t = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.0, 1 + 2.0 ** -7])
+    assert np.array_equal(O.bf16_round(t), [1.0, 1 + 2.0 ** -6, -1.0, 3.0, 1 + 2.0 ** -7])
+
+
 def check_fp8qk_attention(O):
     """E4M3-representable q, k pass through unchanged; otherwise the score product sees the
     rounded operands; the rounding error on normalised inputs stays small."""
@@ -668,6 +682,7 @@ ALL_CHECKS = [
     check_e4m3_decode_table,
     check_e4m3_encode,
     check_e4m3_matches_torch,
+    check_bf16_round,
     check_fp8qk_attention,
     check_chain_shift_invariance,
     check_chain_composition,

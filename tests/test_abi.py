@@ -260,6 +260,40 @@ def test_rmsnorm_rope_rejects(kw, status, word):
     assert word in h3a.last_error(), h3a.last_error()
 
 
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(H=0), h3a.H3A_EINVAL, "H ="),
+    (dict(D=96), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(sy=120), h3a.H3A_ESHAPE, "y: token stride"),
+    (dict(sy=264), h3a.H3A_EUNSUPPORTED, "multiple of 16 bytes"),
+    (dict(y=P + 256), h3a.H3A_EINVAL, "y overlaps x"),
+    (dict(y=None), h3a.H3A_EINVAL, "y is NULL"),
+])
+def test_quantize_e4m3_rejects(kw, status, word):
+    H, D = kw.get("H", 2), kw.get("D", 128)
+    st = h3a.lib().h3a_quantize_e4m3(P, kw.get("y", P + (1 << 24)), 16, H, D, max(H, 1) * D, kw.get("sy", max(H, 1) * D),
+                                     None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(Hkv=3), h3a.H3A_ESHAPE, "does not divide"),
+    (dict(causal=5), h3a.H3A_EINVAL, "causal"),
+    (dict(sq=1032), h3a.H3A_EUNSUPPORTED, "q: token stride"),
+    (dict(sk=64), h3a.H3A_ESHAPE, "k: token stride"),
+    (dict(o=P + 512), h3a.H3A_EINVAL, "o overlaps q"),
+    (dict(D=80), h3a.H3A_EUNSUPPORTED, "head_dim"),
+])
+def test_varlen_attn_fwd_fp8qk_rejects(kw, status, word):
+    Hq, Hkv, D = 8, kw.get("Hkv", 2), kw.get("D", 128)
+    c, cp = i32((0, 100, 300))
+    st = h3a.lib().h3a_varlen_attn_fwd_fp8qk(P, P + (1 << 24), P + (2 << 24), kw.get("o", P + (3 << 24)), 300, Hq, Hkv,
+                                             D, kw.get("sq", Hq * D), kw.get("sk", Hkv * D), Hkv * D, Hq * D, cp, 2,
+                                             0.088, kw.get("causal", 0), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
 def qk_ex(Hq=8, Hk=0, **kw):
     D, hd, hk = 128, Hq * 128, max(Hk, 1) * 128
     return h3a.lib().h3a_qk_rmsnorm_rope_ex(P, P + (1 << 24), P, P + (1 << 24), h3a.H3A_BF16, 16, Hq, Hk, D, hd, hk,

@@ -223,7 +223,15 @@ def _fp8qk_only_q(q, k, v, cu, scale, causal=False):
     return oracle.varlen_attention_gqa(oracle.e4m3_round(q), k, v, cu, scale, causal=causal)
 
 
+def _bf16_round_7_bits(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 6.0)
+    return np.copysign(np.rint(a / ulp) * ulp, x)
+
+
 MUTANTS = {
+    "bf16_round_7_bits": dict(bf16_round=_bf16_round_7_bits),
     "e4m3_decode_bias_8": dict(e4m3_decode=_decode_bias_8),
     "e4m3_round_half_up": dict(e4m3_encode=_encode_half_up),
     "e4m3_no_saturation": dict(e4m3_encode=_encode_no_saturation),

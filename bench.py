@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0
 METRIC = "varlen attn TFLOP/s and % bf16 MFMA peak at S=20,423, 24 heads, d=128"
 HEADLINE = "h3_s20423_bf16"
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE, help="bf16 workload name (synth.configs.BF16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-qk", action="store_true",
+                    help="step = table + q/k norm/rotary writing E4M3 codes + FP8-score attention")
     ap.add_argument("--fused-q", action="store_true",
                     help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -74,9 +77,17 @@ def _short_kernel(name):
     """attn_fwd_*_kernel<D> (bidirectional) or <D, causal>, and the other kernels' short names."""
     import re
 
-    m = re.search(r"(attn_fwd_(?:bf16|f32)_kernel)<(\d+)(?:, *(true|false))?>", name)
+    m = re.search(r"(attn_fwd_(?:bf16|f32)_kernel)<([^>]*)>", name)
     if m:
-        return f"{m.group(1)}<{m.group(2)}{', causal' if m.group(3) == 'true' else ''}>"
+        a = [x.strip() for x in m.group(2).split(",")]
+        tags = [a[0]]
+        if len(a) > 1 and a[1] == "true":
+            tags.append("causal")
+        if len(a) > 3 and a[2] == "true":
+            tags.append(f"qnorm r{32 * int(a[3])}")
+        if len(a) > 4 and a[4] == "true":
+            tags.append("fp8qk")
+        return f"{m.group(1)}<{', '.join(tags)}>"
     m = re.search(r"(qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
                   r"__amd_rocclr_\w+|elementwise_kernel|vectorized_elementwise_kernel|reduce_kernel)", name)
     return m.group(1) if m else name[:60]
@@ -251,17 +262,25 @@ def main():
         return h3a.build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start,
                                        stop=w.lin_stop, stream=stream)
 
-    fused = args.fused_q
-    if fused and (w.causal or w.rot_dim % 32 != 0):
-        print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32 ({w.name})", file=sys.stderr)
+    fused, fp8 = args.fused_q, args.fp8_qk
+    if fused and (w.causal or w.rot_dim % 32 != 0 or fp8):
+        print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32, without --fp8-qk "
+              f"({w.name})", file=sys.stderr)
         return 2
+    if fp8:
+        q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
 
     def norm():
         if fused:
             return h3a.rmsnorm_rope(k, gk, w.eps, tab, w.rot_dim, x_out=kn, stream=stream)
+        if fp8:  # one pass: norm + rotary writing E4M3 codes
+            return h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8, k8=k8, stream=stream)
         return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
 
     def attention(cu):
+        if fp8:
+            return h3a.varlen_attn_fwd_fp8qk(q8, k8, v, cu, w.scale, causal=w.causal, out=o, stream=stream)
         if fused:  # raw q, normalised and rotated in the attention's prologue
             return h3a.varlen_attn_fwd_qnorm(q, kn, v, cu, w.scale, gq, w.eps, tab, w.rot_dim, out=o, stream=stream)
         if w.causal or w.kv != w.heads:
@@ -308,10 +327,15 @@ def main():
 
     F = w.attention_flops()
     attn_tflops = F / attn_s / 1e12
+    # FP8 QK^T (half of F) at the FP8 dense peak and bf16 PV at the bf16 one:
+    # F / (F/2 / 5000 + F/2 / 2500) = 3333 TFLOP/s for the kernel as a whole.
+    peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS) if fp8 else PEAK_BF16_TFLOPS
     S, H, Hkv, D = w.tokens, w.heads, w.kv, w.head_dim
     # q and k (H + Hkv heads; k only when fused) read and written, the table and gains read
     normed_heads = Hkv if fused else H + Hkv
     norm_bytes = 2 * (S * normed_heads * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + (1 if fused else 2) * D * 4
+    if fp8:  # the norm + rotary pass writes one byte per element instead of two
+        norm_bytes -= S * (H + Hkv) * D
     # Q read and O written (H heads), K and V read (Hkv heads), once each
     attn_alg_bytes = 2 * S * H * D * 2 + 2 * S * Hkv * D * 2
     result = {
@@ -325,7 +349,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 QK^T, bf16 PV" if fp8 else "bf16",
         "data": f"synthetic: Q,K,V ~ N(0,1) bf16, gains ~ {w.gamma_mean:g}+N(0,{w.gamma_std:g}) fp32, "
                 f"SplitMix64 seed {w.seed}",
         "config": {
@@ -335,6 +359,7 @@ def main():
             "segments": [list(s) for s in w.segments],
             "parallelism": "single GPU",
             "step": ("rope table + k norm/rotary + attention with q norm/rotary fused in its prologue" if fused
+                     else "rope table + q/k norm/rotary to E4M3 codes + attention with FP8 QK^T" if fp8
                      else "rope table + q/k norm/rotary + attention"),
         },
         "pct_bf16_peak_step": 100.0 * F / step_s / 1e12 / PEAK_BF16_TFLOPS,
@@ -347,11 +372,11 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": attn_tflops,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": attn_tflops / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic() if w.name == HEADLINE else None,
-            "kernel": f"attn_fwd_bf16_kernel<{D}>",
+            "frac": attn_tflops / peak,
+            "traffic": measured_traffic() if (w.name == HEADLINE and not (fp8 or fused)) else None,
+            "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8qk' if fp8 else ''}{', qnorm' if fused else ''}>",
             "algorithmic_flop_per_launch": F,
             "algorithmic_bytes_per_launch": attn_alg_bytes,
         },

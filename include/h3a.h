@@ -267,6 +267,21 @@ h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32
                              int64_t stride_y, hipStream_t stream);
 
 /*
+ * Low-precision attention, steps 0 + 1 fused: h3a_qk_rmsnorm_rope_ex on bf16
+ * q [S, Hq, D] and k [S, Hk, D] writing E4M3 codes q8 [S, Hq, D], k8
+ * [S, Hk, D] (uint8, token strides stride_q8, stride_k8 in bytes, multiples
+ * of 16) instead of bf16: each result is rounded to bf16 and then to E4M3,
+ * so the codes equal h3a_qk_rmsnorm_rope_ex followed by h3a_quantize_e4m3,
+ * in one HBM pass (the GB10 build fuses Q RMSNorm + rot96 RoPE into its
+ * attention's Q quantisation: h3-spark model card, "What this config does").
+ * q and k are not modified.  Errors: as h3a_qk_rmsnorm_rope_ex (bf16 only).
+ */
+h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t Hq,
+                                    int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_q8,
+                                    int64_t stride_k8, const float* gamma_q, const float* gamma_k, float eps,
+                                    const float* cos_sin, int32_t rot_dim, hipStream_t stream);
+
+/*
  * Low-precision attention, step 2: h3a_varlen_attn_fwd_ex with q and k given
  * as E4M3 codes.  The score product q.k runs on the FP8 MFMA (twice the bf16
  * rate) with fp32 accumulation; the softmax, the bf16 probabilities, the PV

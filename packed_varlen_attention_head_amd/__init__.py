@@ -40,6 +40,7 @@ EXPORTS = (
     "h3a_varlen_attn_fwd_qnorm",
     "h3a_varlen_attn_fwd_fp8qk",
     "h3a_quantize_e4m3",
+    "h3a_qk_rmsnorm_rope_e4m3",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.h3a_rmsnorm_rope.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd_qnorm.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                             _i64, _c_i32p, _i32, _f32, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_qk_rmsnorm_rope_e4m3.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+                                           _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_quantize_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
     L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
                                             _c_i32p, _i32, _f32, _i32, _vp]
@@ -103,7 +106,7 @@ def lib() -> ctypes.CDLL:
     L.h3a_plan_tiles_ex.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
                  "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
-                 "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk",
+                 "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -310,6 +313,24 @@ def quantize_e4m3(x, out=None, stream=None):
         raise H3AError(H3A_ESHAPE, f"out must be uint8 {(S, H, D)}, got {out.dtype} {tuple(out.shape)}")
     _check(lib().h3a_quantize_e4m3(x.data_ptr(), out.data_ptr(), S, H, D, sx, sy, _stream_handle(stream)))
     return out
+
+
+def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q8=None, k8=None,
+                         stream=None):
+    """Norm + rotary of bf16 q [S, Hq, D], k [S, Hk, D] written as uint8 E4M3 codes; returns (q8, k8)."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q", q)
+    _, Hk, _, sk = _token_major("k", k)
+    q8 = torch.empty((S, Hq, D), dtype=torch.uint8, device=q.device) if q8 is None else q8
+    k8 = torch.empty((S, Hk, D), dtype=torch.uint8, device=q.device) if k8 is None else k8
+    _, _, _, sq8 = _token_major("q8", q8)
+    _, _, _, sk8 = _token_major("k8", k8)
+    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    _check(lib().h3a_qk_rmsnorm_rope_e4m3(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k8.data_ptr(), S, Hq, Hk, D,
+                                          sq, sk, sq8, sk8, gamma_q.data_ptr(), gamma_k.data_ptr(), float(eps), cs,
+                                          int(rot_dim), _stream_handle(stream)))
+    return q8, k8
 
 
 def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):

@@ -505,6 +505,46 @@ h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32
   return H3A_OK;
 }
 
+h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t Hq,
+                                    int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_q8,
+                                    int64_t stride_k8, const float* gamma_q, const float* gamma_k, float eps,
+                                    const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+  if ((rot_dim / 2) % 8 != 0)
+    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of 8 for this dtype", rot_dim / 2);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+  h3a_status st;
+  if ((st = check_operand("q", q, S, Hq, D, stride_q, 2)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, Hk, D, stride_k, 2)) != H3A_OK) return st;
+  if ((st = check_operand("q8", q8, S, Hq, D, stride_q8, 1)) != H3A_OK) return st;
+  if ((st = check_operand("k8", k8, S, Hk, D, stride_k8, 1)) != H3A_OK) return st;
+  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+  if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
+  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+  if (rot_dim > 0 && S > 0) {
+    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  }
+  if (S == 0) return H3A_OK;
+  // the byte outputs against every other tensor: plain byte ranges
+  const Range rq = tensor_range(q, S, Hq, D, stride_q, 2), rk = tensor_range(k, S, Hk, D, stride_k, 2);
+  const Range rq8 = tensor_range(q8, S, Hq, D, stride_q8, 1), rk8 = tensor_range(k8, S, Hk, D, stride_k8, 1);
+  auto hit = [](const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; };
+  if (hit(rq8, rq) || hit(rq8, rk)) return fail(H3A_EINVAL, "q8 overlaps q or k");
+  if (hit(rk8, rq) || hit(rk8, rk)) return fail(H3A_EINVAL, "k8 overlaps q or k");
+  if (may_overlap(q8, stride_q8, Hq, k8, stride_k8, Hk, S, D, 1)) return fail(H3A_EINVAL, "q8 overlaps k8");
+  hipError_t e = h3a::launch_qk_rmsnorm_rope_e4m3(q, k, q8, k8, S, Hq, Hk, D, stride_q, stride_k, stride_q8,
+                                                  stride_k8, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+  if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope_e4m3 launch", e);
+  return H3A_OK;
+}
+
 h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
                                      int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                      int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,

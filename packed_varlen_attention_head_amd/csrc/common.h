@@ -80,6 +80,13 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, 
                                  int64_t sk, int64_t sv, int64_t so, const WorkItem* items, int64_t n_items,
                                  float scale, int32_t kv_group, bool causal, hipStream_t stream);
 
+// The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
+// token strides sq8, sk8 in bytes).
+hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t H,
+                                       int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8, int64_t sk8,
+                                       const float* gq, const float* gk, float eps, const float* cos_sin,
+                                       int32_t rot_dim, hipStream_t stream);
+
 // bf16 [S, row_elems] rows (token stride sx elements) -> E4M3 codes (token
 // stride sy bytes); row_elems a multiple of 8.
 hipError_t launch_quantize_e4m3(const void* x, void* y, int64_t S, int32_t row_elems, int64_t sx, int64_t sy,

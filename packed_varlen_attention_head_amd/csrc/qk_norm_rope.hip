@@ -17,7 +17,14 @@
 //     positions away, same slot, and is fetched with a lane shuffle;
 //   * all loads of a token are issued before any store, so in-place calls are
 //     safe (each token is owned by a single wave);
-//   * k may have fewer heads than q (grouped K/V heads of causal GQA).
+//   * k may have fewer heads than q (grouped K/V heads of causal GQA);
+//   * optionally (F8OUT) the bf16 results are written as OCP FP8 E4M3 codes
+//     instead, one byte per element: the Q RMSNorm + rotary pass fused with
+//     the quantisation that the low-precision attention consumes (h3-spark
+//     model card, "What this config does": the Q RMSNorm + rot96 RoPE fused
+//     into SageAttention's Q quantisation).  Each value is rounded to bf16
+//     first, so the codes equal those of the bf16 pass followed by the
+//     separate quantiser.
 #include <cstdint>
 
 #include "common.h"
@@ -64,12 +71,23 @@ struct Elem<Bf16Tag> {
   __device__ static uint4 pack(const float* y) {
     return make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
   }
+  // bf16 rounding, then E4M3 (nearest even, saturating at +-448).
+  __device__ static uint2 pack_e4m3(const float* y) {
+    float b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = fminf(fmaxf(float(__bf16(y[e])), -448.0f), 448.0f);
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[0], b[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[2], b[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(b[4], b[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(b[6], b[7], w1, true);
+    return make_uint2(uint32_t(w0), uint32_t(w1));
+  }
 };
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBatch = 8;  // head vectors a lane keeps in flight
 
-template <typename T, int D>
+template <typename T, int D, bool F8OUT>
 __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, int64_t stride_b,
                                               int64_t stride_ob, int32_t token, int32_t H,
                                               const float* g, const float* c, const float* s, int role,
@@ -81,7 +99,7 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
   const int sub = lane % LPV;
   const int grp = lane / LPV;
   const char* row = src + int64_t(token) * stride_b + sub * 16;
-  char* orow = dst + int64_t(token) * stride_ob + sub * 16;
+  char* orow = dst + int64_t(token) * stride_ob + sub * (F8OUT ? V : 16);
   for (int h0 = 0; h0 < H; h0 += G * kBatch) {
     uint4 raw[kBatch];
 #pragma unroll
@@ -109,12 +127,17 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
         out[e] = role == 0 ? fmaf(y[e], c[e], -py * s[e]) : (role == 1 ? fmaf(y[e], c[e], py * s[e]) : y[e]);
       }
       const int h = h0 + b * G + grp;
-      if (h < H) *reinterpret_cast<uint4*>(orow + int64_t(h) * D * esz) = Elem<T>::pack(out);
+      if (h < H) {
+        if constexpr (F8OUT)
+          *reinterpret_cast<uint2*>(orow + int64_t(h) * D) = Elem<T>::pack_e4m3(out);
+        else
+          *reinterpret_cast<uint4*>(orow + int64_t(h) * D * esz) = Elem<T>::pack(out);
+      }
     }
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8OUT = false>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
 qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq_b, int64_t sk_b,
                     int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H, int32_t Hk,
@@ -153,19 +176,22 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq
     g_q[e] = gq[d0 + e];
     g_k[e] = gk[d0 + e];
   }
-  norm_rope_one<T, D>(q, qo, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
-  norm_rope_one<T, D>(k, ko, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(q, qo, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(k, ko, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
 }
 
-template <typename T, int D>
+// Strides in elements of the input type; with F8OUT the output strides are
+// in bytes (one per code).
+template <typename T, int D, bool F8OUT = false>
 hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int32_t Hk, int64_t sq,
                   int64_t sk, int64_t sqo, int64_t sko, const float* gq, const float* gk, float eps,
                   const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
   constexpr int esz = 16 / Elem<T>::V;
+  constexpr int oesz = F8OUT ? 1 : esz;
   const unsigned blocks = unsigned((S + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, F8OUT>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
                      static_cast<const char*>(q), static_cast<const char*>(k), static_cast<char*>(qo),
-                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * esz, sko * esz, int32_t(S), H, Hk, gq,
+                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * oesz, sko * oesz, int32_t(S), H, Hk, gq,
                      gk, eps, cos_sin, rot_dim);
   return hipGetLastError();
 }
@@ -188,6 +214,17 @@ hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void*
     if (D == 64)
       return launch<float, 64>(q, k, q_out, k_out, S, H, Hk, sq, sk, sqo, sko, gq, gk, eps, cos_sin, rot_dim, stream);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t H,
+                                       int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8, int64_t sk8,
+                                       const float* gq, const float* gk, float eps, const float* cos_sin,
+                                       int32_t rot_dim, hipStream_t stream) {
+  if (D == 128)
+    return launch<Bf16Tag, 128, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream);
+  if (D == 64)
+    return launch<Bf16Tag, 64, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream);
   return hipErrorInvalidValue;
 }
 

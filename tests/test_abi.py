@@ -294,6 +294,23 @@ def test_varlen_attn_fwd_fp8qk_rejects(kw, status, word):
     assert word in h3a.last_error(), h3a.last_error()
 
 
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(Hk=0), h3a.H3A_EINVAL, "Hk ="),
+    (dict(rot=40), h3a.H3A_EUNSUPPORTED, "rot_dim / 2"),
+    (dict(sq8=100), h3a.H3A_ESHAPE, "q8: token stride"),
+    (dict(q8=P + 512), h3a.H3A_EINVAL, "q8 overlaps"),
+    (dict(cs=None), h3a.H3A_EINVAL, "cos_sin"),
+])
+def test_qk_rmsnorm_rope_e4m3_rejects(kw, status, word):
+    Hq, Hk, D = 8, kw.get("Hk", 2), 128
+    st = h3a.lib().h3a_qk_rmsnorm_rope_e4m3(P, P + (1 << 24), kw.get("q8", P + (2 << 24)), P + (3 << 24), 16, Hq, Hk,
+                                            D, Hq * D, max(Hk, 1) * D, kw.get("sq8", Hq * D), max(Hk, 1) * D,
+                                            P + (4 << 24), P + (5 << 24), 1e-6, kw.get("cs", P + (6 << 24)),
+                                            kw.get("rot", 96), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
 def qk_ex(Hq=8, Hk=0, **kw):
     D, hd, hk = 128, Hq * 128, max(Hk, 1) * 128
     return h3a.lib().h3a_qk_rmsnorm_rope_ex(P, P + (1 << 24), P, P + (1 << 24), h3a.H3A_BF16, 16, Hq, Hk, D, hd, hk,

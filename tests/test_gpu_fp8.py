@@ -151,3 +151,26 @@ def test_fp8qk_segment_isolation_and_determinism():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(a[:900], c[:900]) and not torch.equal(a[900:], c[900:])
+
+
+@pytest.mark.parametrize("name,kv", [("h3_s20423_bf16", 24), ("two_seg_bf16", 8)])
+def test_fused_norm_rope_e4m3_equals_two_passes(name, kv):
+    """The norm + rotary pass that writes E4M3 codes gives the same bytes as the bf16 pass
+    followed by the quantiser, and leaves q, k untouched."""
+    import torch
+
+    w = configs.ALL[name].replace(kv_heads=kv)
+    T = configs.make_tensors(w)
+    log(f"[fused e4m3] {name} Hq={w.heads} Hk={w.kv}")
+    q, k = to_device(T.q, "bf16"), to_device(T.k, "bf16")
+    q0, k0 = q.clone(), k.clone()
+    gq, gk = torch.from_numpy(T.gamma_q).cuda(), torch.from_numpy(T.gamma_k).cuda()
+    tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    h3a().build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    q8, k8 = h3a().qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    h3a().qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn)
+    q8b, k8b = h3a().quantize_e4m3(qn), h3a().quantize_e4m3(kn)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q0) and torch.equal(k, k0)
+    assert torch.equal(q8, q8b) and torch.equal(k8, k8b)

@@ -449,6 +449,13 @@ def varlen_attention_fp8qk(q, k, v, cu, scale: float, causal: bool = False) -> n
     return varlen_attention_gqa(e4m3_round(q), e4m3_round(k), v, cu, scale, causal=causal)
 
 
+def varlen_attention_fp8(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """varlen_attention_gqa with q, k and v rounded to E4M3 first (the operands of
+    both products); the softmax weights stay exact.  (A kernel that also rounds the
+    weights to E4M3 for the PV product differs from this by that rounding.)"""
+    return varlen_attention_gqa(e4m3_round(q), e4m3_round(k), e4m3_round(v), cu, scale, causal=causal)
+
+
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):
     """The whole chain: table, norm + rotary on q and k, then varlen attention."""
     cu, cos, sin = rope_table(segments, rot_dims, base)

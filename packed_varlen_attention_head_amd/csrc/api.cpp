@@ -602,7 +602,12 @@ h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H,
   *n_items = int64_t(plan.size());
   if (int64_t(plan.size()) > cap) return fail(H3A_ESHAPE, "cap %lld < plan length %lld", (long long)cap, (long long)plan.size());
   if (!plan.empty() && items == nullptr) return fail(H3A_EINVAL, "items is NULL");
-  if (!plan.empty()) std::memcpy(items, plan.data(), plan.size() * sizeof(h3a::WorkItem));
+  for (size_t i = 0; i < plan.size(); ++i) {
+    items[4 * i + 0] = plan[i].seg_start;
+    items[4 * i + 1] = plan[i].seg_len;
+    items[4 * i + 2] = plan[i].q_start;
+    items[4 * i + 3] = plan[i].head;
+  }
   return H3A_OK;
 }
 

@@ -11,14 +11,22 @@ namespace h3a {
 
 // One attention work item: query rows [q_start, q_start + block_m) of one
 // segment and one head.  seg_len == 0 marks a padding item (the workgroup
-// exits at once).
+// exits at once).  vt_col0 is the segment's first column in the transposed
+// E4M3 V layout, where every segment is padded to whole 64-key tiles (the sum
+// of the earlier segments' padded lengths); only the FP8-PV kernel reads it.
 struct WorkItem {
   int32_t seg_start;
   int32_t seg_len;
   int32_t q_start;  // relative to seg_start
   int32_t head;
+  int32_t vt_col0;
+  int32_t reserved[3];
 };
-static_assert(sizeof(WorkItem) == 16, "WorkItem is uploaded as 4 x int32");
+static_assert(sizeof(WorkItem) == 32, "WorkItem is uploaded as 8 x int32");
+
+// Keys per tile of the transposed E4M3 V layout (and of the attention's K/V
+// tiles).
+constexpr int32_t kVtTile = 64;
 
 // ---- host tile planner (planner.cpp) --------------------------------------
 // Items for every (non-empty segment, head, query tile), longest segments

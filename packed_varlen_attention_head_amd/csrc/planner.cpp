@@ -46,6 +46,10 @@ constexpr double kItemOverheadKeys = 128.0;
 
 std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
                                  int32_t n_xcd, bool causal) {
+  // First column of each segment in the padded transposed-V layout.
+  std::vector<int32_t> col0(size_t(nseg) + 1, 0);
+  for (int32_t s = 0; s < nseg; ++s)
+    col0[s + 1] = col0[s] + (cu[s + 1] - cu[s] + kVtTile - 1) / kVtTile * kVtTile;
   std::vector<int32_t> order;
   for (int32_t s = 0; s < nseg; ++s)
     if (cu[s + 1] > cu[s]) order.push_back(s);
@@ -74,7 +78,7 @@ std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads,
     const int32_t len = cu[c.seg + 1] - cu[c.seg];
     for (int32_t i = c.t0; i < c.t1; ++i) {
       const int32_t t = causal ? c.t0 + c.t1 - 1 - i : i;
-      out.push_back({cu[c.seg], len, t * block_m, c.head});
+      out.push_back({cu[c.seg], len, t * block_m, c.head, col0[c.seg], {0, 0, 0}});
     }
   };
 
@@ -97,7 +101,7 @@ std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads,
   }
   size_t longest = 0;
   for (const auto& qx : queue) longest = std::max(longest, qx.size());
-  std::vector<WorkItem> items(longest * size_t(n_xcd), WorkItem{0, 0, 0, 0});
+  std::vector<WorkItem> items(longest * size_t(n_xcd), WorkItem{0, 0, 0, 0, 0, {0, 0, 0}});
   for (int32_t x = 0; x < n_xcd; ++x)
     for (size_t p = 0; p < queue[x].size(); ++p) items[p * size_t(n_xcd) + size_t(x)] = queue[x][p];
   return items;

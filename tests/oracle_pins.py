@@ -600,6 +600,14 @@ def check_fp8qk_attention(O):
     assert 0 < rel < 0.05, rel
     # and rounding only one operand is not the same thing
     assert not np.allclose(a, O.varlen_attention_gqa(O.e4m3_round(q), k, v, cu, 0.25), rtol=0, atol=1e-9)
+    # all three operands: representable values pass through; v's rounding is applied too
+    v8 = O.e4m3_decode(r.integers(0, 0x7F, size=(S, 2, 16)).astype(np.uint8))
+    assert np.array_equal(O.varlen_attention_fp8(q8, k8, v8, cu, 0.05, True),
+                          O.varlen_attention_gqa(q8, k8, v8, cu, 0.05, True))
+    a3 = O.varlen_attention_fp8(q, k, v, cu, 0.25)
+    assert np.allclose(a3, O.varlen_attention_gqa(O.e4m3_round(q), O.e4m3_round(k), O.e4m3_round(v), cu, 0.25),
+                       rtol=0, atol=0)
+    assert not np.allclose(a3, a, rtol=0, atol=1e-6)
 
 
 # ---------------------------------------------------------------------------

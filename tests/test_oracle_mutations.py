@@ -237,6 +237,8 @@ MUTANTS = {
     "e4m3_no_saturation": dict(e4m3_encode=_encode_no_saturation),
     "e4m3_truncating": dict(e4m3_encode=_encode_truncating),
     "fp8qk_rounds_only_q": dict(varlen_attention_fp8qk=_fp8qk_only_q),
+    "fp8_leaves_v_exact": dict(varlen_attention_fp8=lambda q, k, v, cu, scale, causal=False:
+                               oracle.varlen_attention_fp8qk(q, k, v, cu, scale, causal)),
     "causal_one_key_too_many": dict(varlen_attention_gqa=_gqa_with(_masked_diagonal_too)),
     "gqa_modulo_heads": dict(varlen_attention_gqa=_gqa_modulo_heads),
     "gqa_causal_ignored": dict(varlen_attention_gqa=_gqa_causal_ignored),

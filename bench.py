@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE, help="bf16 workload name (synth.configs.BF16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="step = table + q/k norm/rotary to E4M3 + transposed E4M3 V + attention with both products "
+                         "in FP8")
     ap.add_argument("--fp8-qk", action="store_true",
                     help="step = table + q/k norm/rotary writing E4M3 codes + FP8-score attention")
     ap.add_argument("--fused-q", action="store_true",
@@ -85,8 +88,10 @@ def _short_kernel(name):
             tags.append("causal")
         if len(a) > 3 and a[2] == "true":
             tags.append(f"qnorm r{32 * int(a[3])}")
-        if len(a) > 4 and a[4] == "true":
+        if len(a) > 4 and a[4] in ("true", "1"):
             tags.append("fp8qk")
+        if len(a) > 4 and a[4] == "2":
+            tags.append("fp8")
         return f"{m.group(1)}<{', '.join(tags)}>"
     m = re.search(r"(qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
                   r"__amd_rocclr_\w+|elementwise_kernel|vectorized_elementwise_kernel|reduce_kernel)", name)
@@ -262,7 +267,7 @@ def main():
         return h3a.build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start,
                                        stop=w.lin_stop, stream=stream)
 
-    fused, fp8 = args.fused_q, args.fp8_qk
+    fused, fp8, fp8pv = args.fused_q, args.fp8_qk or args.fp8, args.fp8
     if fused and (w.causal or w.rot_dim % 32 != 0 or fp8):
         print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32, without --fp8-qk "
               f"({w.name})", file=sys.stderr)
@@ -270,6 +275,9 @@ def main():
     if fp8:
         q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    if fp8pv:
+        vt8 = torch.empty((w.kv, w.head_dim, h3a.vt_e4m3_columns(np.concatenate([[0], np.cumsum(w.lengths)]))),
+                          dtype=torch.uint8, device=dev)
 
     def norm():
         if fused:
@@ -278,7 +286,13 @@ def main():
             return h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8, k8=k8, stream=stream)
         return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
 
+    def vprep(cu):
+        if fp8pv:  # V as transposed E4M3 tiles (changes every step, like q and k)
+            h3a.prepare_vt_e4m3(v, cu, out=vt8, stream=stream)
+
     def attention(cu):
+        if fp8pv:
+            return h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, w.scale, causal=w.causal, out=o, stream=stream)
         if fp8:
             return h3a.varlen_attn_fwd_fp8qk(q8, k8, v, cu, w.scale, causal=w.causal, out=o, stream=stream)
         if fused:  # raw q, normalised and rotated in the attention's prologue
@@ -290,6 +304,7 @@ def main():
     def step():
         cu = table()
         norm()
+        vprep(cu)
         attention(cu)
         return cu
 
@@ -324,12 +339,14 @@ def main():
     attn_s = timed(lambda: attention(cu), n_ev)
     norm_s = timed(norm, n_ev)
     table_s = timed(table, n_ev)
+    vprep_s = timed(lambda: vprep(cu), n_ev) if fp8pv else 0.0
 
     F = w.attention_flops()
     attn_tflops = F / attn_s / 1e12
     # FP8 QK^T (half of F) at the FP8 dense peak and bf16 PV at the bf16 one:
     # F / (F/2 / 5000 + F/2 / 2500) = 3333 TFLOP/s for the kernel as a whole.
-    peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS) if fp8 else PEAK_BF16_TFLOPS
+    peak = (PEAK_FP8_TFLOPS if fp8pv else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS) if fp8
+            else PEAK_BF16_TFLOPS)
     S, H, Hkv, D = w.tokens, w.heads, w.kv, w.head_dim
     # q and k (H + Hkv heads; k only when fused) read and written, the table and gains read
     normed_heads = Hkv if fused else H + Hkv
@@ -349,7 +366,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 e4m3 QK^T, bf16 PV" if fp8 else "bf16",
+        "dtype": "fp8 e4m3 QK^T and PV" if fp8pv else "fp8 e4m3 QK^T, bf16 PV" if fp8 else "bf16",
         "data": f"synthetic: Q,K,V ~ N(0,1) bf16, gains ~ {w.gamma_mean:g}+N(0,{w.gamma_std:g}) fp32, "
                 f"SplitMix64 seed {w.seed}",
         "config": {
@@ -359,6 +376,8 @@ def main():
             "segments": [list(s) for s in w.segments],
             "parallelism": "single GPU",
             "step": ("rope table + k norm/rotary + attention with q norm/rotary fused in its prologue" if fused
+                     else "rope table + q/k norm/rotary to E4M3 codes + transposed E4M3 V + attention with both "
+                          "products in FP8" if fp8pv
                      else "rope table + q/k norm/rotary to E4M3 codes + attention with FP8 QK^T" if fp8
                      else "rope table + q/k norm/rotary + attention"),
         },
@@ -368,6 +387,7 @@ def main():
         "norm_rope_ms": norm_s * 1e3,
         "norm_rope_GBps": norm_bytes / norm_s / 1e9,
         "rope_table_ms": table_s * 1e3,
+        "v_e4m3_ms": vprep_s * 1e3,
         "checksum_o": checksum,
         "roofline": {
             "bound": "mfma",
@@ -376,7 +396,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": attn_tflops / peak,
             "traffic": measured_traffic() if (w.name == HEADLINE and not (fp8 or fused)) else None,
-            "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8qk' if fp8 else ''}{', qnorm' if fused else ''}>",
+            "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8' if fp8pv else ', fp8qk' if fp8 else ''}"
+                      f"{', qnorm' if fused else ''}>",
             "algorithmic_flop_per_launch": F,
             "algorithmic_bytes_per_launch": attn_alg_bytes,
         },

@@ -303,6 +303,33 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
                                      int32_t causal, hipStream_t stream);
 
 /*
+ * Low-precision attention with both products in FP8.  V goes through a
+ * layout pass first: vt8 [Hkv][D][vt_cols] holds E4M3 codes of v transposed
+ * (rows are head dims), each segment padded to whole 64-key tiles: segment s
+ * occupies columns col0(s) .. col0(s) + L_s - 1, col0(s) = sum over earlier
+ * segments of ceil(L / 64) * 64, and padding columns hold code 0.
+ *
+ * h3a_vt_e4m3_columns: vt_cols for cu_seqlens (host only).
+ * h3a_prepare_vt_e4m3: bf16 v [S, Hkv, D] (token stride stride_v elements)
+ *   -> vt8 (device, Hkv * D * vt_cols bytes, 16-byte aligned); nearest even,
+ *   saturating at +-448.
+ * h3a_varlen_attn_fwd_fp8: as h3a_varlen_attn_fwd_fp8qk, with V given as
+ *   vt8; the probabilities are rounded to E4M3 for the PV product (which
+ *   runs on FP8 MFMA with fp32 accumulation) and the row sum adds them in
+ *   fp32.  Against attention on E4M3-rounded q, k, v with exact weights the
+ *   result carries the E4M3 rounding of the weights.
+ * Errors: as h3a_varlen_attn_fwd_fp8qk, plus ESHAPE for a vt_cols that does
+ * not match cu_seqlens and EUNSUPPORTED when D * vt_cols exceeds INT32_MAX.
+ */
+h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns);
+h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv, int32_t D, int64_t stride_v,
+                               int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream);
+h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int64_t S, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
+                                   int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                   int32_t causal, hipStream_t stream);
+
+/*
  * Varlen attention with grouped K/V heads and an optional causal mask: the
  * encoder text tower's causal GQA (vllm.cpp PR #26, encoder-tower commit,
  * "Causal GQA attention": K/V heads are broadcast across their query group).

@@ -41,6 +41,9 @@ EXPORTS = (
     "h3a_varlen_attn_fwd_fp8qk",
     "h3a_quantize_e4m3",
     "h3a_qk_rmsnorm_rope_e4m3",
+    "h3a_vt_e4m3_columns",
+    "h3a_prepare_vt_e4m3",
+    "h3a_varlen_attn_fwd_fp8",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -95,6 +98,10 @@ def lib() -> ctypes.CDLL:
                                             _i64, _c_i32p, _i32, _f32, _vp, _f32, _vp, _i32, _vp]
     L.h3a_qk_rmsnorm_rope_e4m3.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
                                            _vp, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_vt_e4m3_columns.argtypes = [_c_i32p, _i32, _c_i64p]
+    L.h3a_prepare_vt_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _c_i32p, _i32, _vp]
+    L.h3a_varlen_attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+                                          _c_i32p, _i32, _f32, _i32, _vp]
     L.h3a_quantize_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
     L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
                                             _c_i32p, _i32, _f32, _i32, _vp]
@@ -107,6 +114,7 @@ def lib() -> ctypes.CDLL:
     for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
                  "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
+                 "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
                  "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -331,6 +339,49 @@ def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: i
                                           sq, sk, sq8, sk8, gamma_q.data_ptr(), gamma_k.data_ptr(), float(eps), cs,
                                           int(rot_dim), _stream_handle(stream)))
     return q8, k8
+
+
+def vt_e4m3_columns(cu_seqlens) -> int:
+    """Columns of the transposed E4M3 V layout for cu_seqlens (segments padded to 64 keys)."""
+    cu = _i32_array(cu_seqlens)
+    n = ctypes.c_int64(0)
+    _check(lib().h3a_vt_e4m3_columns(_ptr_i32(cu), len(cu) - 1, ctypes.byref(n)))
+    return int(n.value)
+
+
+def prepare_vt_e4m3(v, cu_seqlens, out=None, stream=None):
+    """bf16 v [S, Hkv, D] -> uint8 [Hkv, D, vt_cols] transposed E4M3 codes (segment-padded)."""
+    import torch
+
+    S, Hkv, D, sv = _token_major("v", v)
+    cu = _i32_array(cu_seqlens)
+    cols = vt_e4m3_columns(cu)
+    if out is None:
+        out = torch.empty((Hkv, D, max(cols, 1)), dtype=torch.uint8, device=v.device)
+    if out.dtype != torch.uint8 or tuple(out.shape[:2]) != (Hkv, D) or out.shape[2] < cols or not out.is_contiguous():
+        raise H3AError(H3A_ESHAPE, f"out must be contiguous uint8 [{Hkv}, {D}, {cols}]")
+    _check(lib().h3a_prepare_vt_e4m3(v.data_ptr(), out.data_ptr(), S, Hkv, D, sv, cols, _ptr_i32(cu), len(cu) - 1,
+                                     _stream_handle(stream)))
+    return out
+
+
+def varlen_attn_fwd_fp8(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
+    """Attention with q8, k8 (uint8 E4M3 [S, H, D]) and vt8 from prepare_vt_e4m3; bf16 output."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q8", q8)
+    _, Hkv, _, sk = _token_major("k8", k8)
+    cu = _i32_array(cu_seqlens)
+    cols = vt_e4m3_columns(cu)
+    if vt8.dtype != torch.uint8 or tuple(vt8.shape[:2]) != (Hkv, D) or not vt8.is_contiguous():
+        raise H3AError(H3A_ESHAPE, f"vt8 must be contiguous uint8 [{Hkv}, {D}, {cols}]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q8.device)
+    _, _, _, so = _token_major("out", out)
+    _check(lib().h3a_varlen_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), out.data_ptr(), S, Hq, Hkv,
+                                         D, sq, sk, cols, so, _ptr_i32(cu), len(cu) - 1, float(scale),
+                                         int(bool(causal)), _stream_handle(stream)))
+    return out
 
 
 def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):

@@ -578,6 +578,82 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
   return H3A_OK;
 }
 
+h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns) {
+  if (columns == nullptr) return fail(H3A_EINVAL, "columns is NULL");
+  if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+  *columns = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+  return H3A_OK;
+}
+
+h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv, int32_t D, int64_t stride_v,
+                               int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
+  const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+  if (vt_cols != need)
+    return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
+                (long long)need);
+  if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
+    return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+  if (need == 0) return H3A_OK;
+  if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
+  if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+  const Range rv = tensor_range(v, S, Hkv, D, stride_v, 2);
+  const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
+  if (rv.lo < t1 && t0 < rv.hi) return fail(H3A_EINVAL, "vt8 overlaps v");
+  hipError_t e = h3a::launch_prepare_vt_e4m3(v, stride_v, cu_seqlens, nseg, Hkv, D, vt8, vt_cols, stream);
+  if (e != hipSuccess) return fail_hip("prepare_vt_e4m3 launch", e);
+  return H3A_OK;
+}
+
+h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int64_t S, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
+                                   int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                   int32_t causal, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+  if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+  const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+  if (vt_cols != need)
+    return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
+                (long long)need);
+  if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
+    return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+  if (S == 0) return H3A_OK;
+  if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
+  if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+  const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+  const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+  const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
+  if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
+  if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
+  if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
+  Plan plan;
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan)) != H3A_OK) return st;
+  hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
+                                          scale, Hq / Hkv, causal != 0, stream);
+  if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
+  return H3A_OK;
+}
+
 h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
                                int64_t stride_q, int64_t stride_k, int64_t stride_v,

@@ -54,13 +54,18 @@
 //     for the sum of squares, the same rotation FMAs and one RNE rounding),
 //     so q' -- and therefore the output -- is bit-identical to the unfused
 //     path.
-//   * Low-precision variant (F8): Q and K arrive as FP8 E4M3 codes and the
-//     score product runs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales),
-//     at twice the bf16 MFMA rate, with K tiles of half the bytes; the
-//     softmax and the PV product (bf16) are unchanged.  Each lane carries 32
-//     consecutive dims of its key (A) and query (B) row per 64-dim step: the
-//     instruction pairs A and B elements by (lane half, byte), so any
-//     assignment shared by both operands contracts correctly.
+//   * Low-precision variants: F8 >= 1 takes Q and K as FP8 E4M3 codes and
+//     runs the score product on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+//     scales), at twice the bf16 MFMA rate, with K tiles of half the bytes.
+//     Each lane carries 32 consecutive dims of its key (A) and query (B) row
+//     per 64-dim step: the instruction pairs A and B elements by (lane half,
+//     byte), so any assignment shared by both operands contracts correctly.
+//     F8 == 2 also runs PV in FP8: V arrives transposed (rows = dims, one
+//     64-key tile per segment-padded column block, E4M3), so the V^T operand
+//     is two plain 16-byte LDS reads, and the probabilities (rounded to
+//     E4M3) leave the score accumulator as the B operand after four lane-half
+//     swaps that give each half 32 consecutive keys.  The row sum adds the
+//     fp32 probabilities.
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -153,8 +158,10 @@ struct QNormArgs {
 namespace {
 
 // RH: 16-dim blocks per rotary half when QNORM (rot_dim = 32 RH), else 0.
-// F8: q and k hold E4M3 codes (token strides sq, sk in bytes).
-template <int D, bool CAUSAL, bool QNORM, int RH, bool F8>
+// F8 >= 1: q and k hold E4M3 codes (token strides sq, sk in bytes).  F8 == 2:
+// v is the transposed E4M3 layout [head][dim][column], sv its row length in
+// bytes, each item's segment starting at column it.vt_col0.
+template <int D, bool CAUSAL, bool QNORM, int RH, int F8>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
@@ -169,17 +176,18 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int ROWB = D * 2;                     // bytes per LDS row
   constexpr int NDMA = kBN * CH / (64 * kWaves);  // 16-byte loads per thread per tile and operand
   static_assert(NDMA >= 1 && CH >= 8, "tile layout");
-  constexpr int KESZ = F8 ? 1 : 2;                 // bytes per K (and Q) element
+  constexpr int KESZ = F8 >= 1 ? 1 : 2;            // bytes per K (and Q) element
   constexpr int KROWB = D * KESZ;                  // bytes per K row
   constexpr int KCH = KROWB / 16;                  // 16-byte chunks per K row
   constexpr int NDMAK = kBN * KCH / (64 * kWaves);
   constexpr int KS8 = D / 64;                      // FP8 MFMA k-steps over the head dim
-  static_assert(NDMAK >= 1 && !(F8 && QNORM), "tile layout / variant");
+  constexpr int NDMAV8 = D * 4 / (64 * kWaves);    // FP8 V^T tile: D rows x 4 chunks
+  static_assert(NDMAK >= 1 && NDMAV8 >= 1 && !(F8 && QNORM), "tile layout / variant");
 
   // One object per ring slot, so alias analysis can tell a load into one slot
   // from reads of another (otherwise every LDS read waits for all loads).
   __shared__ uint16_t k_slot0[kBN * KROWB / 2], k_slot1[kBN * KROWB / 2];
-  __shared__ uint16_t v_slot0[kBN * D], v_slot1[kBN * D];
+  __shared__ uint16_t v_slot0[F8 == 2 ? kBN * D / 2 : kBN * D], v_slot1[F8 == 2 ? kBN * D / 2 : kBN * D];
   // Slot pointers: compile-time choice for IC<> slots, a select otherwise.
   auto kslot = [&](auto slot) -> uint16_t* {
     if constexpr (std::is_integral_v<decltype(slot)>) return slot ? k_slot1 : k_slot0;
@@ -209,7 +217,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   bf16x8 qb[KS];
   // F8: lane holds query (qrow0 + l32), dims ks8*64 + hi*32 .. +32.
   [[maybe_unused]] i32x8 qb8[F8 ? KS8 : 1];
-  if constexpr (!F8) {
+  if constexpr (F8 == 0) {
     const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq) * 2);
     const int off = (l32 * int(sq) + hi * 8) * 2;
 #pragma unroll
@@ -316,11 +324,21 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int row = s / KCH, pc = s % KCH;
     koff[i] = row * int(sk) * KESZ + ((pc ^ (F8 ? k8_swz<D>(row) : k_swz<D>(row))) * 16);
   }
+  if constexpr (F8 < 2) {
 #pragma unroll
-  for (int i = 0; i < NDMA; ++i) {
-    const int s = (i * kWaves + wave) * 64 + lane;
-    const int row = s / CH, pc = s % CH;
-    voff[i] = row * int(sv) * 2 + ((pc ^ v_swz<D>(row)) * 16);
+    for (int i = 0; i < NDMA; ++i) {
+      const int s = (i * kWaves + wave) * 64 + lane;
+      const int row = s / CH, pc = s % CH;
+      voff[i] = row * int(sv) * 2 + ((pc ^ v_swz<D>(row)) * 16);
+    }
+  } else {
+    // V^T tile: row = dim (64 bytes: 4 chunks), swizzled like 64-byte K rows
+#pragma unroll
+    for (int i = 0; i < NDMAV8; ++i) {
+      const int s = (i * kWaves + wave) * 64 + lane;
+      const int row = s / 4, pc = s % 4;
+      voff[i] = row * int(sv) + ((pc ^ ((row >> 2) & 3)) * 16);
+    }
   }
   // K operand reads: row l32 (+32 kb), logical chunk 2 ks + hi.
   int kaddr[KS];
@@ -337,6 +355,16 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
   int vaddr[DB];
+  // F8 == 2 V^T operand reads: row db*32 + l32, chunks 2 hi + {0, 1}.
+  [[maybe_unused]] int vaddr8[F8 == 2 ? DB : 1][2];
+  if constexpr (F8 == 2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = db * 32 + l32;
+        vaddr8[db][j] = row * 64 + (((2 * hi + j) ^ ((row >> 2) & 3)) * 16);
+      }
   {
     const int g = lane >> 4, m = lane & 15;
     const int row = 4 * (g >> 1) + (m >> 2);
@@ -348,7 +376,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 
   const char* kbase = reinterpret_cast<const char*>(k) + (int64_t(it.seg_start) * sk + kv_off) * KESZ;
-  const uint16_t* vbase = v + int64_t(it.seg_start) * sv + kv_off;
+  const char* vbase = F8 == 2 ? reinterpret_cast<const char*>(v) + int64_t(kv_off) * sv + it.vt_col0
+                              : reinterpret_cast<const char*>(v + int64_t(it.seg_start) * sv + kv_off);
   // Keys the item needs: the whole segment, or (causal) up to its last row.
   const int nkeys = CAUSAL ? min(it.seg_len, it.q_start + kBM) : it.seg_len;
   const int ntiles = (nkeys + kBN - 1) / kBN;
@@ -366,18 +395,27 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   auto load_v = [&](int t, auto slot) {
     const int key0 = t * kBN;
-    const auto r = rows_rsrc(vbase + int64_t(key0) * sv, it.seg_len - key0, kBN, int(sv) * 2);
+    if constexpr (F8 < 2) {
+      const auto r = rows_rsrc(vbase + int64_t(key0) * sv * 2, it.seg_len - key0, kBN, int(sv) * 2);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
-                                               voff[i], 0, 0, 0);
+      for (int i = 0; i < NDMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
+                                                 voff[i], 0, 0, 0);
+    } else {
+      // D rows of sv bytes from the tile's first column; padding columns hold 0
+      const auto r = rows_rsrc(vbase + key0, D, D, int(sv));
+#pragma unroll
+      for (int i = 0; i < NDMAV8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
+                                                 voff[i], 0, 0, 0);
+    }
   };
   // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
   auto qk = [&](auto slot, f32x16* sacc) {
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
-      if constexpr (!F8) {
+      if constexpr (F8 == 0) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8 a = *(const LDS bf16x8*)((const LDS char*)kslot(slot) + kaddr[ks] + kb * 32 * ROWB);
@@ -442,6 +480,36 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // the rounded values (v_dot2 against (1, 1)), so the normaliser matches the
   // weights actually applied to V.
   auto probs = [&](const f32x16* sacc, bf16x8* pb) {
+    if constexpr (F8 == 2) {
+      // E4M3 probabilities (p <= 2^8, inside E4M3's range), dword g = keys
+      // 8g + 4 hi + {0..3}; the row sum adds the fp32 values.
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      int d[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        float p4[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, -m_run));
+          ls[w] += p4[w];
+        }
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+        d[g] = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
+      }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      // Swap dwords 4..7 of the low half with dwords 0..3 of the high half:
+      // afterwards B dword m of either half holds keys 32 hi + 4 m + {0..3}.
+      int b[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(d[i], d[4 + i], false, false);
+        b[2 * i] = sw[0];
+        b[2 * i + 1] = sw[1];
+      }
+      pb[0] = __builtin_bit_cast(bf16x8, make_int4(b[0], b[1], b[2], b[3]));
+      pb[1] = __builtin_bit_cast(bf16x8, make_int4(b[4], b[5], b[6], b[7]));
+      return;
+    }
     const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
@@ -460,6 +528,19 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // O^T += V^T P^T for the V tile in `slot`.
   auto pv = [&](auto slot, const bf16x8* pb) {
+    if constexpr (F8 == 2) {
+      const int4 b0 = __builtin_bit_cast(int4, pb[0]), b1 = __builtin_bit_cast(int4, pb[1]);
+      const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const LDS char* vp = (const LDS char*)vslot(slot);
+        const uint4 lo = *(const LDS uint4*)(vp + vaddr8[db][0]);
+        const uint4 up = *(const LDS uint4*)(vp + vaddr8[db][1]);
+        const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, oacc[db], 0, 0, 0, 127, 0, 127);
+      }
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -560,7 +641,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, bool CAUSAL, bool QNORM = false, int RH = 0, bool F8 = false>
+template <int D, bool CAUSAL, bool QNORM = false, int RH = 0, int F8 = 0>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
                   int kv_group, const QNormArgs& qn, hipStream_t stream) {
@@ -598,12 +679,29 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, 
   const QNormArgs none{};
 #define H3A_F8_CASE(DD)                                                                                     \
   if (D == DD)                                                                                              \
-    return causal ? launch<DD, true, false, 0, true>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,     \
-                                                     kv_group, none, stream)                               \
-                  : launch<DD, false, false, 0, true>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,    \
-                                                      kv_group, none, stream);
+    return causal ? launch<DD, true, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,        \
+                                                  kv_group, none, stream)                                  \
+                  : launch<DD, false, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,       \
+                                                   kv_group, none, stream);
   H3A_F8_CASE(128) H3A_F8_CASE(64)
 #undef H3A_F8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int32_t D, int64_t sq,
+                               int64_t sk, int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items,
+                               float scale, int32_t kv_group, bool causal, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  if (kv_group < 1) return hipErrorInvalidValue;
+  const QNormArgs none{};
+#define H3A_F8PV_CASE(DD)                                                                                   \
+  if (D == DD)                                                                                              \
+    return causal ? launch<DD, true, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale, \
+                                                  kv_group, none, stream)                                  \
+                  : launch<DD, false, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale,\
+                                                   kv_group, none, stream);
+  H3A_F8PV_CASE(128) H3A_F8PV_CASE(64)
+#undef H3A_F8PV_CASE
   return hipErrorInvalidValue;
 }
 

@@ -95,6 +95,22 @@ hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, v
                                        const float* gq, const float* gk, float eps, const float* cos_sin,
                                        int32_t rot_dim, hipStream_t stream);
 
+// Attention with q, k as E4M3 codes and V as the transposed E4M3 layout of
+// launch_prepare_vt_e4m3 (row length vt_cols bytes); both products on FP8
+// MFMA.
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int32_t D, int64_t sq,
+                               int64_t sk, int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items,
+                               float scale, int32_t kv_group, bool causal, hipStream_t stream);
+
+// Columns of the transposed E4M3 V layout: every segment padded to whole
+// kVtTile-key tiles.
+int64_t vt_e4m3_columns(const int32_t* cu, int32_t nseg);
+
+// bf16 v [S, H, D] (token stride sv elements) -> vt [H][D][vt_cols] E4M3
+// codes, segment s at columns from the padded prefix sum, padding zeroed.
+hipError_t launch_prepare_vt_e4m3(const void* v, int64_t sv, const int32_t* cu, int32_t nseg, int32_t H, int32_t D,
+                                  void* vt, int64_t vt_cols, hipStream_t stream);
+
 // bf16 [S, row_elems] rows (token stride sx elements) -> E4M3 codes (token
 // stride sy bytes); row_elems a multiple of 8.
 hipError_t launch_quantize_e4m3(const void* x, void* y, int64_t S, int32_t row_elems, int64_t sx, int64_t sy,

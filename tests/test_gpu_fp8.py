@@ -174,3 +174,109 @@ def test_fused_norm_rope_e4m3_equals_two_passes(name, kv):
     torch.cuda.synchronize()
     assert torch.equal(q, q0) and torch.equal(k, k0)
     assert torch.equal(q8, q8b) and torch.equal(k8, k8b)
+
+
+# Both products in FP8: the probabilities are rounded to E4M3 as well, each by
+# at most 2^-4 of itself (three mantissa bits, nearest even), so against
+# attention on E4M3 q, k, v with exact weights an output element moves by at
+# most 2^-4 sum_j p_j |v_j| / sum_j p_j -- attention on |v| -- plus the bf16
+# path's own rounding (TOL_BF16_ABS).  On the oracle the weight rounding moves
+# the S = 5,120 outputs by 2.6e-2 mean-rel; the whole FP8 path sits at 5.3e-2
+# mean-rel from exact attention, with max abs 2.1e-2 (S = 5,120) and 4.8e-2
+# (S = 20,423 sampled rows, whose short segments have the largest outputs).
+P_ROUND = 2.0 ** -4
+TOL_FP8PV_MEANREL = 4e-2
+TOL_FP8_EXACT_ABS, TOL_FP8_EXACT_MEANREL = 1e-1, 8e-2
+
+
+def expected_vt(vbits: np.ndarray, cu) -> np.ndarray:
+    """The transposed, segment-padded E4M3 layout built from the oracle's codec."""
+    S, H, D = vbits.shape
+    codes = oracle.e4m3_encode(rng.bf16_bits_to_f32(vbits).astype(np.float64))
+    lens = np.diff(np.asarray(cu))
+    pad = (lens + 63) // 64 * 64
+    out = np.zeros((H, D, int(pad.sum())), dtype=np.uint8)
+    col = 0
+    for s, L in enumerate(lens):
+        a = int(cu[s])
+        out[:, :, col:col + L] = codes[a:a + L].transpose(1, 2, 0)
+        col += int(pad[s])
+    return out
+
+
+def check(g, r, what, tol_abs, tol_rel):
+    """tol_abs: a number, or an elementwise bound of the same shape as r."""
+    err = np.abs(g - r)
+    max_abs, mean_rel = float(err.max()), float(err.sum() / np.abs(r).sum())
+    worst = float(np.max(err - tol_abs))
+    log(f"  {what}: max_abs={max_abs:.3e} mean_rel={mean_rel:.3e} max(err - bound)={worst:.3e} n={err.size}")
+    assert np.all(np.isfinite(g))
+    assert worst <= 0 and mean_rel <= tol_rel, (max_abs, mean_rel, worst)
+
+
+def weight_rounding_bound(ref_abs_v):
+    from tests.gpu_util import TOL_BF16_ABS
+
+    return P_ROUND * ref_abs_v + TOL_BF16_ABS
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prepare_vt_layout_bit_exact(D):
+    import torch
+
+    lens = [1, 63, 64, 65, 0, 129, 700]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S, H = int(cu[-1]), 3
+    vb = rng.normal_tensor(41 + D, rng.TAG_V, (S, H, D), "bf16", 0.0, 30.0)  # wide enough to saturate some
+    vt = h3a().prepare_vt_e4m3(to_device(vb, "bf16"), cu)
+    torch.cuda.synchronize()
+    want = expected_vt(vb, cu)
+    got = vt.cpu().numpy()
+    log(f"[vt layout] D={D} columns={want.shape[2]} mismatches={int(np.sum(got != want))}")
+    assert got.shape == want.shape and np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_vs_operand_oracle(D, Hq, Hkv, causal):
+    cu = np.concatenate([[0], np.cumsum(EDGE_LENS)]).astype(np.int64)
+    S = int(cu[-1])
+    seed = 500 + D + Hq + (1 if causal else 0)
+    log(f"[fp8 pv] D={D} Hq={Hq} Hkv={Hkv} causal={causal} S={S} seed={seed}")
+    qb = rng.normal_tensor(seed, rng.TAG_Q, (S, Hq, D), "bf16")
+    kb = rng.normal_tensor(seed, rng.TAG_K, (S, Hkv, D), "bf16")
+    vb = rng.normal_tensor(seed, rng.TAG_V, (S, Hkv, D), "bf16")
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    o = h3a().varlen_attn_fwd_fp8(h3a().quantize_e4m3(q), h3a().quantize_e4m3(k), h3a().prepare_vt_e4m3(v, cu), cu,
+                                  1.0 / np.sqrt(D), causal=causal)
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    ref = oracle.varlen_attention_fp8(qf, kf, vf, cu, 1.0 / np.sqrt(D), causal=causal)
+    ref_abs_v = oracle.varlen_attention_fp8(qf, kf, np.abs(vf), cu, 1.0 / np.sqrt(D), causal=causal)
+    check(to_f64(o), ref, "o vs E4M3-operand oracle", weight_rounding_bound(ref_abs_v), TOL_FP8PV_MEANREL)
+
+
+@pytest.mark.parametrize("name", ["two_seg_bf16", "h3_s20423_bf16"])
+def test_fp8_chain(name):
+    import torch
+
+    w = configs.ALL[name]
+    T = configs.make_tensors(w)
+    log(f"[fp8 full chain] {name} S={w.tokens}")
+    q, k, v = (to_device(x, w.dtype) for x in (T.q, T.k, T.v))
+    gq, gk = torch.from_numpy(T.gamma_q).cuda(), torch.from_numpy(T.gamma_k).cuda()
+    tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    cu = h3a().build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    q8, k8 = h3a().qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim)
+    o = to_f64(h3a().varlen_attn_fwd_fp8(q8, k8, h3a().prepare_vt_e4m3(v, cu), cu, w.scale))
+    qf, kf, vf = (rng.as_f64(x, w.dtype) for x in (T.q, T.k, T.v))
+    ocu, cos, sin = oracle.rope_table(w.segments, w.rot_dims, w.base)
+    qn, kn = oracle.qk_rmsnorm_rope(qf, kf, T.gamma_q, T.gamma_k, w.eps, cos, sin, w.rot_dim)
+    rows = sample_rows(ocu, every=97)
+    q8o, k8o = (oracle.e4m3_round(oracle.bf16_round(x)) for x in (qn, kn))
+    ref8 = oracle.varlen_attention_rows(q8o, k8o, oracle.e4m3_round(vf), ocu, w.scale, rows)
+    ref8_abs = oracle.varlen_attention_rows(q8o, k8o, np.abs(oracle.e4m3_round(vf)), ocu, w.scale, rows)
+    check(o[rows], ref8, f"o vs E4M3-operand oracle ({len(rows)} rows)", weight_rounding_bound(ref8_abs),
+          TOL_FP8PV_MEANREL)
+    ref = oracle.varlen_attention_rows(qn, kn, vf, ocu, w.scale, rows)
+    check(o[rows], ref, "o vs exact attention", TOL_FP8_EXACT_ABS, TOL_FP8_EXACT_MEANREL)

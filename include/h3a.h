@@ -6,6 +6,11 @@
  *   1. a step-invariant 3D (t, h, w) rotary table for the packed segments,
  *   2. per-head RMSNorm of Q and K fused with NeoX rotary on the first R dims,
  *   3. bidirectional attention restricted to each cu_seqlens segment.
+ * Variants of the same path (the *_ex and suffixed calls below): other rotary
+ * table modes (fp64 linspace grid, the ViT3D's length-normalised ids,
+ * interleaved M-RoPE), grouped K/V heads and a causal mask (the encoder text
+ * tower), the Q norm + rotary folded into the attention, and low-precision
+ * attention on FP8 E4M3 operands.
  *
  * Sources (the pages this library was built from):
  *   - vllm.cpp PR #26 "feat(minimax-h3): port the MiniMax-H3 omni-modal
@@ -379,7 +384,7 @@ const char* h3a_last_error(void);
  * launched earlier is still running (synchronise its streams first). */
 void h3a_release_caches(void);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch (0.2.0). */
 int32_t h3a_version(void);
 
 #ifdef __cplusplus

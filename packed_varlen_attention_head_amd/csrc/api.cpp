@@ -195,7 +195,7 @@ extern "C" {
 
 const char* h3a_last_error(void) { return g_last_error.c_str(); }
 
-int32_t h3a_version(void) { return 100; }
+int32_t h3a_version(void) { return 200; }
 
 void h3a_release_caches(void) {
   PlanCache& pc = plan_cache();

@@ -46,10 +46,15 @@ constexpr double kItemOverheadKeys = 128.0;
 
 std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
                                  int32_t n_xcd, bool causal) {
-  // First column of each segment in the padded transposed-V layout.
+  // First column of each segment in the padded transposed-V layout (-1 past
+  // INT32_MAX: only the FP8-PV path reads it, and its entry point rejects
+  // layouts that large).
   std::vector<int32_t> col0(size_t(nseg) + 1, 0);
-  for (int32_t s = 0; s < nseg; ++s)
-    col0[s + 1] = col0[s] + (cu[s + 1] - cu[s] + kVtTile - 1) / kVtTile * kVtTile;
+  int64_t col = 0;
+  for (int32_t s = 0; s < nseg; ++s) {
+    col += (int64_t(cu[s + 1]) - cu[s] + kVtTile - 1) / kVtTile * kVtTile;
+    col0[s + 1] = col > int64_t(INT32_MAX) ? -1 : int32_t(col);
+  }
   std::vector<int32_t> order;
   for (int32_t s = 0; s < nseg; ++s)
     if (cu[s + 1] > cu[s]) order.push_back(s);

@@ -64,8 +64,9 @@
 //     64-key tile per segment-padded column block, E4M3), so the V^T operand
 //     is two plain 16-byte LDS reads, and the probabilities (rounded to
 //     E4M3) leave the score accumulator as the B operand after four lane-half
-//     swaps that give each half 32 consecutive keys.  The row sum adds the
-//     fp32 probabilities.
+//     swaps that give each half 32 consecutive keys.  The row sums are one
+//     more FP8 MFMA per tile with an all-ones A operand, so they add exactly
+//     the E4M3 weights PV applies.
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -314,6 +315,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -1e30f;  // reference max of scale*log2(e)*score
   float l_run = 0.f;     // this lane's partial row sum (its 16-of-32 keys)
+  // F8 == 2: the row sums come from the matrix core instead -- an all-ones
+  // A operand against the E4M3 probabilities puts sum_k p[k][q] in every
+  // register of lane q (both halves), the same weights PV applies.
+  [[maybe_unused]] f32x16 lacc = f32x16{};
 
   // LDS-bound loads: slot s = (i * kWaves + wave) * 64 + lane holds physical
   // chunk s % CH of row s / CH; the lane fetches the logical chunk stored there.
@@ -472,6 +477,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;
       l_run *= alpha;
+      if constexpr (F8 == 2) lacc *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
@@ -482,21 +488,16 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto probs = [&](const f32x16* sacc, bf16x8* pb) {
     if constexpr (F8 == 2) {
       // E4M3 probabilities (p <= 2^8, inside E4M3's range), dword g = keys
-      // 8g + 4 hi + {0..3}; the row sum adds the fp32 values.
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      // 8g + 4 hi + {0..3}.
       int d[8];
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         float p4[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, -m_run));
-          ls[w] += p4[w];
-        }
+        for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, -m_run));
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
         d[g] = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
       }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       // Swap dwords 4..7 of the low half with dwords 0..3 of the high half:
       // afterwards B dword m of either half holds keys 32 hi + 4 m + {0..3}.
       int b[8];
@@ -539,6 +540,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, oacc[db], 0, 0, 0, 127, 0, 127);
       }
+      const int one4 = 0x38383838;  // four E4M3 ones
+      const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, b, lacc, 0, 0, 0, 127, 0, 127);
       return;
     }
 #pragma unroll
@@ -625,7 +629,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   if (!active) return;
   const int qi = qrow0 + l32;
-  const float l_tot = l_run + other_half(l_run, hi);
+  const float l_tot = F8 == 2 ? lacc[0] : l_run + other_half(l_run, hi);
   const float inv = 1.0f / l_tot;
   if (qi >= it.seg_len) return;
   uint16_t* op = o + int64_t(it.seg_start + qi) * so + head_off + hi * 4;

@@ -280,3 +280,26 @@ def test_fp8_chain(name):
           TOL_FP8PV_MEANREL)
     ref = oracle.varlen_attention_rows(qn, kn, vf, ocu, w.scale, rows)
     check(o[rows], ref, "o vs exact attention", TOL_FP8_EXACT_ABS, TOL_FP8_EXACT_MEANREL)
+
+
+def test_many_segments_fp8_layout_and_attention():
+    """150 ragged segments (three launches of the V-layout pass), grouped K/V."""
+    import torch
+
+    lens = [int(x) for x in 1 + (rng.uniform(77, rng.TAG_LENS, 150) * 300).astype(np.int64)]
+    lens[7] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S, Hq, Hkv, D = int(cu[-1]), 4, 2, 64
+    log(f"[fp8 many segments] S={S} nseg={len(lens)}")
+    qb = rng.normal_tensor(78, rng.TAG_Q, (S, Hq, D), "bf16")
+    kb = rng.normal_tensor(78, rng.TAG_K, (S, Hkv, D), "bf16")
+    vb = rng.normal_tensor(78, rng.TAG_V, (S, Hkv, D), "bf16")
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    vt = h3a().prepare_vt_e4m3(v, cu)
+    torch.cuda.synchronize()
+    assert np.array_equal(vt.cpu().numpy(), expected_vt(vb, cu))
+    o = h3a().varlen_attn_fwd_fp8(h3a().quantize_e4m3(q), h3a().quantize_e4m3(k), vt, cu, 0.125)
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    ref = oracle.varlen_attention_fp8(qf, kf, vf, cu, 0.125)
+    ref_abs = oracle.varlen_attention_fp8(qf, kf, np.abs(vf), cu, 0.125)
+    check(to_f64(o), ref, "o vs E4M3-operand oracle", weight_rounding_bound(ref_abs), TOL_FP8PV_MEANREL)

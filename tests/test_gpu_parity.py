@@ -296,3 +296,31 @@ def test_hot_path_end_to_end(name):
         rows = sample_rows(ocu)
         ref = oracle.varlen_attention_rows(qn, kn, vf, ocu, w.scale, rows)
         compare(o[rows], ref, w.dtype, f"o ({len(rows)} sampled rows)")
+
+
+def test_plan_cache_eviction():
+    """More distinct packings than the plan cache holds (256): old plans are evicted (after a
+    device synchronisation) and every call still matches the oracle."""
+    import torch
+
+    H, D = 2, 64
+    S = 300
+    qb = rng.normal_tensor(90, rng.TAG_Q, (S, H, D), "bf16")
+    kb = rng.normal_tensor(90, rng.TAG_K, (S, H, D), "bf16")
+    vb = rng.normal_tensor(90, rng.TAG_V, (S, H, D), "bf16")
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    h3a().release_caches()
+    log("[plan cache] 270 packings")
+    outs = []
+    for i in range(270):
+        cu = np.array([0, 1 + i, S], dtype=np.int64)
+        outs.append((cu, h3a().varlen_attn_fwd(q, k, v, cu, 0.125)))
+    torch.cuda.synchronize()
+    for i in (0, 1, 100, 255, 256, 269):
+        cu, o = outs[i]
+        compare(to_f64(o), oracle.varlen_attention(qf, kf, vf, cu, 0.125), "bf16", f"packing {i}")
+    # a packing seen long ago (evicted) is planned again
+    cu, _ = outs[0]
+    compare(to_f64(h3a().varlen_attn_fwd(q, k, v, cu, 0.125)), oracle.varlen_attention(qf, kf, vf, cu, 0.125),
+            "bf16", "packing 0 again")

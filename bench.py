@@ -10,7 +10,10 @@ Prints one JSON line.  `value` is attention TFLOP/s over the whole step,
 F = 4 * D * heads * sum(L^2) divided by the step time; `roofline` reports the
 attention kernel alone (HIP events on its launch stream) against the bf16
 dense MFMA peak; `cpu_baseline` times the fp64 oracle on a bounded sample of
-the same workload.
+the same workload.  The GPU clock is sampled during the timed work
+(`sclk_mhz`) and the attention rate is also given against the peak scaled to
+that clock; the steps run untimed for `--settle` seconds before the warmup
+steps so the clock has left its idle level.
 
 --config runs another bf16 workload of the same family through the same step
 (its own rotary table mode, grouped K/V heads, causal mask); F then counts the
@@ -21,10 +24,12 @@ visible (query, key) pairs, sum(L (L + 1) / 2) when causal.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -56,6 +61,8 @@ def parse():
     ap.add_argument("--fused-q", action="store_true",
                     help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps, so the GPU clock has left its idle state")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     ap.add_argument("--rocprof-summary", metavar="RESULTS_DB",
@@ -153,6 +160,65 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 5}))
     return 0
+
+
+NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peaks assume
+
+
+class SclkSampler:
+    """Samples the GPU's current shader clock (the starred level of the
+    driver's pp_dpm_sclk file) from a host thread while timed work runs; stop()
+    returns the median in MHz, or None when the file is absent or ambiguous
+    (several GPUs and no PCI address to match)."""
+
+    def __init__(self, period_s=0.005):
+        self.period = period_s
+        self.samples = []
+        self.path = None
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(paths) == 1:
+            self.path = paths[0]
+        elif paths:
+            try:
+                import torch
+
+                bus = str(getattr(torch.cuda.get_device_properties(0), "pci_bus_id", "")).lower()
+                match = [p for p in paths if bus and os.path.basename(os.path.realpath(os.path.dirname(p))).lower()
+                         .endswith(bus)]
+                self.path = match[0] if len(match) == 1 else None
+            except Exception:  # noqa: BLE001 - clock reporting is best effort
+                self.path = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    mhz = line.split(":", 1)[1].strip().split("Mhz")[0].split("MHz")[0]
+                    return float(mhz)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except (OSError, ValueError, IndexError):
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.path:
+            self._thread.start()
+
+    def stop(self):
+        if not self.path:
+            return None
+        self._stop.set()
+        self._thread.join()
+        return float(np.median(self.samples)) if self.samples else None
 
 
 def source_hash(path):
@@ -308,9 +374,20 @@ def main():
         attention(cu)
         return cu
 
+    # The GPU idles at a low clock and takes a few hundred ms of load to reach
+    # its working clock: run the step untimed for `settle` seconds first.
+    cu = step()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         cu = step()
     torch.cuda.synchronize()
+    clock = SclkSampler()
+    clock.start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -335,8 +412,23 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / 1e3 / n
 
+    # The attention kernel is long enough for an event pair per launch: its
+    # median is reported beside the mean.
+    def timed_each(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        fn()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        each = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
+        return ev[0].elapsed_time(ev[n]) / 1e3 / n, float(np.median(each))
+
     n_ev = max(args.steps, 10)
-    attn_s = timed(lambda: attention(cu), n_ev)
+    attn_s, attn_med_s = timed_each(lambda: attention(cu), n_ev)
+    sclk = clock.stop()
     norm_s = timed(norm, n_ev)
     table_s = timed(table, n_ev)
     vprep_s = timed(lambda: vprep(cu), n_ev) if fp8pv else 0.0
@@ -383,7 +475,12 @@ def main():
         },
         "pct_bf16_peak_step": 100.0 * F / step_s / 1e12 / PEAK_BF16_TFLOPS,
         "attn_ms": attn_s * 1e3,
+        "attn_ms_median": attn_med_s * 1e3,
         "attn_tflops": attn_tflops,
+        # GPU clock sampled during the timed steps and attention launches, and
+        # the attention rate against the peak scaled to that clock
+        "sclk_mhz": sclk,
+        "pct_peak_at_sclk": (100.0 * attn_tflops / (peak * sclk / NOMINAL_SCLK_MHZ)) if sclk else None,
         "norm_rope_ms": norm_s * 1e3,
         "norm_rope_GBps": norm_bytes / norm_s / 1e9,
         "rope_table_ms": table_s * 1e3,

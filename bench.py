@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--rocprof-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="HBM bytes per launch of each h3a kernel from FETCH_SIZE/WRITE_SIZE runs, scaled by "
                          "the same counters on the --calibrate-copy run; prints JSON")
+    ap.add_argument("--rocprof-counters", nargs="+", metavar="RESULTS_DB",
+                    help="per-dispatch averages of every counter in rocprofv3 --pmc results databases, per kernel, "
+                         "and the attention kernel's MFMA utilisation; prints markdown")
     return ap.parse_args()
 
 
@@ -142,6 +145,58 @@ def rocprof_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
         rb, wb = fetch.get(k, 0.0) * f_scale, write.get(k, 0.0) * w_scale
         out["kernels"][k] = {"hbm_read_bytes": rb, "hbm_write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
     print(json.dumps(out, indent=1))
+    return 0
+
+
+def rocprof_counters(dbs):
+    """Counter values per dispatch (mean over dispatches) for each kernel, from
+    one or more --pmc runs, and for the attention kernel: MFMA flops executed
+    (512 per bf16 MOP) against the algorithmic F of the headline workload, and
+    MFMA-busy cycles over the SIMD-cycles of the dispatch."""
+    import collections
+
+    from synth import configs
+
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for db in dbs:
+        for name, counter, value in _rocpd_rows(db, "select kernel_name, counter_name, value "
+                                                    "from counters_collection"):
+            acc[_short_kernel(name)][counter].append(value)
+    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+    # average dispatch durations (us) where a run also traced the kernels
+    durations = {}
+    for db in dbs:
+        try:
+            for name, avg in _rocpd_rows(db, "select name, average from top_kernels"):
+                durations[_short_kernel(name)] = avg
+        except Exception:  # noqa: BLE001 - a counters-only run has no kernel table
+            pass
+    counters = sorted({c for d in mean.values() for c in d})
+    kernels = sorted(k for k in mean if k.startswith(("attn", "qk_norm", "rope")))
+    print("| kernel | " + " | ".join(counters) + " |")
+    print("|---|" + "---|" * len(counters))
+    for k in kernels:
+        print(f"| {k} | " + " | ".join(f"{mean[k][c]:.4g}" if c in mean[k] else "" for c in counters) + " |")
+    F = configs.BF16[HEADLINE].attention_flops()
+    for k in kernels:
+        m = mean[k]
+        if not k.startswith("attn_fwd_bf16_kernel<128>"):
+            continue
+        print()
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+            flop = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+            print(f"- {k}: bf16 MFMA flops executed {flop:.4g} per dispatch = {flop / F:.4f} x the "
+                  f"algorithmic F = {F:.4g} of {HEADLINE}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m:
+            # GRBM_GUI_ACTIVE adds up the busy cycles of the 8 XCDs
+            simd_cycles = m["GRBM_GUI_ACTIVE"] / 8 * 256 * 4
+            print(f"- {k}: MFMA busy {m['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} cycles / (GRBM_GUI_ACTIVE "
+                  f"{m['GRBM_GUI_ACTIVE']:.4g} / 8 XCDs x 256 CUs x 4 SIMDs) = "
+                  f"{100.0 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.1f}%")
+        dur = durations.get(k)
+        if dur and "GRBM_GUI_ACTIVE" in m:
+            print(f"- {k}: GRBM_GUI_ACTIVE / 8 over the traced average duration {dur / 1e3:.3f} ms = "
+                  f"{m['GRBM_GUI_ACTIVE'] / 8 / dur:.0f} MHz (the clock during the counted dispatches)")
     return 0
 
 
@@ -298,6 +353,8 @@ def main():
         return rocprof_summary(args.rocprof_summary)
     if args.rocprof_traffic:
         return rocprof_traffic(*args.rocprof_traffic)
+    if args.rocprof_counters:
+        return rocprof_counters(args.rocprof_counters)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "

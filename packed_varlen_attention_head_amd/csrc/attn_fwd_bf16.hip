@@ -142,6 +142,15 @@ __device__ __forceinline__ float other_half(float x, int hi) {
   return __builtin_bit_cast(float, hi ? r[0] : r[1]);
 }
 
+// max(x, value of lane ^ 32) in every lane: one v_permlane32_swap of x with
+// itself leaves lanes l and l ^ 32 holding (x[l % 32], x[l % 32 + 32]) in its
+// two results.
+__device__ __forceinline__ float pair_max(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
 template <int N>
 using IC = std::integral_constant<int, N>;
 
@@ -319,6 +328,14 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // A operand against the E4M3 probabilities puts sum_k p[k][q] in every
   // register of lane q (both halves), the same weights PV applies.
   [[maybe_unused]] f32x16 lacc = f32x16{};
+  // The all-ones A operand (four E4M3 ones per dword), built once: opaque to
+  // the compiler so it stays in registers instead of being rebuilt per tile.
+  [[maybe_unused]] i32x8 ones8;
+  if constexpr (F8 == 2) {
+    const int one4 = 0x38383838;
+    ones8 = i32x8{one4, one4, one4, one4, one4, one4, one4, one4};
+    asm volatile("" : "+v"(ones8));
+  }
 
   // LDS-bound loads: slot s = (i * kWaves + wave) * 64 + lane holds physical
   // chunk s % CH of row s / CH; the lane fetches the logical chunk stored there.
@@ -467,7 +484,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, other_half(mx, hi)) * c;
+    mx = pair_max(mx) * c;
     const bool grow = mx > m_run + kRescaleSlack;
     if (__builtin_expect(__any(grow), 0)) {
       // Rare after the first tiles; the empty asm keeps the compiler from
@@ -495,7 +512,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         float p4[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, -m_run));
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+        // bytes 2-3 of the first conversion's destination are overwritten by
+        // the second, so any value serves as its prior contents
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], __builtin_bit_cast(int, p4[0]), false);
         d[g] = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
       }
       // Swap dwords 4..7 of the low half with dwords 0..3 of the high half:
@@ -540,9 +559,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, oacc[db], 0, 0, 0, 127, 0, 127);
       }
-      const int one4 = 0x38383838;  // four E4M3 ones
-      const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
-      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, b, lacc, 0, 0, 0, 127, 0, 127);
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, b, lacc, 0, 0, 0, 127, 0, 127);
       return;
     }
 #pragma unroll

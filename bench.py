@@ -19,7 +19,7 @@ steps so the clock has left its idle level.
 (its own rotary table mode, grouped K/V heads, causal mask); F then counts the
 visible (query, key) pairs, sum(L (L + 1) / 2) when causal.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--config NAME]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--config NAME]
 """
 from __future__ import annotations
 
@@ -49,7 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_h3_s20423_traffic.j
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE, help="bf16 workload name (synth.configs.BF16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,6 +67,8 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     ap.add_argument("--rocprof-summary", metavar="RESULTS_DB",
                     help="print a per-kernel duration table from a rocprofv3 --kernel-trace results.db")
+    ap.add_argument("--summary-last", type=int, default=10, metavar="N",
+                    help="with --rocprof-summary: also average each kernel's last N dispatches (the timed ones)")
     ap.add_argument("--rocprof-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="HBM bytes per launch of each h3a kernel from FETCH_SIZE/WRITE_SIZE runs, scaled by "
                          "the same counters on the --calibrate-copy run; prints JSON")
@@ -108,13 +110,21 @@ def _short_kernel(name):
     return m.group(1) if m else name[:60]
 
 
-def rocprof_summary(db):
-    """Per-kernel table (calls, total, average) from a rocprofv3 results database."""
+def rocprof_summary(db, last):
+    """Per-kernel table (calls, total, average, and the average of the last
+    `last` dispatches) from a rocprofv3 --kernel-trace results database."""
+    import collections
+
     rows = _rocpd_rows(db, "select name, total_calls, total_duration, average, percentage from top_kernels")
-    print("| kernel | calls | total (us) | average (us) | share |")
-    print("|---|---|---|---|---|")
+    durations = collections.defaultdict(list)
+    for name, start, end in _rocpd_rows(db, "select name, start, end from kernels order by start"):
+        durations[name].append((end - start) / 1e3)
+    print(f"| kernel | calls | total (us) | average (us) | average of the last {last} (us) | share |")
+    print("|---|---|---|---|---|---|")
     for name, calls, total, avg, pct in rows:
-        print(f"| {_short_kernel(name)} | {calls} | {total:.1f} | {avg:.1f} | {pct:.2f}% |")
+        tail = durations.get(name, [])[-last:]
+        tail_avg = f"{sum(tail) / len(tail):.1f}" if tail else ""
+        print(f"| {_short_kernel(name)} | {calls} | {total:.1f} | {avg:.1f} | {tail_avg} | {pct:.2f}% |")
     return 0
 
 
@@ -350,7 +360,7 @@ def main():
     if args.calibrate_copy:
         return calibrate_copy()
     if args.rocprof_summary:
-        return rocprof_summary(args.rocprof_summary)
+        return rocprof_summary(args.rocprof_summary, args.summary_last)
     if args.rocprof_traffic:
         return rocprof_traffic(*args.rocprof_traffic)
     if args.rocprof_counters:
@@ -457,11 +467,14 @@ def main():
     # Per-kernel average launch duration: HIP events on the launch stream
     # around n back-to-back launches of that call alone, divided by n.  (An
     # event pair per launch would add the runtime's per-event cost to short
-    # kernels.)
-    def timed(fn, n):
+    # kernels.)  Ten untimed launches are queued right before the first event,
+    # with no host synchronisation between them: the clock drops within
+    # milliseconds whenever the GPU idles and takes tens of milliseconds of
+    # load to recover.
+    def timed(fn, n, warm=10):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        torch.cuda.synchronize()
+        for _ in range(warm):
+            fn()
         a.record(stream)
         for _ in range(n):
             fn()
@@ -471,10 +484,10 @@ def main():
 
     # The attention kernel is long enough for an event pair per launch: its
     # median is reported beside the mean.
-    def timed_each(fn, n):
+    def timed_each(fn, n, warm=10):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        fn()
-        torch.cuda.synchronize()
+        for _ in range(warm):
+            fn()
         ev[0].record(stream)
         for i in range(n):
             fn()

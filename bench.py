@@ -515,6 +515,10 @@ def main():
     norm_bytes = 2 * (S * normed_heads * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + (1 if fused else 2) * D * 4
     if fp8:  # the norm + rotary pass writes one byte per element instead of two
         norm_bytes -= S * (H + Hkv) * D
+    copy_src = torch.empty(norm_bytes // 2, dtype=torch.uint8, device=dev)
+    copy_dst = torch.empty_like(copy_src)
+    copy_gbps = 2 * copy_src.numel() / timed(lambda: copy_dst.copy_(copy_src), n_ev) / 1e9
+    del copy_src, copy_dst
     # Q read and O written (H heads), K and V read (Hkv heads), once each
     attn_alg_bytes = 2 * S * H * D * 2 + 2 * S * Hkv * D * 2
     result = {
@@ -575,6 +579,9 @@ def main():
             "unit": "GB/s",
             "frac": norm_bytes / norm_s / 1e9 / PEAK_HBM_GBPS,
             "algorithmic_bytes_per_launch": norm_bytes,
+            # a plain device-to-device copy moving the same bytes (half read,
+            # half written), timed the same way: what HBM gives a pure stream
+            "copy_reference_GBps": copy_gbps,
         },
     }
     if not args.no_cpu_baseline:

@@ -434,25 +434,42 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
   auto qk = [&](auto slot, f32x16* sacc) {
+    if constexpr (F8 == 0) {
+      // k-steps outer, the 32-key blocks inner (independent accumulators back
+      // to back), each step's K operands read while the previous step's
+      // products issue
+      constexpr int NB = kBN / 32;
+      const LDS char* kp = (const LDS char*)kslot(slot);
+      bf16x8 cur[NB], nxt[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        sacc[kb] = f32x16{};
+        cur[kb] = *(const LDS bf16x8*)(kp + kaddr[0] + kb * 32 * ROWB);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS)
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb) nxt[kb] = *(const LDS bf16x8*)(kp + kaddr[ks + 1] + kb * 32 * ROWB);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[kb], qb[ks], sacc[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) cur[kb] = nxt[kb];
+      }
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
-      if constexpr (F8 == 0) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *(const LDS bf16x8*)((const LDS char*)kslot(slot) + kaddr[ks] + kb * 32 * ROWB);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sacc[kb], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS8; ++ks) {
-          const LDS char* kp = (const LDS char*)kslot(slot) + kb * 32 * KROWB;
-          const uint4 lo = *(const LDS uint4*)(kp + kaddr8[ks][0]);
-          const uint4 up = *(const LDS uint4*)(kp + kaddr8[ks][1]);
-          const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
-          // formats 0/0: E4M3 x E4M3; E8M0 scales 127 = 1.0
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[ks], sacc[kb], 0, 0, 0, 127, 0, 127);
-        }
+      for (int ks = 0; ks < KS8; ++ks) {
+        const LDS char* kp = (const LDS char*)kslot(slot) + kb * 32 * KROWB;
+        const uint4 lo = *(const LDS uint4*)(kp + kaddr8[ks][0]);
+        const uint4 up = *(const LDS uint4*)(kp + kaddr8[ks][1]);
+        const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
+        // formats 0/0: E4M3 x E4M3; E8M0 scales 127 = 1.0
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[ks], sacc[kb], 0, 0, 0, 127, 0, 127);
       }
     }
   };
@@ -562,16 +579,24 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, b, lacc, 0, 0, 0, 127, 0, 127);
       return;
     }
+    // Products in (16-key step, dim block) order, so consecutive MFMAs use
+    // different accumulators; each V^T operand is read two products ahead.
+    constexpr int NP = DB * (kBN / 16);
+    auto read_vt = [&](int i) {
+      const int kk = i / DB, db = i % DB;
+      const LDS char* p0 = (const LDS char*)vslot(slot) + vaddr[db] + kk * 16 * ROWB;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0));
+      const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0 + 8 * ROWB));
+      return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 op[3];
+    op[0] = read_vt(0);
+    op[1] = read_vt(1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kk = 0; kk < kBN / 16; ++kk) {
-        const LDS char* p0 = (const LDS char*)vslot(slot) + vaddr[db] + kk * 16 * ROWB;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0));
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS bf16x4*)(p0 + 8 * ROWB));
-        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < NP; ++i) {
+      if (i + 2 < NP) op[(i + 2) % 3] = read_vt(i + 2);
+      oacc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pb[i / DB], oacc[i % DB], 0, 0, 0);
+    }
   };
   auto publish = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's LDS-bound loads landed

@@ -42,9 +42,11 @@
 //     past it read as zeros with no per-lane branches; those keys are masked
 //     to -inf in the last tile only, and query rows past the end are computed
 //     but not stored.
-//   * exp2 with scale * log2(e) folded into one FMA; the running max is
-//     only raised (and the accumulator rescaled) when a tile exceeds it by
-//     more than 2^8, which is exact and skips the rescale on most tiles.
+//   * exp2 with scale * log2(e) folded into one FMA.  The running max is a
+//     reference only: it is raised (and the accumulator rescaled, which is
+//     exact) when a tile exceeds it by more than 2^8 -- or, in the bf16 steady
+//     loop, which takes no per-tile max at all, when a lane's sum of its
+//     tile probabilities exceeds 2^13, after which the tile is recomputed.
 //   * Optionally (QNORM) the Q rows are RMS-normalised and rotated in the
 //     prologue, from raw q, fusing the Q half of the norm + rotary pass into
 //     the attention (the GB10 build fuses Q RMSNorm + rot96 RoPE into its
@@ -92,6 +94,7 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
 [[maybe_unused]] constexpr int kBN = 64;  // keys per tile
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running max moves
+[[maybe_unused]] constexpr float kSumBound = 8192.0f;   // bf16 steady state: bound on a lane's tile sum
 static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 
 #define LDS __attribute__((address_space(3)))
@@ -144,11 +147,16 @@ __device__ __forceinline__ float other_half(float x, int hi) {
 
 // max(x, value of lane ^ 32) in every lane: one v_permlane32_swap of x with
 // itself leaves lanes l and l ^ 32 holding (x[l % 32], x[l % 32 + 32]) in its
-// two results.
+// two results.  The optimiser takes the two results of swapping a value with
+// itself for equal and folds the max away (keeping only the lower half's
+// keys in the row max), so the second result passes through an empty asm
+// that hides its value.
 __device__ __forceinline__ float pair_max(float x) {
   const int xi = __builtin_bit_cast(int, x);
   const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  int lo = r[0], up = r[1];
+  asm volatile("" : "+v"(up));
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, up));
 }
 
 template <int N>
@@ -516,9 +524,55 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
   };
-  // p = 2^(c*s - m_run), rounded to bf16 for the PV product; the row sum adds
-  // the rounded values (v_dot2 against (1, 1)), so the normaliser matches the
-  // weights actually applied to V.
+  // p = 2^(c*s - m_run), rounded to bf16 for the PV product, for one tile;
+  // returns the lane's sum of the rounded values (v_dot2 against (1, 1)), so
+  // the normaliser matches the weights actually applied to V.
+  auto probs_part = [&](const f32x16* sacc, bf16x8* pb) {
+    const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+    float part = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 v8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], c, -m_run)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 pr = {v8[2 * i], v8[2 * i + 1]};
+          part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part, false);
+        }
+        pb[kb * 2 + hh] = v8;
+      }
+    return part;
+  };
+  // bf16 steady state takes no per-tile max: the reference m_run only has to
+  // keep every probability bounded, and a lane's sum `part` of its 32
+  // probabilities bounds each of them.  When some lane's sum exceeds
+  // kSumBound (a probability may be large, or infinite), the tile's true row
+  // max raises the reference, the output and row sum are rescaled, and the
+  // tile is recomputed; this is exact, as numerator and denominator share the
+  // reference.  Otherwise every probability is at most kSumBound.  Must run
+  // before the tile's PV product is issued.
+  auto probs_checked = [&](const f32x16* sacc, bf16x8* pb, float part) {
+    if (__builtin_expect(__any(!(part <= kSumBound)), 0)) {
+      asm volatile("" ::: "memory");  // keep the rare path a real branch
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      mx = pair_max(mx) * c;
+      const float m_new = mx > m_run ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      part = probs_part(sacc, pb);
+    }
+    l_run += part;
+  };
   auto probs = [&](const f32x16* sacc, bf16x8* pb) {
     if constexpr (F8 == 2) {
       // E4M3 probabilities (p <= 2^8, inside E4M3's range), dword g = keys
@@ -547,21 +601,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       pb[1] = __builtin_bit_cast(bf16x8, make_int4(b[4], b[5], b[6], b[7]));
       return;
     }
-    const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8 v8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], c, -m_run)));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x2 pr = {v8[2 * i], v8[2 * i + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-        }
-        pb[kb * 2 + hh] = v8;
-      }
+    l_run += probs_part(sacc, pb);
   };
   // O^T += V^T P^T for the V tile in `slot`.
   auto pv = [&](auto slot, const bf16x8* pb) {
@@ -638,10 +678,20 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // Every wave computes here, also one whose rows all lie past the segment
     // end (rare: last query tile only; its rows are not stored), so the loads
     // and the MFMA/softmax work form one block the scheduler can interleave.
-    probs(s, pb);
-    qk(IC<P ^ 1>{}, s);
-    pv(IC<P>{}, pb);
-    update_max(s);
+    if constexpr (F8 == 0) {
+      // tile t's probabilities beside tile t+1's scores; the check (rarely
+      // taken) still sees tile t's scores in sold
+      const f32x16 sold[kBN / 32] = {s[0], s[1]};
+      const float part = probs_part(sold, pb);
+      qk(IC<P ^ 1>{}, s);
+      probs_checked(sold, pb, part);
+      pv(IC<P>{}, pb);
+    } else {
+      probs(s, pb);
+      qk(IC<P ^ 1>{}, s);
+      pv(IC<P>{}, pb);
+      update_max(s);
+    }
     publish();
   };
   int t = 0;
@@ -656,7 +706,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t + 2 < ntiles) load_k(t + 2, par);
     if (t + 1 < ntiles) load_v(t + 1, par ^ 1);
     if (active) {
-      probs(s, pb);
+      if constexpr (F8 == 0) probs_checked(s, pb, probs_part(s, pb));
+      else probs(s, pb);
       if (t + 1 < ntiles) {
         qk(par ^ 1, s);
         pv(par, pb);

@@ -189,6 +189,29 @@ def test_varlen_attention_sharp_softmax():
     assert np.abs(ref).mean() > 0.2
 
 
+def test_varlen_attention_rising_logits():
+    """Logits that grow along the keys (and one tile 40x larger than the rest):
+    later tiles exceed the running reference by far more than the bf16 steady
+    loop's bound on a tile's probability sum, so its recompute path runs many
+    times, once where an unchecked tile would overflow to infinity."""
+    H, D = 2, 128
+    lens = [700, 300, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    log("[rising logits]")
+    q, k0, v = (rng.normal_tensor(14, tag, (S, H, D), "bf16") for tag in (1, 2, 3))
+    gain = np.ones(S)
+    gain[:700] = 1.0 + np.arange(700) / 50.0      # logit std grows to ~15 along segment 0
+    gain[700 + 192:700 + 256] = 40.0              # one 64-key tile of segment 1 dominates
+    kf = rng.as_f64(k0, "bf16") * gain[:, None, None]
+    k = rng.f32_to_bf16_bits(kf.astype(np.float32))
+    o = to_f64(run_attn(*(to_device(x, "bf16") for x in (q, k, v)), cu, 1 / np.sqrt(D)))
+    ref = oracle.varlen_attention(*(rng.as_f64(x, "bf16") for x in (q, k, v)), cu, 1 / np.sqrt(D))
+    compare(o, ref, "bf16", "o")
+    # peaked rows: far from the uniform mean, so the comparison has teeth
+    assert np.abs(ref[:700]).mean() > 0.3 and np.abs(ref[700:1000]).mean() > 0.3
+
+
 def test_varlen_attention_segment_isolation():
     import torch
 

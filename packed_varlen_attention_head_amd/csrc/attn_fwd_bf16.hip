@@ -156,7 +156,9 @@ __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
   int lo = r[0], up = r[1];
   asm volatile("" : "+v"(up));
-  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, up));
+  // compare and select: no NaN-quieting of the swapped values (fmaxf adds it)
+  const float a = __builtin_bit_cast(float, lo), b = __builtin_bit_cast(float, up);
+  return a > b ? a : b;
 }
 
 template <int N>

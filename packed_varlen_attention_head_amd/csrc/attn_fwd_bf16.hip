@@ -548,7 +548,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
     return part;
   };
-  // bf16 steady state takes no per-tile max: the reference m_run only has to
+  // With bf16 probabilities the steady state takes no per-tile max: the
+  // reference m_run only has to
   // keep every probability bounded, and a lane's sum `part` of its 32
   // probabilities bounds each of them.  When some lane's sum exceeds
   // kSumBound (a probability may be large, or infinite), the tile's true row
@@ -680,9 +681,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // Every wave computes here, also one whose rows all lie past the segment
     // end (rare: last query tile only; its rows are not stored), so the loads
     // and the MFMA/softmax work form one block the scheduler can interleave.
-    if constexpr (F8 == 0) {
-      // tile t's probabilities beside tile t+1's scores; the check (rarely
-      // taken) still sees tile t's scores in sold
+    if constexpr (F8 <= 1) {
+      // bf16 probabilities (also behind FP8 scores): tile t's probabilities
+      // beside tile t+1's scores; the check (rarely taken) still sees tile
+      // t's scores in sold
       const f32x16 sold[kBN / 32] = {s[0], s[1]};
       const float part = probs_part(sold, pb);
       qk(IC<P ^ 1>{}, s);
@@ -708,7 +710,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t + 2 < ntiles) load_k(t + 2, par);
     if (t + 1 < ntiles) load_v(t + 1, par ^ 1);
     if (active) {
-      if constexpr (F8 == 0) probs_checked(s, pb, probs_part(s, pb));
+      if constexpr (F8 <= 1) probs_checked(s, pb, probs_part(s, pb));
       else probs(s, pb);
       if (t + 1 < ntiles) {
         qk(par ^ 1, s);

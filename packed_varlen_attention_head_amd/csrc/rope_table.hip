@@ -58,8 +58,16 @@ __global__ void __launch_bounds__(256) rope_table_kernel(RopeArgs a, float* __re
 #pragma clang fp contract(off)
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= int64_t(ntok) * a.half) return;
-  const int32_t token = first_token + int32_t(idx / a.half);
-  const int32_t j = int32_t(idx % a.half);
+  // 32-bit division where the index fits (every practical table)
+  int32_t tl, j;
+  if (idx <= int64_t(INT32_MAX)) {
+    tl = int32_t(idx) / a.half;
+    j = int32_t(idx) - tl * a.half;
+  } else {
+    tl = int32_t(idx / a.half);
+    j = int32_t(idx % a.half);
+  }
+  const int32_t token = first_token + tl;
   int s = 0;
   while (s + 1 < a.nseg && token >= a.start[s + 1]) ++s;
   const int32_t n = token - a.start[s];
@@ -80,8 +88,10 @@ __global__ void __launch_bounds__(256) rope_table_kernel(RopeArgs a, float* __re
   }
   const double theta = p * a.inv_freq[j];
   const int64_t o = int64_t(token) * a.half + j;
-  cos_sin[o] = float(cos(theta));
-  cos_sin[a.S * a.half + o] = float(sin(theta));
+  double sn, cs;
+  sincos(theta, &sn, &cs);  // one shared range reduction
+  cos_sin[o] = float(cs);
+  cos_sin[a.S * a.half + o] = float(sn);
 }
 
 }  // namespace

@@ -43,6 +43,10 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "varlen attn TFLOP/s and % bf16 MFMA peak at S=20,423, 24 heads, d=128"
 HEADLINE = "h3_s20423_bf16"
 ATTN_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "attn_fwd_bf16.hip")
+NORM_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "qk_norm_rope.hip")
+TABLE_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "rope_table.hip")
+ATTN_KERNEL = "attn_fwd_bf16_kernel<128>"
+NORM_KERNEL = "qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, false>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_h3_s20423_traffic.json")
 
 
@@ -147,8 +151,9 @@ def rocprof_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
     f_scale = copy_bytes / cf[cname]
     w_scale = copy_bytes / cw[max(cw, key=cw.get)]
     fetch, write = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
-    out = {"kernel_source_sha256_16": source_hash(ATTN_SRC), "copy_kernel": cname,
-           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    out = {"kernel_source_sha256_16": source_hash(ATTN_SRC),
+           "source_sha256_16": {os.path.basename(p): source_hash(p) for p in (ATTN_SRC, NORM_SRC, TABLE_SRC)},
+           "copy_kernel": cname, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for k in sorted(set(fetch) | set(write)):
         if not (k.startswith("attn") or k.startswith("qk_norm") or k.startswith("rope")):
             continue
@@ -291,17 +296,17 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def measured_traffic(kernel, src):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current source `src` of that kernel; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != source_hash(ATTN_SRC):
+    if t.get("source_sha256_16", {}).get(os.path.basename(src)) != source_hash(src):
         return None
-    k = t.get("kernels", {}).get("attn_fwd_bf16_kernel<128>")
+    k = t.get("kernels", {}).get(kernel)
     return k.get("hbm_bytes_per_launch") if k else None
 
 
@@ -566,7 +571,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": attn_tflops / peak,
-            "traffic": measured_traffic() if (w.name == HEADLINE and not (fp8 or fused)) else None,
+            "traffic": measured_traffic(ATTN_KERNEL, ATTN_SRC) if (w.name == HEADLINE and not (fp8 or fused)) else None,
             "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8' if fp8pv else ', fp8qk' if fp8 else ''}"
                       f"{', qnorm' if fused else ''}>",
             "algorithmic_flop_per_launch": F,
@@ -578,6 +583,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": norm_bytes / norm_s / 1e9 / PEAK_HBM_GBPS,
+            "traffic": measured_traffic(NORM_KERNEL, NORM_SRC) if (w.name == HEADLINE and not (fp8 or fused)) else None,
+            "kernel": "qk_norm_rope_kernel<bf16, 128>",
             "algorithmic_bytes_per_launch": norm_bytes,
             # a plain device-to-device copy moving the same bytes (half read,
             # half written), timed the same way: what HBM gives a pure stream

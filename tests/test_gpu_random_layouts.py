@@ -1,0 +1,82 @@
+"""GPU parity on seeded random packings: many segments per launch whose lengths
+mix empty, single-token, tile-boundary (63/64/65, 127/128/129) and arbitrary
+ragged values, with random head layout (grouped K/V or not), head dim,
+causality and dtype per case.  Every output row is compared with the fp64
+oracle, so each case covers the planner's item list for that packing, partial
+query and key tiles at every segment end, and segment isolation together."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import rng
+from tests.gpu_util import compare, log, require_gpu, to_device, to_f64
+
+BOUNDARY = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+HEADS = [(1, 1), (3, 3), (2, 1), (4, 2), (6, 2)]
+N_CASES = 16
+
+
+@pytest.fixture(scope="module")
+def _gpu():
+    require_gpu()
+    yield
+    import packed_varlen_attention_head_amd as h3a
+
+    h3a.release_caches()
+
+
+def layout(case: int):
+    """Case parameters from the SplitMix64 stream (tag TAG_LENS): 1..40 segments,
+    each either a boundary length or uniform in [0, 700), at most ~6,000 tokens."""
+    u = rng.uniform(1000 + case, rng.TAG_LENS, 128)
+    nseg = 1 + int(u[0] * 40)
+    lens = []
+    for i in range(nseg):
+        a, b = u[8 + 2 * i], u[9 + 2 * i]
+        lens.append(BOUNDARY[int(b * len(BOUNDARY))] if a < 0.5 else int(b * 700))
+    Hq, Hkv = HEADS[int(u[1] * len(HEADS))]
+    D = 64 if u[2] < 0.5 else 128
+    causal = bool(u[3] < 0.4)
+    dtype = "f32" if u[4] < 0.25 else "bf16"
+    return lens, Hq, Hkv, D, causal, dtype
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_packing(case, _gpu):
+    import packed_varlen_attention_head_amd as h3a
+
+    lens, Hq, Hkv, D, causal, dtype = layout(case)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S = int(cu[-1])
+    seed = 2000 + case
+    log(f"[random packing] case={case} nseg={len(lens)} S={S} Hq={Hq} Hkv={Hkv} D={D} "
+        f"causal={causal} dtype={dtype}")
+    if S == 0:
+        pytest.skip("empty packing (covered by the ABI tests)")
+    q = rng.normal_tensor(seed, rng.TAG_Q, (S, Hq, D), dtype)
+    k = rng.normal_tensor(seed, rng.TAG_K, (S, Hkv, D), dtype)
+    v = rng.normal_tensor(seed, rng.TAG_V, (S, Hkv, D), dtype)
+    scale = 1.0 / np.sqrt(D)
+    o = to_f64(h3a.varlen_attn_fwd_ex(*(to_device(x, dtype) for x in (q, k, v)), cu, scale, causal=causal))
+    ref = oracle.varlen_attention_gqa(*(rng.as_f64(x, dtype) for x in (q, k, v)), cu, scale, causal=causal)
+    assert np.all(np.isfinite(o))
+    compare(o, ref, dtype, "o")
+
+
+def test_layouts_cover_the_edges():
+    """The seeded cases together hit the shapes they are meant to (checked on the
+    host, so a change of the generator cannot silently thin the coverage)."""
+    cases = [layout(c) for c in range(N_CASES)]
+    lens = [L for c in cases for L in c[0]]
+    assert 0 in lens and 1 in lens
+    assert any(L in (63, 65, 127, 129, 255, 257) for L in lens)
+    assert any(L > 256 and L % 64 for L in lens)
+    assert {c[3] for c in cases} == {64, 128}
+    assert {c[4] for c in cases} == {False, True}
+    assert {c[5] for c in cases} == {"bf16", "f32"}
+    assert any(c[1] != c[2] for c in cases)
+    assert max(len(c[0]) for c in cases) >= 20
+    assert max(sum(c[0]) for c in cases) <= 30000

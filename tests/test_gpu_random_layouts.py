@@ -80,3 +80,35 @@ def test_layouts_cover_the_edges():
     assert any(c[1] != c[2] for c in cases)
     assert max(len(c[0]) for c in cases) >= 20
     assert max(sum(c[0]) for c in cases) <= 30000
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_packing_fp8(case, _gpu):
+    """The same packings through both low-precision kernels (bf16 inputs quantised to
+    E4M3 on the GPU): FP8 scores against attention on E4M3 q, k at the bf16
+    tolerance; both products in FP8, with V in the per-segment transposed layout,
+    within the E4M3 weight-rounding bound of attention on E4M3 q, k, v."""
+    import packed_varlen_attention_head_amd as h3a
+    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, weight_rounding_bound
+
+    lens, Hq, Hkv, D, causal, _ = layout(case)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S = int(cu[-1])
+    seed = 3000 + case
+    log(f"[random packing fp8] case={case} nseg={len(lens)} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    q = rng.normal_tensor(seed, rng.TAG_Q, (S, Hq, D), "bf16")
+    k = rng.normal_tensor(seed, rng.TAG_K, (S, Hkv, D), "bf16")
+    v = rng.normal_tensor(seed, rng.TAG_V, (S, Hkv, D), "bf16")
+    scale = 1.0 / np.sqrt(D)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    q8, k8 = h3a.quantize_e4m3(qd), h3a.quantize_e4m3(kd)
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
+    o = to_f64(h3a.varlen_attn_fwd_fp8qk(q8, k8, vd, cu, scale, causal=causal))
+    assert np.all(np.isfinite(o))
+    compare(o, oracle.varlen_attention_fp8qk(qf, kf, vf, cu, scale, causal=causal), "bf16", "o, FP8 scores")
+    o = to_f64(h3a.varlen_attn_fwd_fp8(q8, k8, h3a.prepare_vt_e4m3(vd, cu), cu, scale, causal=causal))
+    assert np.all(np.isfinite(o))
+    ref = oracle.varlen_attention_fp8(qf, kf, vf, cu, scale, causal=causal)
+    ref_abs_v = oracle.varlen_attention_fp8(qf, kf, np.abs(vf), cu, scale, causal=causal)
+    check(o, ref, "o, both products FP8", weight_rounding_bound(ref_abs_v), TOL_FP8PV_MEANREL)

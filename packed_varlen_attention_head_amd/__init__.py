@@ -179,7 +179,54 @@ def _token_major(name: str, t):
         raise H3AError(H3A_ESHAPE, f"{name}: heads and dims must be contiguous, strides {t.stride()}")
     if not t.is_cuda:
         raise H3AError(H3A_EINVAL, f"{name} must be a GPU tensor")
+    _on_current_device(name, t)
     return S, H, D, t.stride(0)
+
+
+def _on_current_device(name: str, t):
+    import torch
+
+    if t.device.index != torch.cuda.current_device():
+        raise H3AError(H3A_EINVAL, f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _expect(name: str, t, shape, dtype, contiguous: bool = True):
+    """A GPU tensor on the current device with exactly this shape and dtype: the
+    library reads or writes its whole extent through a raw pointer."""
+    if t is None:
+        raise H3AError(H3A_EINVAL, f"{name} is None")
+    if not t.is_cuda:
+        raise H3AError(H3A_EINVAL, f"{name} must be a GPU tensor")
+    _on_current_device(name, t)
+    if t.dtype != dtype:
+        raise H3AError(H3A_EDTYPE, f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise H3AError(H3A_ESHAPE, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise H3AError(H3A_ESHAPE, f"{name} must be contiguous")
+
+
+def _gain(name: str, g, D: int) -> int:
+    import torch
+
+    _expect(name, g, (D,), torch.float32)
+    return g.data_ptr()
+
+
+def _table(cos_sin, S: int, rot_dim: int):
+    """Pointer of the [2, S, rot_dim/2] fp32 rotary table (None allowed when nothing rotates)."""
+    import torch
+
+    if cos_sin is None:
+        return None
+    if rot_dim > 0 and S > 0:
+        _expect("cos_sin", cos_sin, (2, S, rot_dim // 2), torch.float32)
+    return cos_sin.data_ptr()
+
+
+def _same(name: str, t, shape, dtype):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} must be {tuple(shape)}/{dtype}")
 
 
 # ---------------------------------------------------------------------------
@@ -195,7 +242,7 @@ def build_rope_table(segments, axis_dims, base: float, cos_sin, stream=None) -> 
     dims = _i32_array(axis_dims)
     S = int(segs[:, 3].sum()) if len(segs) else 0
     cu = np.zeros(len(segs) + 1, dtype=np.int32)
-    ptr = cos_sin.data_ptr() if cos_sin is not None else None
+    ptr = _table(cos_sin, S, int(dims.sum()))
     _check(lib().h3a_build_rope_table(_ptr_i32(segs), len(segs), _ptr_i32(dims), float(base), ptr, S,
                                       _ptr_i32(cu), _stream_handle(stream)))
     return cu
@@ -219,7 +266,7 @@ def build_rope_table_ex(segments, mode: int, axis_dims, base: float, cos_sin, st
     S = int(segs[:, 3].sum()) if len(segs) else 0
     cu = np.zeros(len(segs) + 1, dtype=np.int32)
     spec = rope_spec(mode, axis_dims, base, start, stop)
-    ptr = cos_sin.data_ptr() if cos_sin is not None else None
+    ptr = _table(cos_sin, S, int(sum(int(a) for a in axis_dims)))
     _check(lib().h3a_build_rope_table_ex(_ptr_i32(segs), len(segs), ctypes.byref(spec), ptr, S, _ptr_i32(cu),
                                          _stream_handle(stream)))
     return cu
@@ -239,10 +286,10 @@ def qk_rmsnorm_rope(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q
     for name, t, h in (("k", k, Hk), ("q_out", q_out, H), ("k_out", k_out, Hk)):
         if tuple(t.shape) != (S, h, D) or t.dtype != q.dtype:
             raise H3AError(H3A_ESHAPE, f"{name} shape/dtype {tuple(t.shape)}/{t.dtype} does not match q")
-    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    cs = _table(cos_sin, S, int(rot_dim))
     args = (q.data_ptr(), k.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), _dtype_code(q), S)
-    rest = (D, sq, sk, sqo, sko, gamma_q.data_ptr(), gamma_k.data_ptr(), float(eps), cs, int(rot_dim),
-            _stream_handle(stream))
+    rest = (D, sq, sk, sqo, sko, _gain("gamma_q", gamma_q, D), _gain("gamma_k", gamma_k, D), float(eps), cs,
+            int(rot_dim), _stream_handle(stream))
     if Hk == H:
         _check(lib().h3a_qk_rmsnorm_rope(*args, H, *rest))
     else:
@@ -263,6 +310,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens, scale: float, out=None, stream=None):
     if out is None:
         out = torch.empty((S, H, D), dtype=q.dtype, device=q.device)
     _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, H, D), q.dtype)
     cu = _i32_array(cu_seqlens)
     _check(lib().h3a_varlen_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
                                      S, H, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
@@ -277,9 +325,9 @@ def rmsnorm_rope(x, gamma, eps: float, cos_sin, rot_dim: int, x_out=None, stream
     _, _, _, sxo = _token_major("x_out", x_out)
     if tuple(x_out.shape) != (S, H, D) or x_out.dtype != x.dtype:
         raise H3AError(H3A_ESHAPE, f"x_out shape/dtype {tuple(x_out.shape)}/{x_out.dtype} differs from x")
-    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    cs = _table(cos_sin, S, int(rot_dim))
     _check(lib().h3a_rmsnorm_rope(x.data_ptr(), x_out.data_ptr(), _dtype_code(x), S, H, D, sx, sxo,
-                                  gamma.data_ptr(), float(eps), cs, int(rot_dim), _stream_handle(stream)))
+                                  _gain("gamma", gamma, D), float(eps), cs, int(rot_dim), _stream_handle(stream)))
     return x_out
 
 
@@ -298,11 +346,12 @@ def varlen_attn_fwd_qnorm(q, k, v, cu_seqlens, scale: float, gamma_q, eps: float
     if out is None:
         out = torch.empty((S, Hq, D), dtype=q.dtype, device=q.device)
     _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), q.dtype)
     cu = _i32_array(cu_seqlens)
-    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    cs = _table(cos_sin, S, int(rot_dim))
     _check(lib().h3a_varlen_attn_fwd_qnorm(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                            _dtype_code(q), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
-                                           float(scale), gamma_q.data_ptr(), float(eps), cs, int(rot_dim),
+                                           float(scale), _gain("gamma_q", gamma_q, D), float(eps), cs, int(rot_dim),
                                            _stream_handle(stream)))
     return out
 
@@ -334,10 +383,16 @@ def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: i
     k8 = torch.empty((S, Hk, D), dtype=torch.uint8, device=q.device) if k8 is None else k8
     _, _, _, sq8 = _token_major("q8", q8)
     _, _, _, sk8 = _token_major("k8", k8)
-    cs = cos_sin.data_ptr() if cos_sin is not None else None
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"q/k must be bfloat16, got {q.dtype}/{k.dtype}")
+    if tuple(k.shape) != (S, Hk, D):
+        raise H3AError(H3A_ESHAPE, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _same("q8", q8, (S, Hq, D), torch.uint8)
+    _same("k8", k8, (S, Hk, D), torch.uint8)
+    cs = _table(cos_sin, S, int(rot_dim))
     _check(lib().h3a_qk_rmsnorm_rope_e4m3(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k8.data_ptr(), S, Hq, Hk, D,
-                                          sq, sk, sq8, sk8, gamma_q.data_ptr(), gamma_k.data_ptr(), float(eps), cs,
-                                          int(rot_dim), _stream_handle(stream)))
+                                          sq, sk, sq8, sk8, _gain("gamma_q", gamma_q, D), _gain("gamma_k", gamma_k, D),
+                                          float(eps), cs, int(rot_dim), _stream_handle(stream)))
     return q8, k8
 
 
@@ -354,12 +409,14 @@ def prepare_vt_e4m3(v, cu_seqlens, out=None, stream=None):
     import torch
 
     S, Hkv, D, sv = _token_major("v", v)
+    if v.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"v must be bfloat16, got {v.dtype}")
     cu = _i32_array(cu_seqlens)
     cols = vt_e4m3_columns(cu)
     if out is None:
         out = torch.empty((Hkv, D, max(cols, 1)), dtype=torch.uint8, device=v.device)
-    if out.dtype != torch.uint8 or tuple(out.shape[:2]) != (Hkv, D) or out.shape[2] < cols or not out.is_contiguous():
-        raise H3AError(H3A_ESHAPE, f"out must be contiguous uint8 [{Hkv}, {D}, {cols}]")
+    # rows of exactly `cols` columns (one column when every segment is empty)
+    _expect("out", out, (Hkv, D, max(cols, 1)), torch.uint8)
     _check(lib().h3a_prepare_vt_e4m3(v.data_ptr(), out.data_ptr(), S, Hkv, D, sv, cols, _ptr_i32(cu), len(cu) - 1,
                                      _stream_handle(stream)))
     return out
@@ -371,13 +428,18 @@ def varlen_attn_fwd_fp8(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = Fa
 
     S, Hq, D, sq = _token_major("q8", q8)
     _, Hkv, _, sk = _token_major("k8", k8)
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise H3AError(H3A_EDTYPE, f"q8/k8 must hold uint8 E4M3 codes, got {q8.dtype}/{k8.dtype}")
+    if tuple(k8.shape) != (S, Hkv, D):
+        raise H3AError(H3A_ESHAPE, f"k8 shape {tuple(k8.shape)} does not match q8 {tuple(q8.shape)}")
     cu = _i32_array(cu_seqlens)
     cols = vt_e4m3_columns(cu)
-    if vt8.dtype != torch.uint8 or tuple(vt8.shape[:2]) != (Hkv, D) or not vt8.is_contiguous():
-        raise H3AError(H3A_ESHAPE, f"vt8 must be contiguous uint8 [{Hkv}, {D}, {cols}]")
+    # the kernel addresses vt8 with exactly `cols` columns per row
+    _expect("vt8", vt8, (Hkv, D, max(cols, 1)), torch.uint8)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q8.device)
     _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), torch.bfloat16)
     _check(lib().h3a_varlen_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), out.data_ptr(), S, Hq, Hkv,
                                          D, sq, sk, cols, so, _ptr_i32(cu), len(cu) - 1, float(scale),
                                          int(bool(causal)), _stream_handle(stream)))
@@ -398,6 +460,7 @@ def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fa
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=v.device)
     _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), torch.bfloat16)
     cu = _i32_array(cu_seqlens)
     _check(lib().h3a_varlen_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), S, Hq, Hkv, D,
                                            sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale), int(bool(causal)),
@@ -419,6 +482,7 @@ def varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale: float, causal: bool = False, 
     if out is None:
         out = torch.empty((S, Hq, D), dtype=q.dtype, device=q.device)
     _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), q.dtype)
     cu = _i32_array(cu_seqlens)
     _check(lib().h3a_varlen_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
                                         S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),

@@ -99,3 +99,40 @@ def test_long_fp8_both():
     ref = oracle.varlen_attention_rows(q8, k8, v8, cu, 1.0 / np.sqrt(D), rows)
     ref_abs_v = oracle.varlen_attention_rows(q8, k8, np.abs(v8), cu, 1.0 / np.sqrt(D), rows)
     check(o, ref, f"o ({len(rows)} rows)", weight_rounding_bound(ref_abs_v), TOL_FP8PV_MEANREL)
+
+
+def test_long_table_and_norm():
+    """The rotary table (all 2^18 rows, positions up to t = 96, h = 44, w = 996) and
+    the norm + rotary pass (4 query and 2 K/V heads; sampled rows) at this size."""
+    import torch
+
+    import packed_varlen_attention_head_amd as h3a
+
+    segs = [(97, 45, 60, LENS[0]), (1, 1, LENS[1], LENS[1])]
+    dims, base, eps, R, Hq, Hk = (32, 32, 32), 10000.0, 1e-6, 96, 4, 2
+    S = sum(LENS)
+    log(f"[long] table + norm S={S}")
+    tab = torch.empty((2, S, R // 2), dtype=torch.float32, device="cuda")
+    cu = h3a.build_rope_table(segs, dims, base, tab)
+    ocu, cos, sin = oracle.rope_table(segs, dims, base)
+    assert np.array_equal(cu, ocu)
+    g = to_f64(tab)
+    err = max(np.abs(g[0] - cos).max(), np.abs(g[1] - sin).max())
+    log(f"  table: max |gpu - oracle| = {err:.3e}")
+    assert err <= 1.2e-7
+    q = rng.normal_tensor(64, rng.TAG_Q, (S, Hq, D), "bf16")
+    k = rng.normal_tensor(64, rng.TAG_K, (S, Hk, D), "bf16")
+    gq = (1.0 + 0.1 * rng.normal(64, rng.TAG_GAMMA_Q, D)).astype(np.float32)
+    gk = (1.0 + 0.1 * rng.normal(64, rng.TAG_GAMMA_K, D)).astype(np.float32)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    qo, ko = torch.empty_like(qd), torch.empty_like(kd)
+    h3a.qk_rmsnorm_rope(qd, kd, torch.from_numpy(gq).cuda(), torch.from_numpy(gk).cuda(), eps, tab, R,
+                        q_out=qo, k_out=ko)
+    rows = rows_to_check(cu)
+    gqo, gko = to_f64(qo[rows.tolist()]), to_f64(ko[rows.tolist()])
+    rq, rk = oracle.qk_rmsnorm_rope(rng.as_f64(q[rows], "bf16"), rng.as_f64(k[rows], "bf16"), gq, gk, eps,
+                                    cos[rows], sin[rows], R)
+    compare(gqo, rq, "bf16", f"q' ({len(rows)} rows)")
+    compare(gko, rk, "bf16", f"k' ({len(rows)} rows)")
+    for gg, r in ((gqo, rq), (gko, rk)):
+        assert np.all(np.abs(gg - r) <= 2.0 ** -8 * np.abs(r) + 1e-5)

@@ -38,6 +38,13 @@
  *   - Work is enqueued on `stream` (0 = the null stream); no call
  *     synchronises the stream.  Results are bitwise deterministic and
  *     independent of the stream used.
+ *   - Graph capture: once an attention call has run with a given cu_seqlens,
+ *     head count and device (its tile plan is then cached), every call
+ *     only launches kernels on `stream`: no allocation, copy, memset or
+ *     synchronisation, so such calls (and every non-attention call) can be
+ *     captured in a HIP graph and replayed; replays read the buffers'
+ *     current contents.  The first call for a new packing allocates and
+ *     uploads its plan synchronously and cannot be captured.
  *   - Tensors are token-major: element (n, h, d) of a [S, H, D] tensor with
  *     token stride `stride` (in elements) is at base[n * stride + h * D + d].
  *   - Floating point: H3A_BF16 tensors hold bfloat16; arithmetic is fp32 and

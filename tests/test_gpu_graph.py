@@ -1,0 +1,89 @@
+"""The norm + rotary pass and the attention can be captured in a HIP graph once
+the tile plan for the packing is cached: every launch goes to the caller's
+stream, nothing is allocated or copied at call time.  Each replay must give the
+eager bytes, also after the inputs are overwritten between replays (the graph
+reads the buffers' current contents) and with unrelated eager work and
+synchronisation in between."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from synth import configs, rng
+from tests.gpu_util import log, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    import packed_varlen_attention_head_amd as h3a
+
+    h3a.release_caches()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_capture_and_replay(fp8):
+    import torch
+
+    import packed_varlen_attention_head_amd as h3a
+
+    w = configs.BF16["two_seg_bf16"]
+    S, H, D = w.tokens, w.heads, w.head_dim
+    log(f"[graph] {w.name} fp8={fp8}")
+    tab = torch.empty((2, S, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    cu = h3a.build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    gq = torch.from_numpy((1.0 + 0.1 * rng.normal(71, rng.TAG_GAMMA_Q, D)).astype(np.float32)).cuda()
+    gk = torch.from_numpy((1.0 + 0.1 * rng.normal(71, rng.TAG_GAMMA_K, D)).astype(np.float32)).cuda()
+    inputs = [tuple(to_device(rng.normal_tensor(71 + i, tag, (S, H, D), "bf16"), "bf16")
+                    for tag in (rng.TAG_Q, rng.TAG_K, rng.TAG_V)) for i in range(2)]
+    q, k, v = (torch.empty_like(x) for x in inputs[0])
+    qo, ko, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+    k8 = torch.empty_like(q8)
+    vt8 = torch.empty((H, D, h3a.vt_e4m3_columns(cu)), dtype=torch.uint8, device="cuda")
+    scale = w.scale
+
+    def step(stream=None):
+        if fp8:
+            h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8, k8=k8, stream=stream)
+            h3a.prepare_vt_e4m3(v, cu, out=vt8, stream=stream)
+            h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, scale, out=o, stream=stream)
+        else:
+            h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qo, k_out=ko, stream=stream)
+            h3a.varlen_attn_fwd(qo, ko, v, cu, scale, out=o, stream=stream)
+
+    def load(i):
+        for dst, src in zip((q, k, v), inputs[i]):
+            dst.copy_(src)
+
+    eager = []
+    for i in range(2):
+        load(i)
+        step()
+        torch.cuda.synchronize()
+        eager.append(o.clone())
+    assert not torch.equal(eager[0], eager[1])
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream: the plan is cached before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for rep, i in enumerate((0, 1, 1, 0)):
+        load(i)
+        o.fill_(float("nan"))  # eager work between replays; the replay must overwrite it
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(o, eager[i])
+        log(f"  replay {rep} (inputs {i}): equal to eager = {same}")
+        assert same

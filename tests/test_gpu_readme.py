@@ -1,0 +1,44 @@
+"""The usage example in README.md runs as written and its output matches the
+oracle on sampled rows."""
+from __future__ import annotations
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import compare, log, require_gpu, sample_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_readme_example():
+    require_gpu()
+    import torch
+
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = re.findall(r"```python\n(.*?)```", text, re.S)
+    assert len(blocks) == 1
+    torch.manual_seed(0)
+    env = {}
+    # keep a copy of q, k, v before the in-place norm: run the block up to the norm first
+    code = blocks[0]
+    head, tail = code.split("h3a.qk_rmsnorm_rope", 1)
+    exec(head, env)
+    q0, k0, v0 = (env[n].clone() for n in ("q", "k", "v"))
+    exec("h3a.qk_rmsnorm_rope" + tail, env)
+    torch.cuda.synchronize()
+    o, cu, segments = env["o"], env["cu"], env["segments"]
+    log(f"[readme] S={o.shape[0]}")
+    assert o.dtype == torch.bfloat16 and torch.isfinite(o.float()).all()
+    rows = sample_rows(cu, every=211)
+    _, cos, sin = oracle.rope_table(segments, (32, 32, 32), 10000.0)
+    qf, kf, vf = (to_f64(t) for t in (q0, k0, v0))
+    ones = np.ones(qf.shape[2])
+    qn, kn = oracle.qk_rmsnorm_rope(qf, kf, ones, ones, 1e-6, cos, sin, 96)
+    ref = oracle.varlen_attention_rows(qn, kn, vf, cu, 1.0 / np.sqrt(qf.shape[2]), rows)
+    compare(to_f64(o)[rows], ref, "bf16", f"o ({len(rows)} rows)")

@@ -310,6 +310,20 @@ def measured_traffic(kernel, src):
     return k.get("hbm_bytes_per_launch") if k else None
 
 
+def cpu_model():
+    """The host CPU's model name (Linux), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, T, target_s):
     """fp64 oracle on a bounded sample of query rows (all heads, rows spread
     evenly over the packed sequence), scaled to TFLOP/s with the same F (a
@@ -353,6 +367,7 @@ def cpu_baseline(w, T, target_s):
         "value": done_flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle attention on {done_rows} query rows spread evenly over the "
                   f"S={w.tokens} packed sequence, all {w.heads} heads, each against its segment's keys "

@@ -36,7 +36,7 @@ sqrt are the only library primitives used):
    section 5b; the low-precision variant (Q and K rounded to FP8 E4M3 before
    the score product) is section 5c.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
 shared by all heads; RMSNorm before RoPE; V gets neither; empty segments are
 legal and contribute nothing.

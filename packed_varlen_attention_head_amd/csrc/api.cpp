@@ -96,6 +96,7 @@ h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, 
 struct Plan {
   h3a::WorkItem* dev = nullptr;
   int64_t n = 0;
+  int device = 0;  // where dev lives
 };
 
 constexpr size_t kMaxPlans = 256;
@@ -127,7 +128,12 @@ int n_xcd_of(int device) {
   return n;
 }
 
-h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, Plan* out) {
+// On success `*hold` owns the cache lock: the caller launches the kernel that
+// reads the plan before releasing it, so no other thread can evict (free) the
+// plan between this lookup and that launch.  An eviction synchronises the
+// device first, so launches already made have finished with the plan.
+h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, Plan* out,
+                    std::unique_lock<std::mutex>* hold) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail_hip("hipGetDevice", e);
@@ -139,25 +145,35 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
   key.append(reinterpret_cast<const char*>(cu), size_t(nseg + 1) * sizeof(int32_t));
 
   PlanCache& pc = plan_cache();
-  std::lock_guard<std::mutex> lock(pc.mu);
+  std::unique_lock<std::mutex> lock(pc.mu);
   auto it = pc.map.find(key);
   if (it != pc.map.end()) {
     *out = it->second;
+    *hold = std::move(lock);
     return H3A_OK;
   }
   std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd, causal);
   Plan p;
   p.n = int64_t(items.size());
+  p.device = device;
   if (p.n > 0) {
     if (p.n > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "attention plan has %lld items", (long long)p.n);
     if (pc.map.size() >= kMaxPlans) {
-      // Evicting frees device memory an earlier launch may still read.
-      e = hipDeviceSynchronize();
-      if (e != hipSuccess) return fail_hip("hipDeviceSynchronize (plan eviction)", e);
+      // Evicting frees device memory an earlier launch may still read: wait
+      // for the device the victim lives on (not necessarily the current one).
       const std::string& old = pc.order.front();
       auto victim = pc.map.find(old);
       if (victim != pc.map.end()) {
-        (void)hipFree(victim->second.dev);
+        if (victim->second.dev != nullptr) {
+          const int vdev = victim->second.device;
+          if (vdev != device && (e = hipSetDevice(vdev)) != hipSuccess)
+            return fail_hip("hipSetDevice (plan eviction)", e);
+          e = hipDeviceSynchronize();
+          if (e == hipSuccess) e = hipFree(victim->second.dev);
+          const hipError_t back = vdev != device ? hipSetDevice(device) : hipSuccess;
+          if (e != hipSuccess) return fail_hip("hipDeviceSynchronize / hipFree (plan eviction)", e);
+          if (back != hipSuccess) return fail_hip("hipSetDevice (plan eviction)", back);
+        }
         pc.map.erase(victim);
       }
       pc.order.pop_front();
@@ -174,6 +190,7 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
   pc.map.emplace(key, p);
   pc.order.push_back(key);
   *out = p;
+  *hold = std::move(lock);
   return H3A_OK;
 }
 
@@ -429,8 +446,9 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
 
   const bool bf16 = dtype == H3A_BF16;
   Plan plan;
+  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
   if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
-                     &plan)) != H3A_OK)
+                     &plan, &plan_lock)) != H3A_OK)
     return st;
   const int32_t group = Hq / Hkv;
   hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
@@ -478,7 +496,8 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
   if (may_overlap(o, stride_o, Hq, k, stride_k, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
   if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
   Plan plan;
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan)) != H3A_OK) return st;
+  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan, &plan_lock)) != H3A_OK) return st;
   hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
                                                  plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
   if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
@@ -571,7 +590,8 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
   if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
   if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
   Plan plan;
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan)) != H3A_OK) return st;
+  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
   hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
                                             scale, Hq / Hkv, causal != 0, stream);
   if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
@@ -647,7 +667,8 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
   if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
   if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
   Plan plan;
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan)) != H3A_OK) return st;
+  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
   hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
                                           scale, Hq / Hkv, causal != 0, stream);
   if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);

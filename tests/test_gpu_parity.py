@@ -347,3 +347,49 @@ def test_plan_cache_eviction():
     cu, _ = outs[0]
     compare(to_f64(h3a().varlen_attn_fwd(q, k, v, cu, 0.125)), oracle.varlen_attention(qf, kf, vf, cu, 0.125),
             "bf16", "packing 0 again")
+
+
+def test_plan_cache_threads():
+    """Four host threads, each on its own stream, attend over 80 distinct packings
+    each (320 > the 256 cached plans): lookups, launches and evictions interleave
+    across threads.  A plan is looked up and its kernel enqueued under the cache
+    lock, and an eviction waits for the device first, so every output must still
+    match the oracle."""
+    import threading
+
+    import torch
+
+    H, D, S = 2, 64, 300
+    qb = rng.normal_tensor(91, rng.TAG_Q, (S, H, D), "bf16")
+    kb = rng.normal_tensor(91, rng.TAG_K, (S, H, D), "bf16")
+    vb = rng.normal_tensor(91, rng.TAG_V, (S, H, D), "bf16")
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    h3a().release_caches()
+    log("[plan cache] 4 threads x 80 packings")
+    results, errors = {}, []
+
+    def worker(w):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for i in range(80):
+                    cut = 1 + (w * 80 + i) % (S - 1)
+                    cu = np.array([0, cut, S], dtype=np.int64)
+                    results[(w, i)] = (cu, h3a().varlen_attn_fwd(q, k, v, cu, 0.125, stream=stream))
+            stream.synchronize()
+        except Exception as e:  # reported after join
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert len(results) == 320
+    for key in ((0, 0), (1, 40), (2, 79), (3, 79), (3, 0)):
+        cu, o = results[key]
+        compare(to_f64(o), oracle.varlen_attention(qf, kf, vf, cu, 0.125), "bf16", f"thread {key[0]} packing {key[1]}")
+    h3a().release_caches()

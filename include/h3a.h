@@ -34,7 +34,11 @@
  *   - Every argument is validated before anything is launched.  On error the
  *     call returns a non-zero status, records a message naming the offending
  *     argument (h3a_last_error), and writes nothing.  No C++ exception crosses
- *     the boundary.
+ *     the boundary: a failed host allocation inside the library returns
+ *     EUNSUPPORTED.  Attention calls (and h3a_plan_tiles) refuse, with
+ *     EUNSUPPORTED and before building anything, a packing whose tile plan
+ *     would exceed 2^26 work items (far beyond any packing whose tensors fit
+ *     in one GPU's memory).
  *   - Work is enqueued on `stream` (0 = the null stream); no call
  *     synchronises the stream.  Results are bitwise deterministic and
  *     independent of the stream used.

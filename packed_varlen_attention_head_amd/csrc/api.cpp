@@ -13,6 +13,8 @@
 #include <cstring>
 #include <list>
 #include <mutex>
+#include <new>
+#include <stdexcept>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -30,8 +32,25 @@ h3a_status fail(h3a_status st, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
+  try {
+    g_last_error = buf;
+  } catch (...) {  // keep the status even if the message cannot be stored
+  }
   return st;
+}
+
+// Turns the exception being handled into a status: nothing thrown inside the
+// library (host allocations of plans, keys and tables) crosses the C ABI.
+h3a_status fail_exception(const char* fn) noexcept {
+  try {
+    throw;
+  } catch (const std::bad_alloc&) {
+    return fail(H3A_EUNSUPPORTED, "%s: host memory allocation failed", fn);
+  } catch (const std::exception& e) {
+    return fail(H3A_EUNSUPPORTED, "%s: %s", fn, e.what());
+  } catch (...) {
+    return fail(H3A_EUNSUPPORTED, "%s: unexpected C++ exception", fn);
+  }
 }
 
 h3a_status fail_hip(const char* what, hipError_t e) {
@@ -101,6 +120,19 @@ struct Plan {
 
 constexpr size_t kMaxPlans = 256;
 
+// Largest plan built: 2^26 items (2 GiB of host vector).  Any packing whose
+// q, k, v fit in one GPU's memory needs far fewer (S * H / 128 items; under
+// 2^23 for 288 GB), so larger requests are malformed and are rejected before
+// anything is allocated.
+constexpr int64_t kMaxPlanItems = int64_t(1) << 26;
+
+// Whether the plan for cu_seqlens fits kMaxPlanItems (counted without building it).
+bool plan_fits(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m) {
+  int64_t tiles = 0;  // at most S + nseg < 2^33
+  for (int32_t s = 0; s < nseg; ++s) tiles += (int64_t(cu[s + 1]) - cu[s] + block_m - 1) / block_m;
+  return tiles <= kMaxPlanItems / H;
+}
+
 struct PlanCache {
   std::mutex mu;
   std::unordered_map<std::string, Plan> map;
@@ -152,6 +184,8 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
     *hold = std::move(lock);
     return H3A_OK;
   }
+  if (!plan_fits(cu, nseg, H, block_m))
+    return fail(H3A_EUNSUPPORTED, "attention plan would exceed %lld work items", (long long)kMaxPlanItems);
   std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd, causal);
   Plan p;
   p.n = int64_t(items.size());
@@ -215,109 +249,120 @@ const char* h3a_last_error(void) { return g_last_error.c_str(); }
 int32_t h3a_version(void) { return 200; }
 
 void h3a_release_caches(void) {
-  PlanCache& pc = plan_cache();
-  std::lock_guard<std::mutex> lock(pc.mu);
-  for (auto& kv : pc.map)
-    if (kv.second.dev) (void)hipFree(kv.second.dev);
-  pc.map.clear();
-  pc.order.clear();
+  try {
+    PlanCache& pc = plan_cache();
+    std::lock_guard<std::mutex> lock(pc.mu);
+    for (auto& kv : pc.map)
+      if (kv.second.dev) (void)hipFree(kv.second.dev);
+    pc.map.clear();
+    pc.order.clear();
+  } catch (...) {  // nothing may cross the C ABI; the cache is left as it was
+  }
 }
 
 h3a_status h3a_build_rope_table_ex(const int32_t* segments, int32_t nseg, const h3a_rope_spec* spec,
                                    float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
                                    hipStream_t stream) {
-  if (segments == nullptr) return fail(H3A_EINVAL, "segments is NULL");
-  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
-  if (spec == nullptr) return fail(H3A_EINVAL, "spec is NULL");
-  const int32_t mode = spec->mode;
-  if (mode < H3A_ROPE_GRID || mode > H3A_ROPE_INTERLEAVED) return fail(H3A_EINVAL, "unknown rotary table mode %d", mode);
-  const int32_t* axis_dims = spec->axis_dims;
-  int64_t R = 0;
-  for (int a = 0; a < 3; ++a) {
-    if (axis_dims[a] < 0 || axis_dims[a] % 2 != 0)
-      return fail(H3A_EINVAL, "axis_dims[%d] = %d must be even and >= 0", a, axis_dims[a]);
-    R += axis_dims[a];
-  }
-  if (R > 128) return fail(H3A_EUNSUPPORTED, "rotated dims %lld > 128", (long long)R);
-  const double base = spec->base;
-  if (!(base > 0.0) || !std::isfinite(base)) return fail(H3A_EINVAL, "base = %g must be finite and > 0", base);
-  if (mode == H3A_ROPE_LINSPACE)
-    for (int a = 0; a < 3; ++a)
-      if (!std::isfinite(spec->start[a]) || !std::isfinite(spec->stop[a]))
-        return fail(H3A_EINVAL, "linspace start/stop of axis %d must be finite", a);
-  int64_t total = 0;
-  for (int32_t s = 0; s < nseg; ++s) {
-    const int32_t* g = segments + 4 * int64_t(s);
-    if (g[0] < 1 || g[1] < 1 || g[2] < 1)
-      return fail(H3A_EINVAL, "segment %d grid (%d, %d, %d) must be >= 1 on every axis", s, g[0], g[1], g[2]);
-    const int64_t cap = int64_t(g[0]) * g[1] * g[2];
-    if (cap > int64_t(INT32_MAX))
-      return fail(H3A_EINVAL, "segment %d grid %d x %d x %d exceeds INT32_MAX tokens", s, g[0], g[1], g[2]);
-    if (g[3] < 0) return fail(H3A_EINVAL, "segment %d length %d is negative", s, g[3]);
-    if (mode != H3A_ROPE_NORMALIZED && int64_t(g[3]) > cap)
-      return fail(H3A_EINVAL, "segment %d length %d outside [0, T*H*W = %lld]", s, g[3], (long long)cap);
-    total += g[3];
-  }
-  if (total != S) return fail(H3A_ESHAPE, "S = %lld but the segment lengths sum to %lld", (long long)S, (long long)total);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (R > 0 && S > 0) {
-    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL");
-    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
-  }
-
-  std::vector<int32_t> starts(size_t(nseg) + 1, 0);
-  for (int32_t s = 0; s < nseg; ++s) starts[s + 1] = starts[s] + segments[4 * int64_t(s) + 3];
-  const int32_t half = int32_t(R / 2);
-  std::vector<double> inv_freq;
-  std::vector<int32_t> axis_of;
-  if (mode == H3A_ROPE_INTERLEAVED) {
-    // One ladder base^(-2j/R); angle j takes h while j % 3 == 1 and the h
-    // share lasts, w likewise for j % 3 == 2, t otherwise.
-    const int32_t n_h = axis_dims[1] / 2, n_w = axis_dims[2] / 2;
-    int32_t count[3] = {0, 0, 0};
-    for (int32_t j = 0; j < half; ++j) {
-      const int32_t a = (j % 3 == 1 && j < 3 * n_h) ? 1 : ((j % 3 == 2 && j < 3 * n_w) ? 2 : 0);
-      axis_of.push_back(a);
-      ++count[a];
-      inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(R)));
-    }
-    for (int a = 0; a < 3; ++a)
-      if (count[a] != axis_dims[a] / 2)
-        return fail(H3A_EINVAL, "axis_dims (%d, %d, %d) cannot be interleaved t, h, w", axis_dims[0],
-                    axis_dims[1], axis_dims[2]);
-  } else {
-    for (int a = 0; a < 3; ++a)
-      for (int32_t j = 0; j < axis_dims[a] / 2; ++j) {
-        inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(axis_dims[a])));
-        axis_of.push_back(a);
-      }
-  }
-  if (half > 0 && S > 0) {
-    h3a::RopeTableSpec ts{};
-    ts.mode = mode;
-    ts.half = half;
-    ts.inv_freq = inv_freq.data();
-    ts.axis_of = axis_of.data();
+  try {
+    if (segments == nullptr) return fail(H3A_EINVAL, "segments is NULL");
+    if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+    if (spec == nullptr) return fail(H3A_EINVAL, "spec is NULL");
+    const int32_t mode = spec->mode;
+    if (mode < H3A_ROPE_GRID || mode > H3A_ROPE_INTERLEAVED) return fail(H3A_EINVAL, "unknown rotary table mode %d", mode);
+    const int32_t* axis_dims = spec->axis_dims;
+    int64_t R = 0;
     for (int a = 0; a < 3; ++a) {
-      ts.lin_start[a] = mode == H3A_ROPE_LINSPACE ? spec->start[a] : 0.0;
-      ts.lin_stop[a] = mode == H3A_ROPE_LINSPACE ? spec->stop[a] : 0.0;
+      if (axis_dims[a] < 0 || axis_dims[a] % 2 != 0)
+        return fail(H3A_EINVAL, "axis_dims[%d] = %d must be even and >= 0", a, axis_dims[a]);
+      R += axis_dims[a];
     }
-    hipError_t e = h3a::launch_rope_table(ts, segments, starts.data(), nseg, cos_sin, S, stream);
-    if (e != hipSuccess) return fail_hip("rope table launch", e);
+    if (R > 128) return fail(H3A_EUNSUPPORTED, "rotated dims %lld > 128", (long long)R);
+    const double base = spec->base;
+    if (!(base > 0.0) || !std::isfinite(base)) return fail(H3A_EINVAL, "base = %g must be finite and > 0", base);
+    if (mode == H3A_ROPE_LINSPACE)
+      for (int a = 0; a < 3; ++a)
+        if (!std::isfinite(spec->start[a]) || !std::isfinite(spec->stop[a]))
+          return fail(H3A_EINVAL, "linspace start/stop of axis %d must be finite", a);
+    int64_t total = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+      const int32_t* g = segments + 4 * int64_t(s);
+      if (g[0] < 1 || g[1] < 1 || g[2] < 1)
+        return fail(H3A_EINVAL, "segment %d grid (%d, %d, %d) must be >= 1 on every axis", s, g[0], g[1], g[2]);
+      const int64_t cap = int64_t(g[0]) * g[1] * g[2];
+      if (cap > int64_t(INT32_MAX))
+        return fail(H3A_EINVAL, "segment %d grid %d x %d x %d exceeds INT32_MAX tokens", s, g[0], g[1], g[2]);
+      if (g[3] < 0) return fail(H3A_EINVAL, "segment %d length %d is negative", s, g[3]);
+      if (mode != H3A_ROPE_NORMALIZED && int64_t(g[3]) > cap)
+        return fail(H3A_EINVAL, "segment %d length %d outside [0, T*H*W = %lld]", s, g[3], (long long)cap);
+      total += g[3];
+    }
+    if (total != S) return fail(H3A_ESHAPE, "S = %lld but the segment lengths sum to %lld", (long long)S, (long long)total);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (R > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL");
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+
+    std::vector<int32_t> starts(size_t(nseg) + 1, 0);
+    for (int32_t s = 0; s < nseg; ++s) starts[s + 1] = starts[s] + segments[4 * int64_t(s) + 3];
+    const int32_t half = int32_t(R / 2);
+    std::vector<double> inv_freq;
+    std::vector<int32_t> axis_of;
+    if (mode == H3A_ROPE_INTERLEAVED) {
+      // One ladder base^(-2j/R); angle j takes h while j % 3 == 1 and the h
+      // share lasts, w likewise for j % 3 == 2, t otherwise.
+      const int32_t n_h = axis_dims[1] / 2, n_w = axis_dims[2] / 2;
+      int32_t count[3] = {0, 0, 0};
+      for (int32_t j = 0; j < half; ++j) {
+        const int32_t a = (j % 3 == 1 && j < 3 * n_h) ? 1 : ((j % 3 == 2 && j < 3 * n_w) ? 2 : 0);
+        axis_of.push_back(a);
+        ++count[a];
+        inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(R)));
+      }
+      for (int a = 0; a < 3; ++a)
+        if (count[a] != axis_dims[a] / 2)
+          return fail(H3A_EINVAL, "axis_dims (%d, %d, %d) cannot be interleaved t, h, w", axis_dims[0],
+                      axis_dims[1], axis_dims[2]);
+    } else {
+      for (int a = 0; a < 3; ++a)
+        for (int32_t j = 0; j < axis_dims[a] / 2; ++j) {
+          inv_freq.push_back(std::pow(base, -2.0 * double(j) / double(axis_dims[a])));
+          axis_of.push_back(a);
+        }
+    }
+    if (half > 0 && S > 0) {
+      h3a::RopeTableSpec ts{};
+      ts.mode = mode;
+      ts.half = half;
+      ts.inv_freq = inv_freq.data();
+      ts.axis_of = axis_of.data();
+      for (int a = 0; a < 3; ++a) {
+        ts.lin_start[a] = mode == H3A_ROPE_LINSPACE ? spec->start[a] : 0.0;
+        ts.lin_stop[a] = mode == H3A_ROPE_LINSPACE ? spec->stop[a] : 0.0;
+      }
+      hipError_t e = h3a::launch_rope_table(ts, segments, starts.data(), nseg, cos_sin, S, stream);
+      if (e != hipSuccess) return fail_hip("rope table launch", e);
+    }
+    if (cu_seqlens_out != nullptr) std::memcpy(cu_seqlens_out, starts.data(), starts.size() * sizeof(int32_t));
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_build_rope_table_ex");
   }
-  if (cu_seqlens_out != nullptr) std::memcpy(cu_seqlens_out, starts.data(), starts.size() * sizeof(int32_t));
-  return H3A_OK;
 }
 
 h3a_status h3a_build_rope_table(const int32_t* segments, int32_t nseg, const int32_t* axis_dims,
                                 double base, float* cos_sin, int64_t S, int32_t* cu_seqlens_out,
                                 hipStream_t stream) {
-  if (axis_dims == nullptr) return fail(H3A_EINVAL, "axis_dims is NULL");
-  h3a_rope_spec spec{};
-  spec.mode = H3A_ROPE_GRID;
-  for (int a = 0; a < 3; ++a) spec.axis_dims[a] = axis_dims[a];
-  spec.base = base;
-  return h3a_build_rope_table_ex(segments, nseg, &spec, cos_sin, S, cu_seqlens_out, stream);
+  try {
+    if (axis_dims == nullptr) return fail(H3A_EINVAL, "axis_dims is NULL");
+    h3a_rope_spec spec{};
+    spec.mode = H3A_ROPE_GRID;
+    for (int a = 0; a < 3; ++a) spec.axis_dims[a] = axis_dims[a];
+    spec.base = base;
+    return h3a_build_rope_table_ex(segments, nseg, &spec, cos_sin, S, cu_seqlens_out, stream);
+  } catch (...) {
+    return fail_exception("h3a_build_rope_table");
+  }
 }
 
 h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, void* k_out,
@@ -326,83 +371,91 @@ h3a_status h3a_qk_rmsnorm_rope_ex(const void* q, const void* k, void* q_out, voi
                                   int64_t stride_ko, const float* gamma_q, const float* gamma_k,
                                   float eps, const float* cos_sin, int32_t rot_dim,
                                   hipStream_t stream) {
-  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  const int V = dtype == H3A_BF16 ? 8 : 4;
-  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
-    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
-  if ((rot_dim / 2) % V != 0)
-    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
-  const size_t esz = elem_size(dtype);
-  h3a_status st;
-  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, Hk, D, stride_k, esz)) != H3A_OK) return st;
-  if ((st = check_operand("q_out", q_out, S, Hq, D, stride_qo, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k_out", k_out, S, Hk, D, stride_ko, esz)) != H3A_OK) return st;
-  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
-  if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
-  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
-  if (rot_dim > 0 && S > 0) {
-    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
-    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
-  }
-  if (S == 0) return H3A_OK;
-  const bool q_inplace = q_out == q && stride_qo == stride_q;
-  const bool k_inplace = k_out == k && stride_ko == stride_k;
-  if (!q_inplace && may_overlap(q_out, stride_qo, Hq, q, stride_q, Hq, S, D, esz))
-    return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
-  if (!k_inplace && may_overlap(k_out, stride_ko, Hk, k, stride_k, Hk, S, D, esz))
-    return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
-  if (may_overlap(q_out, stride_qo, Hq, k, stride_k, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k");
-  if (may_overlap(k_out, stride_ko, Hk, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "k_out overlaps q");
-  if (may_overlap(q_out, stride_qo, Hq, k_out, stride_ko, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k_out");
+  try {
+    if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    const int V = dtype == H3A_BF16 ? 8 : 4;
+    if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+      return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+    if ((rot_dim / 2) % V != 0)
+      return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+    const size_t esz = elem_size(dtype);
+    h3a_status st;
+    if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+    if ((st = check_operand("k", k, S, Hk, D, stride_k, esz)) != H3A_OK) return st;
+    if ((st = check_operand("q_out", q_out, S, Hq, D, stride_qo, esz)) != H3A_OK) return st;
+    if ((st = check_operand("k_out", k_out, S, Hk, D, stride_ko, esz)) != H3A_OK) return st;
+    if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+    if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
+    if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+    if (rot_dim > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+    if (S == 0) return H3A_OK;
+    const bool q_inplace = q_out == q && stride_qo == stride_q;
+    const bool k_inplace = k_out == k && stride_ko == stride_k;
+    if (!q_inplace && may_overlap(q_out, stride_qo, Hq, q, stride_q, Hq, S, D, esz))
+      return fail(H3A_EINVAL, "q_out overlaps q without being q itself");
+    if (!k_inplace && may_overlap(k_out, stride_ko, Hk, k, stride_k, Hk, S, D, esz))
+      return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
+    if (may_overlap(q_out, stride_qo, Hq, k, stride_k, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k");
+    if (may_overlap(k_out, stride_ko, Hk, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "k_out overlaps q");
+    if (may_overlap(q_out, stride_qo, Hq, k_out, stride_ko, Hk, S, D, esz)) return fail(H3A_EINVAL, "q_out overlaps k_out");
 
-  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, Hq, Hk, D, stride_q,
-                                             stride_k, stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin,
-                                             rot_dim, stream);
-  if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope launch", e);
-  return H3A_OK;
+    hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, q, k, q_out, k_out, S, Hq, Hk, D, stride_q,
+                                               stride_k, stride_qo, stride_ko, gamma_q, gamma_k, eps, cos_sin,
+                                               rot_dim, stream);
+    if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_qk_rmsnorm_rope_ex");
+  }
 }
 
 h3a_status h3a_rmsnorm_rope(const void* x, void* x_out, h3a_dtype dtype, int64_t S, int32_t H, int32_t D,
                             int64_t stride_x, int64_t stride_xo, const float* gamma, float eps,
                             const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
-  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  const int V = dtype == H3A_BF16 ? 8 : 4;
-  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
-    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
-  if ((rot_dim / 2) % V != 0)
-    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
-  const size_t esz = elem_size(dtype);
-  h3a_status st;
-  if ((st = check_operand("x", x, S, H, D, stride_x, esz)) != H3A_OK) return st;
-  if ((st = check_operand("x_out", x_out, S, H, D, stride_xo, esz)) != H3A_OK) return st;
-  if (gamma == nullptr) return fail(H3A_EINVAL, "gamma is NULL");
-  if (!aligned(gamma, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
-  if (rot_dim > 0 && S > 0) {
-    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
-    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  try {
+    if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    const int V = dtype == H3A_BF16 ? 8 : 4;
+    if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+      return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+    if ((rot_dim / 2) % V != 0)
+      return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of %d for this dtype", rot_dim / 2, V);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+    const size_t esz = elem_size(dtype);
+    h3a_status st;
+    if ((st = check_operand("x", x, S, H, D, stride_x, esz)) != H3A_OK) return st;
+    if ((st = check_operand("x_out", x_out, S, H, D, stride_xo, esz)) != H3A_OK) return st;
+    if (gamma == nullptr) return fail(H3A_EINVAL, "gamma is NULL");
+    if (!aligned(gamma, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+    if (rot_dim > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+    if (S == 0) return H3A_OK;
+    const bool inplace = x_out == x && stride_xo == stride_x;
+    if (!inplace && may_overlap(x_out, stride_xo, H, x, stride_x, H, S, D, esz))
+      return fail(H3A_EINVAL, "x_out overlaps x without being x itself");
+    // The fused kernel with no q heads: only its k pass runs.
+    hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, x, x, x_out, x_out, S, 0, H, D, stride_x,
+                                               stride_x, stride_xo, stride_xo, gamma, gamma, eps, cos_sin, rot_dim,
+                                               stream);
+    if (e != hipSuccess) return fail_hip("rmsnorm_rope launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_rmsnorm_rope");
   }
-  if (S == 0) return H3A_OK;
-  const bool inplace = x_out == x && stride_xo == stride_x;
-  if (!inplace && may_overlap(x_out, stride_xo, H, x, stride_x, H, S, D, esz))
-    return fail(H3A_EINVAL, "x_out overlaps x without being x itself");
-  // The fused kernel with no q heads: only its k pass runs.
-  hipError_t e = h3a::launch_qk_rmsnorm_rope(dtype == H3A_BF16, x, x, x_out, x_out, S, 0, H, D, stride_x,
-                                             stride_x, stride_xo, stride_xo, gamma, gamma, eps, cos_sin, rot_dim,
-                                             stream);
-  if (e != hipSuccess) return fail_hip("rmsnorm_rope launch", e);
-  return H3A_OK;
 }
 
 h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* k_out,
@@ -411,8 +464,12 @@ h3a_status h3a_qk_rmsnorm_rope(const void* q, const void* k, void* q_out, void* 
                                int64_t stride_ko, const float* gamma_q, const float* gamma_k,
                                float eps, const float* cos_sin, int32_t rot_dim,
                                hipStream_t stream) {
-  return h3a_qk_rmsnorm_rope_ex(q, k, q_out, k_out, dtype, S, H, H, D, stride_q, stride_k, stride_qo, stride_ko,
-                                gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+  try {
+    return h3a_qk_rmsnorm_rope_ex(q, k, q_out, k_out, dtype, S, H, H, D, stride_q, stride_k, stride_qo, stride_ko,
+                                  gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+  } catch (...) {
+    return fail_exception("h3a_qk_rmsnorm_rope");
+  }
 }
 
 h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
@@ -420,43 +477,47 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
                                   int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                   int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
                                   float scale, int32_t causal, hipStream_t stream) {
-  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
-  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  const size_t esz = elem_size(dtype);
-  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
-  if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
-  if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
-  if (S == 0) return H3A_OK;
-  auto overlaps = [&](const void* x, int64_t sx, int32_t h) {
-    return may_overlap(o, stride_o, Hq, x, sx, h, S, D, esz);
-  };
-  if (overlaps(q, stride_q, Hq)) return fail(H3A_EINVAL, "o overlaps q");
-  if (overlaps(k, stride_k, Hkv)) return fail(H3A_EINVAL, "o overlaps k");
-  if (overlaps(v, stride_v, Hkv)) return fail(H3A_EINVAL, "o overlaps v");
+  try {
+    if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    const size_t esz = elem_size(dtype);
+    if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+    if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
+    if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    auto overlaps = [&](const void* x, int64_t sx, int32_t h) {
+      return may_overlap(o, stride_o, Hq, x, sx, h, S, D, esz);
+    };
+    if (overlaps(q, stride_q, Hq)) return fail(H3A_EINVAL, "o overlaps q");
+    if (overlaps(k, stride_k, Hkv)) return fail(H3A_EINVAL, "o overlaps k");
+    if (overlaps(v, stride_v, Hkv)) return fail(H3A_EINVAL, "o overlaps v");
 
-  const bool bf16 = dtype == H3A_BF16;
-  Plan plan;
-  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-  if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
-                     &plan, &plan_lock)) != H3A_OK)
-    return st;
-  const int32_t group = Hq / Hkv;
-  hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                  plan.n, scale, group, causal != 0, stream)
-                      : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                 plan.n, scale, group, causal != 0, stream);
-  if (e != hipSuccess) return fail_hip("varlen attention launch", e);
-  return H3A_OK;
+    const bool bf16 = dtype == H3A_BF16;
+    Plan plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
+                       &plan, &plan_lock)) != H3A_OK)
+      return st;
+    const int32_t group = Hq / Hkv;
+    hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                    plan.n, scale, group, causal != 0, stream)
+                        : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                   plan.n, scale, group, causal != 0, stream);
+    if (e != hipSuccess) return fail_hip("varlen attention launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_ex");
+  }
 }
 
 h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v, void* o, h3a_dtype dtype,
@@ -464,215 +525,243 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
                                      int64_t stride_k, int64_t stride_v, int64_t stride_o,
                                      const int32_t* cu_seqlens, int32_t nseg, float scale, const float* gamma_q,
                                      float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
-  if (dtype != H3A_BF16)
-    return dtype == H3A_F32 ? fail(H3A_EUNSUPPORTED, "dtype: the fused Q norm path is bf16 only")
-                            : fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
-    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
-  if (rot_dim % 32 != 0) return fail(H3A_EUNSUPPORTED, "rot_dim = %d must be a multiple of 32 on the fused path", rot_dim);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
-  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
-  if (!aligned(gamma_q, 16)) return fail(H3A_EUNSUPPORTED, "gamma_q is not 16-byte aligned");
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  const size_t esz = elem_size(dtype);
-  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
-  if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
-  if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
-  if (rot_dim > 0 && S > 0) {
-    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
-    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  try {
+    if (dtype != H3A_BF16)
+      return dtype == H3A_F32 ? fail(H3A_EUNSUPPORTED, "dtype: the fused Q norm path is bf16 only")
+                              : fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+      return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+    if (rot_dim % 32 != 0) return fail(H3A_EUNSUPPORTED, "rot_dim = %d must be a multiple of 32 on the fused path", rot_dim);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+    if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+    if (!aligned(gamma_q, 16)) return fail(H3A_EUNSUPPORTED, "gamma_q is not 16-byte aligned");
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    const size_t esz = elem_size(dtype);
+    if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+    if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
+    if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
+    if (rot_dim > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+    if (S == 0) return H3A_OK;
+    if (may_overlap(o, stride_o, Hq, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
+    if (may_overlap(o, stride_o, Hq, k, stride_k, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
+    if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
+    Plan plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan, &plan_lock)) != H3A_OK) return st;
+    hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
+                                                   plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
+    if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_qnorm");
   }
-  if (S == 0) return H3A_OK;
-  if (may_overlap(o, stride_o, Hq, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
-  if (may_overlap(o, stride_o, Hq, k, stride_k, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
-  if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
-  Plan plan;
-  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan, &plan_lock)) != H3A_OK) return st;
-  hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                 plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
-  if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
-  return H3A_OK;
 }
 
 h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32_t D, int64_t stride_x,
                              int64_t stride_y, hipStream_t stream) {
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  h3a_status st;
-  if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
-  if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
-  if (S == 0) return H3A_OK;
-  // y (bytes) against x (bf16): plain byte ranges.
-  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
-  const uintptr_t x1 = x0 + uintptr_t(((S - 1) * stride_x + int64_t(H) * D) * 2);
-  const uintptr_t y1 = y0 + uintptr_t((S - 1) * stride_y + int64_t(H) * D);
-  if (x0 < y1 && y0 < x1) return fail(H3A_EINVAL, "y overlaps x");
-  hipError_t e = h3a::launch_quantize_e4m3(x, y, S, H * D, stride_x, stride_y, stream);
-  if (e != hipSuccess) return fail_hip("quantize_e4m3 launch", e);
-  return H3A_OK;
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    h3a_status st;
+    if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
+    if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    // y (bytes) against x (bf16): plain byte ranges.
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t x1 = x0 + uintptr_t(((S - 1) * stride_x + int64_t(H) * D) * 2);
+    const uintptr_t y1 = y0 + uintptr_t((S - 1) * stride_y + int64_t(H) * D);
+    if (x0 < y1 && y0 < x1) return fail(H3A_EINVAL, "y overlaps x");
+    hipError_t e = h3a::launch_quantize_e4m3(x, y, S, H * D, stride_x, stride_y, stream);
+    if (e != hipSuccess) return fail_hip("quantize_e4m3 launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_quantize_e4m3");
+  }
 }
 
 h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t Hq,
                                     int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_q8,
                                     int64_t stride_k8, const float* gamma_q, const float* gamma_k, float eps,
                                     const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
-    return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
-  if ((rot_dim / 2) % 8 != 0)
-    return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of 8 for this dtype", rot_dim / 2);
-  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
-  h3a_status st;
-  if ((st = check_operand("q", q, S, Hq, D, stride_q, 2)) != H3A_OK) return st;
-  if ((st = check_operand("k", k, S, Hk, D, stride_k, 2)) != H3A_OK) return st;
-  if ((st = check_operand("q8", q8, S, Hq, D, stride_q8, 1)) != H3A_OK) return st;
-  if ((st = check_operand("k8", k8, S, Hk, D, stride_k8, 1)) != H3A_OK) return st;
-  if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
-  if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
-  if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
-  if (rot_dim > 0 && S > 0) {
-    if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
-    if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+      return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+    if ((rot_dim / 2) % 8 != 0)
+      return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of 8 for this dtype", rot_dim / 2);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+    h3a_status st;
+    if ((st = check_operand("q", q, S, Hq, D, stride_q, 2)) != H3A_OK) return st;
+    if ((st = check_operand("k", k, S, Hk, D, stride_k, 2)) != H3A_OK) return st;
+    if ((st = check_operand("q8", q8, S, Hq, D, stride_q8, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k8", k8, S, Hk, D, stride_k8, 1)) != H3A_OK) return st;
+    if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+    if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
+    if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+    if (rot_dim > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+    if (S == 0) return H3A_OK;
+    // the byte outputs against every other tensor: plain byte ranges
+    const Range rq = tensor_range(q, S, Hq, D, stride_q, 2), rk = tensor_range(k, S, Hk, D, stride_k, 2);
+    const Range rq8 = tensor_range(q8, S, Hq, D, stride_q8, 1), rk8 = tensor_range(k8, S, Hk, D, stride_k8, 1);
+    auto hit = [](const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; };
+    if (hit(rq8, rq) || hit(rq8, rk)) return fail(H3A_EINVAL, "q8 overlaps q or k");
+    if (hit(rk8, rq) || hit(rk8, rk)) return fail(H3A_EINVAL, "k8 overlaps q or k");
+    if (may_overlap(q8, stride_q8, Hq, k8, stride_k8, Hk, S, D, 1)) return fail(H3A_EINVAL, "q8 overlaps k8");
+    hipError_t e = h3a::launch_qk_rmsnorm_rope_e4m3(q, k, q8, k8, S, Hq, Hk, D, stride_q, stride_k, stride_q8,
+                                                    stride_k8, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+    if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope_e4m3 launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_qk_rmsnorm_rope_e4m3");
   }
-  if (S == 0) return H3A_OK;
-  // the byte outputs against every other tensor: plain byte ranges
-  const Range rq = tensor_range(q, S, Hq, D, stride_q, 2), rk = tensor_range(k, S, Hk, D, stride_k, 2);
-  const Range rq8 = tensor_range(q8, S, Hq, D, stride_q8, 1), rk8 = tensor_range(k8, S, Hk, D, stride_k8, 1);
-  auto hit = [](const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; };
-  if (hit(rq8, rq) || hit(rq8, rk)) return fail(H3A_EINVAL, "q8 overlaps q or k");
-  if (hit(rk8, rq) || hit(rk8, rk)) return fail(H3A_EINVAL, "k8 overlaps q or k");
-  if (may_overlap(q8, stride_q8, Hq, k8, stride_k8, Hk, S, D, 1)) return fail(H3A_EINVAL, "q8 overlaps k8");
-  hipError_t e = h3a::launch_qk_rmsnorm_rope_e4m3(q, k, q8, k8, S, Hq, Hk, D, stride_q, stride_k, stride_q8,
-                                                  stride_k8, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
-  if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope_e4m3 launch", e);
-  return H3A_OK;
 }
 
 h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
                                      int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                      int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
                                      int32_t causal, hipStream_t stream) {
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
-  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
-  if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
-  if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
-  if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
-  if (S == 0) return H3A_OK;
-  // o (bf16) against the byte-coded q and k, and against v (bf16)
-  const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
-  const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
-  if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
-  if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
-  if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
-  Plan plan;
-  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
-  hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
-                                            scale, Hq / Hkv, causal != 0, stream);
-  if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
-  return H3A_OK;
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+    if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    // o (bf16) against the byte-coded q and k, and against v (bf16)
+    const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+    const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+    if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
+    if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
+    if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
+    Plan plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
+    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
+                                              scale, Hq / Hkv, causal != 0, stream);
+    if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_fp8qk");
+  }
 }
 
 h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns) {
-  if (columns == nullptr) return fail(H3A_EINVAL, "columns is NULL");
-  if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
-  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
-  *columns = h3a::vt_e4m3_columns(cu_seqlens, nseg);
-  return H3A_OK;
+  try {
+    if (columns == nullptr) return fail(H3A_EINVAL, "columns is NULL");
+    if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+    if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+    *columns = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_vt_e4m3_columns");
+  }
 }
 
 h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv, int32_t D, int64_t stride_v,
                                int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream) {
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
-  const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
-  if (vt_cols != need)
-    return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
-                (long long)need);
-  if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
-    return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
-  if (need == 0) return H3A_OK;
-  if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
-  if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
-  const Range rv = tensor_range(v, S, Hkv, D, stride_v, 2);
-  const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
-  if (rv.lo < t1 && t0 < rv.hi) return fail(H3A_EINVAL, "vt8 overlaps v");
-  hipError_t e = h3a::launch_prepare_vt_e4m3(v, stride_v, cu_seqlens, nseg, Hkv, D, vt8, vt_cols, stream);
-  if (e != hipSuccess) return fail_hip("prepare_vt_e4m3 launch", e);
-  return H3A_OK;
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
+    const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+    if (vt_cols != need)
+      return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
+                  (long long)need);
+    if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
+      return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+    if (need == 0) return H3A_OK;
+    if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
+    if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+    const Range rv = tensor_range(v, S, Hkv, D, stride_v, 2);
+    const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
+    if (rv.lo < t1 && t0 < rv.hi) return fail(H3A_EINVAL, "vt8 overlaps v");
+    hipError_t e = h3a::launch_prepare_vt_e4m3(v, stride_v, cu_seqlens, nseg, Hkv, D, vt8, vt_cols, stream);
+    if (e != hipSuccess) return fail_hip("prepare_vt_e4m3 launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_prepare_vt_e4m3");
+  }
 }
 
 h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int64_t S, int32_t Hq,
                                    int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
                                    int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
                                    int32_t causal, hipStream_t stream) {
-  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
-  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
-  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-  h3a_status st;
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-  if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
-  if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
-  if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
-  const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
-  if (vt_cols != need)
-    return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
-                (long long)need);
-  if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
-    return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
-  if (S == 0) return H3A_OK;
-  if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
-  if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
-  const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
-  const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
-  const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
-  if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
-  if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
-  if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
-  Plan plan;
-  std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-  if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
-  hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
-                                          scale, Hq / Hkv, causal != 0, stream);
-  if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
-  return H3A_OK;
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+    const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+    if (vt_cols != need)
+      return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
+                  (long long)need);
+    if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
+      return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+    if (S == 0) return H3A_OK;
+    if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
+    if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+    const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+    const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+    const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
+    if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
+    if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
+    if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
+    Plan plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
+    hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
+                                            scale, Hq / Hkv, causal != 0, stream);
+    if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_fp8");
+  }
 }
 
 h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void* o,
@@ -680,37 +769,51 @@ h3a_status h3a_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                int64_t stride_q, int64_t stride_k, int64_t stride_v,
                                int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
                                float scale, hipStream_t stream) {
-  return h3a_varlen_attn_fwd_ex(q, k, v, o, dtype, S, H, H, D, stride_q, stride_k, stride_v, stride_o,
-                                cu_seqlens, nseg, scale, 0, stream);
+  try {
+    return h3a_varlen_attn_fwd_ex(q, k, v, o, dtype, S, H, H, D, stride_q, stride_k, stride_v, stride_o,
+                                  cu_seqlens, nseg, scale, 0, stream);
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd");
+  }
 }
 
 h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
                              int32_t n_xcd, int32_t causal, int32_t* items, int64_t cap, int64_t* n_items) {
-  if (n_items == nullptr) return fail(H3A_EINVAL, "n_items is NULL");
-  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
-  if (block_m < 1) return fail(H3A_EINVAL, "block_m = %d must be >= 1", block_m);
-  if (n_xcd < 1) return fail(H3A_EINVAL, "n_xcd = %d must be >= 1", n_xcd);
-  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
-  h3a_status st;
-  if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
-  if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
-  if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
-  std::vector<h3a::WorkItem> plan = h3a::plan_tiles(cu_seqlens, nseg, H, block_m, n_xcd, causal != 0);
-  *n_items = int64_t(plan.size());
-  if (int64_t(plan.size()) > cap) return fail(H3A_ESHAPE, "cap %lld < plan length %lld", (long long)cap, (long long)plan.size());
-  if (!plan.empty() && items == nullptr) return fail(H3A_EINVAL, "items is NULL");
-  for (size_t i = 0; i < plan.size(); ++i) {
-    items[4 * i + 0] = plan[i].seg_start;
-    items[4 * i + 1] = plan[i].seg_len;
-    items[4 * i + 2] = plan[i].q_start;
-    items[4 * i + 3] = plan[i].head;
+  try {
+    if (n_items == nullptr) return fail(H3A_EINVAL, "n_items is NULL");
+    if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+    if (block_m < 1) return fail(H3A_EINVAL, "block_m = %d must be >= 1", block_m);
+    if (n_xcd < 1) return fail(H3A_EINVAL, "n_xcd = %d must be >= 1", n_xcd);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    h3a_status st;
+    if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+    if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+    if (!plan_fits(cu_seqlens, nseg, H, block_m))
+      return fail(H3A_EUNSUPPORTED, "plan would exceed %lld work items", (long long)kMaxPlanItems);
+    std::vector<h3a::WorkItem> plan = h3a::plan_tiles(cu_seqlens, nseg, H, block_m, n_xcd, causal != 0);
+    *n_items = int64_t(plan.size());
+    if (int64_t(plan.size()) > cap) return fail(H3A_ESHAPE, "cap %lld < plan length %lld", (long long)cap, (long long)plan.size());
+    if (!plan.empty() && items == nullptr) return fail(H3A_EINVAL, "items is NULL");
+    for (size_t i = 0; i < plan.size(); ++i) {
+      items[4 * i + 0] = plan[i].seg_start;
+      items[4 * i + 1] = plan[i].seg_len;
+      items[4 * i + 2] = plan[i].q_start;
+      items[4 * i + 3] = plan[i].head;
+    }
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_plan_tiles_ex");
   }
-  return H3A_OK;
 }
 
 h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
                           int32_t n_xcd, int32_t* items, int64_t cap, int64_t* n_items) {
-  return h3a_plan_tiles_ex(cu_seqlens, nseg, H, block_m, n_xcd, 0, items, cap, n_items);
+  try {
+    return h3a_plan_tiles_ex(cu_seqlens, nseg, H, block_m, n_xcd, 0, items, cap, n_items);
+  } catch (...) {
+    return fail_exception("h3a_plan_tiles");
+  }
 }
 
 }  // extern "C"

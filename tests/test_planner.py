@@ -113,3 +113,14 @@ def test_causal_and_bidirectional_plans_differ_only_in_order():
     a = h3a.plan_tiles(cu, 24, 128, 1)
     b = h3a.plan_tiles(cu, 24, 128, 1, causal=True)
     assert sorted(map(tuple, a.tolist())) == sorted(map(tuple, b.tolist()))
+
+
+def test_oversized_plan_rejected_before_building():
+    """A packing whose plan would exceed 2^26 work items is refused up front with
+    EUNSUPPORTED, before any host memory is spent building it, also just above
+    the bound (8,193 query tiles x 2^13 heads = 2^26 + 2^13 items)."""
+    for cu, heads, block_m in (([0, 1 << 20], 1 << 14, 1), ([0, (1 << 20) + 1], 1 << 13, 128)):
+        with pytest.raises(h3a.H3AError) as e:
+            h3a.plan_tiles(np.array(cu, dtype=np.int64), heads=heads, block_m=block_m, n_xcd=8)
+        assert e.value.status == h3a.H3A_EUNSUPPORTED
+        assert "work items" in str(e.value)

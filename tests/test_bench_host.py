@@ -1,0 +1,71 @@
+"""Host-side pieces of bench.py that turn rocprofv3 results into the reported
+numbers: kernel-name mapping and the HBM-traffic conversion (counter KiB per
+dispatch, scaled by what the same counter reads for a copy of known size).
+Runs on synthetic result databases with the tables rocprofv3 writes."""
+from __future__ import annotations
+
+import contextlib
+import io
+import json
+import sqlite3
+
+import pytest
+
+import bench
+
+ATTN = ("void h3a::(anonymous namespace)::attn_fwd_bf16_kernel<128, false, false, 0, 0>(unsigned short const*, "
+        "unsigned short const*, unsigned short const*, unsigned short*, long, long, long, long, h3a::WorkItem const*, "
+        "float, int, h3a::QNormArgs)")
+NORM = ("void h3a::(anonymous namespace)::qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, false>"
+        "(char const*, char const*, char*, char*, long, long, long, long, int, int, int, float const*, "
+        "float const*, float, float const*, int)")
+TABLE = "h3a::(anonymous namespace)::rope_table_kernel(h3a::(anonymous namespace)::RopeArgs, float*, int, int)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+@pytest.mark.parametrize("name,short", [
+    (ATTN, "attn_fwd_bf16_kernel<128>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, true, false, 0, 0>"), "attn_fwd_bf16_kernel<128, causal>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, false, false, 0, 2>"), "attn_fwd_bf16_kernel<128, fp8>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, false, false, 0, 1>"), "attn_fwd_bf16_kernel<128, fp8qk>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, false, true, 3, 0>"), "attn_fwd_bf16_kernel<128, qnorm r96>"),
+    (NORM, bench.NORM_KERNEL),
+    (TABLE, "rope_table_kernel"),
+    (COPY, COPY),
+])
+def test_short_kernel_names(name, short):
+    assert bench._short_kernel(name) == short
+
+
+def _counter_db(path, rows):
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    return str(path)
+
+
+def test_traffic_conversion(tmp_path):
+    """A 1 GiB copy whose FETCH_SIZE reads 0.5 GiB and WRITE_SIZE 1 GiB sets the
+    scales to 2 and 1; per-kernel bytes are the dispatch average times the scale."""
+    gib_kib = float(1 << 20)
+    fetch = _counter_db(tmp_path / "f.db", [(ATTN, "FETCH_SIZE", 1000.0), (ATTN, "FETCH_SIZE", 3000.0),
+                                            (NORM, "FETCH_SIZE", 500.0), (COPY, "FETCH_SIZE", 7.0)])
+    write = _counter_db(tmp_path / "w.db", [(ATTN, "WRITE_SIZE", 100.0), (NORM, "WRITE_SIZE", 400.0)])
+    cfetch = _counter_db(tmp_path / "cf.db", [(COPY, "FETCH_SIZE", gib_kib / 2)])
+    cwrite = _counter_db(tmp_path / "cw.db", [(COPY, "WRITE_SIZE", gib_kib)])
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        assert bench.rocprof_traffic(fetch, write, cfetch, cwrite) == 0
+    out = json.loads(buf.getvalue())
+    assert out["fetch_scale"] == pytest.approx(2.0) and out["write_scale"] == pytest.approx(1.0)
+    a = out["kernels"][bench.ATTN_KERNEL]
+    assert a["hbm_read_bytes"] == pytest.approx(2000.0 * 1024 * 2)
+    assert a["hbm_write_bytes"] == pytest.approx(100.0 * 1024)
+    assert a["hbm_bytes_per_launch"] == pytest.approx(a["hbm_read_bytes"] + a["hbm_write_bytes"])
+    n = out["kernels"][bench.NORM_KERNEL]
+    assert n["hbm_read_bytes"] == pytest.approx(500.0 * 1024 * 2)
+    assert COPY not in out["kernels"]  # only the library's kernels are reported
+    assert set(out["source_sha256_16"]) == {"attn_fwd_bf16.hip", "qk_norm_rope.hip", "rope_table.hip"}
+

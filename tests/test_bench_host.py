@@ -69,3 +69,32 @@ def test_traffic_conversion(tmp_path):
     assert COPY not in out["kernels"]  # only the library's kernels are reported
     assert set(out["source_sha256_16"]) == {"attn_fwd_bf16.hip", "qk_norm_rope.hip", "rope_table.hip"}
 
+
+
+def test_kernel_trace_summary(tmp_path):
+    """The kernel-trace table: rocprofv3's own per-kernel totals (microseconds) plus
+    the average of the last N dispatches from their start/end stamps (nanoseconds)."""
+    db = tmp_path / "t.db"
+    con = sqlite3.connect(db)
+    con.execute("create table top_kernels (name text, total_calls int, total_duration real, average real, "
+                "percentage real)")
+    con.execute("create table kernels (name text, start int, end int)")
+    con.executemany("insert into top_kernels values (?, ?, ?, ?, ?)",
+                    [(ATTN, 4, 11000.0, 2750.0, 97.0), (NORM, 4, 340.0, 85.0, 3.0)])
+    t, rows = 0, []
+    for dur_us in (3000.0, 2800.0, 2600.0, 2600.0):  # ATTN, then NORM after each
+        rows.append((ATTN, t, t + int(dur_us * 1e3)))
+        t += int(dur_us * 1e3) + 1000
+        rows.append((NORM, t, t + 85000))
+        t += 86000
+    con.executemany("insert into kernels values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        assert bench.rocprof_summary(str(db), 2) == 0
+    lines = buf.getvalue().splitlines()
+    attn = next(line for line in lines if line.startswith(f"| {bench.ATTN_KERNEL} |"))
+    cells = [c.strip() for c in attn.strip("|").split("|")]
+    assert cells == [bench.ATTN_KERNEL, "4", "11000.0", "2750.0", "2600.0", "97.00%"]
+    assert any(line.startswith(f"| {bench.NORM_KERNEL} | 4 |") for line in lines)

@@ -98,3 +98,16 @@ def test_kernel_trace_summary(tmp_path):
     cells = [c.strip() for c in attn.strip("|").split("|")]
     assert cells == [bench.ATTN_KERNEL, "4", "11000.0", "2750.0", "2600.0", "97.00%"]
     assert any(line.startswith(f"| {bench.NORM_KERNEL} | 4 |") for line in lines)
+
+
+def test_more_than_one_gpu_is_refused():
+    """`bench.py --gpus N` with N > 1 stops with a message before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout + r.stderr

@@ -55,7 +55,7 @@ def test_random_packing(case, _gpu):
     log(f"[random packing] case={case} nseg={len(lens)} S={S} Hq={Hq} Hkv={Hkv} D={D} "
         f"causal={causal} dtype={dtype}")
     if S == 0:
-        pytest.skip("empty packing (covered by the ABI tests)")
+        pytest.skip("empty packing (covered by test_gpu_validation.py)")
     q = rng.normal_tensor(seed, rng.TAG_Q, (S, Hq, D), dtype)
     k = rng.normal_tensor(seed, rng.TAG_K, (S, Hkv, D), dtype)
     v = rng.normal_tensor(seed, rng.TAG_V, (S, Hkv, D), dtype)

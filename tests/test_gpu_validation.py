@@ -114,3 +114,28 @@ def test_fp8_operands():
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     assert np.isfinite(o.float().cpu().numpy()).all()
+
+
+def test_all_empty_packing_is_a_no_op():
+    """Every call accepts a packing whose segments are all empty (S = 0, zero-size
+    tensors whose data pointers may be null) and returns empty results."""
+    import torch
+
+    import packed_varlen_attention_head_amd as h3a
+
+    segs = [(1, 1, 1, 0), (2, 3, 4, 0)]  # valid grids, no tokens
+    tab = torch.empty((2, 0, R // 2), dtype=torch.float32, device="cuda")
+    cu = h3a.build_rope_table(segs, (32, 32, 32), 10000.0, tab)
+    assert list(cu) == [0, 0, 0]
+    q, k, v = (torch.empty((0, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    gam = torch.ones(D, dtype=torch.float32, device="cuda")
+    h3a.qk_rmsnorm_rope(q, k, gam, gam, 1e-6, tab, R)
+    assert h3a.varlen_attn_fwd(q, k, v, cu, 0.1).shape == (0, H, D)
+    assert h3a.varlen_attn_fwd_ex(q, k, v, cu, 0.1, causal=True).shape == (0, H, D)
+    assert h3a.varlen_attn_fwd_qnorm(q, k, v, cu, 0.1, gam, 1e-6, tab, R).shape == (0, H, D)
+    q8, k8 = h3a.qk_rmsnorm_rope_e4m3(q, k, gam, gam, 1e-6, tab, R)
+    assert h3a.vt_e4m3_columns(cu) == 0
+    vt8 = h3a.prepare_vt_e4m3(v, cu)
+    assert h3a.varlen_attn_fwd_fp8qk(q8, k8, v, cu, 0.1).shape == (0, H, D)
+    assert h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, 0.1).shape == (0, H, D)
+    torch.cuda.synchronize()

@@ -391,8 +391,9 @@ h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H,
 /* Message of the last failed call on this thread ("" if none). */
 const char* h3a_last_error(void);
 
-/* Frees every cached attention plan.  The caller must make sure no attention
- * launched earlier is still running (synchronise its streams first). */
+/* Frees every cached attention plan, after waiting for each device that holds
+ * one (attention kernels launched earlier may still read it).  If a device
+ * cannot be synchronised, nothing is freed.  Calls on other threads wait. */
 void h3a_release_caches(void);
 
 /* Library version, major * 10000 + minor * 100 + patch (0.2.0). */

@@ -7,6 +7,7 @@
 // rather than mis-slice (vllm.cpp PR #26, commits on the streamed bf16 stager
 // and the condition-noise row accounting); here that becomes a status code
 // plus a message naming the argument.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -252,6 +253,23 @@ void h3a_release_caches(void) {
   try {
     PlanCache& pc = plan_cache();
     std::lock_guard<std::mutex> lock(pc.mu);
+    // Wait for every device that holds a plan (kernels enqueued earlier may
+    // still read it), then free them all.
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return;
+    std::vector<int> devices;
+    for (auto& kv : pc.map)
+      if (kv.second.dev && std::find(devices.begin(), devices.end(), kv.second.device) == devices.end())
+        devices.push_back(kv.second.device);
+    for (int d : devices) {
+      // a device that cannot be reached or is in error: keep the plans rather
+      // than free memory a kernel may still use
+      if ((d != cur && hipSetDevice(d) != hipSuccess) || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipSetDevice(cur);
+        return;
+      }
+    }
+    (void)hipSetDevice(cur);
     for (auto& kv : pc.map)
       if (kv.second.dev) (void)hipFree(kv.second.dev);
     pc.map.clear();

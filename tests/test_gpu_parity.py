@@ -393,3 +393,27 @@ def test_plan_cache_threads():
         cu, o = results[key]
         compare(to_f64(o), oracle.varlen_attention(qf, kf, vf, cu, 0.125), "bf16", f"thread {key[0]} packing {key[1]}")
     h3a().release_caches()
+
+
+def test_release_caches_with_kernels_in_flight():
+    """Releasing the plan cache right after queuing attention calls (no host
+    synchronisation in between) waits for them: every output still matches."""
+    import torch
+
+    H, D, S = 2, 64, 300
+    qb = rng.normal_tensor(92, rng.TAG_Q, (S, H, D), "bf16")
+    kb = rng.normal_tensor(92, rng.TAG_K, (S, H, D), "bf16")
+    vb = rng.normal_tensor(92, rng.TAG_V, (S, H, D), "bf16")
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    log("[plan cache] release with 12 launches queued")
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(12):
+        cu = np.array([0, 7 + 23 * i, S], dtype=np.int64)
+        outs.append((cu, h3a().varlen_attn_fwd(q, k, v, cu, 0.125)))
+    h3a().release_caches()
+    torch.cuda.synchronize()
+    for i in (0, 5, 11):
+        cu, o = outs[i]
+        compare(to_f64(o), oracle.varlen_attention(qf, kf, vf, cu, 0.125), "bf16", f"packing {i}")

@@ -237,9 +237,13 @@ NOMINAL_SCLK_MHZ = 2400.0  # the clock the published MFMA peaks assume
 
 class SclkSampler:
     """Samples the GPU's current shader clock (the starred level of the
-    driver's pp_dpm_sclk file) from a host thread while timed work runs; stop()
-    returns the median in MHz, or None when the file is absent or ambiguous
-    (several GPUs and no PCI address to match)."""
+    driver's pp_dpm_sclk file) and board power (hwmon power1_input of the same
+    device) from a host thread while timed work runs; stop() returns the
+    median clock in MHz, or None when the file is absent or ambiguous (several
+    GPUs and no PCI address to match), and leaves the median power in
+    `power_w` (None without a power sensor).  The clock file shows the DPM
+    level the driver requested; under load the hardware's own current and
+    power limiters can run the shader clock below it."""
 
     def __init__(self, period_s=0.005):
         self.period = period_s
@@ -258,6 +262,12 @@ class SclkSampler:
                 self.path = match[0] if len(match) == 1 else None
             except Exception:  # noqa: BLE001 - clock reporting is best effort
                 self.path = None
+        self.power_path = None
+        self.power_samples = []
+        self.power_w = None
+        if self.path:
+            pw = sorted(glob.glob(os.path.join(os.path.dirname(self.path), "hwmon", "hwmon*", "power1_input")))
+            self.power_path = pw[0] if pw else None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -275,6 +285,9 @@ class SclkSampler:
                 v = self._read()
                 if v:
                     self.samples.append(v)
+                if self.power_path:
+                    with open(self.power_path) as f:
+                        self.power_samples.append(int(f.read()) / 1e6)  # microwatts
             except (OSError, ValueError, IndexError):
                 return
             self._stop.wait(self.period)
@@ -288,6 +301,7 @@ class SclkSampler:
             return None
         self._stop.set()
         self._thread.join()
+        self.power_w = float(np.median(self.power_samples)) if self.power_samples else None
         return float(np.median(self.samples)) if self.samples else None
 
 
@@ -331,12 +345,18 @@ def cpu_baseline(w, T, target_s):
     import oracle
     from synth import rng
 
+    # The oracle's products run in numpy's BLAS: give it every core this
+    # process may run on, and report that count beside the machine's.
+    allowed = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else list(range(os.cpu_count() or 1))
+    limiter = None
+    np.ones((2, 2)) @ np.ones((2, 2))  # load the BLAS so threadpoolctl sees it
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+        limiter = threadpool_limits(limits=len(allowed), user_api="blas")
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = os.cpu_count() or 1
+        cores = len(allowed)
     cu = oracle.cu_seqlens(w.segments)
     qf = rng.as_f64(T.q, w.dtype)
     kf = rng.as_f64(T.k, w.dtype)
@@ -363,10 +383,14 @@ def cpu_baseline(w, T, target_s):
         if dt >= target_s * 0.5 or n >= w.tokens:
             break
         n = min(w.tokens, int(n * max(2.0, min(16.0, target_s / max(dt, 1e-3)))))
+    if limiter is not None:
+        limiter.unregister()
     return {
         "value": done_flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_count": os.cpu_count(),
+        "affinity_cores": len(allowed),
         "cpu": cpu_model(),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle attention on {done_rows} query rows spread evenly over the "
@@ -574,6 +598,8 @@ def main():
         # GPU clock sampled during the timed steps and attention launches, and
         # the attention rate against the peak scaled to that clock
         "sclk_mhz": sclk,
+        # board power over the same samples (hwmon power1_input; MI355X's board limit is 1,400 W)
+        "power_w": clock.power_w,
         "pct_peak_at_sclk": (100.0 * attn_tflops / (peak * sclk / NOMINAL_SCLK_MHZ)) if sclk else None,
         "norm_rope_ms": norm_s * 1e3,
         "norm_rope_GBps": norm_bytes / norm_s / 1e9,

@@ -48,7 +48,14 @@
  *     synchronisation, so such calls (and every non-attention call) can be
  *     captured in a HIP graph and replayed; replays read the buffers'
  *     current contents.  The first call for a new packing allocates and
- *     uploads its plan synchronously and cannot be captured.
+ *     uploads its plan synchronously (and, with 256 plans cached, frees the
+ *     oldest after synchronising its device): made on a capturing stream it
+ *     fails with EUNSUPPORTED and enqueues nothing, and it must not run
+ *     while another stream captures in hipStreamCaptureModeGlobal.
+ *   - Plan lifetime: a plan used by a call on a capturing stream is pinned --
+ *     the graph keeps its device address -- and is never evicted; only
+ *     h3a_release_caches frees it, so destroy graphs holding attention
+ *     launches before calling h3a_release_caches.
  *   - Tensors are token-major: element (n, h, d) of a [S, H, D] tensor with
  *     token stride `stride` (in elements) is at base[n * stride + h * D + d].
  *   - Floating point: H3A_BF16 tensors hold bfloat16; arithmetic is fp32 and
@@ -272,7 +279,9 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
  * Low-precision attention, step 1: bf16 [S, H, D] (token stride stride_x
  * elements) to OCP FP8 E4M3 codes ("fn" variant: no infinities, largest
  * finite 448), one byte per element in y [S, H, D] (token stride stride_y
- * bytes, a multiple of 16).  Round to nearest even, saturating at +-448.
+ * bytes, a multiple of 16).  Round to nearest even, saturating at +-448
+ * (infinities included); a NaN becomes an E4M3 NaN code (0x7f, 0xff), so NaN
+ * inputs stay NaN through the FP8 attention as through the bf16 one.
  * This quantises q' and k' for h3a_varlen_attn_fwd_fp8qk (the pages' GB10
  * builds run Q and K through low-precision attention kernels --
  * SageAttention 2++, Comfy Kitchen's INT8 attention -- after the Q RMSNorm +
@@ -328,7 +337,7 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
  * h3a_vt_e4m3_columns: vt_cols for cu_seqlens (host only).
  * h3a_prepare_vt_e4m3: bf16 v [S, Hkv, D] (token stride stride_v elements)
  *   -> vt8 (device, Hkv * D * vt_cols bytes, 16-byte aligned); nearest even,
- *   saturating at +-448.
+ *   saturating at +-448, NaN to an E4M3 NaN code.
  * h3a_varlen_attn_fwd_fp8: as h3a_varlen_attn_fwd_fp8qk, with V given as
  *   vt8; the probabilities are rounded to E4M3 for the PV product (which
  *   runs on FP8 MFMA with fp32 accumulation) and the row sum adds them in
@@ -391,9 +400,11 @@ h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H,
 /* Message of the last failed call on this thread ("" if none). */
 const char* h3a_last_error(void);
 
-/* Frees every cached attention plan, after waiting for each device that holds
- * one (attention kernels launched earlier may still read it).  If a device
- * cannot be synchronised, nothing is freed.  Calls on other threads wait. */
+/* Frees every cached attention plan, pinned ones included, after waiting for
+ * each device that holds one (attention kernels launched earlier may still
+ * read it).  If a device cannot be synchronised, nothing is freed.  Calls on
+ * other threads wait.  A graph that captured an attention call must not be
+ * replayed after this (its plan is gone); capture it again. */
 void h3a_release_caches(void);
 
 /* Library version, major * 10000 + minor * 100 + patch (0.2.0). */

@@ -116,7 +116,8 @@ h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, 
 struct Plan {
   h3a::WorkItem* dev = nullptr;
   int64_t n = 0;
-  int device = 0;  // where dev lives
+  int device = 0;       // where dev lives
+  bool pinned = false;  // used under stream capture: a graph may hold dev, never evict it
 };
 
 constexpr size_t kMaxPlans = 256;
@@ -165,11 +166,19 @@ int n_xcd_of(int device) {
 // reads the plan before releasing it, so no other thread can evict (free) the
 // plan between this lookup and that launch.  An eviction synchronises the
 // device first, so launches already made have finished with the plan.
-h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, Plan* out,
-                    std::unique_lock<std::mutex>* hold) {
+// A call on a capturing stream only looks the plan up: building one allocates,
+// copies synchronously and may synchronise the device for an eviction, none of
+// which a capture allows.  The plan it uses is pinned, since the captured
+// graph keeps its device pointer for every later replay: pinned plans are
+// never evicted, only h3a_release_caches frees them.
+h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, hipStream_t stream,
+                    Plan* out, std::unique_lock<std::mutex>* hold) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail_hip("hipGetDevice", e);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(stream, &capture)) != hipSuccess) return fail_hip("hipStreamIsCapturing", e);
+  const bool capturing = capture != hipStreamCaptureStatusNone;
   const int n_xcd = n_xcd_of(device);
   std::string key;
   key.reserve(20 + size_t(nseg + 1) * 4);
@@ -181,10 +190,15 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
   std::unique_lock<std::mutex> lock(pc.mu);
   auto it = pc.map.find(key);
   if (it != pc.map.end()) {
+    if (capturing) it->second.pinned = true;
     *out = it->second;
     *hold = std::move(lock);
     return H3A_OK;
   }
+  if (capturing)
+    return fail(H3A_EUNSUPPORTED,
+                "stream is capturing and the tile plan for this cu_seqlens / head count / device is not cached: "
+                "make one attention call with it outside capture first");
   if (!plan_fits(cu, nseg, H, block_m))
     return fail(H3A_EUNSUPPORTED, "attention plan would exceed %lld work items", (long long)kMaxPlanItems);
   std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd, causal);
@@ -193,11 +207,14 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
   p.device = device;
   if (p.n > 0) {
     if (p.n > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "attention plan has %lld items", (long long)p.n);
-    if (pc.map.size() >= kMaxPlans) {
+    // Evict the oldest plan no captured graph uses (if every cached plan is
+    // pinned, the cache grows instead).
+    auto old = pc.order.begin();
+    while (old != pc.order.end() && pc.map.at(*old).pinned) ++old;
+    if (pc.map.size() >= kMaxPlans && old != pc.order.end()) {
       // Evicting frees device memory an earlier launch may still read: wait
       // for the device the victim lives on (not necessarily the current one).
-      const std::string& old = pc.order.front();
-      auto victim = pc.map.find(old);
+      auto victim = pc.map.find(*old);
       if (victim != pc.map.end()) {
         if (victim->second.dev != nullptr) {
           const int vdev = victim->second.device;
@@ -211,7 +228,7 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
         }
         pc.map.erase(victim);
       }
-      pc.order.pop_front();
+      pc.order.erase(old);
     }
     e = hipMalloc(reinterpret_cast<void**>(&p.dev), items.size() * sizeof(h3a::WorkItem));
     if (e != hipSuccess) return fail_hip("hipMalloc (attention plan)", e);
@@ -524,7 +541,7 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
     if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
-                       &plan, &plan_lock)) != H3A_OK)
+                       stream, &plan, &plan_lock)) != H3A_OK)
       return st;
     const int32_t group = Hq / Hkv;
     hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
@@ -577,7 +594,7 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
     if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, &plan, &plan_lock)) != H3A_OK) return st;
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, stream, &plan, &plan_lock)) != H3A_OK) return st;
     hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
                                                    plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
@@ -683,7 +700,7 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
     if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
     hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
                                               scale, Hq / Hkv, causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
@@ -772,7 +789,7 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
     if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, &plan, &plan_lock)) != H3A_OK) return st;
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
     hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
                                             scale, Hq / Hkv, causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);

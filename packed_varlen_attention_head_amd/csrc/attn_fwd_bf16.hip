@@ -660,11 +660,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (ntiles > 1) load_k(1, IC<1>{});
   if constexpr (QNORM) qnorm_apply();
   publish();
-  if (active) {
-    qk(IC<0>{}, s);
-    if (needs_mask(0)) mask(s, 0);
-    update_max(s);
-  }
+  // Every wave computes the first scores, also one whose rows all lie past
+  // the segment end: its Q rows read as zeros, so its scores are 0 (or -inf
+  // where masked) and the steady loop below, which every wave runs, starts
+  // from defined scores and a finite reference.
+  qk(IC<0>{}, s);
+  if (needs_mask(0)) mask(s, 0);
+  update_max(s);
   // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
   __syncthreads();
 

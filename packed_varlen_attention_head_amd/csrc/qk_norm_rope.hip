@@ -72,11 +72,15 @@ struct Elem<Bf16Tag> {
   __device__ static uint4 pack(const float* y) {
     return make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
   }
-  // bf16 rounding, then E4M3 (nearest even, saturating at +-448).
+  // bf16 rounding, then E4M3 (nearest even, saturating at +-448; a NaN stays
+  // NaN, which fminf/fmaxf alone would turn into -448).
   __device__ static uint2 pack_e4m3(const float* y) {
     float b[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = fminf(fmaxf(float(__bf16(y[e])), -448.0f), 448.0f);
+    for (int e = 0; e < 8; ++e) {
+      const float r = float(__bf16(y[e]));
+      b[e] = r != r ? r : fminf(fmaxf(r, -448.0f), 448.0f);
+    }
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[0], b[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[2], b[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(b[4], b[5], 0, false);

@@ -5,7 +5,8 @@
 //
 // HBM-bound elementwise pass: each thread converts 8 consecutive elements
 // (16 bytes in, 8 bytes out) with the hardware packed conversion, after
-// clamping to the largest finite value so nothing overflows to NaN.
+// clamping finite and infinite values to the largest finite magnitude so
+// nothing overflows to NaN; a NaN input stays NaN (an E4M3 NaN code).
 #include <cstdint>
 
 #include "common.h"
@@ -14,6 +15,10 @@ namespace h3a {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Saturate to +-448 before the E4M3 conversion; NaN passes through unchanged
+// (fminf/fmaxf alone would turn it into -448).
+__device__ __forceinline__ float e4m3_sat(float x) { return x != x ? x : fminf(fmaxf(x, -448.0f), 448.0f); }
 
 __global__ void __launch_bounds__(kThreads)
 quantize_e4m3_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ y, int64_t S, int32_t row_vecs,
@@ -34,7 +39,7 @@ quantize_e4m3_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ y, in
       f[2 * j + 1] = __uint_as_float(w[2 * i + j] & 0xffff0000u);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = fminf(fmaxf(f[e], -448.0f), 448.0f);
+    for (int e = 0; e < 4; ++e) f[e] = e4m3_sat(f[e]);
     int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
     packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
     out[i] = uint32_t(packed);
@@ -92,7 +97,7 @@ prepare_vt_e4m3_kernel(VtArgs a, const uint16_t* __restrict__ v, int64_t sv, uin
       for (int i = 0; i < 4; ++i) {
         const uint32_t word = w[i][e / 2];
         f[i] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
-        f[i] = fminf(fmaxf(f[i], -448.0f), 448.0f);
+        f[i] = e4m3_sat(f[i]);
       }
       int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
       packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);

@@ -87,3 +87,54 @@ def test_capture_and_replay(fp8):
         same = torch.equal(o, eager[i])
         log(f"  replay {rep} (inputs {i}): equal to eager = {same}")
         assert same
+
+
+def test_captured_plan_survives_eviction():
+    """A graph keeps the device address of the tile plan its attention launch
+    read.  That plan must outlive cache evictions: capture, then run more distinct
+    packings than the cache holds (256, each evicting the oldest unpinned plan),
+    then replay -- still the eager bytes.  A call whose plan is not cached fails
+    on a capturing stream (building one would allocate and synchronise) and
+    leaves the capture usable."""
+    import torch
+
+    import packed_varlen_attention_head_amd as h3a
+
+    h3a.release_caches()
+    S, H, D = 1000, 2, 128
+    cu = np.array([0, 300, 1000])
+    q, k, v = (to_device(rng.normal_tensor(91, tag, (S, H, D), "bf16"), "bf16")
+               for tag in (rng.TAG_Q, rng.TAG_K, rng.TAG_V))
+    scale = 1.0 / np.sqrt(D)
+    o = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        h3a.varlen_attn_fwd(q, k, v, cu, scale, out=o)  # caches the plan
+    torch.cuda.synchronize()
+    eager = o.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h3a.varlen_attn_fwd(q, k, v, cu, scale, out=o)
+        with pytest.raises(RuntimeError, match="not cached"):
+            h3a.varlen_attn_fwd(q, k, v, np.array([0, 301, 1000]), scale, out=o)
+    torch.cuda.synchronize()
+
+    # 300 other packings: every one a new plan, evicting the oldest unpinned ones
+    tmp = torch.empty_like(q)
+    for i in range(300):
+        h3a.varlen_attn_fwd(q, k, v, np.array([0, 2 + i, 1000]), scale, out=tmp)
+    torch.cuda.synchronize()
+    log("[graph] 300 packings after capture; replaying")
+    for rep in range(3):
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(o, eager)
+        log(f"  replay {rep}: equal to eager = {same}")
+        assert same
+    del g
+    torch.cuda.synchronize()
+    h3a.release_caches()

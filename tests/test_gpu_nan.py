@@ -1,0 +1,109 @@
+"""NaN and infinity handling of the low-precision path against the bf16 one.
+
+OCP E4M3 ("fn") has no infinities and two NaN codes (0x7f, 0xff).  The
+quantisers saturate finite and infinite values at +-448 and turn a NaN into
+a NaN code, so a NaN in q, k or v reaches the attention output through the
+FP8 kernels exactly as through the bf16 kernel: a NaN query element makes
+that query row NaN, a NaN key element makes every row of its segment and
+head NaN, a NaN value element that dim of every row of its segment and head,
+and nothing else is touched."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import rng
+from tests.gpu_util import log, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+LENS = [150, 0, 77, 29]
+H, D = 2, 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    import packed_varlen_attention_head_amd as h3a
+
+    h3a.release_caches()
+
+
+def h3a():
+    import packed_varlen_attention_head_amd as m
+
+    return m
+
+
+def _bits(x: float) -> int:
+    return int(np.array([x], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+def _inputs(seed):
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int64)
+    S = int(cu[-1])
+    q, k, v = (rng.normal_tensor(seed, tag, (S, H, D), "bf16") for tag in (rng.TAG_Q, rng.TAG_K, rng.TAG_V))
+    return cu, q, k, v
+
+
+def test_quantize_nan_and_infinities():
+    import torch
+
+    _, q, _, _ = _inputs(3)
+    x = q.copy()
+    x[5, 1, 7] = _bits(np.nan)
+    x[9, 0, 3] = _bits(np.inf)
+    x[11, 1, 100] = _bits(-np.inf)
+    codes = h3a().quantize_e4m3(to_device(x, "bf16")).cpu().numpy()
+    torch.cuda.synchronize()
+    log(f"[nan] codes: nan={codes[5, 1, 7]:#x} +inf={codes[9, 0, 3]:#x} -inf={codes[11, 1, 100]:#x}")
+    assert codes[5, 1, 7] in (0x7F, 0xFF)
+    assert codes[9, 0, 3] == 0x7E and codes[11, 1, 100] == 0xFE
+    finite = np.ones(x.shape, dtype=bool)
+    finite[5, 1, 7] = finite[9, 0, 3] = finite[11, 1, 100] = False
+    ref = oracle.e4m3_encode(rng.as_f64(x, "bf16")[finite])
+    assert np.array_equal(codes[finite], ref)
+
+
+def _nan_rows(o, cu, row=None, seg=None, head=0):
+    """Expected NaN mask of the output: one query row, or every row of a segment, in one head."""
+    m = np.zeros(o.shape[:2], dtype=bool)
+    if row is not None:
+        m[row, head] = True
+    if seg is not None:
+        m[int(cu[seg]):int(cu[seg + 1]), head] = True
+    return m
+
+
+@pytest.mark.parametrize("where", ["q", "k", "v"])
+def test_nan_propagates_like_bf16(where):
+    import torch
+
+    cu, q, k, v = _inputs(7)
+    # a NaN in row 160 (segment 2, local row 10), head 1, dim 40
+    row, head = 160, 1
+    t = {"q": q, "k": k, "v": v}[where]
+    t[row, head, 40] = _bits(np.nan)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    scale = 1.0 / np.sqrt(D)
+    seg = int(np.searchsorted(cu, row, side="right") - 1)
+    expect = _nan_rows(np.zeros((int(cu[-1]), H)), cu, row=row if where == "q" else None,
+                       seg=None if where == "q" else seg, head=head)
+    outs = {
+        "bf16": h3a().varlen_attn_fwd(qd, kd, vd, cu, scale),
+        "fp8qk": h3a().varlen_attn_fwd_fp8qk(h3a().quantize_e4m3(qd), h3a().quantize_e4m3(kd), vd, cu, scale),
+        "fp8": h3a().varlen_attn_fwd_fp8(h3a().quantize_e4m3(qd), h3a().quantize_e4m3(kd),
+                                         h3a().prepare_vt_e4m3(vd, cu), cu, scale),
+    }
+    torch.cuda.synchronize()
+    for name, o in outs.items():
+        nan = torch.isnan(o.float()).cpu().numpy()
+        rows_nan = nan.any(axis=2)
+        log(f"[nan] {where} {name}: NaN rows {int(rows_nan.sum())} expected {int(expect.sum())}")
+        assert np.array_equal(rows_nan, expect), name
+        if where == "v":  # o = sum_j p_j v_j: only the NaN's own dim
+            assert np.array_equal(nan[:, :, 40], expect) and not nan[:, :, :40].any() and not nan[:, :, 41:].any()
+        else:  # a NaN score reaches the row's normaliser: every dim
+            assert np.array_equal(nan.all(axis=2), expect), name

@@ -397,6 +397,39 @@ h3a_status h3a_plan_tiles(const int32_t* cu_seqlens, int32_t nseg, int32_t H, in
 h3a_status h3a_plan_tiles_ex(const int32_t* cu_seqlens, int32_t nseg, int32_t H, int32_t block_m,
                              int32_t n_xcd, int32_t causal, int32_t* items, int64_t cap, int64_t* n_items);
 
+/*
+ * h3a_varlen_attn_fwd_ex without device allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, validation, kernels and
+ * output bytes as h3a_varlen_attn_fwd_ex; the only difference is where the
+ * attention's tile plan (its work queue) lives.
+ *
+ * The plan goes into a fixed array in device memory that the library
+ * reserves for this call, 2 MiB on each GPU it runs on, held until the
+ * process ends; nothing is allocated, freed or cached per call, and the
+ * call never synchronises the host.  The plan is built on `stream` from a
+ * per-segment table (segments longest first, query tiles dealt to the XCDs
+ * in chunks of 16; no per-XCD balancing as in the cached plan).
+ *
+ * Limits: at most 256 non-empty segments and 65,536 work items (one item is
+ * 128 query rows of one head in bf16, 64 in fp32; the item count is padded up
+ * to a multiple of 16 per XCD): e.g. S * H up to ~8.3M rows in bf16.  Beyond
+ * them the call fails with EUNSUPPORTED before touching the device.
+ *
+ * Sharing: every call on one GPU uses that GPU's array; it keeps the last
+ * call's plan.  Calls are ordered through it on the GPU (each waits, on its
+ * stream, for the previous call's attention kernel, whatever stream that ran
+ * on), so overlapping calls on one GPU do not corrupt each other but do not
+ * run concurrently either.  The first call on a device resolves the array's
+ * address and creates one event (set-up, once per device).
+ * Errors: as h3a_varlen_attn_fwd_ex, plus the limits above.
+ */
+h3a_status h3a_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, h3a_dtype dtype,
+                                       int64_t S, int32_t Hq, int32_t Hkv, int32_t D, int64_t stride_q,
+                                       int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                       const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal,
+                                       hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* h3a_last_error(void);
 

@@ -37,6 +37,7 @@ EXPORTS = (
     "h3a_rmsnorm_rope",
     "h3a_varlen_attn_fwd",
     "h3a_varlen_attn_fwd_ex",
+    "h3a_varlen_attn_fwd_noalloc",
     "h3a_varlen_attn_fwd_qnorm",
     "h3a_varlen_attn_fwd_fp8qk",
     "h3a_quantize_e4m3",
@@ -109,13 +110,14 @@ def lib() -> ctypes.CDLL:
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                          _i64, _c_i32p, _i32, _f32, _i32, _vp]
+    L.h3a_varlen_attn_fwd_noalloc.argtypes = L.h3a_varlen_attn_fwd_ex.argtypes
     L.h3a_plan_tiles.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     L.h3a_plan_tiles_ex.argtypes = [_c_i32p, _i32, _i32, _i32, _i32, _i32, _c_i32p, _i64, _c_i64p]
     for name in ("h3a_build_rope_table", "h3a_build_rope_table_ex", "h3a_qk_rmsnorm_rope", "h3a_qk_rmsnorm_rope_ex",
                  "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
-                 "h3a_varlen_attn_fwd_ex", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
+                 "h3a_varlen_attn_fwd_ex", "h3a_varlen_attn_fwd_noalloc", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
     L.h3a_last_error.argtypes = []
@@ -468,7 +470,8 @@ def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fa
     return out
 
 
-def varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
+def varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None,
+                       _entry="h3a_varlen_attn_fwd_ex"):
     """Grouped-K/V (k, v: [S, Hkv, D], Hkv | Hq) and optionally causal per-segment attention."""
     import torch
 
@@ -484,10 +487,18 @@ def varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale: float, causal: bool = False, 
     _, _, _, so = _token_major("out", out)
     _same("out", out, (S, Hq, D), q.dtype)
     cu = _i32_array(cu_seqlens)
-    _check(lib().h3a_varlen_attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
-                                        S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
-                                        int(bool(causal)), _stream_handle(stream)))
+    _check(getattr(lib(), _entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(q),
+                                  S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale),
+                                  int(bool(causal)), _stream_handle(stream)))
     return out
+
+
+def varlen_attn_fwd_noalloc(q, k, v, cu_seqlens, scale: float, out, causal: bool = False, stream=None):
+    """varlen_attn_fwd_ex without device allocation: `out` must be given, and the
+    tile plan goes into the library's fixed per-GPU array (at most 256 non-empty
+    segments and 65,536 work items)."""
+    return varlen_attn_fwd_ex(q, k, v, cu_seqlens, scale, causal=causal, out=out, stream=stream,
+                              _entry="h3a_varlen_attn_fwd_noalloc")
 
 
 def plan_tiles(cu_seqlens, heads: int, block_m: int, n_xcd: int, causal: bool = False) -> np.ndarray:

@@ -258,6 +258,37 @@ h3a_status check_cu_seqlens(const int32_t* cu, int32_t nseg, int64_t S) {
   return H3A_OK;
 }
 
+// Argument checks shared by h3a_varlen_attn_fwd_ex and its allocation-free
+// variant: every error they report, before anything is launched.
+h3a_status check_attn_ex(const void* q, const void* k, const void* v, const void* o, h3a_dtype dtype, int64_t S,
+                         int32_t Hq, int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                         int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal) {
+  if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+  if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+  if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+  if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  const size_t esz = elem_size(dtype);
+  if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
+  if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
+  if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
+  if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  auto overlaps = [&](const void* x, int64_t sx, int32_t h) {
+    return may_overlap(o, stride_o, Hq, x, sx, h, S, D, esz);
+  };
+  if (overlaps(q, stride_q, Hq)) return fail(H3A_EINVAL, "o overlaps q");
+  if (overlaps(k, stride_k, Hkv)) return fail(H3A_EINVAL, "o overlaps k");
+  if (overlaps(v, stride_v, Hkv)) return fail(H3A_EINVAL, "o overlaps v");
+  return H3A_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -513,30 +544,9 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
                                   int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
                                   float scale, int32_t causal, hipStream_t stream) {
   try {
-    if (dtype != H3A_F32 && dtype != H3A_BF16) return fail(H3A_EDTYPE, "unknown dtype %d", int(dtype));
-    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
-    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
-    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
-    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
-    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
-    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
-    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
-    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
-    h3a_status st;
-    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-    const size_t esz = elem_size(dtype);
-    if ((st = check_operand("q", q, S, Hq, D, stride_q, esz)) != H3A_OK) return st;
-    if ((st = check_operand("k", k, S, Hkv, D, stride_k, esz)) != H3A_OK) return st;
-    if ((st = check_operand("v", v, S, Hkv, D, stride_v, esz)) != H3A_OK) return st;
-    if ((st = check_operand("o", o, S, Hq, D, stride_o, esz)) != H3A_OK) return st;
-    if (S == 0) return H3A_OK;
-    auto overlaps = [&](const void* x, int64_t sx, int32_t h) {
-      return may_overlap(o, stride_o, Hq, x, sx, h, S, D, esz);
-    };
-    if (overlaps(q, stride_q, Hq)) return fail(H3A_EINVAL, "o overlaps q");
-    if (overlaps(k, stride_k, Hkv)) return fail(H3A_EINVAL, "o overlaps k");
-    if (overlaps(v, stride_v, Hkv)) return fail(H3A_EINVAL, "o overlaps v");
-
+    h3a_status st = check_attn_ex(q, k, v, o, dtype, S, Hq, Hkv, D, stride_q, stride_k, stride_v, stride_o,
+                                  cu_seqlens, nseg, scale, causal);
+    if (st != H3A_OK || S == 0) return st;
     const bool bf16 = dtype == H3A_BF16;
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
@@ -552,6 +562,65 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
     return H3A_OK;
   } catch (...) {
     return fail_exception("h3a_varlen_attn_fwd_ex");
+  }
+}
+
+h3a_status h3a_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       h3a_dtype dtype, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int64_t stride_q, int64_t stride_k, int64_t stride_v,
+                                       int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg,
+                                       float scale, int32_t causal, hipStream_t stream) {
+  try {
+    h3a_status st = check_attn_ex(q, k, v, o, dtype, S, Hq, Hkv, D, stride_q, stride_k, stride_v, stride_o,
+                                  cu_seqlens, nseg, scale, causal);
+    if (st != H3A_OK || S == 0) return st;
+    const bool bf16 = dtype == H3A_BF16;
+    // The segment table, in fixed storage: the non-empty segments, longest
+    // first (a stable insertion sort over at most kNoAllocMaxSegs entries).
+    h3a::NoAllocPlanArgs a{};
+    a.block_m = bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32;
+    int32_t n = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+      const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
+      if (len == 0) continue;
+      if (n == h3a::kNoAllocMaxSegs)
+        return fail(H3A_EUNSUPPORTED, "cu_seqlens has more than %d non-empty segments (the allocation-free "
+                    "entry point's limit)", h3a::kNoAllocMaxSegs);
+      int32_t j = n++;
+      for (; j > 0 && a.len[j - 1] < len; --j) {
+        a.len[j] = a.len[j - 1];
+        a.start[j] = a.start[j - 1];
+      }
+      a.len[j] = len;
+      a.start[j] = cu_seqlens[s];
+    }
+    a.nseg = n;
+    int64_t items = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      a.first[i] = int32_t(std::min<int64_t>(items, INT32_MAX));
+      items += int64_t((a.len[i] + a.block_m - 1) / a.block_m) * Hq;
+    }
+    if (items > h3a::kNoAllocMaxItems)
+      return fail(H3A_EUNSUPPORTED, "the attention needs %lld work items; the allocation-free entry point holds at "
+                  "most %d (use h3a_varlen_attn_fwd_ex)", (long long)items, h3a::kNoAllocMaxItems);
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail_hip("hipGetDevice", e);
+    a.n_xcd = n_xcd_of(device);
+    a.n_items = int32_t(items);
+    const int64_t chunks = (items + 15) / 16;
+    const int64_t blocks = int64_t(a.n_xcd) * 16 * ((chunks + a.n_xcd - 1) / a.n_xcd);
+    if (blocks > h3a::kNoAllocMaxItems)
+      return fail(H3A_EUNSUPPORTED, "the attention needs %lld work items once padded over %d XCDs; the "
+                  "allocation-free entry point holds at most %d (use h3a_varlen_attn_fwd_ex)", (long long)blocks,
+                  a.n_xcd, h3a::kNoAllocMaxItems);
+    a.n_blocks = int32_t(blocks);
+    e = h3a::launch_attn_noalloc(a, bf16, q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, scale, Hq / Hkv,
+                                 causal != 0, stream);
+    if (e != hipSuccess) return fail_hip("allocation-free varlen attention launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_noalloc");
   }
 }
 

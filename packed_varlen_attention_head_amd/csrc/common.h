@@ -121,4 +121,32 @@ hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void
                                const WorkItem* items, int64_t n_items, float scale,
                                int32_t kv_group, bool causal, hipStream_t stream);
 
+// ---- allocation-free attention (attn_noalloc.hip) --------------------------
+// Largest padded plan (work items) and number of non-empty segments the
+// allocation-free entry point takes: 2 MiB of plan storage per GPU, and a
+// segment table that fits in the plan kernel's arguments.
+constexpr int32_t kNoAllocMaxItems = 1 << 16;
+constexpr int32_t kNoAllocMaxSegs = 256;
+
+// Per-segment table of the allocation-free plan: the non-empty segments,
+// longest first, and the index of each one's first item in the natural order
+// (segment-major, then head, then query tile).
+struct NoAllocPlanArgs {
+  int32_t nseg;
+  int32_t block_m;
+  int32_t n_xcd;
+  int32_t n_items;   // natural items (sum of query tiles times heads)
+  int32_t n_blocks;  // padded launch size: n_xcd * kChunk * ceil(ceil(n_items / 16) / n_xcd)
+  int32_t start[kNoAllocMaxSegs];
+  int32_t len[kNoAllocMaxSegs];
+  int32_t first[kNoAllocMaxSegs];
+};
+
+// Expands the table into the file-scope plan array on `stream`, then launches
+// the bf16 or fp32 attention kernel on it (after any earlier such launch on
+// this device, whatever its stream).
+hipError_t launch_attn_noalloc(const NoAllocPlanArgs& plan, bool bf16, const void* q, const void* k, const void* v,
+                               void* o, int32_t D, int64_t sq, int64_t sk, int64_t sv, int64_t so, float scale,
+                               int32_t kv_group, bool causal, hipStream_t stream);
+
 }  // namespace h3a

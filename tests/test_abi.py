@@ -330,3 +330,37 @@ def test_binding_reports_errors_by_exception():
     with pytest.raises(h3a.H3AError) as e:
         h3a.plan_tiles([0, 5, 3], heads=2, block_m=128, n_xcd=8)
     assert e.value.status == h3a.H3A_EINVAL and "decreases" in e.value.message
+
+
+def attn_noalloc(cu, Hq=2, Hkv=2, D=128, dtype=h3a.H3A_BF16, causal=0):
+    """h3a_varlen_attn_fwd_noalloc with never-dereferenced, disjoint operand addresses."""
+    c, cp = i32(cu)
+    S = int(c[-1])
+    q, k, v, o = (P + i * (1 << 40) for i in range(4))
+    return h3a.lib().h3a_varlen_attn_fwd_noalloc(q, k, v, o, dtype, S, Hq, Hkv, D, Hq * D, Hkv * D, Hkv * D,
+                                                 Hq * D, cp, len(c) - 1, 0.088, causal, None)
+
+
+@pytest.mark.parametrize("cu,H,word", [
+    (np.arange(258) * 3, 2, "257"),                               # 257 non-empty segments
+    (np.concatenate([[0], np.arange(1, 258) * 3, [800] * 40]), 2, "257"),  # empty ones do not help
+    ([0, 1 << 20], 16, "131072 work items"),                      # 8,192 query tiles x 16 heads
+    ([0, 60000, 120000], 70, "65,536"),                           # 65,660 items
+])
+def test_noalloc_limits_rejected_before_the_device(cu, H, word):
+    """Past its fixed plan array the allocation-free entry point fails with
+    EUNSUPPORTED before any HIP call, naming the limit."""
+    assert attn_noalloc(cu, Hq=H, Hkv=H) == h3a.H3A_EUNSUPPORTED
+    msg = h3a.last_error()
+    assert ("256" in msg or "65536" in msg), msg
+    assert word.replace(",", "") in msg.replace(",", "") or "non-empty segments" in msg, msg
+
+
+def test_noalloc_validates_like_the_cached_entry():
+    """Same argument checks as h3a_varlen_attn_fwd_ex (shared code): bad head
+    counts, dtype, cu_seqlens and overlapping outputs fail the same way."""
+    assert attn_noalloc([0, 10], Hq=3, Hkv=2) == h3a.H3A_ESHAPE
+    assert attn_noalloc([0, 10], D=96) == h3a.H3A_EUNSUPPORTED
+    assert attn_noalloc([0, 10], dtype=7) == h3a.H3A_EDTYPE
+    assert attn_noalloc([0, 10, 9]) == h3a.H3A_EINVAL and "decreases" in h3a.last_error()
+    assert attn_noalloc([0, 10], causal=2) == h3a.H3A_EINVAL

@@ -18,7 +18,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libh3a.so")
+# H3A_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libh3a.so.
+LIB_PATH = os.environ.get("H3A_LIBRARY") or os.path.join(_HERE, "libh3a.so")
 
 H3A_OK, H3A_EINVAL, H3A_ESHAPE, H3A_EDTYPE, H3A_EUNSUPPORTED, H3A_EHIP = range(6)
 H3A_F32, H3A_BF16 = 0, 1

@@ -70,11 +70,53 @@ def build(jobs: int = 6, verbose: bool = False) -> str:
     return LIB
 
 
+# Host code only (the C ABI's validation, plan cache and planner): compiled
+# with g++ under AddressSanitizer and UndefinedBehaviorSanitizer, linked with
+# the ordinary kernel objects.  The GPU code is never sanitised.
+HOST_SOURCES = ["api.cpp", "planner.cpp"]
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libh3a_san.so")
+SAN_FLAGS = ["-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+             "-I", INCLUDE, "-I", CSRC]
+
+
+def build_sanitized(jobs: int = 6, verbose: bool = False) -> str:
+    """libh3a_san.so: api.cpp and planner.cpp built by g++ with ASan + UBSan, the
+    HIP sources as in build().  Load it with H3A_LIBRARY and LD_PRELOAD of
+    g++'s libasan (`g++ -print-file-name=libasan.so`)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    kernels = [s for s in SOURCES if s not in HOST_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        kobjs = list(ex.map(_compile, kernels))
+    hobjs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = ["g++", *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compiling {src} (sanitizers) failed:\n{' '.join(cmd)}\n{r.stderr}")
+        hobjs.append(obj)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *hobjs, *kobjs, "-lasan", "-lubsan",
+           "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking {SAN_LIB} failed:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=6)
+    ap.add_argument("--sanitize", action="store_true",
+                    help="build _build/san/libh3a_san.so (host code under ASan + UBSan) instead")
     args = ap.parse_args(argv)
-    build(args.jobs, verbose=True)
+    if args.sanitize:
+        build_sanitized(args.jobs, verbose=True)
+    else:
+        build(args.jobs, verbose=True)
     return 0
 
 

@@ -34,7 +34,7 @@ sqrt are the only library primitives used):
    The encoder text tower's causal grouped-query attention (query i of a
    segment sees keys 0..i; K/V heads broadcast over their query groups) is
    section 5b; the low-precision variant (Q and K rounded to FP8 E4M3 before
-   the score product) is section 5c.
+   the score product) is section 5c, and its per-block-scaled form section 5d.
 
 Readings where the pages are silent:
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
@@ -454,6 +454,93 @@ def varlen_attention_fp8(q, k, v, cu, scale: float, causal: bool = False) -> np.
     both products); the softmax weights stay exact.  (A kernel that also rounds the
     weights to E4M3 for the PV product differs from this by that rounding.)"""
     return varlen_attention_gqa(e4m3_round(q), e4m3_round(k), e4m3_round(v), cu, scale, causal=causal)
+
+
+# ----------------------------------------------------------------------------
+# 5d. Low-precision attention with per-block scales
+#
+# The pages' GB10 builds run their low-precision attention with per-block
+# quantisation calibrated on the activations themselves (SageAttention 2++
+# "quality attention with real-activation calibration", Comfy Kitchen's INT8
+# Q/K/V kernel; h3-spark model card, "What this config does" and runtime
+# options).  Reading where the pages stop short: every block of 32 consecutive
+# elements along the contraction of a product -- 32 head dims of one token
+# and head for q and k, 32 keys of one head dim for v, the key blocks aligned
+# at the segment start -- shares one power-of-two scale 2^X, the smallest that
+# brings the block's largest magnitude to at most 448 (E4M3's largest finite
+# value), so no element saturates.  Each element is x * 2^-X rounded to E4M3
+# (nearest even) and stands for decode(code) * 2^X.  An all-zero block has
+# X = -127.  The softmax weights stay exact here, as in section 5c.
+# ----------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """X = ceil(log2(amax / 448)) for amax > 0, from amax's binary exponent E and
+    mantissa M in [1, 2): X = E - 8 while M * 2^8 <= 448 (M <= 1.75), else
+    E - 7; -127 for amax == 0; clamped to [-127, 127]."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(a)  # a = m * 2^e, m in [0.5, 1)
+    X = np.where(2.0 * m <= 1.75, e - 1 - 8, e - 1 - 7)
+    X = np.where(a == 0, -127, X)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def mx_quantize(x, axis: int = -1):
+    """(codes uint8 of x's shape, exponents X int64 with the block axis shortened
+    by 32): blocks of 32 consecutive elements along `axis` (length a multiple
+    of 32)."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+    n = x.shape[-1]
+    assert n % MX_BLOCK == 0, "block axis must be a multiple of 32"
+    blocks = x.reshape(x.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    X = mx_block_exponent(np.abs(blocks).max(axis=-1))
+    codes = e4m3_encode(blocks * np.exp2(-X.astype(np.float64))[..., None]).reshape(x.shape)
+    return np.moveaxis(codes, -1, axis), np.moveaxis(X, -1, axis)
+
+
+def mx_dequantize(codes, X, axis: int = -1) -> np.ndarray:
+    """The values codes stand for: decode(code) * 2^X of the code's block."""
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    e = np.moveaxis(np.asarray(X), axis, -1)
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    v = v * np.exp2(e.astype(np.float64))[..., None]
+    return np.moveaxis(v.reshape(c.shape), -1, axis)
+
+
+def mx_round(x, axis: int = -1) -> np.ndarray:
+    """x rounded through per-block-scaled E4M3 along `axis`."""
+    return mx_dequantize(*mx_quantize(x, axis), axis=axis)
+
+
+def mx_round_keys(v, cu) -> np.ndarray:
+    """v [S, H, D] rounded with blocks of 32 keys per head dim, aligned at each
+    segment's start; a segment's last block is padded with zeros (which leave
+    its largest magnitude unchanged)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    for a, b in zip(cu[:-1], cu[1:]):
+        a, b = int(a), int(b)
+        if b == a:
+            continue
+        n = -(-(b - a) // MX_BLOCK) * MX_BLOCK
+        pad = np.zeros((n,) + v.shape[1:])
+        pad[: b - a] = v[a:b]
+        out[a:b] = mx_round(pad, axis=0)[: b - a]
+    return out
+
+
+def varlen_attention_mx_qk(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """varlen_attention_gqa with q and k rounded per 32-dim block (section 5d)."""
+    return varlen_attention_gqa(mx_round(q), mx_round(k), v, cu, scale, causal=causal)
+
+
+def varlen_attention_mx(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """varlen_attention_gqa with q, k rounded per 32-dim block and v per 32-key
+    block of each segment; exact softmax weights.  (A kernel that also rounds
+    the weights to E4M3 for the PV product differs from this by that rounding.)"""
+    return varlen_attention_gqa(mx_round(q), mx_round(k), mx_round_keys(v, cu), cu, scale, causal=causal)
 
 
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):

@@ -610,6 +610,120 @@ def check_fp8qk_attention(O):
     assert not np.allclose(a3, a, rtol=0, atol=1e-6)
 
 
+def check_mx_block_exponent(O):
+    """Hand-derived scale exponents, and on 5,000 magnitudes over 2^-110..2^110: the scaled
+    maximum never exceeds 448 and doubling it would (the exponent is the smallest one)."""
+    g = golden()["mx"]
+    for a, X in g["exponent"].items():
+        assert int(O.mx_block_exponent(float(a))) == X, (a, X)
+    for e, X in g["exponent_pow2"].items():
+        assert int(O.mx_block_exponent(2.0 ** int(e))) == X, (e, X)
+    r = _rng(31)
+    a = r.uniform(1, 2, 5000) * 2.0 ** r.integers(-110, 110, 5000).astype(np.float64)
+    scaled = a * 2.0 ** -O.mx_block_exponent(a).astype(np.float64)
+    assert np.all(scaled <= 448.0) and np.all(2.0 * scaled > 448.0)
+
+
+def check_mx_quantize(O):
+    """Hand-derived blocks; representable blocks pass through; exact equivariance under powers
+    of two; the E4M3 error bound relative to each block's scale; independent blocks; blocks that
+    need no scaling give the plain codec's codes."""
+    g = golden()["mx"]
+    ga, gb = g["block_a"], g["block_b"]
+    x = np.zeros(64)
+    x[: len(ga["x"])] = ga["x"]
+    x[32: 32 + len(gb["x"])] = gb["x"]
+    codes, X = O.mx_quantize(x)
+    assert list(X) == [ga["X"], gb["X"]]
+    assert list(codes[: len(ga["codes"])]) == ga["codes"] and list(codes[32: 32 + len(gb["codes"])]) == gb["codes"]
+    vals = O.mx_dequantize(codes, X)
+    assert np.array_equal(vals[: len(ga["values"])], ga["values"])
+    assert np.array_equal(vals[32: 32 + len(gb["values"])], gb["values"])
+
+    def rnd(v, axis=-1):
+        return O.mx_dequantize(*O.mx_quantize(v, axis), axis=axis)
+
+    assert np.array_equal(O.mx_round(x), rnd(x))
+    r = _rng(32)
+    # representable: random codes whose block max code lies in [224, 448], times 2^X
+    codes = r.integers(0, 0x7F, size=(40, 64)).astype(np.uint8)
+    codes[:, ::32] = r.integers(0x70, 0x7F, size=(40, 2))
+    Xs = r.integers(-60, 60, size=(40, 2))
+    x = (O.e4m3_decode(codes).reshape(40, 2, 32) * 2.0 ** Xs[..., None]).reshape(40, 64)
+    x *= r.choice([-1.0, 1.0], size=x.shape)
+    assert np.array_equal(rnd(x), x)
+    # equivariance and error bound on wide-range data
+    y = r.normal(size=(50, 128)) * 2.0 ** r.integers(-30, 30, size=(50, 1)).astype(np.float64)
+    y[3, 40:60] = 0.0
+    for k in (-9, 5, 17):
+        assert np.array_equal(rnd(y * 2.0 ** k), rnd(y) * 2.0 ** k)
+    c, X = O.mx_quantize(y)
+    scale = np.repeat(2.0 ** X.astype(np.float64), 32, axis=-1)
+    err = np.abs(rnd(y) - y)
+    normal = np.abs(y) >= scale * 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(y[normal]))
+    assert np.all(err[~normal] <= scale[~normal] * 2.0 ** -10)
+    # blocks are independent, and the block axis can be any axis
+    y2 = y.copy()
+    y2[:, 32:64] *= 1000.0
+    c2, X2 = O.mx_quantize(y2)
+    keep = np.r_[0:32, 64:128]
+    assert np.array_equal(c2[:, keep], c[:, keep]) and np.array_equal(X2[:, [0, 2, 3]], X[:, [0, 2, 3]])
+    assert np.array_equal(rnd(y.T, axis=0), rnd(y).T)
+    # no scaling needed -> the plain E4M3 codec
+    z = r.uniform(-448, 448, size=(10, 32))
+    z[:, 0] = 400.0
+    cz, Xz = O.mx_quantize(z)
+    assert np.all(Xz == 0) and np.array_equal(cz, O.e4m3_encode(z))
+
+
+def check_mx_keys_and_attention(O):
+    """V blocks of 32 keys start at each segment's start (a segment rounds the same alone or
+    packed, checked against a scalar loop); attention on representable operands is the exact
+    attention; scaling v by a power of two scales the output exactly, which the unscaled E4M3
+    path cannot do for v at 2^-12 or 2^10."""
+    r = _rng(33)
+    lens = [40, 0, 77, 1, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S, D = int(cu[-1]), 32
+    # segments 2^14 apart in magnitude: a block straddling two of them would flush the
+    # smaller one's values (scaling commutes with E4M3 rounding only inside its range)
+    mag = np.repeat(2.0 ** np.array([-12.0, 0.0, 12.0, 0.0, -6.0]), lens)
+    v = r.normal(size=(S, 2, D)) * mag[:, None, None]
+    rv = O.mx_round_keys(v, cu)
+    assert np.all(np.abs(rv - v) <= 2.0 ** -4 * np.abs(v) + 2.0 ** -20 * np.abs(v).max(axis=0))
+    for a, b in zip(cu[:-1], cu[1:]):
+        if b > a:
+            assert np.array_equal(rv[a:b], O.mx_round_keys(v[a:b], np.array([0, b - a])))
+    # scalar loop for one head dim of the 77-key segment
+    a0, h, d = int(cu[2]), 1, 5
+    for blk in range(3):
+        idx = [a0 + blk * 32 + i for i in range(32) if blk * 32 + i < 77]
+        amax = max(abs(v[i, h, d]) for i in idx)
+        X = int(O.mx_block_exponent(amax))
+        for i in idx:
+            want = O.e4m3_decode(O.e4m3_encode(np.array([v[i, h, d] * 2.0 ** -X])))[0] * 2.0 ** X
+            assert rv[i, h, d] == want
+    q, k = r.normal(size=(S, 4, D)), r.normal(size=(S, 2, D))
+    qr, kr, vr = O.mx_round(q), O.mx_round(k), O.mx_round_keys(v, cu)
+    for causal in (False, True):
+        assert np.array_equal(O.varlen_attention_mx(qr, kr, vr, cu, 0.2, causal),
+                              O.varlen_attention_gqa(qr, kr, vr, cu, 0.2, causal))
+    assert np.array_equal(O.varlen_attention_mx_qk(q, k, v, cu, 0.2), O.varlen_attention_gqa(qr, kr, v, cu, 0.2))
+    v1 = r.normal(size=(S, 2, D))
+    base = O.varlen_attention_mx(q, k, v1, cu, 0.2)
+    # a length-1 segment returns its own value as the block rounding of it stands
+    i1 = int(cu[3])
+    own = O.mx_round_keys(v1[i1:i1 + 1], np.array([0, 1]))[0]  # [Hkv, D]; query heads 2h, 2h+1 read K/V head h
+    assert np.array_equal(base[i1], np.repeat(own, 2, axis=0))
+    assert not np.array_equal(base[i1], np.repeat(v1[i1], 2, axis=0))
+    exact = O.varlen_attention_gqa(q, k, v1, cu, 0.2)
+    for e in (-12, 10):
+        assert np.array_equal(O.varlen_attention_mx(q, k, v1 * 2.0 ** e, cu, 0.2), base * 2.0 ** e)
+        unscaled = O.varlen_attention_fp8(q, k, v1 * 2.0 ** e, cu, 0.2) / 2.0 ** e
+        assert np.abs(unscaled - exact).sum() > 4 * np.abs(base - exact).sum(), e
+
+
 # ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
@@ -692,6 +806,9 @@ ALL_CHECKS = [
     check_e4m3_matches_torch,
     check_bf16_round,
     check_fp8qk_attention,
+    check_mx_block_exponent,
+    check_mx_quantize,
+    check_mx_keys_and_attention,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

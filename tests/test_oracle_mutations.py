@@ -230,6 +230,34 @@ def _bf16_round_7_bits(x):
     return np.copysign(np.rint(a / ulp) * ulp, x)
 
 
+def _mx_exponent_floor(amax):
+    """The OCP-style floor(log2 amax) - 8: block maxima above 1.75 * 2^E saturate."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.clip(np.where(a == 0, -127, e - 1 - 8), -127, 127).astype(np.int64)
+
+
+def _mx_quantize_blocks(width):
+    def q(x, axis=-1):
+        x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+        n = x.shape[-1]
+        blocks = x.reshape(x.shape[:-1] + (n // width, width))
+        X = oracle.mx_block_exponent(np.abs(blocks).max(axis=-1))
+        codes = oracle.e4m3_encode(blocks * np.exp2(-X.astype(np.float64))[..., None]).reshape(x.shape)
+        X32 = X.reshape(X.shape[:-1] + (n // 32, 32 // width))[..., 0] if width < 32 else np.repeat(X, width // 32, -1)
+        return np.moveaxis(codes, -1, axis), np.moveaxis(X32, -1, axis)
+    return q
+
+
+def _mx_keys_global_blocks(v, cu):
+    """Key blocks aligned at token 0 of the packing instead of each segment's start."""
+    v = np.asarray(v, dtype=np.float64)
+    n = -(-v.shape[0] // 32) * 32
+    pad = np.zeros((n,) + v.shape[1:])
+    pad[: v.shape[0]] = v
+    return oracle.mx_round(pad, axis=0)[: v.shape[0]]
+
+
 MUTANTS = {
     "bf16_round_7_bits": dict(bf16_round=_bf16_round_7_bits),
     "e4m3_decode_bias_8": dict(e4m3_decode=_decode_bias_8),
@@ -237,6 +265,12 @@ MUTANTS = {
     "e4m3_no_saturation": dict(e4m3_encode=_encode_no_saturation),
     "e4m3_truncating": dict(e4m3_encode=_encode_truncating),
     "fp8qk_rounds_only_q": dict(varlen_attention_fp8qk=_fp8qk_only_q),
+    "mx_exponent_floor": dict(mx_block_exponent=_mx_exponent_floor),
+    "mx_blocks_of_16": dict(mx_quantize=_mx_quantize_blocks(16)),
+    "mx_one_scale_per_64": dict(mx_quantize=_mx_quantize_blocks(64)),
+    "mx_keys_not_segment_aligned": dict(mx_round_keys=_mx_keys_global_blocks),
+    "mx_v_left_exact": dict(varlen_attention_mx=lambda q, k, v, cu, scale, causal=False:
+                            oracle.varlen_attention_mx_qk(q, k, v, cu, scale, causal)),
     "fp8_leaves_v_exact": dict(varlen_attention_fp8=lambda q, k, v, cu, scale, causal=False:
                                oracle.varlen_attention_fp8qk(q, k, v, cu, scale, causal)),
     "causal_one_key_too_many": dict(varlen_attention_gqa=_gqa_with(_masked_diagonal_too)),

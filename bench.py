@@ -449,23 +449,27 @@ def main():
         print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32, without --fp8-qk "
               f"({w.name})", file=sys.stderr)
         return 2
-    if fp8:
-        q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
-        k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
-    if fp8pv:
-        vt8 = torch.empty((w.kv, w.head_dim, h3a.vt_e4m3_columns(np.concatenate([[0], np.cumsum(w.lengths)]))),
-                          dtype=torch.uint8, device=dev)
+    if fp8:  # E4M3 codes and one E8M0 scale per 32 head dims
+        q8 = (torch.empty(q.shape, dtype=torch.uint8, device=dev),
+              torch.empty(q.shape[:2] + (q.shape[2] // 32,), dtype=torch.uint8, device=dev))
+        k8 = (torch.empty(k.shape, dtype=torch.uint8, device=dev),
+              torch.empty(k.shape[:2] + (k.shape[2] // 32,), dtype=torch.uint8, device=dev))
+    if fp8pv:  # transposed codes and one scale per 32 keys of each head dim
+        cols = h3a.vt_e4m3_columns(np.concatenate([[0], np.cumsum(w.lengths)]))
+        vt8 = (torch.empty((w.kv, w.head_dim, cols), dtype=torch.uint8, device=dev),
+               torch.empty((w.kv, cols // 64, 2, 32, w.head_dim // 32), dtype=torch.uint8, device=dev))
 
     def norm():
         if fused:
             return h3a.rmsnorm_rope(k, gk, w.eps, tab, w.rot_dim, x_out=kn, stream=stream)
         if fp8:  # one pass: norm + rotary writing E4M3 codes
-            return h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8, k8=k8, stream=stream)
+            return h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8[0], k8=k8[0], q_scale=q8[1],
+                                            k_scale=k8[1], stream=stream)
         return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
 
     def vprep(cu):
         if fp8pv:  # V as transposed E4M3 tiles (changes every step, like q and k)
-            h3a.prepare_vt_e4m3(v, cu, out=vt8, stream=stream)
+            h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
 
     def attention(cu):
         if fp8pv:
@@ -557,8 +561,8 @@ def main():
     # q and k (H + Hkv heads; k only when fused) read and written, the table and gains read
     normed_heads = Hkv if fused else H + Hkv
     norm_bytes = 2 * (S * normed_heads * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + (1 if fused else 2) * D * 4
-    if fp8:  # the norm + rotary pass writes one byte per element instead of two
-        norm_bytes -= S * (H + Hkv) * D
+    if fp8:  # the norm + rotary pass writes one byte per element (and a scale per 32) instead of two
+        norm_bytes -= S * (H + Hkv) * D - S * (H + Hkv) * (D // 32)
     copy_src = torch.empty(norm_bytes // 2, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     copy_gbps = 2 * copy_src.numel() / timed(lambda: copy_dst.copy_(copy_src), n_ev) / 1e9

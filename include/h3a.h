@@ -276,56 +276,72 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
                                      float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
 /*
- * Low-precision attention, step 1: bf16 [S, H, D] (token stride stride_x
- * elements) to OCP FP8 E4M3 codes ("fn" variant: no infinities, largest
- * finite 448), one byte per element in y [S, H, D] (token stride stride_y
- * bytes, a multiple of 16).  Round to nearest even, saturating at +-448
- * (infinities included); a NaN becomes an E4M3 NaN code (0x7f, 0xff), so NaN
- * inputs stay NaN through the FP8 attention as through the bf16 one.
- * This quantises q' and k' for h3a_varlen_attn_fwd_fp8qk (the pages' GB10
- * builds run Q and K through low-precision attention kernels --
- * SageAttention 2++, Comfy Kitchen's INT8 attention -- after the Q RMSNorm +
- * rotary; h3-spark model card, runtime options and "What this config does").
- * Errors: EINVAL (null, sizes, overlap), ESHAPE, EUNSUPPORTED, EHIP.
+ * Low-precision attention: FP8 E4M3 codes with per-block scales.
+ *
+ * The pages' GB10 builds run Q, K and V through low-precision attention
+ * kernels quantised per block and calibrated on the activations themselves
+ * (SageAttention 2++, Comfy Kitchen's INT8 attention; h3-spark model card,
+ * runtime options and "What this config does"), after the Q RMSNorm + rot96
+ * rotary.  Here every block of 32 elements along the contraction of a product
+ * shares one power-of-two scale 2^X (an E8M0 code X + 127, one byte): 32 head
+ * dims of one token and head for q and k, 32 keys of one head dim for v (key
+ * blocks aligned at each segment's start).  X is the smallest integer with
+ * max|x| * 2^-X <= 448 over the block, so no finite element saturates; X =
+ * -127 for an all-zero block.  Each element is stored as the OCP FP8 E4M3
+ * ("fn") code of x * 2^-X, round to nearest even; infinities saturate to
+ * +-448 * 2^X and a NaN becomes an E4M3 NaN code (0x7f, 0xff), so NaN inputs
+ * stay NaN through the FP8 attention as through the bf16 one.  The gfx950
+ * scaled FP8 MFMA applies the scales inside the instruction.
+ *
+ * Scale arrays are caller-owned, packed and 2-byte (D = 64) or 4-byte
+ * (D = 128) aligned: q_scale [S][Hq][D/32], k_scale [S][Hk][D/32] (byte
+ * (n * H + h) * D/32 + b holds block b of token n, head h), and for the
+ * transposed V layout vt_scale [Hkv][vt_cols / 64][2][32][D/32] (block j of
+ * tile t, dim 32 b + r at [h][t][j][r][b]).
+ *
+ * h3a_quantize_e4m3: bf16 x [S, H, D] (token stride stride_x elements) to
+ *   codes y [S, H, D] (uint8, token stride stride_y bytes, a multiple of 16)
+ *   and y_scale [S][H][D/32].  Errors: EINVAL (null, sizes, overlap),
+ *   ESHAPE, EUNSUPPORTED, EHIP.
  */
-h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32_t D, int64_t stride_x,
-                             int64_t stride_y, hipStream_t stream);
+h3a_status h3a_quantize_e4m3(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                             int64_t stride_x, int64_t stride_y, hipStream_t stream);
 
 /*
- * Low-precision attention, steps 0 + 1 fused: h3a_qk_rmsnorm_rope_ex on bf16
- * q [S, Hq, D] and k [S, Hk, D] writing E4M3 codes q8 [S, Hq, D], k8
+ * Norm + rotary and quantisation in one HBM pass: h3a_qk_rmsnorm_rope_ex on
+ * bf16 q [S, Hq, D] and k [S, Hk, D] writing codes q8 [S, Hq, D], k8
  * [S, Hk, D] (uint8, token strides stride_q8, stride_k8 in bytes, multiples
- * of 16) instead of bf16: each result is rounded to bf16 and then to E4M3,
- * so the codes equal h3a_qk_rmsnorm_rope_ex followed by h3a_quantize_e4m3,
- * in one HBM pass (the GB10 build fuses Q RMSNorm + rot96 RoPE into its
+ * of 16) and scales q_scale, k_scale instead of bf16: each result is rounded
+ * to bf16 first, so codes and scales equal h3a_qk_rmsnorm_rope_ex followed by
+ * h3a_quantize_e4m3 (the GB10 build fuses Q RMSNorm + rot96 RoPE into its
  * attention's Q quantisation: h3-spark model card, "What this config does").
  * q and k are not modified.  Errors: as h3a_qk_rmsnorm_rope_ex (bf16 only).
  */
-h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t Hq,
-                                    int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_q8,
-                                    int64_t stride_k8, const float* gamma_q, const float* gamma_k, float eps,
-                                    const float* cos_sin, int32_t rot_dim, hipStream_t stream);
+h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, void* q_scale, void* k_scale,
+                                    int64_t S, int32_t Hq, int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k,
+                                    int64_t stride_q8, int64_t stride_k8, const float* gamma_q, const float* gamma_k,
+                                    float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
 /*
- * Low-precision attention, step 2: h3a_varlen_attn_fwd_ex with q and k given
- * as E4M3 codes.  The score product q.k runs on the FP8 MFMA (twice the bf16
- * rate) with fp32 accumulation; the softmax, the bf16 probabilities, the PV
- * product with bf16 v and the bf16 output are those of the bf16 path.
+ * h3a_varlen_attn_fwd_ex with q and k given as scaled E4M3 codes.  The score
+ * product q.k runs on the scaled FP8 MFMA (twice the bf16 rate) with fp32
+ * accumulation; the softmax, the bf16 probabilities, the PV product with
+ * bf16 v and the bf16 output are those of the bf16 path.
  *
- * q8             device uint8 [S, Hq, D] E4M3 codes, token stride stride_q
- *                bytes (a multiple of 16).
- * k8             device uint8 [S, Hkv, D] E4M3 codes, token stride stride_k
- *                bytes.
+ * q8, q_scale    device uint8 [S, Hq, D] codes (token stride stride_q bytes,
+ *                a multiple of 16) and their scales.
+ * k8, k_scale    device uint8 [S, Hkv, D] codes (token stride stride_k bytes)
+ *                and their scales.
  * v, o           device bf16 as for h3a_varlen_attn_fwd_ex.
- * The result equals attention on the E4M3-rounded q, k up to the bf16 path's
- * rounding; against exact attention on unrounded q, k it carries the E4M3
- * rounding of the scores (three mantissa bits per operand element).
- * Errors: as h3a_varlen_attn_fwd_ex.
+ * The result equals attention on the block-scaled E4M3 values of q, k up to
+ * the bf16 path's rounding.  Errors: as h3a_varlen_attn_fwd_ex, plus EINVAL /
+ * EUNSUPPORTED for null or misaligned scale arrays.
  */
-h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
-                                     int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
-                                     int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
-                                     int32_t causal, hipStream_t stream);
+h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                     const void* v, void* o, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                     const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal,
+                                     hipStream_t stream);
 
 /*
  * Low-precision attention with both products in FP8.  V goes through a
@@ -336,23 +352,28 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
  *
  * h3a_vt_e4m3_columns: vt_cols for cu_seqlens (host only).
  * h3a_prepare_vt_e4m3: bf16 v [S, Hkv, D] (token stride stride_v elements)
- *   -> vt8 (device, Hkv * D * vt_cols bytes, 16-byte aligned); nearest even,
- *   saturating at +-448, NaN to an E4M3 NaN code.
+ *   -> vt8 (device, Hkv * D * vt_cols bytes, 16-byte aligned) and vt_scale
+ *   (Hkv * vt_cols * D / 32 bytes), blocks of 32 keys of each segment.
  * h3a_varlen_attn_fwd_fp8: as h3a_varlen_attn_fwd_fp8qk, with V given as
- *   vt8; the probabilities are rounded to E4M3 for the PV product (which
- *   runs on FP8 MFMA with fp32 accumulation) and the row sum adds them in
- *   fp32.  Against attention on E4M3-rounded q, k, v with exact weights the
- *   result carries the E4M3 rounding of the weights.
+ *   vt8, vt_scale; the probabilities, offset by 2^4 against the running
+ *   reference so the largest weights stay in E4M3's normal range, are rounded
+ *   to E4M3 for the PV product (scaled FP8 MFMA, fp32 accumulation) and the
+ *   row sum adds exactly those weights.  Against attention on the block-scaled
+ *   E4M3 values of q, k, v with exact weights the result carries the E4M3
+ *   rounding of the weights.
  * Errors: as h3a_varlen_attn_fwd_fp8qk, plus ESHAPE for a vt_cols that does
  * not match cu_seqlens and EUNSUPPORTED when D * vt_cols exceeds INT32_MAX.
  */
 h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns);
-h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv, int32_t D, int64_t stride_v,
-                               int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream);
-h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int64_t S, int32_t Hq,
+h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, void* vt_scale, int64_t S, int32_t Hkv, int32_t D,
+                               int64_t stride_v, int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg,
+                               hipStream_t stream);
+h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                   const void* k_scale, const void* vt_scale, void* o, int64_t S, int32_t Hq,
                                    int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
                                    int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
                                    int32_t causal, hipStream_t stream);
+
 
 /*
  * Varlen attention with grouped K/V heads and an optional causal mask: the

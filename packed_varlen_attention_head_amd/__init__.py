@@ -99,14 +99,16 @@ def lib() -> ctypes.CDLL:
     L.h3a_rmsnorm_rope.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _vp, _f32, _vp, _i32, _vp]
     L.h3a_varlen_attn_fwd_qnorm.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
                                             _i64, _c_i32p, _i32, _f32, _vp, _f32, _vp, _i32, _vp]
-    L.h3a_qk_rmsnorm_rope_e4m3.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
-                                           _vp, _vp, _f32, _vp, _i32, _vp]
+    L.h3a_qk_rmsnorm_rope_e4m3.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
+                                           _i64, _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_vt_e4m3_columns.argtypes = [_c_i32p, _i32, _c_i64p]
-    L.h3a_prepare_vt_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _c_i32p, _i32, _vp]
-    L.h3a_varlen_attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+    L.h3a_prepare_vt_e4m3.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _c_i32p, _i32, _vp]
+    L.h3a_varlen_attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64,
+                                          _i64, _i64,
                                           _c_i32p, _i32, _f32, _i32, _vp]
-    L.h3a_quantize_e4m3.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
-    L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+    L.h3a_quantize_e4m3.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
+    L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64,
+                                            _i64, _i64,
                                             _c_i32p, _i32, _f32, _i32, _vp]
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
@@ -360,8 +362,28 @@ def varlen_attn_fwd_qnorm(q, k, v, cu_seqlens, scale: float, gamma_q, eps: float
     return out
 
 
-def quantize_e4m3(x, out=None, stream=None):
-    """bf16 [S, H, D] -> uint8 [S, H, D] OCP FP8 E4M3 codes (nearest even, saturating)."""
+# Low-precision operands are (codes, scales) pairs: uint8 E4M3 codes and one
+# uint8 E8M0 scale per 32 elements along the contraction -- [S, H, D // 32]
+# for q and k, [Hkv, vt_cols // 64, 2, 32, D // 32] for the transposed V.
+
+def _scales(name, t, shape, device):
+    """A scale array must be exactly the packed shape the kernels address."""
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=torch.uint8, device=device)
+    _expect(name, t, shape, torch.uint8)
+    return t
+
+
+def _pair(name, x):
+    if not (isinstance(x, (tuple, list)) and len(x) == 2):
+        raise H3AError(H3A_EINVAL, f"{name} must be a (codes, scales) pair")
+    return x[0], x[1]
+
+
+def quantize_e4m3(x, out=None, scale_out=None, stream=None):
+    """bf16 [S, H, D] -> (uint8 [S, H, D] E4M3 codes, uint8 [S, H, D // 32] block scales)."""
     import torch
 
     S, H, D, sx = _token_major("x", x)
@@ -372,13 +394,16 @@ def quantize_e4m3(x, out=None, stream=None):
     _, _, _, sy = _token_major("out", out)
     if tuple(out.shape) != (S, H, D) or out.dtype != torch.uint8:
         raise H3AError(H3A_ESHAPE, f"out must be uint8 {(S, H, D)}, got {out.dtype} {tuple(out.shape)}")
-    _check(lib().h3a_quantize_e4m3(x.data_ptr(), out.data_ptr(), S, H, D, sx, sy, _stream_handle(stream)))
-    return out
+    sc = _scales("scale_out", scale_out, (S, H, D // 32), x.device)
+    _check(lib().h3a_quantize_e4m3(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy,
+                                   _stream_handle(stream)))
+    return out, sc
 
 
 def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q8=None, k8=None,
-                         stream=None):
-    """Norm + rotary of bf16 q [S, Hq, D], k [S, Hk, D] written as uint8 E4M3 codes; returns (q8, k8)."""
+                         q_scale=None, k_scale=None, stream=None):
+    """Norm + rotary of bf16 q [S, Hq, D], k [S, Hk, D] written as block-scaled E4M3;
+    returns ((q8, q_scale), (k8, k_scale))."""
     import torch
 
     S, Hq, D, sq = _token_major("q", q)
@@ -393,11 +418,14 @@ def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: i
         raise H3AError(H3A_ESHAPE, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     _same("q8", q8, (S, Hq, D), torch.uint8)
     _same("k8", k8, (S, Hk, D), torch.uint8)
+    qs = _scales("q_scale", q_scale, (S, Hq, D // 32), q.device)
+    ks = _scales("k_scale", k_scale, (S, Hk, D // 32), q.device)
     cs = _table(cos_sin, S, int(rot_dim))
-    _check(lib().h3a_qk_rmsnorm_rope_e4m3(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k8.data_ptr(), S, Hq, Hk, D,
-                                          sq, sk, sq8, sk8, _gain("gamma_q", gamma_q, D), _gain("gamma_k", gamma_k, D),
+    _check(lib().h3a_qk_rmsnorm_rope_e4m3(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k8.data_ptr(), qs.data_ptr(),
+                                          ks.data_ptr(), S, Hq, Hk, D, sq, sk, sq8, sk8,
+                                          _gain("gamma_q", gamma_q, D), _gain("gamma_k", gamma_k, D),
                                           float(eps), cs, int(rot_dim), _stream_handle(stream)))
-    return q8, k8
+    return (q8, qs), (k8, ks)
 
 
 def vt_e4m3_columns(cu_seqlens) -> int:
@@ -408,8 +436,9 @@ def vt_e4m3_columns(cu_seqlens) -> int:
     return int(n.value)
 
 
-def prepare_vt_e4m3(v, cu_seqlens, out=None, stream=None):
-    """bf16 v [S, Hkv, D] -> uint8 [Hkv, D, vt_cols] transposed E4M3 codes (segment-padded)."""
+def prepare_vt_e4m3(v, cu_seqlens, out=None, scale_out=None, stream=None):
+    """bf16 v [S, Hkv, D] -> (uint8 [Hkv, D, vt_cols] transposed E4M3 codes, segment-padded;
+    uint8 [Hkv, vt_cols // 64, 2, 32, D // 32] block scales)."""
     import torch
 
     S, Hkv, D, sv = _token_major("v", v)
@@ -421,15 +450,18 @@ def prepare_vt_e4m3(v, cu_seqlens, out=None, stream=None):
         out = torch.empty((Hkv, D, max(cols, 1)), dtype=torch.uint8, device=v.device)
     # rows of exactly `cols` columns (one column when every segment is empty)
     _expect("out", out, (Hkv, D, max(cols, 1)), torch.uint8)
-    _check(lib().h3a_prepare_vt_e4m3(v.data_ptr(), out.data_ptr(), S, Hkv, D, sv, cols, _ptr_i32(cu), len(cu) - 1,
-                                     _stream_handle(stream)))
-    return out
+    sc = _scales("scale_out", scale_out, (Hkv, max(cols, 64) // 64, 2, 32, D // 32), v.device)
+    _check(lib().h3a_prepare_vt_e4m3(v.data_ptr(), out.data_ptr(), sc.data_ptr(), S, Hkv, D, sv, cols, _ptr_i32(cu),
+                                     len(cu) - 1, _stream_handle(stream)))
+    return out, sc
 
 
 def varlen_attn_fwd_fp8(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
-    """Attention with q8, k8 (uint8 E4M3 [S, H, D]) and vt8 from prepare_vt_e4m3; bf16 output."""
+    """Attention with q8, k8 (codes, scales) pairs [S, H, D] and vt8 (codes, scales) from
+    prepare_vt_e4m3; bf16 output."""
     import torch
 
+    (q8, qs), (k8, ks), (vt8, vs) = _pair("q8", q8), _pair("k8", k8), _pair("vt8", vt8)
     S, Hq, D, sq = _token_major("q8", q8)
     _, Hkv, _, sk = _token_major("k8", k8)
     if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
@@ -440,20 +472,24 @@ def varlen_attn_fwd_fp8(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = Fa
     cols = vt_e4m3_columns(cu)
     # the kernel addresses vt8 with exactly `cols` columns per row
     _expect("vt8", vt8, (Hkv, D, max(cols, 1)), torch.uint8)
+    qs = _scales("q_scale", qs, (S, Hq, D // 32), q8.device)
+    ks = _scales("k_scale", ks, (S, Hkv, D // 32), q8.device)
+    vs = _scales("vt_scale", vs, (Hkv, max(cols, 64) // 64, 2, 32, D // 32), q8.device)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q8.device)
     _, _, _, so = _token_major("out", out)
     _same("out", out, (S, Hq, D), torch.bfloat16)
-    _check(lib().h3a_varlen_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), out.data_ptr(), S, Hq, Hkv,
-                                         D, sq, sk, cols, so, _ptr_i32(cu), len(cu) - 1, float(scale),
-                                         int(bool(causal)), _stream_handle(stream)))
+    _check(lib().h3a_varlen_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+                                         vs.data_ptr(), out.data_ptr(), S, Hq, Hkv, D, sq, sk, cols, so, _ptr_i32(cu),
+                                         len(cu) - 1, float(scale), int(bool(causal)), _stream_handle(stream)))
     return out
 
 
 def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
-    """Attention with q8 [S, Hq, D] and k8 [S, Hkv, D] as uint8 E4M3 codes, v bf16 [S, Hkv, D]."""
+    """Attention with q8 [S, Hq, D] and k8 [S, Hkv, D] as (codes, scales) pairs, v bf16 [S, Hkv, D]."""
     import torch
 
+    (q8, qs), (k8, ks) = _pair("q8", q8), _pair("k8", k8)
     S, Hq, D, sq = _token_major("q8", q8)
     _, Hkv, _, sk = _token_major("k8", k8)
     _, _, _, sv = _token_major("v", v)
@@ -461,14 +497,16 @@ def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fa
         raise H3AError(H3A_EDTYPE, f"q8/k8 must hold uint8 E4M3 codes, got {q8.dtype}/{k8.dtype}")
     if tuple(k8.shape) != (S, Hkv, D) or tuple(v.shape) != (S, Hkv, D) or v.dtype != torch.bfloat16:
         raise H3AError(H3A_ESHAPE, f"k8 {tuple(k8.shape)} / v {tuple(v.shape)} {v.dtype} do not match q8")
+    qs = _scales("q_scale", qs, (S, Hq, D // 32), q8.device)
+    ks = _scales("k_scale", ks, (S, Hkv, D // 32), q8.device)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=v.device)
     _, _, _, so = _token_major("out", out)
     _same("out", out, (S, Hq, D), torch.bfloat16)
     cu = _i32_array(cu_seqlens)
-    _check(lib().h3a_varlen_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(), S, Hq, Hkv, D,
-                                           sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1, float(scale), int(bool(causal)),
-                                           _stream_handle(stream)))
+    _check(lib().h3a_varlen_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), qs.data_ptr(), ks.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
+                                           float(scale), int(bool(causal)), _stream_handle(stream)))
     return out
 
 

@@ -258,6 +258,23 @@ h3a_status check_cu_seqlens(const int32_t* cu, int32_t nseg, int64_t S) {
   return H3A_OK;
 }
 
+// A packed array of E8M0 block scales: `bytes` long, aligned to `align`
+// (the kernels read D / 32 scales of a row as one word).
+h3a_status check_scales(const char* name, const void* p, int64_t bytes, int64_t align) {
+  if (bytes == 0) return H3A_OK;
+  if (p == nullptr) return fail(H3A_EINVAL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % uintptr_t(align) != 0)
+    return fail(H3A_EUNSUPPORTED, "%s is not %lld-byte aligned", name, (long long)align);
+  return H3A_OK;
+}
+
+Range byte_range(const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + uintptr_t(bytes)};
+}
+
+bool ranges_hit(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
 // Argument checks shared by h3a_varlen_attn_fwd_ex and its allocation-free
 // variant: every error they report, before anything is launched.
 h3a_status check_attn_ex(const void* q, const void* k, const void* v, const void* o, h3a_dtype dtype, int64_t S,
@@ -673,8 +690,8 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
   }
 }
 
-h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32_t D, int64_t stride_x,
-                             int64_t stride_y, hipStream_t stream) {
+h3a_status h3a_quantize_e4m3(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                             int64_t stride_x, int64_t stride_y, hipStream_t stream) {
   try {
     if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
     if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
@@ -683,13 +700,18 @@ h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32
     h3a_status st;
     if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
     if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+    const int64_t sbytes = S * H * (D / 32);
+    if ((st = check_scales("y_scale", y_scale, sbytes, 1)) != H3A_OK) return st;
     if (S == 0) return H3A_OK;
     // y (bytes) against x (bf16): plain byte ranges.
     const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
     const uintptr_t x1 = x0 + uintptr_t(((S - 1) * stride_x + int64_t(H) * D) * 2);
     const uintptr_t y1 = y0 + uintptr_t((S - 1) * stride_y + int64_t(H) * D);
     if (x0 < y1 && y0 < x1) return fail(H3A_EINVAL, "y overlaps x");
-    hipError_t e = h3a::launch_quantize_e4m3(x, y, S, H * D, stride_x, stride_y, stream);
+    const Range rs = byte_range(y_scale, sbytes);
+    if (ranges_hit(rs, Range{x0, x1}) || ranges_hit(rs, Range{y0, y1}))
+      return fail(H3A_EINVAL, "y_scale overlaps x or y");
+    hipError_t e = h3a::launch_quantize_e4m3(x, y, y_scale, S, H * D, stride_x, stride_y, stream);
     if (e != hipSuccess) return fail_hip("quantize_e4m3 launch", e);
     return H3A_OK;
   } catch (...) {
@@ -697,10 +719,10 @@ h3a_status h3a_quantize_e4m3(const void* x, void* y, int64_t S, int32_t H, int32
   }
 }
 
-h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t Hq,
-                                    int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_q8,
-                                    int64_t stride_k8, const float* gamma_q, const float* gamma_k, float eps,
-                                    const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, void* q_scale, void* k_scale,
+                                    int64_t S, int32_t Hq, int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k,
+                                    int64_t stride_q8, int64_t stride_k8, const float* gamma_q, const float* gamma_k,
+                                    float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
   try {
     if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
     if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
@@ -717,6 +739,9 @@ h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void
     if ((st = check_operand("k", k, S, Hk, D, stride_k, 2)) != H3A_OK) return st;
     if ((st = check_operand("q8", q8, S, Hq, D, stride_q8, 1)) != H3A_OK) return st;
     if ((st = check_operand("k8", k8, S, Hk, D, stride_k8, 1)) != H3A_OK) return st;
+    const int64_t qsb = S * Hq * (D / 32), ksb = S * Hk * (D / 32);
+    if ((st = check_scales("q_scale", q_scale, qsb, 1)) != H3A_OK) return st;
+    if ((st = check_scales("k_scale", k_scale, ksb, 1)) != H3A_OK) return st;
     if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
     if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
     if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
@@ -732,8 +757,13 @@ h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void
     if (hit(rq8, rq) || hit(rq8, rk)) return fail(H3A_EINVAL, "q8 overlaps q or k");
     if (hit(rk8, rq) || hit(rk8, rk)) return fail(H3A_EINVAL, "k8 overlaps q or k");
     if (may_overlap(q8, stride_q8, Hq, k8, stride_k8, Hk, S, D, 1)) return fail(H3A_EINVAL, "q8 overlaps k8");
-    hipError_t e = h3a::launch_qk_rmsnorm_rope_e4m3(q, k, q8, k8, S, Hq, Hk, D, stride_q, stride_k, stride_q8,
-                                                    stride_k8, gamma_q, gamma_k, eps, cos_sin, rot_dim, stream);
+    const Range rqs = byte_range(q_scale, qsb), rks = byte_range(k_scale, ksb);
+    for (const Range& r : {rq, rk, rq8, rk8})
+      if (ranges_hit(rqs, r) || ranges_hit(rks, r)) return fail(H3A_EINVAL, "q_scale or k_scale overlaps a tensor");
+    if (ranges_hit(rqs, rks)) return fail(H3A_EINVAL, "q_scale overlaps k_scale");
+    hipError_t e = h3a::launch_qk_rmsnorm_rope_e4m3(q, k, q8, k8, q_scale, k_scale, S, Hq, Hk, D, stride_q, stride_k,
+                                                    stride_q8, stride_k8, gamma_q, gamma_k, eps, cos_sin, rot_dim,
+                                                    stream);
     if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope_e4m3 launch", e);
     return H3A_OK;
   } catch (...) {
@@ -741,10 +771,11 @@ h3a_status h3a_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void
   }
 }
 
-h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int64_t S, int32_t Hq,
-                                     int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t stride_v,
-                                     int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
-                                     int32_t causal, hipStream_t stream) {
+h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                     const void* v, void* o, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                     const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal,
+                                     hipStream_t stream) {
   try {
     if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
     if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
@@ -760,18 +791,24 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
     if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
     if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
     if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+    const int64_t qsb = S * Hq * (D / 32), ksb = S * Hkv * (D / 32);
+    if ((st = check_scales("q_scale", q_scale, qsb, D / 32)) != H3A_OK) return st;
+    if ((st = check_scales("k_scale", k_scale, ksb, D / 32)) != H3A_OK) return st;
     if (S == 0) return H3A_OK;
-    // o (bf16) against the byte-coded q and k, and against v (bf16)
+    // o (bf16) against the byte-coded q and k, their scales, and v (bf16)
     const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
     const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
     if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
     if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
+    if (ranges_hit(ro, byte_range(q_scale, qsb)) || ranges_hit(ro, byte_range(k_scale, ksb)))
+      return fail(H3A_EINVAL, "o overlaps q_scale or k_scale");
     if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
     if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev, plan.n,
-                                              scale, Hq / Hkv, causal != 0, stream);
+    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k, Hq * (D / 32),
+                                              Hkv * (D / 32), stride_v, stride_o, plan.dev, plan.n, scale, Hq / Hkv,
+                                              causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
     return H3A_OK;
   } catch (...) {
@@ -793,8 +830,9 @@ h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t*
   }
 }
 
-h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv, int32_t D, int64_t stride_v,
-                               int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream) {
+h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, void* vt_scale, int64_t S, int32_t Hkv, int32_t D,
+                               int64_t stride_v, int64_t vt_cols, const int32_t* cu_seqlens, int32_t nseg,
+                               hipStream_t stream) {
   try {
     if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
     if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
@@ -812,10 +850,14 @@ h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv,
     if (need == 0) return H3A_OK;
     if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
     if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+    const int64_t vsb = int64_t(Hkv) * vt_cols * (D / 32);
+    if ((st = check_scales("vt_scale", vt_scale, vsb, D / 32)) != H3A_OK) return st;
     const Range rv = tensor_range(v, S, Hkv, D, stride_v, 2);
     const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
     if (rv.lo < t1 && t0 < rv.hi) return fail(H3A_EINVAL, "vt8 overlaps v");
-    hipError_t e = h3a::launch_prepare_vt_e4m3(v, stride_v, cu_seqlens, nseg, Hkv, D, vt8, vt_cols, stream);
+    const Range rs = byte_range(vt_scale, vsb);
+    if (ranges_hit(rs, rv) || ranges_hit(rs, Range{t0, t1})) return fail(H3A_EINVAL, "vt_scale overlaps v or vt8");
+    hipError_t e = h3a::launch_prepare_vt_e4m3(v, stride_v, cu_seqlens, nseg, Hkv, D, vt8, vt_scale, vt_cols, stream);
     if (e != hipSuccess) return fail_hip("prepare_vt_e4m3 launch", e);
     return H3A_OK;
   } catch (...) {
@@ -823,7 +865,8 @@ h3a_status h3a_prepare_vt_e4m3(const void* v, void* vt8, int64_t S, int32_t Hkv,
   }
 }
 
-h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int64_t S, int32_t Hq,
+h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                   const void* k_scale, const void* vt_scale, void* o, int64_t S, int32_t Hq,
                                    int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
                                    int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
                                    int32_t causal, hipStream_t stream) {
@@ -847,6 +890,10 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
                   (long long)need);
     if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
       return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+    const int64_t qsb = S * Hq * (D / 32), ksb = S * Hkv * (D / 32), vsb = int64_t(Hkv) * vt_cols * (D / 32);
+    if ((st = check_scales("q_scale", q_scale, qsb, D / 32)) != H3A_OK) return st;
+    if ((st = check_scales("k_scale", k_scale, ksb, D / 32)) != H3A_OK) return st;
+    if ((st = check_scales("vt_scale", vt_scale, vsb, D / 32)) != H3A_OK) return st;
     if (S == 0) return H3A_OK;
     if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
     if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
@@ -856,11 +903,14 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
     if (ro.lo < rq.hi && rq.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps q");
     if (ro.lo < rk.hi && rk.lo < ro.hi) return fail(H3A_EINVAL, "o overlaps k");
     if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
+    for (const Range& r : {byte_range(q_scale, qsb), byte_range(k_scale, ksb), byte_range(vt_scale, vsb)})
+      if (ranges_hit(ro, r)) return fail(H3A_EINVAL, "o overlaps a scale array");
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
     if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, o, D, stride_q, stride_k, vt_cols, stride_o, plan.dev, plan.n,
-                                            scale, Hq / Hkv, causal != 0, stream);
+    hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, vt_scale, o, D, stride_q, stride_k,
+                                            Hq * (D / 32), Hkv * (D / 32), vt_cols, stride_o, plan.dev, plan.n, scale,
+                                            Hq / Hkv, causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
     return H3A_OK;
   } catch (...) {

@@ -56,19 +56,26 @@
 //     for the sum of squares, the same rotation FMAs and one RNE rounding),
 //     so q' -- and therefore the output -- is bit-identical to the unfused
 //     path.
-//   * Low-precision variants: F8 >= 1 takes Q and K as FP8 E4M3 codes and
-//     runs the score product on v_mfma_scale_f32_32x32x64_f8f6f4 (unit
-//     scales), at twice the bf16 MFMA rate, with K tiles of half the bytes.
-//     Each lane carries 32 consecutive dims of its key (A) and query (B) row
-//     per 64-dim step: the instruction pairs A and B elements by (lane half,
-//     byte), so any assignment shared by both operands contracts correctly.
+//   * Low-precision variants: F8 >= 1 takes Q and K as FP8 E4M3 codes with
+//     one power-of-two (E8M0) scale per 32 head dims of each token, and runs
+//     the score product on v_mfma_scale_f32_32x32x64_f8f6f4, which applies
+//     those scales inside the instruction (no VALU), at twice the bf16 MFMA
+//     rate, with K tiles of half the bytes.  The instruction numbers the 64
+//     contraction elements of a step so that byte b of a lane in half h is
+//     element 32 (b / 16) + 16 h + b % 16, and takes the scale of the block of
+//     32 elements starting at 32 j from the lane in half j: a lane therefore
+//     carries dims 16 h .. 16 h + 15 and 32 + 16 h .. +15 of its key (A) and
+//     query (B) row per 64-dim step, and supplies the scale of block 2 ks + h.
 //     F8 == 2 also runs PV in FP8: V arrives transposed (rows = dims, one
-//     64-key tile per segment-padded column block, E4M3), so the V^T operand
-//     is two plain 16-byte LDS reads, and the probabilities (rounded to
-//     E4M3) leave the score accumulator as the B operand after four lane-half
-//     swaps that give each half 32 consecutive keys.  The row sums are one
-//     more FP8 MFMA per tile with an all-ones A operand, so they add exactly
-//     the E4M3 weights PV applies.
+//     64-key tile per segment-padded column block, E4M3) with one scale per
+//     dim and 32-key block, so the V^T operand is two plain 16-byte LDS reads
+//     (keys 16 h .. +15 and 32 + 16 h .. +15) and one scale word per tile; the
+//     probabilities, offset by 2^4 against the running reference (which moves
+//     once a tile exceeds it by 2^4) so the weights of the largest scores stay
+//     in E4M3's normal range and below 448, leave the score accumulator as the
+//     B operand after four lane-half swaps that give each lane the same keys.
+//     The row sums are one more FP8 MFMA per tile with an all-ones A operand,
+//     so they add exactly the E4M3 weights PV applies; the 2^4 cancels.
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -94,6 +101,8 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
 [[maybe_unused]] constexpr int kBN = 64;  // keys per tile
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running max moves
+[[maybe_unused]] constexpr float kRescaleSlackF8 = 4.0f;  // E4M3 probabilities: 2^(4 + 4) = 256 <= 448
+[[maybe_unused]] constexpr float kProbOffsetF8 = 4.0f;    // E4M3 probabilities are 2^4 p
 [[maybe_unused]] constexpr float kSumBound = 8192.0f;   // bf16 steady state: bound on a lane's tile sum
 static_assert(kBM == kAttnBlockM_BF16, "plan block size must match the kernel");
 
@@ -164,6 +173,23 @@ __device__ __forceinline__ float pair_max(float x) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 x E4M3 with the E8M0 scales in
+// byte sel_a of sa (A rows) and byte sel_b of sb (B columns); the selectors
+// must be constants, so each value gets its own call.
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int sel_a, uint32_t sa, int sel_b,
+                                          uint32_t sb) {
+#define H3A_MF8(SA, SB) __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SA, int(sa), SB, int(sb))
+  switch (sel_a * 4 + sel_b) {
+    case 0: return H3A_MF8(0, 0);
+    case 10: return H3A_MF8(2, 2);
+    case 4: return H3A_MF8(1, 0);
+    case 8: return H3A_MF8(2, 0);
+    case 12: return H3A_MF8(3, 0);
+    default: return H3A_MF8(0, 0);
+  }
+#undef H3A_MF8
+}
+
 }  // namespace
 
 // Arguments of the fused Q norm + rotary (QNORM variant).
@@ -173,6 +199,19 @@ struct QNormArgs {
   int64_t S;             // rows of the table
   int32_t half;          // rot_dim / 2
   float eps;
+};
+
+// Per-block E8M0 scales of the FP8 operands (F8 >= 1): q [S][Hq][D/32] and
+// k [S][Hkv][D/32] (token strides q_stride, k_stride bytes); F8 == 2 also v
+// [Hkv][v_tiles][2][32][D/32] (dim 32 b + r of 32-key block j of a tile at
+// [j][r][b]).
+struct F8Scales {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  int32_t q_stride;
+  int32_t k_stride;
+  int32_t v_tiles;
 };
 
 namespace {
@@ -186,7 +225,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
                      int64_t sk, int64_t sv, int64_t so, const WorkItem* __restrict__ items,
-                     float c, int kv_group, QNormArgs qn) {
+                     float c, int kv_group, QNormArgs qn, F8Scales fs) {
   // The body uses LDS address-space pointers and gfx950-only builtins, which
   // exist only in the device pass; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -235,8 +274,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // Q as the B operand: lane holds query (qrow0 + l32), dims ks*16 + hi*8 .. +8.
   bf16x8 qb[KS];
-  // F8: lane holds query (qrow0 + l32), dims ks8*64 + hi*32 .. +32.
+  // F8: lane holds query (qrow0 + l32), dims ks8*64 + hi*16 .. +16 and
+  // ks8*64 + 32 + hi*16 .. +16; qsc: the row's scales, shifted so that byte
+  // 2 ks8 is block 2 ks8 + hi.
   [[maybe_unused]] i32x8 qb8[F8 ? KS8 : 1];
+  [[maybe_unused]] uint32_t qsc = 0;
+  const int kv_head = __builtin_amdgcn_readfirstlane(it.head / kv_group);
   if constexpr (F8 == 0) {
     const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq) * 2);
     const int off = (l32 * int(sq) + hi * 8) * 2;
@@ -246,13 +289,19 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   } else {
     const uint8_t* q8 = reinterpret_cast<const uint8_t*>(q);
     const auto rq = rows_rsrc(q8 + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq));
-    const int off = l32 * int(sq) + hi * 32;
+    const int off = l32 * int(sq) + hi * 16;
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) {
       const auto lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64, 0, 0);
-      const auto up = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64 + 16, 0, 0);
+      const auto up = __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 64 + 32, 0, 0);
       qb8[ks] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(up[0]), int(up[1]), int(up[2]), int(up[3])};
     }
+    // rows past the segment end read scale code 0 (their codes are 0 too)
+    const auto rqs = rows_rsrc(fs.q + (int64_t(it.seg_start) + qrow0) * fs.q_stride + it.head * (D / 32),
+                               it.seg_len - qrow0, 32, fs.q_stride);
+    const uint32_t w = D == 128 ? __builtin_amdgcn_raw_buffer_load_b32(rqs, l32 * fs.q_stride, 0, 0)
+                                : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rqs, l32 * fs.q_stride, 0, 0));
+    qsc = w >> (8 * hi);
   }
   // QNORM operands (the gain of each of the lane's dims, cos/sin of its
   // rotated pairs) load together with Q, so their latency overlaps; the
@@ -376,18 +425,18 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   int kaddr[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ k_swz<D>(l32)) * 16);
-  // F8 K operand reads: row l32 (+32 kb), chunks 4 ks8 + 2 hi + {0, 1}.
+  // F8 K operand reads: row l32 (+32 kb), chunks 4 ks8 + hi + {0, 2}.
   [[maybe_unused]] int kaddr8[F8 ? KS8 : 1][2];
   if constexpr (F8)
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) kaddr8[ks][j] = l32 * KROWB + (((4 * ks + 2 * hi + j) ^ k8_swz<D>(l32)) * 16);
+      for (int j = 0; j < 2; ++j) kaddr8[ks][j] = l32 * KROWB + (((4 * ks + hi + 2 * j) ^ k8_swz<D>(l32)) * 16);
   // V^T operand reads (transposing): 16-lane group g reads keys
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
   int vaddr[DB];
-  // F8 == 2 V^T operand reads: row db*32 + l32, chunks 2 hi + {0, 1}.
+  // F8 == 2 V^T operand reads: row db*32 + l32, chunks hi + {0, 2}.
   [[maybe_unused]] int vaddr8[F8 == 2 ? DB : 1][2];
   if constexpr (F8 == 2)
 #pragma unroll
@@ -395,7 +444,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = db * 32 + l32;
-        vaddr8[db][j] = row * 64 + (((2 * hi + j) ^ ((row >> 2) & 3)) * 16);
+        vaddr8[db][j] = row * 64 + (((hi + 2 * j) ^ ((row >> 2) & 3)) * 16);
       }
   {
     const int g = lane >> 4, m = lane & 15;
@@ -417,6 +466,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   [[maybe_unused]] const int tdiag = it.q_start / kBN;
 
   // ---- building blocks ------------------------------------------------------
+  // F8: per ring slot, the scales of the K tile's keys 32 kb + l32 (loaded
+  // with the tile) and, F8 == 2, of the V^T tile's dims for key block hi.
+  [[maybe_unused]] uint32_t ksc[2][2] = {{0u, 0u}, {0u, 0u}};
+  [[maybe_unused]] uint32_t vsc[2] = {0u, 0u};
+  auto put = [](auto slot, uint32_t* s0, uint32_t* s1, int i, uint32_t w) {
+    if constexpr (std::is_integral_v<decltype(slot)>) {
+      if (slot) s1[i] = w;
+      else s0[i] = w;
+    } else {
+      (decltype(slot)::value ? s1 : s0)[i] = w;
+    }
+  };
+  auto get = [](auto slot, const uint32_t* s0, const uint32_t* s1, int i) -> uint32_t {
+    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? s1[i] : s0[i];
+    else return (decltype(slot)::value ? s1 : s0)[i];
+  };
   auto load_k = [&](int t, auto slot) {
     const int key0 = t * kBN;
     const auto r = rows_rsrc(kbase + int64_t(key0) * sk * KESZ, it.seg_len - key0, kBN, int(sk) * KESZ);
@@ -424,6 +489,18 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int i = 0; i < NDMAK; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                koff[i], 0, 0, 0);
+    if constexpr (F8 >= 1) {
+      // keys past the segment end read scale code 0 (their codes are 0 too)
+      const auto rs = rows_rsrc(fs.k + (int64_t(it.seg_start) + key0) * fs.k_stride + kv_head * (D / 32),
+                                it.seg_len - key0, kBN, fs.k_stride);
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        const int off = (32 * kb + l32) * fs.k_stride;
+        const uint32_t w = D == 128 ? __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)
+                                    : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
+        put(slot, ksc[0], ksc[1], kb, w);
+      }
+    }
   };
   auto load_v = [&](int t, auto slot) {
     const int key0 = t * kBN;
@@ -440,6 +517,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int i = 0; i < NDMAV8; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                  voff[i], 0, 0, 0);
+      // the tile's scales, lane (l32, hi): dims 32 b + l32 of key block hi, byte b
+      const uint8_t* vs =
+          fs.v + ((int64_t(kv_head) * fs.v_tiles + it.vt_col0 / kVtTile + t) * 64 + hi * 32 + l32) * (D / 32);
+      const uint32_t w = D == 128 ? *reinterpret_cast<const uint32_t*>(vs)
+                                  : uint32_t(*reinterpret_cast<const uint16_t*>(vs));
+      put(slot, vsc, vsc + 1, 0, w);
     }
   };
   // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
@@ -472,14 +555,15 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
+      // byte 2 ks of either scale word: block 2 ks + hi of the row
+      const uint32_t ks_w = get(slot, ksc[0], ksc[1], kb) >> (8 * hi);
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks) {
         const LDS char* kp = (const LDS char*)kslot(slot) + kb * 32 * KROWB;
         const uint4 lo = *(const LDS uint4*)(kp + kaddr8[ks][0]);
         const uint4 up = *(const LDS uint4*)(kp + kaddr8[ks][1]);
         const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
-        // formats 0/0: E4M3 x E4M3; E8M0 scales 127 = 1.0
-        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qb8[ks], sacc[kb], 0, 0, 0, 127, 0, 127);
+        sacc[kb] = mfma_f8(a, qb8[ks], sacc[kb], 2 * ks, ks_w, 2 * ks, qsc);
       }
     }
   };
@@ -512,7 +596,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = pair_max(mx) * c;
-    const bool grow = mx > m_run + kRescaleSlack;
+    const bool grow = mx > m_run + (F8 == 2 ? kRescaleSlackF8 : kRescaleSlack);
     if (__builtin_expect(__any(grow), 0)) {
       // Rare after the first tiles; the empty asm keeps the compiler from
       // speculating the accumulator rescale onto every tile.
@@ -578,25 +662,28 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   auto probs = [&](const f32x16* sacc, bf16x8* pb) {
     if constexpr (F8 == 2) {
-      // E4M3 probabilities (p <= 2^8, inside E4M3's range), dword g = keys
-      // 8g + 4 hi + {0..3}.
+      // E4M3 weights 2^4 p (p <= 2^4 against the reference, so <= 256), dword
+      // g = keys 8g + 4 hi + {0..3}.
+      const float moff = kProbOffsetF8 - m_run;
       int d[8];
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         float p4[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, -m_run));
+        for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, moff));
         // bytes 2-3 of the first conversion's destination are overwritten by
         // the second, so any value serves as its prior contents
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], __builtin_bit_cast(int, p4[0]), false);
         d[g] = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
       }
-      // Swap dwords 4..7 of the low half with dwords 0..3 of the high half:
-      // afterwards B dword m of either half holds keys 32 hi + 4 m + {0..3}.
+      // Swap dwords 2, 3, 6, 7 of the low half with dwords 0, 1, 4, 5 of the
+      // high half: afterwards B dword m of half hi holds keys
+      // 32 (m / 4) + 16 hi + 4 (m % 4) + {0..3}, the instruction's numbering.
       int b[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(d[i], d[4 + i], false, false);
+        const int x = (i / 2) * 4 + i % 2;  // 0, 1, 4, 5
+        const auto sw = __builtin_amdgcn_permlane32_swap(d[x], d[x + 2], false, false);
         b[2 * i] = sw[0];
         b[2 * i + 1] = sw[1];
       }
@@ -611,13 +698,14 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if constexpr (F8 == 2) {
       const int4 b0 = __builtin_bit_cast(int4, pb[0]), b1 = __builtin_bit_cast(int4, pb[1]);
       const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const uint32_t vs_w = get(slot, vsc, vsc + 1, 0);  // byte db: dim block db, key block hi
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const LDS char* vp = (const LDS char*)vslot(slot);
         const uint4 lo = *(const LDS uint4*)(vp + vaddr8[db][0]);
         const uint4 up = *(const LDS uint4*)(vp + vaddr8[db][1]);
         const i32x8 a = {int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(up.x), int(up.y), int(up.z), int(up.w)};
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, oacc[db], 0, 0, 0, 127, 0, 127);
+        oacc[db] = mfma_f8(a, b, oacc[db], db, vs_w, 0, 127u);
       }
       lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, b, lacc, 0, 0, 0, 127, 0, 127);
       return;
@@ -747,12 +835,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 template <int D, bool CAUSAL, bool QNORM = false, int RH = 0, int F8 = 0>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                  int kv_group, const QNormArgs& qn, hipStream_t stream) {
+                  int kv_group, const QNormArgs& qn, hipStream_t stream, const F8Scales& fs = F8Scales{}) {
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QNORM, RH, F8>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c,
-                     kv_group, qn);
+                     kv_group, qn, fs);
   return hipGetLastError();
 }
 
@@ -774,35 +862,40 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int32_t D, int64_t sq,
-                                 int64_t sk, int64_t sv, int64_t so, const WorkItem* items, int64_t n_items,
-                                 float scale, int32_t kv_group, bool causal, hipStream_t stream) {
+hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
+                                 void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks, int64_t sv,
+                                 int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
+                                 bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
   const QNormArgs none{};
+  const F8Scales fs{static_cast<const uint8_t*>(q8s), static_cast<const uint8_t*>(k8s), nullptr, sqs, sks, 0};
 #define H3A_F8_CASE(DD)                                                                                     \
   if (D == DD)                                                                                              \
     return causal ? launch<DD, true, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,        \
-                                                  kv_group, none, stream)                                  \
+                                                  kv_group, none, stream, fs)                              \
                   : launch<DD, false, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,       \
-                                                   kv_group, none, stream);
+                                                   kv_group, none, stream, fs);
   H3A_F8_CASE(128) H3A_F8_CASE(64)
 #undef H3A_F8_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int32_t D, int64_t sq,
-                               int64_t sk, int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items,
-                               float scale, int32_t kv_group, bool causal, hipStream_t stream) {
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
+                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks,
+                               int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
+                               int32_t kv_group, bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
   const QNormArgs none{};
+  const F8Scales fs{static_cast<const uint8_t*>(q8s), static_cast<const uint8_t*>(k8s),
+                    static_cast<const uint8_t*>(vt8s), sqs, sks, int32_t(vt_cols / kVtTile)};
 #define H3A_F8PV_CASE(DD)                                                                                   \
   if (D == DD)                                                                                              \
     return causal ? launch<DD, true, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale, \
-                                                  kv_group, none, stream)                                  \
+                                                  kv_group, none, stream, fs)                              \
                   : launch<DD, false, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale,\
-                                                   kv_group, none, stream);
+                                                   kv_group, none, stream, fs);
   H3A_F8PV_CASE(128) H3A_F8PV_CASE(64)
 #undef H3A_F8PV_CASE
   return hipErrorInvalidValue;

@@ -82,39 +82,47 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
                                       const float* gamma_q, float eps, const float* cos_sin, int64_t S,
                                       int32_t rot_dim, hipStream_t stream);
 
-// Attention whose q and k are FP8 E4M3 codes (token strides in bytes); the
-// score product runs on FP8 MFMA, the rest as launch_attn_fwd_bf16.
-hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* v, void* o, int32_t D, int64_t sq,
-                                 int64_t sk, int64_t sv, int64_t so, const WorkItem* items, int64_t n_items,
-                                 float scale, int32_t kv_group, bool causal, hipStream_t stream);
+// Attention whose q and k are FP8 E4M3 codes (token strides in bytes) with
+// one E8M0 scale per 32 head dims (q8s [S][Hq][D/32], k8s [S][Hkv][D/32];
+// token strides sqs, sks bytes); the score product runs on the scaled FP8
+// MFMA, the rest as launch_attn_fwd_bf16.
+hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
+                                 void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks, int64_t sv,
+                                 int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
+                                 bool causal, hipStream_t stream);
 
 // The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
-// token strides sq8, sk8 in bytes).
-hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t H,
-                                       int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8, int64_t sk8,
-                                       const float* gq, const float* gk, float eps, const float* cos_sin,
-                                       int32_t rot_dim, hipStream_t stream);
+// token strides sq8, sk8 in bytes) with one E8M0 scale per 32 head dims in
+// q8s [S][H][D/32], k8s [S][Hk][D/32].
+hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, void* q8s, void* k8s,
+                                       int64_t S, int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk,
+                                       int64_t sq8, int64_t sk8, const float* gq, const float* gk, float eps,
+                                       const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
-// Attention with q, k as E4M3 codes and V as the transposed E4M3 layout of
-// launch_prepare_vt_e4m3 (row length vt_cols bytes); both products on FP8
-// MFMA.
-hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, void* o, int32_t D, int64_t sq,
-                               int64_t sk, int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items,
-                               float scale, int32_t kv_group, bool causal, hipStream_t stream);
+// Attention with q, k as scaled E4M3 codes (as launch_attn_fwd_fp8qk) and V
+// as the transposed E4M3 layout of launch_prepare_vt_e4m3 (row length vt_cols
+// bytes, scales vt8s); both products on the scaled FP8 MFMA.
+hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
+                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks,
+                               int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
+                               int32_t kv_group, bool causal, hipStream_t stream);
 
 // Columns of the transposed E4M3 V layout: every segment padded to whole
 // kVtTile-key tiles.
 int64_t vt_e4m3_columns(const int32_t* cu, int32_t nseg);
 
 // bf16 v [S, H, D] (token stride sv elements) -> vt [H][D][vt_cols] E4M3
-// codes, segment s at columns from the padded prefix sum, padding zeroed.
+// codes, segment s at columns from the padded prefix sum, padding zeroed;
+// one E8M0 scale per head dim and 32-key block in vs
+// [H][vt_cols / 64][2][32][D / 32] (dim 32 b + r, block j at [j][r][b]).
 hipError_t launch_prepare_vt_e4m3(const void* v, int64_t sv, const int32_t* cu, int32_t nseg, int32_t H, int32_t D,
-                                  void* vt, int64_t vt_cols, hipStream_t stream);
+                                  void* vt, void* vs, int64_t vt_cols, hipStream_t stream);
 
 // bf16 [S, row_elems] rows (token stride sx elements) -> E4M3 codes (token
-// stride sy bytes); row_elems a multiple of 8.
-hipError_t launch_quantize_e4m3(const void* x, void* y, int64_t S, int32_t row_elems, int64_t sx, int64_t sy,
-                                hipStream_t stream);
+// stride sy bytes) with one E8M0 scale per 32 consecutive elements in ys
+// [S][row_elems / 32]; row_elems a multiple of 32.
+hipError_t launch_quantize_e4m3(const void* x, void* y, void* ys, int64_t S, int32_t row_elems, int64_t sx,
+                                int64_t sy, hipStream_t stream);
 
 hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,
                                int64_t sq, int64_t sk, int64_t sv, int64_t so,

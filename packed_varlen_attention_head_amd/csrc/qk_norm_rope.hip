@@ -24,11 +24,14 @@
 //     the quantisation that the low-precision attention consumes (h3-spark
 //     model card, "What this config does": the Q RMSNorm + rot96 RoPE fused
 //     into SageAttention's Q quantisation).  Each value is rounded to bf16
-//     first, so the codes equal those of the bf16 pass followed by the
-//     separate quantiser.
+//     first and every block of 32 head dims shares one power-of-two scale
+//     (mx_scale.h; the four lanes of a block exchange their maxima), so the
+//     codes and scales equal those of the bf16 pass followed by the separate
+//     quantiser.
 #include <cstdint>
 
 #include "common.h"
+#include "mx_scale.h"
 
 namespace h3a {
 namespace {
@@ -72,15 +75,23 @@ struct Elem<Bf16Tag> {
   __device__ static uint4 pack(const float* y) {
     return make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
   }
-  // bf16 rounding, then E4M3 (nearest even, saturating at +-448; a NaN stays
-  // NaN, which fminf/fmaxf alone would turn into -448).
-  __device__ static uint2 pack_e4m3(const float* y) {
+  // bf16 rounding, then E4M3 codes of the values times 2^-X, X the scale
+  // exponent of the lane's 32-dim block (shared with its three neighbours);
+  // returns the codes and leaves X in *X.
+  __device__ static uint2 pack_e4m3(const float* y, int* X) {
     float b[8];
+    float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float r = float(__bf16(y[e]));
-      b[e] = r != r ? r : fminf(fmaxf(r, -448.0f), 448.0f);
+      b[e] = float(__bf16(y[e]));
+      amax = abs_max(amax, b[e]);
     }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    *X = mx_exponent(amax);
+    const float inv = mx_inv_scale(*X);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = e4m3_sat(b[e] * inv);
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[0], b[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(b[2], b[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(b[4], b[5], 0, false);
@@ -95,9 +106,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWavesPerBlock = 4;
 constexpr int kBatch = 8;  // head vectors a lane keeps in flight
 
+// F8OUT: dst_scale [S][H][D / 32] E8M0 codes (token stride H * D / 32 bytes).
 template <typename T, int D, bool F8OUT>
-__device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, int64_t stride_b,
-                                              int64_t stride_ob, int32_t token, int32_t H,
+__device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, uint8_t* dst_scale,
+                                              int64_t stride_b, int64_t stride_ob, int32_t token, int32_t H,
                                               const float* g, const float* c, const float* s, int role,
                                               int partner, float eps, int lane) {
   constexpr int V = Elem<T>::V;
@@ -139,8 +151,10 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
         // Streaming (non-temporal) stores: the outputs are not re-read by
         // this pass; measured 14% faster than ordinary stores at S = 20,423.
         if constexpr (F8OUT) {
-          const uint2 pk = Elem<T>::pack_e4m3(out);
+          int X = 0;
+          const uint2 pk = Elem<T>::pack_e4m3(out, &X);
           __builtin_nontemporal_store(u32x2{pk.x, pk.y}, reinterpret_cast<u32x2*>(orow + int64_t(h) * D));
+          if ((sub & 3) == 0) dst_scale[(int64_t(token) * H + h) * (D / 32) + sub / 4] = uint8_t(X + 127);
         } else {
           const uint4 pk = Elem<T>::pack(out);
           __builtin_nontemporal_store(u32x4{pk.x, pk.y, pk.z, pk.w},
@@ -153,8 +167,8 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
 
 template <typename T, int D, bool F8OUT = false>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq_b, int64_t sk_b,
-                    int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H, int32_t Hk,
+qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, uint8_t* qos, uint8_t* kos, int64_t sq_b,
+                    int64_t sk_b, int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H, int32_t Hk,
                     const float* __restrict__ gq, const float* __restrict__ gk, float eps,
                     const float* __restrict__ cos_sin, int32_t rot_dim) {
   constexpr int V = Elem<T>::V;
@@ -190,8 +204,8 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq
     g_q[e] = gq[d0 + e];
     g_k[e] = gk[d0 + e];
   }
-  norm_rope_one<T, D, F8OUT>(q, qo, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
-  norm_rope_one<T, D, F8OUT>(k, ko, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(q, qo, qos, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(k, ko, kos, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
 }
 
 // Strides in elements of the input type; with F8OUT the output strides are
@@ -199,13 +213,15 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, int64_t sq
 template <typename T, int D, bool F8OUT = false>
 hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int32_t Hk, int64_t sq,
                   int64_t sk, int64_t sqo, int64_t sko, const float* gq, const float* gk, float eps,
-                  const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+                  const float* cos_sin, int32_t rot_dim, hipStream_t stream, void* qos = nullptr,
+                  void* kos = nullptr) {
   constexpr int esz = 16 / Elem<T>::V;
   constexpr int oesz = F8OUT ? 1 : esz;
   const unsigned blocks = unsigned((S + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, F8OUT>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
                      static_cast<const char*>(q), static_cast<const char*>(k), static_cast<char*>(qo),
-                     static_cast<char*>(ko), sq * esz, sk * esz, sqo * oesz, sko * oesz, int32_t(S), H, Hk, gq,
+                     static_cast<char*>(ko), static_cast<uint8_t*>(qos), static_cast<uint8_t*>(kos), sq * esz,
+                     sk * esz, sqo * oesz, sko * oesz, int32_t(S), H, Hk, gq,
                      gk, eps, cos_sin, rot_dim);
   return hipGetLastError();
 }
@@ -231,14 +247,16 @@ hipError_t launch_qk_rmsnorm_rope(bool bf16, const void* q, const void* k, void*
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, int64_t S, int32_t H,
-                                       int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8, int64_t sk8,
-                                       const float* gq, const float* gk, float eps, const float* cos_sin,
-                                       int32_t rot_dim, hipStream_t stream) {
+hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, void* q8s, void* k8s,
+                                       int64_t S, int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk,
+                                       int64_t sq8, int64_t sk8, const float* gq, const float* gk, float eps,
+                                       const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
   if (D == 128)
-    return launch<Bf16Tag, 128, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream);
+    return launch<Bf16Tag, 128, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream,
+                                      q8s, k8s);
   if (D == 64)
-    return launch<Bf16Tag, 64, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream);
+    return launch<Bf16Tag, 64, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream,
+                                     q8s, k8s);
   return hipErrorInvalidValue;
 }
 

@@ -267,11 +267,13 @@ def test_rmsnorm_rope_rejects(kw, status, word):
     (dict(sy=264), h3a.H3A_EUNSUPPORTED, "multiple of 16 bytes"),
     (dict(y=P + 256), h3a.H3A_EINVAL, "y overlaps x"),
     (dict(y=None), h3a.H3A_EINVAL, "y is NULL"),
+    (dict(ys=None), h3a.H3A_EINVAL, "y_scale is NULL"),
+    (dict(ys=P + (1 << 24) + 4000), h3a.H3A_EINVAL, "y_scale overlaps"),
 ])
 def test_quantize_e4m3_rejects(kw, status, word):
     H, D = kw.get("H", 2), kw.get("D", 128)
-    st = h3a.lib().h3a_quantize_e4m3(P, kw.get("y", P + (1 << 24)), 16, H, D, max(H, 1) * D, kw.get("sy", max(H, 1) * D),
-                                     None)
+    st = h3a.lib().h3a_quantize_e4m3(P, kw.get("y", P + (1 << 24)), kw.get("ys", P + (2 << 24)), 16, H, D,
+                                     max(H, 1) * D, kw.get("sy", max(H, 1) * D), None)
     assert st == status
     assert word in h3a.last_error(), h3a.last_error()
 
@@ -283,11 +285,15 @@ def test_quantize_e4m3_rejects(kw, status, word):
     (dict(sk=64), h3a.H3A_ESHAPE, "k: token stride"),
     (dict(o=P + 512), h3a.H3A_EINVAL, "o overlaps q"),
     (dict(D=80), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(qs=None), h3a.H3A_EINVAL, "q_scale is NULL"),
+    (dict(ks=P + (5 << 24) + 2), h3a.H3A_EUNSUPPORTED, "k_scale is not 4-byte aligned"),
+    (dict(qs=P + (3 << 24) + 64), h3a.H3A_EINVAL, "o overlaps q_scale"),
 ])
 def test_varlen_attn_fwd_fp8qk_rejects(kw, status, word):
     Hq, Hkv, D = 8, kw.get("Hkv", 2), kw.get("D", 128)
     c, cp = i32((0, 100, 300))
-    st = h3a.lib().h3a_varlen_attn_fwd_fp8qk(P, P + (1 << 24), P + (2 << 24), kw.get("o", P + (3 << 24)), 300, Hq, Hkv,
+    st = h3a.lib().h3a_varlen_attn_fwd_fp8qk(P, P + (1 << 24), kw.get("qs", P + (4 << 24)), kw.get("ks", P + (5 << 24)),
+                                             P + (2 << 24), kw.get("o", P + (3 << 24)), 300, Hq, Hkv,
                                              D, kw.get("sq", Hq * D), kw.get("sk", Hkv * D), Hkv * D, Hq * D, cp, 2,
                                              0.088, kw.get("causal", 0), None)
     assert st == status
@@ -300,13 +306,50 @@ def test_varlen_attn_fwd_fp8qk_rejects(kw, status, word):
     (dict(sq8=100), h3a.H3A_ESHAPE, "q8: token stride"),
     (dict(q8=P + 512), h3a.H3A_EINVAL, "q8 overlaps"),
     (dict(cs=None), h3a.H3A_EINVAL, "cos_sin"),
+    (dict(ks=None), h3a.H3A_EINVAL, "k_scale is NULL"),
+    (dict(qs=P + (2 << 24) + 8), h3a.H3A_EINVAL, "q_scale or k_scale overlaps"),
+    (dict(ks=P + (7 << 24) + 100), h3a.H3A_EINVAL, "q_scale overlaps k_scale"),
 ])
 def test_qk_rmsnorm_rope_e4m3_rejects(kw, status, word):
     Hq, Hk, D = 8, kw.get("Hk", 2), 128
-    st = h3a.lib().h3a_qk_rmsnorm_rope_e4m3(P, P + (1 << 24), kw.get("q8", P + (2 << 24)), P + (3 << 24), 16, Hq, Hk,
+    st = h3a.lib().h3a_qk_rmsnorm_rope_e4m3(P, P + (1 << 24), kw.get("q8", P + (2 << 24)), P + (3 << 24),
+                                            kw.get("qs", P + (7 << 24)), kw.get("ks", P + (8 << 24)), 16, Hq, Hk,
                                             D, Hq * D, max(Hk, 1) * D, kw.get("sq8", Hq * D), max(Hk, 1) * D,
                                             P + (4 << 24), P + (5 << 24), 1e-6, kw.get("cs", P + (6 << 24)),
                                             kw.get("rot", 96), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(cols=320), h3a.H3A_ESHAPE, "vt_cols = 320"),
+    (dict(vt=P + (1 << 24) + 8), h3a.H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned"),
+    (dict(vs=None), h3a.H3A_EINVAL, "vt_scale is NULL"),
+    (dict(vs=P + (2 << 24) + 1), h3a.H3A_EUNSUPPORTED, "vt_scale is not 4-byte aligned"),
+    (dict(vs=P + (1 << 24) + 4096), h3a.H3A_EINVAL, "vt_scale overlaps v or vt8"),
+])
+def test_prepare_vt_e4m3_rejects(kw, status, word):
+    Hkv, D = 2, 128
+    c, cp = i32((0, 100, 300))  # 128 + 256 padded columns
+    st = h3a.lib().h3a_prepare_vt_e4m3(P, kw.get("vt", P + (1 << 24)), kw.get("vs", P + (2 << 24)), 300, Hkv, D,
+                                       Hkv * D, kw.get("cols", 384), cp, 2, None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(cols=448), h3a.H3A_ESHAPE, "vt_cols = 448"),
+    (dict(vs=None), h3a.H3A_EINVAL, "vt_scale is NULL"),
+    (dict(qs=P + (4 << 24) + 1), h3a.H3A_EUNSUPPORTED, "q_scale is not 4-byte aligned"),
+    (dict(vs=P + (3 << 24) + 256), h3a.H3A_EINVAL, "o overlaps a scale array"),
+    (dict(vt=None), h3a.H3A_EINVAL, "vt8 is NULL"),
+])
+def test_varlen_attn_fwd_fp8_rejects(kw, status, word):
+    Hq, Hkv, D = 8, 2, 128
+    c, cp = i32((0, 100, 300))
+    st = h3a.lib().h3a_varlen_attn_fwd_fp8(P, P + (1 << 24), kw.get("vt", P + (2 << 24)), kw.get("qs", P + (4 << 24)),
+                                           P + (5 << 24), kw.get("vs", P + (6 << 24)), P + (3 << 24), 300, Hq, Hkv, D,
+                                           Hq * D, Hkv * D, kw.get("cols", 384), Hq * D, cp, 2, 0.088, 0, None)
     assert st == status
     assert word in h3a.last_error(), h3a.last_error()
 

@@ -98,20 +98,21 @@ def row_abs_dot_max(qf, kf, cu, causal):
 
 
 def test_rising_logits_fp8_scores():
-    """FP8 score product, bf16 probabilities: against attention on E4M3 q, k."""
+    """FP8 score product, bf16 probabilities: against attention on block-rounded q, k."""
     D, H = 128, 2
     cu, q, k, v = rising_inputs(31, H, H, D)
     log("[rising] fp8 scores")
     qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
     o = to_f64(h3a().varlen_attn_fwd_fp8qk(h3a().quantize_e4m3(qd), h3a().quantize_e4m3(kd), vd, cu, 1.0 / np.sqrt(D)))
     qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
-    compare(o, oracle.varlen_attention_fp8qk(qf, kf, vf, cu, 1.0 / np.sqrt(D)), "bf16", "o vs E4M3 oracle")
+    compare(o, oracle.varlen_attention_mx_qk(qf, kf, vf, cu, 1.0 / np.sqrt(D)), "bf16", "o vs block-scaled oracle")
 
 
 def test_rising_logits_fp8_both():
-    """Both products in FP8: within the E4M3 weight-rounding bound of attention on E4M3
-    q, k, v (2^-4 attention on |v|, plus the bf16 path's tolerance)."""
-    from tests.gpu_util import TOL_BF16_ABS
+    """Both products in FP8: within the bound of rounding the weights to E4M3, against
+    attention on block-rounded q, k, v.  The rising keys make the running reference
+    climb many times per row, so every rescale of the FP8 accumulators is crossed."""
+    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, mx_operands, weight_rounding_bound
 
     D, H = 128, 2
     cu, q, k, v = rising_inputs(41, H, H, D)
@@ -119,15 +120,8 @@ def test_rising_logits_fp8_both():
     qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
     o = to_f64(h3a().varlen_attn_fwd_fp8(h3a().quantize_e4m3(qd), h3a().quantize_e4m3(kd),
                                          h3a().prepare_vt_e4m3(vd, cu), cu, 1.0 / np.sqrt(D)))
-    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
-    ref = oracle.varlen_attention_fp8(qf, kf, vf, cu, 1.0 / np.sqrt(D))
-    ref_abs = oracle.varlen_attention_fp8(qf, kf, np.abs(vf), cu, 1.0 / np.sqrt(D))
-    err = np.abs(o - ref)
-    bound = 2.0 ** -4 * ref_abs + TOL_BF16_ABS
-    mean_rel = float(err.sum() / np.abs(ref).sum())
-    log(f"  max_abs={err.max():.3e} mean_rel={mean_rel:.3e} max(err - bound)={float(np.max(err - bound)):.3e}")
-    assert np.all(np.isfinite(o))
-    assert np.all(err <= bound) and mean_rel <= 4e-2
+    bound, ref = weight_rounding_bound(*mx_operands(q, k, v, cu), cu, 1.0 / np.sqrt(D))
+    check(o, ref, "o vs block-scaled oracle", bound, TOL_FP8PV_MEANREL)
 
 
 def test_rising_logits_fused_q_bitwise():

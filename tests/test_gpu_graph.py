@@ -41,15 +41,19 @@ def test_capture_and_replay(fp8):
                     for tag in (rng.TAG_Q, rng.TAG_K, rng.TAG_V)) for i in range(2)]
     q, k, v = (torch.empty_like(x) for x in inputs[0])
     qo, ko, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
-    q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
-    k8 = torch.empty_like(q8)
-    vt8 = torch.empty((H, D, h3a.vt_e4m3_columns(cu)), dtype=torch.uint8, device="cuda")
+    cols = h3a.vt_e4m3_columns(cu)
+    q8 = (torch.empty(q.shape, dtype=torch.uint8, device="cuda"),
+          torch.empty((S, H, D // 32), dtype=torch.uint8, device="cuda"))
+    k8 = tuple(torch.empty_like(x) for x in q8)
+    vt8 = (torch.empty((H, D, cols), dtype=torch.uint8, device="cuda"),
+           torch.empty((H, cols // 64, 2, 32, D // 32), dtype=torch.uint8, device="cuda"))
     scale = w.scale
 
     def step(stream=None):
         if fp8:
-            h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8, k8=k8, stream=stream)
-            h3a.prepare_vt_e4m3(v, cu, out=vt8, stream=stream)
+            h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8[0], k8=k8[0], q_scale=q8[1],
+                                     k_scale=k8[1], stream=stream)
+            h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
             h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, scale, out=o, stream=stream)
         else:
             h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qo, k_out=ko, stream=stream)

@@ -78,8 +78,9 @@ def test_long_causal_grouped_bf16():
 
 
 def test_long_fp8_both():
-    """Both products in FP8 (V as 262,208 transposed E4M3 columns per dim row):
-    within the E4M3 weight-rounding bound of attention on E4M3 q, k, v."""
+    """Both products in FP8 (V as 262,208 transposed E4M3 columns per dim row, with
+    their block scales): within the weight-rounding bound of attention on
+    block-rounded q, k, v."""
     import packed_varlen_attention_head_amd as h3a
     from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, weight_rounding_bound
 
@@ -91,14 +92,13 @@ def test_long_fp8_both():
     o = h3a.varlen_attn_fwd_fp8(h3a.quantize_e4m3(qd), h3a.quantize_e4m3(kd), h3a.prepare_vt_e4m3(vd, cu), cu,
                                 1.0 / np.sqrt(D))
     o = to_f64(o[rows.tolist()])
-    # only the sampled query rows are read by the row oracle
+    # only the sampled query rows are read by the bound's attention
     qf = rng.as_f64(q, "bf16")
     q8 = np.zeros_like(qf)
-    q8[rows] = oracle.e4m3_round(qf[rows])
-    k8, v8 = (oracle.e4m3_round(rng.as_f64(x, "bf16")) for x in (k, v))
-    ref = oracle.varlen_attention_rows(q8, k8, v8, cu, 1.0 / np.sqrt(D), rows)
-    ref_abs_v = oracle.varlen_attention_rows(q8, k8, np.abs(v8), cu, 1.0 / np.sqrt(D), rows)
-    check(o, ref, f"o ({len(rows)} rows)", weight_rounding_bound(ref_abs_v), TOL_FP8PV_MEANREL)
+    q8[rows] = oracle.mx_round(qf[rows])
+    k8, v8 = oracle.mx_round(rng.as_f64(k, "bf16")), oracle.mx_round_keys(rng.as_f64(v, "bf16"), cu)
+    bound, ref = weight_rounding_bound(q8, k8, v8, cu, 1.0 / np.sqrt(D), rows=rows)
+    check(o, ref, f"o ({len(rows)} rows)", bound, TOL_FP8PV_MEANREL)
 
 
 def test_long_table_and_norm():

@@ -1,12 +1,14 @@
 """NaN and infinity handling of the low-precision path against the bf16 one.
 
-OCP E4M3 ("fn") has no infinities and two NaN codes (0x7f, 0xff).  The
-quantisers saturate finite and infinite values at +-448 and turn a NaN into
-a NaN code, so a NaN in q, k or v reaches the attention output through the
-FP8 kernels exactly as through the bf16 kernel: a NaN query element makes
-that query row NaN, a NaN key element makes every row of its segment and
-head NaN, a NaN value element that dim of every row of its segment and head,
-and nothing else is touched."""
+OCP E4M3 ("fn") has no infinities and two NaN codes (0x7f, 0xff).  A block's
+scale comes from its largest finite-or-infinite magnitude, NaN ignored: an
+infinity gives the block the scale 2^120 and saturates to +-448 under it (the
+rest of its block then rounds to zero), and a NaN becomes a NaN code without
+changing its block's scale.  So a NaN in q, k or v reaches the attention
+output through the FP8 kernels exactly as through the bf16 kernel: a NaN query
+element makes that query row NaN, a NaN key element makes every row of its
+segment and head NaN, a NaN value element that dim of every row of its segment
+and head, and nothing else is touched."""
 from __future__ import annotations
 
 import numpy as np
@@ -56,15 +58,27 @@ def test_quantize_nan_and_infinities():
     x[5, 1, 7] = _bits(np.nan)
     x[9, 0, 3] = _bits(np.inf)
     x[11, 1, 100] = _bits(-np.inf)
-    codes = h3a().quantize_e4m3(to_device(x, "bf16")).cpu().numpy()
+    codes, scales = (t.cpu().numpy() for t in h3a().quantize_e4m3(to_device(x, "bf16")))
     torch.cuda.synchronize()
-    log(f"[nan] codes: nan={codes[5, 1, 7]:#x} +inf={codes[9, 0, 3]:#x} -inf={codes[11, 1, 100]:#x}")
+    log(f"[nan] codes: nan={codes[5, 1, 7]:#x} +inf={codes[9, 0, 3]:#x} -inf={codes[11, 1, 100]:#x}; "
+        f"scales {scales[5, 1, 0]} {scales[9, 0, 0]} {scales[11, 1, 3]}")
     assert codes[5, 1, 7] in (0x7F, 0xFF)
     assert codes[9, 0, 3] == 0x7E and codes[11, 1, 100] == 0xFE
-    finite = np.ones(x.shape, dtype=bool)
-    finite[5, 1, 7] = finite[9, 0, 3] = finite[11, 1, 100] = False
-    ref = oracle.e4m3_encode(rng.as_f64(x, "bf16")[finite])
-    assert np.array_equal(codes[finite], ref)
+    assert scales[9, 0, 0] == 247 and scales[11, 1, 3] == 247  # 2^120
+    # the other elements of an infinity's block, N(0,1) times 2^-120, round to (signed) zero
+    for (t, h, b), d in (((9, 0, 0), 3), ((11, 1, 3), 100 - 96)):
+        rest = np.delete(codes[t, h, 32 * b:32 * b + 32], d)
+        assert np.all((rest & 0x7F) == 0)
+    # every other block, the NaN's included (its NaN read as zero), as the oracle's codec
+    xf = rng.as_f64(x, "bf16")
+    xf[5, 1, 7] = 0.0
+    want, X = oracle.mx_quantize(np.where(np.isinf(xf), 0.0, xf), axis=-1)
+    keep = np.ones(scales.shape, dtype=bool)
+    keep[9, 0, 0] = keep[11, 1, 3] = False
+    assert np.array_equal(scales[keep], (X + 127).astype(np.uint8)[keep])
+    code_keep = np.repeat(keep, 32, axis=-1)
+    code_keep[5, 1, 7] = False
+    assert np.array_equal(codes[code_keep], want[code_keep])
 
 
 def _nan_rows(o, cu, row=None, seg=None, head=0):

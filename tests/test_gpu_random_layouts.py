@@ -86,11 +86,12 @@ def test_layouts_cover_the_edges():
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_packing_fp8(case, _gpu):
     """The same packings through both low-precision kernels (bf16 inputs quantised to
-    E4M3 on the GPU): FP8 scores against attention on E4M3 q, k at the bf16
-    tolerance; both products in FP8, with V in the per-segment transposed layout,
-    within the E4M3 weight-rounding bound of attention on E4M3 q, k, v."""
+    block-scaled E4M3 on the GPU): FP8 scores against attention on block-rounded q,
+    k at the bf16 tolerance; both products in FP8, with V in the per-segment
+    transposed layout, within the weight-rounding bound of attention on
+    block-rounded q, k, v."""
     import packed_varlen_attention_head_amd as h3a
-    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, weight_rounding_bound
+    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, mx_operands, weight_rounding_bound
 
     lens, Hq, Hkv, D, causal, _ = layout(case)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
@@ -106,9 +107,8 @@ def test_random_packing_fp8(case, _gpu):
     qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
     o = to_f64(h3a.varlen_attn_fwd_fp8qk(q8, k8, vd, cu, scale, causal=causal))
     assert np.all(np.isfinite(o))
-    compare(o, oracle.varlen_attention_fp8qk(qf, kf, vf, cu, scale, causal=causal), "bf16", "o, FP8 scores")
+    compare(o, oracle.varlen_attention_mx_qk(qf, kf, vf, cu, scale, causal=causal), "bf16", "o, FP8 scores")
     o = to_f64(h3a.varlen_attn_fwd_fp8(q8, k8, h3a.prepare_vt_e4m3(vd, cu), cu, scale, causal=causal))
     assert np.all(np.isfinite(o))
-    ref = oracle.varlen_attention_fp8(qf, kf, vf, cu, scale, causal=causal)
-    ref_abs_v = oracle.varlen_attention_fp8(qf, kf, np.abs(vf), cu, scale, causal=causal)
-    check(o, ref, "o, both products FP8", weight_rounding_bound(ref_abs_v), TOL_FP8PV_MEANREL)
+    bound, ref = weight_rounding_bound(*mx_operands(q, k, v, cu), cu, scale, causal)
+    check(o, ref, "o, both products FP8", bound, TOL_FP8PV_MEANREL)

@@ -103,13 +103,24 @@ def test_fp8_operands():
     refused(lambda: h3a.prepare_vt_e4m3(v.float(), cu), h3a.H3A_EDTYPE)
     vt8 = h3a.prepare_vt_e4m3(v, cu)
     out = torch.zeros((S, H, D), dtype=torch.bfloat16, device="cuda")
-    refused(lambda: h3a.varlen_attn_fwd_fp8(q8, k8, vt8[:, :, :-64].contiguous(), cu, 0.1, out=out), h3a.H3A_ESHAPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_fp8(q8, k8, (vt8[0][:, :, :-64].contiguous(), vt8[1]), cu, 0.1, out=out),
+            h3a.H3A_ESHAPE, out)
     refused(lambda: h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, 0.1, out=out[:-1]), h3a.H3A_ESHAPE, out)
-    refused(lambda: h3a.varlen_attn_fwd_fp8(q.view(torch.uint8)[:, :, :D].contiguous().view(torch.int8), k8, vt8, cu,
-                                            0.1, out=out), h3a.H3A_EDTYPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_fp8((q.view(torch.uint8)[:, :, :D].contiguous().view(torch.int8), q8[1]), k8,
+                                            vt8, cu, 0.1, out=out), h3a.H3A_EDTYPE, out)
     refused(lambda: h3a.varlen_attn_fwd_fp8qk(q8, k8, v, cu, 0.1, out=out[:, :1]), h3a.H3A_ESHAPE, out)
     q8o = torch.zeros((S - 1, H, D), dtype=torch.uint8, device="cuda")
     refused(lambda: h3a.qk_rmsnorm_rope_e4m3(q, k, gam, gam, 1e-6, tab, R, q8=q8o), h3a.H3A_ESHAPE, q8o)
+    # scale arrays: exact packed shapes, uint8, contiguous; operands as (codes, scales) pairs
+    qs_short = torch.zeros((S, H, D // 32 - 1), dtype=torch.uint8, device="cuda")
+    refused(lambda: h3a.varlen_attn_fwd_fp8qk((q8[0], qs_short), k8, v, cu, 0.1, out=out), h3a.H3A_ESHAPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_fp8qk((q8[0], q8[1].view(torch.int8)), k8, v, cu, 0.1, out=out),
+            h3a.H3A_EDTYPE, out)
+    vs_strided = torch.zeros(vt8[1].shape[:-1] + (2 * (D // 32),), dtype=torch.uint8, device="cuda")[..., ::2]
+    refused(lambda: h3a.varlen_attn_fwd_fp8(q8, k8, (vt8[0], vs_strided), cu, 0.1, out=out), h3a.H3A_ESHAPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_fp8(q8[0], k8, vt8, cu, 0.1, out=out), h3a.H3A_EINVAL, out)
+    refused(lambda: h3a.quantize_e4m3(q, scale_out=qs_short), h3a.H3A_ESHAPE)
+    refused(lambda: h3a.prepare_vt_e4m3(v, cu, scale_out=vt8[1][:, :-1].contiguous()), h3a.H3A_ESHAPE)
     o = h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, 0.1, out=out)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()

@@ -451,9 +451,9 @@ def main():
         return 2
     if fp8:  # E4M3 codes and one E8M0 scale per 32 head dims
         q8 = (torch.empty(q.shape, dtype=torch.uint8, device=dev),
-              torch.empty(q.shape[:2] + (q.shape[2] // 32,), dtype=torch.uint8, device=dev))
+              torch.empty((q.shape[1], q.shape[0], q.shape[2] // 32), dtype=torch.uint8, device=dev))
         k8 = (torch.empty(k.shape, dtype=torch.uint8, device=dev),
-              torch.empty(k.shape[:2] + (k.shape[2] // 32,), dtype=torch.uint8, device=dev))
+              torch.empty((k.shape[1], k.shape[0], k.shape[2] // 32), dtype=torch.uint8, device=dev))
     if fp8pv:  # transposed codes and one scale per 32 keys of each head dim
         cols = h3a.vt_e4m3_columns(np.concatenate([[0], np.cumsum(w.lengths)]))
         vt8 = (torch.empty((w.kv, w.head_dim, cols), dtype=torch.uint8, device=dev),

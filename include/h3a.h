@@ -294,14 +294,16 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
  * scaled FP8 MFMA applies the scales inside the instruction.
  *
  * Scale arrays are caller-owned, packed and 2-byte (D = 64) or 4-byte
- * (D = 128) aligned: q_scale [S][Hq][D/32], k_scale [S][Hk][D/32] (byte
- * (n * H + h) * D/32 + b holds block b of token n, head h), and for the
- * transposed V layout vt_scale [Hkv][vt_cols / 64][2][32][D/32] (block j of
- * tile t, dim 32 b + r at [h][t][j][r][b]).
+ * (D = 128) aligned.  q and k scales are head-major, q_scale [Hq][S][D/32]
+ * and k_scale [Hk][S][D/32]: byte (h * S + n) * D/32 + b holds block b of
+ * token n, head h, so the scales of a tile of consecutive keys are one
+ * contiguous run.  For the transposed V layout vt_scale
+ * [Hkv][vt_cols / 64][2][32][D/32] (block j of tile t, dim 32 b + r at
+ * [h][t][j][r][b]).
  *
  * h3a_quantize_e4m3: bf16 x [S, H, D] (token stride stride_x elements) to
  *   codes y [S, H, D] (uint8, token stride stride_y bytes, a multiple of 16)
- *   and y_scale [S][H][D/32].  Errors: EINVAL (null, sizes, overlap),
+ *   and y_scale [H][S][D/32].  Errors: EINVAL (null, sizes, overlap),
  *   ESHAPE, EUNSUPPORTED, EHIP.
  */
 h3a_status h3a_quantize_e4m3(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,

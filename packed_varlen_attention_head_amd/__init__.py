@@ -363,8 +363,8 @@ def varlen_attn_fwd_qnorm(q, k, v, cu_seqlens, scale: float, gamma_q, eps: float
 
 
 # Low-precision operands are (codes, scales) pairs: uint8 E4M3 codes and one
-# uint8 E8M0 scale per 32 elements along the contraction -- [S, H, D // 32]
-# for q and k, [Hkv, vt_cols // 64, 2, 32, D // 32] for the transposed V.
+# uint8 E8M0 scale per 32 elements along the contraction -- head-major
+# [H, S, D // 32] for q and k (a tile's keys contiguous), [Hkv, vt_cols // 64, 2, 32, D // 32] for the transposed V.
 
 def _scales(name, t, shape, device):
     """A scale array must be exactly the packed shape the kernels address."""
@@ -383,7 +383,7 @@ def _pair(name, x):
 
 
 def quantize_e4m3(x, out=None, scale_out=None, stream=None):
-    """bf16 [S, H, D] -> (uint8 [S, H, D] E4M3 codes, uint8 [S, H, D // 32] block scales)."""
+    """bf16 [S, H, D] -> (uint8 [S, H, D] E4M3 codes, uint8 [H, S, D // 32] block scales)."""
     import torch
 
     S, H, D, sx = _token_major("x", x)
@@ -394,7 +394,7 @@ def quantize_e4m3(x, out=None, scale_out=None, stream=None):
     _, _, _, sy = _token_major("out", out)
     if tuple(out.shape) != (S, H, D) or out.dtype != torch.uint8:
         raise H3AError(H3A_ESHAPE, f"out must be uint8 {(S, H, D)}, got {out.dtype} {tuple(out.shape)}")
-    sc = _scales("scale_out", scale_out, (S, H, D // 32), x.device)
+    sc = _scales("scale_out", scale_out, (H, S, D // 32), x.device)
     _check(lib().h3a_quantize_e4m3(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy,
                                    _stream_handle(stream)))
     return out, sc
@@ -418,8 +418,8 @@ def qk_rmsnorm_rope_e4m3(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: i
         raise H3AError(H3A_ESHAPE, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     _same("q8", q8, (S, Hq, D), torch.uint8)
     _same("k8", k8, (S, Hk, D), torch.uint8)
-    qs = _scales("q_scale", q_scale, (S, Hq, D // 32), q.device)
-    ks = _scales("k_scale", k_scale, (S, Hk, D // 32), q.device)
+    qs = _scales("q_scale", q_scale, (Hq, S, D // 32), q.device)
+    ks = _scales("k_scale", k_scale, (Hk, S, D // 32), q.device)
     cs = _table(cos_sin, S, int(rot_dim))
     _check(lib().h3a_qk_rmsnorm_rope_e4m3(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k8.data_ptr(), qs.data_ptr(),
                                           ks.data_ptr(), S, Hq, Hk, D, sq, sk, sq8, sk8,
@@ -472,8 +472,8 @@ def varlen_attn_fwd_fp8(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = Fa
     cols = vt_e4m3_columns(cu)
     # the kernel addresses vt8 with exactly `cols` columns per row
     _expect("vt8", vt8, (Hkv, D, max(cols, 1)), torch.uint8)
-    qs = _scales("q_scale", qs, (S, Hq, D // 32), q8.device)
-    ks = _scales("k_scale", ks, (S, Hkv, D // 32), q8.device)
+    qs = _scales("q_scale", qs, (Hq, S, D // 32), q8.device)
+    ks = _scales("k_scale", ks, (Hkv, S, D // 32), q8.device)
     vs = _scales("vt_scale", vs, (Hkv, max(cols, 64) // 64, 2, 32, D // 32), q8.device)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q8.device)
@@ -497,8 +497,8 @@ def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fa
         raise H3AError(H3A_EDTYPE, f"q8/k8 must hold uint8 E4M3 codes, got {q8.dtype}/{k8.dtype}")
     if tuple(k8.shape) != (S, Hkv, D) or tuple(v.shape) != (S, Hkv, D) or v.dtype != torch.bfloat16:
         raise H3AError(H3A_ESHAPE, f"k8 {tuple(k8.shape)} / v {tuple(v.shape)} {v.dtype} do not match q8")
-    qs = _scales("q_scale", qs, (S, Hq, D // 32), q8.device)
-    ks = _scales("k_scale", ks, (S, Hkv, D // 32), q8.device)
+    qs = _scales("q_scale", qs, (Hq, S, D // 32), q8.device)
+    ks = _scales("k_scale", ks, (Hkv, S, D // 32), q8.device)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=v.device)
     _, _, _, so = _token_major("out", out)

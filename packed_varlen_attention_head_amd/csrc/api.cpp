@@ -711,7 +711,7 @@ h3a_status h3a_quantize_e4m3(const void* x, void* y, void* y_scale, int64_t S, i
     const Range rs = byte_range(y_scale, sbytes);
     if (ranges_hit(rs, Range{x0, x1}) || ranges_hit(rs, Range{y0, y1}))
       return fail(H3A_EINVAL, "y_scale overlaps x or y");
-    hipError_t e = h3a::launch_quantize_e4m3(x, y, y_scale, S, H * D, stride_x, stride_y, stream);
+    hipError_t e = h3a::launch_quantize_e4m3(x, y, y_scale, S, H, D, stride_x, stride_y, stream);
     if (e != hipSuccess) return fail_hip("quantize_e4m3 launch", e);
     return H3A_OK;
   } catch (...) {
@@ -806,8 +806,8 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
     Plan plan;
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
     if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k, Hq * (D / 32),
-                                              Hkv * (D / 32), stride_v, stride_o, plan.dev, plan.n, scale, Hq / Hkv,
+    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k, S * (D / 32),
+                                              S * (D / 32), stride_v, stride_o, plan.dev, plan.n, scale, Hq / Hkv,
                                               causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
     return H3A_OK;
@@ -909,7 +909,7 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
     std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
     if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
     hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, vt_scale, o, D, stride_q, stride_k,
-                                            Hq * (D / 32), Hkv * (D / 32), vt_cols, stride_o, plan.dev, plan.n, scale,
+                                            S * (D / 32), S * (D / 32), vt_cols, stride_o, plan.dev, plan.n, scale,
                                             Hq / Hkv, causal != 0, stream);
     if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
     return H3A_OK;

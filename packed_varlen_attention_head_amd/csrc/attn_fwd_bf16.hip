@@ -201,16 +201,16 @@ struct QNormArgs {
   float eps;
 };
 
-// Per-block E8M0 scales of the FP8 operands (F8 >= 1): q [S][Hq][D/32] and
-// k [S][Hkv][D/32] (token strides q_stride, k_stride bytes); F8 == 2 also v
-// [Hkv][v_tiles][2][32][D/32] (dim 32 b + r of 32-key block j of a tile at
-// [j][r][b]).
+// Per-block E8M0 scales of the FP8 operands (F8 >= 1), head-major so a
+// tile's rows are contiguous: q [Hq][S][D/32] and k [Hkv][S][D/32] (head
+// strides q_head, k_head bytes); F8 == 2 also v [Hkv][v_tiles][2][32][D/32]
+// (dim 32 b + r of 32-key block j of a tile at [j][r][b]).
 struct F8Scales {
   const uint8_t* q;
   const uint8_t* k;
   const uint8_t* v;
-  int32_t q_stride;
-  int32_t k_stride;
+  int64_t q_head;
+  int64_t k_head;
   int32_t v_tiles;
 };
 
@@ -258,6 +258,35 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     else if constexpr (decltype(slot)::value == 0) return v_slot0;
     else return v_slot1;
   };
+  // F8: the block scales of a ring slot's tile, one dword per row (the row's
+  // D / 32 bytes, zero-extended: an LDS-bound load narrower than a dword
+  // still fills one dword per lane): the K tile's 64 keys; F8 == 2 also the
+  // V^T tile's (key block j, dim 32 b + r) words in lane order 32 j + r.  One
+  // wave fetches each with one LDS-bound load, shared by the workgroup like
+  // the tile itself.
+  constexpr int SCB = F8 ? kBN * 4 : 4;
+  __shared__ __align__(16) uint8_t ks_slot0[SCB], ks_slot1[SCB];
+  __shared__ __align__(16) uint8_t vs_slot0[F8 == 2 ? SCB : 4], vs_slot1[F8 == 2 ? SCB : 4];
+  auto kscl = [&](auto slot) -> uint8_t* {
+    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? ks_slot1 : ks_slot0;
+    else if constexpr (decltype(slot)::value == 0) return ks_slot0;
+    else return ks_slot1;
+  };
+  auto vscl = [&](auto slot) -> uint8_t* {
+    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? vs_slot1 : vs_slot0;
+    else if constexpr (decltype(slot)::value == 0) return vs_slot0;
+    else return vs_slot1;
+  };
+  // Row `row`'s scale word.
+  auto scale_word = [](const uint8_t* p, int row) -> uint32_t {
+    return *(const LDS uint32_t*)((const LDS char*)p + row * 4);
+  };
+  // One LDS-bound load of 64 scale rows (lane i: row i) into `dst`.
+  auto load_scales = [](__amdgpu_buffer_rsrc_t r, uint8_t* dst) {
+    const int ln = int(threadIdx.x & 63);
+    if constexpr (D == 128) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 4, ln * 4, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 2, ln * 2, 0, 0, 0);
+  };
 
   const WorkItem it = items[blockIdx.x];
   if (it.seg_len <= 0) return;
@@ -297,10 +326,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       qb8[ks] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(up[0]), int(up[1]), int(up[2]), int(up[3])};
     }
     // rows past the segment end read scale code 0 (their codes are 0 too)
-    const auto rqs = rows_rsrc(fs.q + (int64_t(it.seg_start) + qrow0) * fs.q_stride + it.head * (D / 32),
-                               it.seg_len - qrow0, 32, fs.q_stride);
-    const uint32_t w = D == 128 ? __builtin_amdgcn_raw_buffer_load_b32(rqs, l32 * fs.q_stride, 0, 0)
-                                : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rqs, l32 * fs.q_stride, 0, 0));
+    const auto rqs = rows_rsrc(fs.q + it.head * fs.q_head + (int64_t(it.seg_start) + qrow0) * (D / 32),
+                               it.seg_len - qrow0, 32, D / 32);
+    const uint32_t w = D == 128 ? __builtin_amdgcn_raw_buffer_load_b32(rqs, l32 * 4, 0, 0)
+                                : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rqs, l32 * 2, 0, 0));
     qsc = w >> (8 * hi);
   }
   // QNORM operands (the gain of each of the lane's dims, cos/sin of its
@@ -466,22 +495,6 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   [[maybe_unused]] const int tdiag = it.q_start / kBN;
 
   // ---- building blocks ------------------------------------------------------
-  // F8: per ring slot, the scales of the K tile's keys 32 kb + l32 (loaded
-  // with the tile) and, F8 == 2, of the V^T tile's dims for key block hi.
-  [[maybe_unused]] uint32_t ksc[2][2] = {{0u, 0u}, {0u, 0u}};
-  [[maybe_unused]] uint32_t vsc[2] = {0u, 0u};
-  auto put = [](auto slot, uint32_t* s0, uint32_t* s1, int i, uint32_t w) {
-    if constexpr (std::is_integral_v<decltype(slot)>) {
-      if (slot) s1[i] = w;
-      else s0[i] = w;
-    } else {
-      (decltype(slot)::value ? s1 : s0)[i] = w;
-    }
-  };
-  auto get = [](auto slot, const uint32_t* s0, const uint32_t* s1, int i) -> uint32_t {
-    if constexpr (std::is_integral_v<decltype(slot)>) return slot ? s1[i] : s0[i];
-    else return (decltype(slot)::value ? s1 : s0)[i];
-  };
   auto load_k = [&](int t, auto slot) {
     const int key0 = t * kBN;
     const auto r = rows_rsrc(kbase + int64_t(key0) * sk * KESZ, it.seg_len - key0, kBN, int(sk) * KESZ);
@@ -490,15 +503,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                koff[i], 0, 0, 0);
     if constexpr (F8 >= 1) {
+      // the tile's 64 scale rows, contiguous (head-major scales): lane = key;
       // keys past the segment end read scale code 0 (their codes are 0 too)
-      const auto rs = rows_rsrc(fs.k + (int64_t(it.seg_start) + key0) * fs.k_stride + kv_head * (D / 32),
-                                it.seg_len - key0, kBN, fs.k_stride);
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        const int off = (32 * kb + l32) * fs.k_stride;
-        const uint32_t w = D == 128 ? __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)
-                                    : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0));
-        put(slot, ksc[0], ksc[1], kb, w);
+      if (wave == 0) {
+        const auto rs = rows_rsrc(fs.k + kv_head * fs.k_head + (int64_t(it.seg_start) + key0) * (D / 32),
+                                  it.seg_len - key0, kBN, D / 32);
+        load_scales(rs, kscl(slot));
       }
     }
   };
@@ -517,12 +527,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int i = 0; i < NDMAV8; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(vslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                  voff[i], 0, 0, 0);
-      // the tile's scales, lane (l32, hi): dims 32 b + l32 of key block hi, byte b
-      const uint8_t* vs =
-          fs.v + ((int64_t(kv_head) * fs.v_tiles + it.vt_col0 / kVtTile + t) * 64 + hi * 32 + l32) * (D / 32);
-      const uint32_t w = D == 128 ? *reinterpret_cast<const uint32_t*>(vs)
-                                  : uint32_t(*reinterpret_cast<const uint16_t*>(vs));
-      put(slot, vsc, vsc + 1, 0, w);
+      // the tile's 64 scale words (lane (l32, hi): dims 32 b + l32 of key
+      // block hi, byte b), fetched by another wave than the K scales
+      if (wave == 1 % kWaves) {
+        const uint8_t* vs = fs.v + (int64_t(kv_head) * fs.v_tiles + it.vt_col0 / kVtTile + t) * 64 * (D / 32);
+        const auto r = rows_rsrc(vs, 64, 64, D / 32);
+        load_scales(r, vscl(slot));
+      }
     }
   };
   // S^T = K Q^T for the K tile in `slot` (an IC<> for immediate offsets).
@@ -555,8 +566,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
-      // byte 2 ks of either scale word: block 2 ks + hi of the row
-      const uint32_t ks_w = get(slot, ksc[0], ksc[1], kb) >> (8 * hi);
+      // key 32 kb + l32's word; byte 2 ks after the shift: dim block 2 ks + hi
+      const uint32_t ks_w = scale_word(kscl(slot), 32 * kb + l32) >> (8 * hi);
 #pragma unroll
       for (int ks = 0; ks < KS8; ++ks) {
         const LDS char* kp = (const LDS char*)kslot(slot) + kb * 32 * KROWB;
@@ -698,7 +709,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if constexpr (F8 == 2) {
       const int4 b0 = __builtin_bit_cast(int4, pb[0]), b1 = __builtin_bit_cast(int4, pb[1]);
       const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      const uint32_t vs_w = get(slot, vsc, vsc + 1, 0);  // byte db: dim block db, key block hi
+      const uint32_t vs_w = scale_word(vscl(slot), lane);  // byte db: dim block db, key block hi
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const LDS char* vp = (const LDS char*)vslot(slot);
@@ -863,7 +874,7 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
 }
 
 hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
-                                 void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks, int64_t sv,
+                                 void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks, int64_t sv,
                                  int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
                                  bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
@@ -882,7 +893,7 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s
 }
 
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
-                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks,
+                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
                                int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
                                int32_t kv_group, bool causal, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;

@@ -83,17 +83,17 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
                                       int32_t rot_dim, hipStream_t stream);
 
 // Attention whose q and k are FP8 E4M3 codes (token strides in bytes) with
-// one E8M0 scale per 32 head dims (q8s [S][Hq][D/32], k8s [S][Hkv][D/32];
-// token strides sqs, sks bytes); the score product runs on the scaled FP8
-// MFMA, the rest as launch_attn_fwd_bf16.
+// one E8M0 scale per 32 head dims, head-major (q8s [Hq][S][D/32], k8s
+// [Hkv][S][D/32]; head strides sqs, sks bytes); the score product runs on the
+// scaled FP8 MFMA, the rest as launch_attn_fwd_bf16.
 hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
-                                 void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks, int64_t sv,
+                                 void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks, int64_t sv,
                                  int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
                                  bool causal, hipStream_t stream);
 
 // The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
 // token strides sq8, sk8 in bytes) with one E8M0 scale per 32 head dims in
-// q8s [S][H][D/32], k8s [S][Hk][D/32].
+// q8s [H][S][D/32], k8s [Hk][S][D/32].
 hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, void* k8, void* q8s, void* k8s,
                                        int64_t S, int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk,
                                        int64_t sq8, int64_t sk8, const float* gq, const float* gk, float eps,
@@ -103,7 +103,7 @@ hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, v
 // as the transposed E4M3 layout of launch_prepare_vt_e4m3 (row length vt_cols
 // bytes, scales vt8s); both products on the scaled FP8 MFMA.
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
-                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int32_t sqs, int32_t sks,
+                               const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
                                int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
                                int32_t kv_group, bool causal, hipStream_t stream);
 
@@ -118,10 +118,10 @@ int64_t vt_e4m3_columns(const int32_t* cu, int32_t nseg);
 hipError_t launch_prepare_vt_e4m3(const void* v, int64_t sv, const int32_t* cu, int32_t nseg, int32_t H, int32_t D,
                                   void* vt, void* vs, int64_t vt_cols, hipStream_t stream);
 
-// bf16 [S, row_elems] rows (token stride sx elements) -> E4M3 codes (token
-// stride sy bytes) with one E8M0 scale per 32 consecutive elements in ys
-// [S][row_elems / 32]; row_elems a multiple of 32.
-hipError_t launch_quantize_e4m3(const void* x, void* y, void* ys, int64_t S, int32_t row_elems, int64_t sx,
+// bf16 [S, H, D] rows (token stride sx elements) -> E4M3 codes (token stride
+// sy bytes) with one E8M0 scale per 32 consecutive elements of a head in ys
+// [H][S][D / 32]; D a multiple of 32.
+hipError_t launch_quantize_e4m3(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
                                 int64_t sy, hipStream_t stream);
 
 hipError_t launch_attn_fwd_f32(const void* q, const void* k, const void* v, void* o, int32_t D,

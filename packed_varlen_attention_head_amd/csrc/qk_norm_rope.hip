@@ -106,10 +106,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWavesPerBlock = 4;
 constexpr int kBatch = 8;  // head vectors a lane keeps in flight
 
-// F8OUT: dst_scale [S][H][D / 32] E8M0 codes (token stride H * D / 32 bytes).
+// F8OUT: dst_scale [H][S][D / 32] E8M0 codes (head-major: a head's tokens are
+// contiguous, the order the attention reads a tile's keys in).
 template <typename T, int D, bool F8OUT>
 __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, uint8_t* dst_scale,
-                                              int64_t stride_b, int64_t stride_ob, int32_t token, int32_t H,
+                                              int64_t stride_b, int64_t stride_ob, int32_t token, int32_t S,
+                                              int32_t H,
                                               const float* g, const float* c, const float* s, int role,
                                               int partner, float eps, int lane) {
   constexpr int V = Elem<T>::V;
@@ -154,7 +156,7 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
           int X = 0;
           const uint2 pk = Elem<T>::pack_e4m3(out, &X);
           __builtin_nontemporal_store(u32x2{pk.x, pk.y}, reinterpret_cast<u32x2*>(orow + int64_t(h) * D));
-          if ((sub & 3) == 0) dst_scale[(int64_t(token) * H + h) * (D / 32) + sub / 4] = uint8_t(X + 127);
+          if ((sub & 3) == 0) dst_scale[(int64_t(h) * S + token) * (D / 32) + sub / 4] = uint8_t(X + 127);
         } else {
           const uint4 pk = Elem<T>::pack(out);
           __builtin_nontemporal_store(u32x4{pk.x, pk.y, pk.z, pk.w},
@@ -204,8 +206,8 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, uint8_t* q
     g_q[e] = gq[d0 + e];
     g_k[e] = gk[d0 + e];
   }
-  norm_rope_one<T, D, F8OUT>(q, qo, qos, sq_b, sqo_b, token, H, g_q, c, s, role, partner, eps, lane);
-  norm_rope_one<T, D, F8OUT>(k, ko, kos, sk_b, sko_b, token, Hk, g_k, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(q, qo, qos, sq_b, sqo_b, token, S, H, g_q, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, F8OUT>(k, ko, kos, sk_b, sko_b, token, S, Hk, g_k, c, s, role, partner, eps, lane);
 }
 
 // Strides in elements of the input type; with F8OUT the output strides are

@@ -20,10 +20,11 @@ namespace {
 constexpr int kThreads = 256;
 
 // row_vecs (8-element vectors per token) is a multiple of 4, so the four
-// lanes of a block are consecutive and exit together at the end.
+// lanes of a block are consecutive and exit together at the end.  Scales are
+// head-major: ys[h][token][b] for block b of head h (d32 blocks per head).
 __global__ void __launch_bounds__(kThreads)
 quantize_e4m3_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ y, uint8_t* __restrict__ ys,
-                     int64_t S, int32_t row_vecs, int64_t sx, int64_t sy) {
+                     int64_t S, int32_t row_vecs, int32_t d32, int64_t sx, int64_t sy) {
   const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (idx >= S * row_vecs) return;
   const int64_t token = idx / row_vecs;
@@ -50,7 +51,10 @@ quantize_e4m3_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ y, ui
     out[i] = uint32_t(packed);
   }
   *reinterpret_cast<uint2*>(y + token * sy + vec * 8) = make_uint2(out[0], out[1]);
-  if ((vec & 3) == 0) ys[token * (row_vecs / 4) + vec / 4] = uint8_t(X + 127);
+  if ((vec & 3) == 0) {
+    const int32_t blk = vec / 4, h = blk / d32;
+    ys[(int64_t(h) * S + token) * d32 + blk % d32] = uint8_t(X + 127);
+  }
 }
 
 // ---- V as transposed E4M3 tiles -------------------------------------------
@@ -189,16 +193,17 @@ hipError_t launch_prepare_vt_e4m3(const void* v, int64_t sv, const int32_t* cu, 
   return hipSuccess;
 }
 
-hipError_t launch_quantize_e4m3(const void* x, void* y, void* ys, int64_t S, int32_t row_elems, int64_t sx,
+hipError_t launch_quantize_e4m3(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
                                 int64_t sy, hipStream_t stream) {
   if (S <= 0) return hipSuccess;
-  if (row_elems % 32 != 0) return hipErrorInvalidValue;
+  if (D % 32 != 0 || H < 1) return hipErrorInvalidValue;
+  const int32_t row_elems = H * D;
   const int32_t row_vecs = row_elems / 8;
   const int64_t n = S * row_vecs;
   const unsigned blocks = unsigned((n + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(quantize_e4m3_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<uint8_t*>(y), static_cast<uint8_t*>(ys), S,
-                     row_vecs, sx, sy);
+                     row_vecs, D / 32, sx, sy);
   return hipGetLastError();
 }
 

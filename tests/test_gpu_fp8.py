@@ -50,9 +50,10 @@ def h3a():
 
 
 def mx_codes(bits: np.ndarray):
-    """(E4M3 codes, E8M0 scale codes) of bf16 bits [..., D] in blocks of 32 along D."""
+    """(E4M3 codes [S, H, D], E8M0 scale codes head-major [H, S, D / 32]) of bf16
+    bits [S, H, D] in blocks of 32 along D."""
     codes, X = oracle.mx_quantize(rng.bf16_bits_to_f32(bits).astype(np.float64), axis=-1)
-    return codes, (X + 127).astype(np.uint8)
+    return codes, np.ascontiguousarray((X + 127).astype(np.uint8).transpose(1, 0, 2))
 
 
 def expected_vt(vbits: np.ndarray, cu):

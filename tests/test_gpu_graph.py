@@ -43,7 +43,7 @@ def test_capture_and_replay(fp8):
     qo, ko, o = torch.empty_like(q), torch.empty_like(k), torch.empty_like(q)
     cols = h3a.vt_e4m3_columns(cu)
     q8 = (torch.empty(q.shape, dtype=torch.uint8, device="cuda"),
-          torch.empty((S, H, D // 32), dtype=torch.uint8, device="cuda"))
+          torch.empty((H, S, D // 32), dtype=torch.uint8, device="cuda"))
     k8 = tuple(torch.empty_like(x) for x in q8)
     vt8 = (torch.empty((H, D, cols), dtype=torch.uint8, device="cuda"),
            torch.empty((H, cols // 64, 2, 32, D // 32), dtype=torch.uint8, device="cuda"))

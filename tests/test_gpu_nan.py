@@ -61,10 +61,10 @@ def test_quantize_nan_and_infinities():
     codes, scales = (t.cpu().numpy() for t in h3a().quantize_e4m3(to_device(x, "bf16")))
     torch.cuda.synchronize()
     log(f"[nan] codes: nan={codes[5, 1, 7]:#x} +inf={codes[9, 0, 3]:#x} -inf={codes[11, 1, 100]:#x}; "
-        f"scales {scales[5, 1, 0]} {scales[9, 0, 0]} {scales[11, 1, 3]}")
+        f"scales {scales[1, 5, 0]} {scales[0, 9, 0]} {scales[1, 11, 3]}")
     assert codes[5, 1, 7] in (0x7F, 0xFF)
     assert codes[9, 0, 3] == 0x7E and codes[11, 1, 100] == 0xFE
-    assert scales[9, 0, 0] == 247 and scales[11, 1, 3] == 247  # 2^120
+    assert scales[0, 9, 0] == 247 and scales[1, 11, 3] == 247  # 2^120 (scales are [head, token, block])
     # the other elements of an infinity's block, N(0,1) times 2^-120, round to (signed) zero
     for (t, h, b), d in (((9, 0, 0), 3), ((11, 1, 3), 100 - 96)):
         rest = np.delete(codes[t, h, 32 * b:32 * b + 32], d)
@@ -73,9 +73,9 @@ def test_quantize_nan_and_infinities():
     xf = rng.as_f64(x, "bf16")
     xf[5, 1, 7] = 0.0
     want, X = oracle.mx_quantize(np.where(np.isinf(xf), 0.0, xf), axis=-1)
-    keep = np.ones(scales.shape, dtype=bool)
+    keep = np.ones(X.shape, dtype=bool)  # [token, head, block]
     keep[9, 0, 0] = keep[11, 1, 3] = False
-    assert np.array_equal(scales[keep], (X + 127).astype(np.uint8)[keep])
+    assert np.array_equal(scales.transpose(1, 0, 2)[keep], (X + 127).astype(np.uint8)[keep])
     code_keep = np.repeat(keep, 32, axis=-1)
     code_keep[5, 1, 7] = False
     assert np.array_equal(codes[code_keep], want[code_keep])

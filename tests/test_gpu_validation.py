@@ -112,7 +112,7 @@ def test_fp8_operands():
     q8o = torch.zeros((S - 1, H, D), dtype=torch.uint8, device="cuda")
     refused(lambda: h3a.qk_rmsnorm_rope_e4m3(q, k, gam, gam, 1e-6, tab, R, q8=q8o), h3a.H3A_ESHAPE, q8o)
     # scale arrays: exact packed shapes, uint8, contiguous; operands as (codes, scales) pairs
-    qs_short = torch.zeros((S, H, D // 32 - 1), dtype=torch.uint8, device="cuda")
+    qs_short = torch.zeros((H, S, D // 32 - 1), dtype=torch.uint8, device="cuda")
     refused(lambda: h3a.varlen_attn_fwd_fp8qk((q8[0], qs_short), k8, v, cu, 0.1, out=out), h3a.H3A_ESHAPE, out)
     refused(lambda: h3a.varlen_attn_fwd_fp8qk((q8[0], q8[1].view(torch.int8)), k8, v, cu, 0.1, out=out),
             h3a.H3A_EDTYPE, out)

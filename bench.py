@@ -64,6 +64,8 @@ def parse():
                     help="step = table + q/k norm/rotary writing E4M3 codes + FP8-score attention")
     ap.add_argument("--fused-q", action="store_true",
                     help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
+    ap.add_argument("--split", choices=("auto", "never", "always"), default="auto",
+                    help="key-range splitting of attention plans (h3a_set_split_policy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps, so the GPU clock has left its idle state")
@@ -426,6 +428,8 @@ def main():
         return 2
     w = configs.BF16[args.config]
     T = configs.make_tensors(w)
+    h3a.set_split_policy({"auto": h3a.H3A_SPLIT_AUTO, "never": h3a.H3A_SPLIT_NEVER,
+                          "always": h3a.H3A_SPLIT_ALWAYS}[args.split])
     dev = "cuda:0"
     torch.cuda.set_device(0)
     bf = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
@@ -589,6 +593,7 @@ def main():
             "rot_dims": list(w.rot_dims), "rope_mode": w.rope_mode,
             "segments": [list(s) for s in w.segments],
             "parallelism": "single GPU",
+            "split": args.split,
             "step": ("rope table + k norm/rotary + attention with q norm/rotary fused in its prologue" if fused
                      else "rope table + q/k norm/rotary to E4M3 codes + transposed E4M3 V + attention with both "
                           "products in FP8" if fp8pv

@@ -463,6 +463,31 @@ const char* h3a_last_error(void);
  * replayed after this (its plan is gone); capture it again. */
 void h3a_release_caches(void);
 
+/* Key-range splitting of attention plans (the bf16-tile kernels: bf16, fused
+ * Q norm, FP8; bidirectional plans only).  When a packing has few, long work
+ * items -- fewer (segment, head, query tile) items than the GPU has workgroup
+ * slots, or whole rounds of long items that leave slots idle at the end --
+ * an item's keys can be cut into ranges of whole 64-key tiles, each range its
+ * own work item storing its unnormalised rows with their running max and row
+ * sum; a merge kernel then combines the ranges of each item in key order, as
+ * the streaming softmax itself combines tiles (each packing's vllm.cpp PR #26
+ * cu_seqlens call stays one call: the split is internal).  Results are
+ * deterministic run to run; they differ from the unsplit kernel's only by
+ * fp32 rounding of the combination.
+ *
+ * policy: H3A_SPLIT_AUTO (default) splits when a list-scheduling estimate of
+ * the kernel time, charging the merge pass for reading every partial result
+ * back, improves by more than 10%; H3A_SPLIT_NEVER never; H3A_SPLIT_ALWAYS
+ * cuts every item of four or more key tiles into about three ranges (for
+ * tests).  The policy applies to plans built afterwards; cached plans keep
+ * theirs (they are keyed by it).  Calls under stream capture always use the
+ * unsplit items of a cached plan, so a graph never holds the shared partial
+ * workspace; calls outside capture that use one plan's split items are
+ * ordered on the GPU (each waits for the previous one's merge).
+ * Errors: EINVAL for an unknown policy. */
+typedef enum { H3A_SPLIT_AUTO = 0, H3A_SPLIT_NEVER = 1, H3A_SPLIT_ALWAYS = 2 } h3a_split_policy;
+h3a_status h3a_set_split_policy(int32_t policy);
+
 /* Library version, major * 10000 + minor * 100 + patch (0.2.0). */
 int32_t h3a_version(void);
 

@@ -51,6 +51,7 @@ EXPORTS = (
     "h3a_plan_tiles_ex",
     "h3a_last_error",
     "h3a_release_caches",
+    "h3a_set_split_policy",
     "h3a_version",
 )
 
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
     L.h3a_release_caches.argtypes = []
     L.h3a_version.restype = ctypes.c_int32
     L.h3a_version.argtypes = []
+    L.h3a_set_split_policy.restype = ctypes.c_int
+    L.h3a_set_split_policy.argtypes = [_i32]
     _lib = L
     return L
 
@@ -148,6 +151,14 @@ def version() -> int:
 
 def release_caches() -> None:
     lib().h3a_release_caches()
+
+
+H3A_SPLIT_AUTO, H3A_SPLIT_NEVER, H3A_SPLIT_ALWAYS = range(3)
+
+
+def set_split_policy(policy: int) -> None:
+    """Key-range splitting of attention plans built from now on (H3A_SPLIT_*)."""
+    _check(lib().h3a_set_split_policy(int(policy)))
 
 
 def _i32_array(values) -> np.ndarray:

@@ -8,6 +8,7 @@
 // and the condition-noise row accounting); here that becomes a status code
 // plus a message naming the argument.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -114,10 +115,29 @@ h3a_status check_operand(const char* name, const void* p, int64_t S, int32_t H, 
 // cu_seqlens content, heads, block size and device.
 // ---------------------------------------------------------------------------
 struct Plan {
-  h3a::WorkItem* dev = nullptr;
+  h3a::WorkItem* dev = nullptr;  // one allocation: the items, then the split variant below
   int64_t n = 0;
+  // Split variant (bidirectional plans whose longest items would set the
+  // time): items cutting some keys into ranges, the merge list, and the
+  // partial-row workspace they share.  Only calls outside stream capture use
+  // it; its workspace is reused by every such call, so each call waits for
+  // the previous one's merge (event `released`) before writing it.
+  h3a::WorkItem* sdev = nullptr;
+  int64_t sn = 0;
+  h3a::MergeItem* merges = nullptr;
+  int64_t n_merges = 0;
+  h3a::SplitArgs sp{};
+  hipEvent_t released = nullptr;
+  bool used = false;
   int device = 0;       // where dev lives
   bool pinned = false;  // used under stream capture: a graph may hold dev, never evict it
+};
+
+// What one call uses: the cached plan (valid while the cache lock is held)
+// and whether the call's stream is capturing.
+struct PlanUse {
+  Plan* plan = nullptr;
+  bool capturing = false;
 };
 
 constexpr size_t kMaxPlans = 256;
@@ -146,43 +166,60 @@ PlanCache& plan_cache() {
   return *c;
 }
 
-int n_xcd_of(int device) {
+// Split policy for plans built from now on (h3a_set_split_policy).
+std::atomic<int32_t> g_split_policy{h3a::kSplitAuto};
+
+struct DeviceShape {
+  int cus = 0;
+  int n_xcd = 1;
+};
+
+DeviceShape shape_of(int device) {
   static std::mutex mu;
-  static std::unordered_map<int, int> known;
+  static std::unordered_map<int, DeviceShape> known;
   std::lock_guard<std::mutex> lock(mu);
   auto it = known.find(device);
   if (it != known.end()) return it->second;
-  int cus = 0;
-  int n = 1;
+  DeviceShape d;
   // MI355X: 8 XCDs of 32 CUs; the dispatcher deals workgroups round-robin.
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
-      cus >= 64 && cus % 32 == 0)
-    n = cus / 32;
-  known[device] = n;
-  return n;
+  if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) d.cus = 0;
+  if (d.cus >= 64 && d.cus % 32 == 0) d.n_xcd = d.cus / 32;
+  known[device] = d;
+  return d;
 }
 
-// On success `*hold` owns the cache lock: the caller launches the kernel that
-// reads the plan before releasing it, so no other thread can evict (free) the
+void free_plan(Plan& p) {
+  if (p.dev != nullptr) (void)hipFree(p.dev);
+  if (p.released != nullptr) (void)hipEventDestroy(p.released);
+  p.dev = nullptr;
+  p.released = nullptr;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// On success `*hold` owns the cache lock: the caller launches the kernels that
+// read the plan before releasing it, so no other thread can evict (free) the
 // plan between this lookup and that launch.  An eviction synchronises the
 // device first, so launches already made have finished with the plan.
 // A call on a capturing stream only looks the plan up: building one allocates,
 // copies synchronously and may synchronise the device for an eviction, none of
 // which a capture allows.  The plan it uses is pinned, since the captured
 // graph keeps its device pointer for every later replay: pinned plans are
-// never evicted, only h3a_release_caches frees them.
-h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, hipStream_t stream,
-                    Plan* out, std::unique_lock<std::mutex>* hold) {
+// never evicted, only h3a_release_caches frees them.  split_ok: the caller's
+// kernels handle split items (the bf16-tile kernels; not the fp32 one).
+h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m, bool causal, bool split_ok,
+                    hipStream_t stream, PlanUse* out, std::unique_lock<std::mutex>* hold) {
   int device = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return fail_hip("hipGetDevice", e);
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   if ((e = hipStreamIsCapturing(stream, &capture)) != hipSuccess) return fail_hip("hipStreamIsCapturing", e);
   const bool capturing = capture != hipStreamCaptureStatusNone;
-  const int n_xcd = n_xcd_of(device);
+  const DeviceShape shape = shape_of(device);
+  const int32_t policy = split_ok && !causal ? g_split_policy.load() : h3a::kSplitNever;
   std::string key;
-  key.reserve(20 + size_t(nseg + 1) * 4);
-  const int32_t hdr[5] = {device, H, block_m, n_xcd, causal ? 1 : 0};
+  key.reserve(24 + size_t(nseg + 1) * 4);
+  const int32_t hdr[6] = {device, H, block_m, shape.n_xcd, causal ? 1 : 0, policy};
   key.append(reinterpret_cast<const char*>(hdr), sizeof(hdr));
   key.append(reinterpret_cast<const char*>(cu), size_t(nseg + 1) * sizeof(int32_t));
 
@@ -191,7 +228,8 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
   auto it = pc.map.find(key);
   if (it != pc.map.end()) {
     if (capturing) it->second.pinned = true;
-    *out = it->second;
+    out->plan = &it->second;
+    out->capturing = capturing;
     *hold = std::move(lock);
     return H3A_OK;
   }
@@ -201,12 +239,21 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
                 "make one attention call with it outside capture first");
   if (!plan_fits(cu, nseg, H, block_m))
     return fail(H3A_EUNSUPPORTED, "attention plan would exceed %lld work items", (long long)kMaxPlanItems);
-  std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, n_xcd, causal);
+  std::vector<h3a::WorkItem> items = h3a::plan_tiles(cu, nseg, H, block_m, shape.n_xcd, causal);
+  std::vector<h3a::WorkItem> sitems;
+  std::vector<h3a::MergeItem> merges;
+  int64_t n_parts = 0;
+  if (policy != h3a::kSplitNever && shape.cus > 0) {
+    sitems = h3a::plan_tiles_split(cu, nseg, H, block_m, shape.n_xcd, 2 * shape.cus, causal, policy, &merges,
+                                   &n_parts);
+    if (merges.empty()) sitems.clear();
+  }
   Plan p;
   p.n = int64_t(items.size());
   p.device = device;
   if (p.n > 0) {
-    if (p.n > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "attention plan has %lld items", (long long)p.n);
+    if (p.n > int64_t(INT32_MAX) || int64_t(sitems.size()) > int64_t(INT32_MAX))
+      return fail(H3A_EUNSUPPORTED, "attention plan has %lld items", (long long)p.n);
     // Evict the oldest plan no captured graph uses (if every cached plan is
     // pinned, the cache grows instead).
     auto old = pc.order.begin();
@@ -221,28 +268,72 @@ h3a_status get_plan(const int32_t* cu, int32_t nseg, int32_t H, int32_t block_m,
           if (vdev != device && (e = hipSetDevice(vdev)) != hipSuccess)
             return fail_hip("hipSetDevice (plan eviction)", e);
           e = hipDeviceSynchronize();
-          if (e == hipSuccess) e = hipFree(victim->second.dev);
+          if (e == hipSuccess) free_plan(victim->second);
           const hipError_t back = vdev != device ? hipSetDevice(device) : hipSuccess;
-          if (e != hipSuccess) return fail_hip("hipDeviceSynchronize / hipFree (plan eviction)", e);
+          if (e != hipSuccess) return fail_hip("hipDeviceSynchronize (plan eviction)", e);
           if (back != hipSuccess) return fail_hip("hipSetDevice (plan eviction)", back);
         }
         pc.map.erase(victim);
       }
       pc.order.erase(old);
     }
-    e = hipMalloc(reinterpret_cast<void**>(&p.dev), items.size() * sizeof(h3a::WorkItem));
+    // [items | split items | merges | per-row (max, sum) | partial rows (D <= 128)]
+    const size_t o_items = 0, b_items = round256(items.size() * sizeof(h3a::WorkItem));
+    const size_t o_sitems = o_items + b_items, b_sitems = round256(sitems.size() * sizeof(h3a::WorkItem));
+    const size_t o_merges = o_sitems + b_sitems, b_merges = round256(merges.size() * sizeof(h3a::MergeItem));
+    const size_t rows = size_t(n_parts) * size_t(block_m);
+    const size_t o_ml = o_merges + b_merges, b_ml = round256(rows * 2 * sizeof(float));
+    const size_t o_po = o_ml + b_ml, b_po = round256(rows * 128 * sizeof(float));
+    char* base = nullptr;
+    e = hipMalloc(reinterpret_cast<void**>(&base), o_po + b_po);
     if (e != hipSuccess) return fail_hip("hipMalloc (attention plan)", e);
-    // Synchronous upload: the plan is complete before any stream can use it.
+    p.dev = reinterpret_cast<h3a::WorkItem*>(base + o_items);
+    // Synchronous uploads: the plan is complete before any stream can use it.
     e = hipMemcpy(p.dev, items.data(), items.size() * sizeof(h3a::WorkItem), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !sitems.empty()) {
+      p.sdev = reinterpret_cast<h3a::WorkItem*>(base + o_sitems);
+      p.sn = int64_t(sitems.size());
+      p.merges = reinterpret_cast<h3a::MergeItem*>(base + o_merges);
+      p.n_merges = int64_t(merges.size());
+      p.sp = h3a::SplitArgs{reinterpret_cast<float*>(base + o_po), reinterpret_cast<float*>(base + o_ml)};
+      e = hipMemcpy(p.sdev, sitems.data(), sitems.size() * sizeof(h3a::WorkItem), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(p.merges, merges.data(), merges.size() * sizeof(h3a::MergeItem), hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&p.released, hipEventDisableTiming);
+    }
     if (e != hipSuccess) {
-      (void)hipFree(p.dev);
-      return fail_hip("hipMemcpy (attention plan)", e);
+      free_plan(p);
+      return fail_hip("hipMemcpy / hipEventCreate (attention plan)", e);
     }
   }
-  pc.map.emplace(key, p);
+  auto ins = pc.map.emplace(key, p);
   pc.order.push_back(key);
-  *out = p;
+  out->plan = &ins.first->second;
+  out->capturing = false;
   *hold = std::move(lock);
+  return H3A_OK;
+}
+
+// Launches the attention over a plan: the split variant (then the merge pass)
+// outside capture when the plan has one, else the plain items.  launch(items,
+// n, sp) enqueues the attention kernel.  Called with the cache lock held.
+template <typename F>
+h3a_status run_plan(const PlanUse& u, hipStream_t stream, void* o, int32_t D, int64_t stride_o, const char* what,
+                    F&& launch) {
+  Plan& p = *u.plan;
+  hipError_t e;
+  if (p.n_merges == 0 || u.capturing) {
+    if ((e = launch(p.dev, p.n, h3a::SplitArgs{})) != hipSuccess) return fail_hip(what, e);
+    return H3A_OK;
+  }
+  // the previous split call's merge must have read the workspace
+  if (p.used && (e = hipStreamWaitEvent(stream, p.released, 0)) != hipSuccess)
+    return fail_hip("hipStreamWaitEvent (split workspace)", e);
+  if ((e = launch(p.sdev, p.sn, p.sp)) != hipSuccess) return fail_hip(what, e);
+  if ((e = h3a::launch_attn_merge(p.merges, p.n_merges, p.sp, o, D, stride_o, stream)) != hipSuccess)
+    return fail_hip("split merge launch", e);
+  if ((e = hipEventRecord(p.released, stream)) != hipSuccess) return fail_hip("hipEventRecord (split workspace)", e);
+  p.used = true;
   return H3A_OK;
 }
 
@@ -314,6 +405,20 @@ const char* h3a_last_error(void) { return g_last_error.c_str(); }
 
 int32_t h3a_version(void) { return 200; }
 
+h3a_status h3a_set_split_policy(int32_t policy) {
+  try {
+    if (policy != H3A_SPLIT_AUTO && policy != H3A_SPLIT_NEVER && policy != H3A_SPLIT_ALWAYS)
+      return fail(H3A_EINVAL, "unknown split policy %d", policy);
+    static_assert(int(H3A_SPLIT_AUTO) == h3a::kSplitAuto && int(H3A_SPLIT_NEVER) == h3a::kSplitNever &&
+                      int(H3A_SPLIT_ALWAYS) == h3a::kSplitAlways,
+                  "split policy values");
+    g_split_policy.store(policy);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_set_split_policy");
+  }
+}
+
 void h3a_release_caches(void) {
   try {
     PlanCache& pc = plan_cache();
@@ -335,8 +440,7 @@ void h3a_release_caches(void) {
       }
     }
     (void)hipSetDevice(cur);
-    for (auto& kv : pc.map)
-      if (kv.second.dev) (void)hipFree(kv.second.dev);
+    for (auto& kv : pc.map) free_plan(kv.second);
     pc.map.clear();
     pc.order.clear();
   } catch (...) {  // nothing may cross the C ABI; the cache is left as it was
@@ -565,18 +669,19 @@ h3a_status h3a_varlen_attn_fwd_ex(const void* q, const void* k, const void* v, v
                                   cu_seqlens, nseg, scale, causal);
     if (st != H3A_OK || S == 0) return st;
     const bool bf16 = dtype == H3A_BF16;
-    Plan plan;
-    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0,
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, bf16 ? h3a::kAttnBlockM_BF16 : h3a::kAttnBlockM_F32, causal != 0, bf16,
                        stream, &plan, &plan_lock)) != H3A_OK)
       return st;
     const int32_t group = Hq / Hkv;
-    hipError_t e = bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                    plan.n, scale, group, causal != 0, stream)
-                        : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                   plan.n, scale, group, causal != 0, stream);
-    if (e != hipSuccess) return fail_hip("varlen attention launch", e);
-    return H3A_OK;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return bf16 ? h3a::launch_attn_fwd_bf16(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o,
+                                                              items, n, scale, group, causal != 0, stream, sp)
+                                  : h3a::launch_attn_fwd_f32(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o,
+                                                             items, n, scale, group, causal != 0, stream);
+                    });
   } catch (...) {
     return fail_exception("h3a_varlen_attn_fwd_ex");
   }
@@ -623,7 +728,7 @@ h3a_status h3a_varlen_attn_fwd_noalloc(const void* q, const void* k, const void*
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail_hip("hipGetDevice", e);
-    a.n_xcd = n_xcd_of(device);
+    a.n_xcd = shape_of(device).n_xcd;
     a.n_items = int32_t(items);
     const int64_t chunks = (items + 15) / 16;
     const int64_t blocks = int64_t(a.n_xcd) * 16 * ((chunks + a.n_xcd - 1) / a.n_xcd);
@@ -678,13 +783,16 @@ h3a_status h3a_varlen_attn_fwd_qnorm(const void* q, const void* k, const void* v
     if (may_overlap(o, stride_o, Hq, q, stride_q, Hq, S, D, esz)) return fail(H3A_EINVAL, "o overlaps q");
     if (may_overlap(o, stride_o, Hq, k, stride_k, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps k");
     if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, esz)) return fail(H3A_EINVAL, "o overlaps v");
-    Plan plan;
-    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o, plan.dev,
-                                                   plan.n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S, rot_dim, stream);
-    if (e != hipSuccess) return fail_hip("varlen attention (fused q norm) launch", e);
-    return H3A_OK;
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, false, true, stream, &plan, &plan_lock)) != H3A_OK)
+      return st;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention (fused q norm) launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return h3a::launch_attn_fwd_bf16_qnorm(q, k, v, o, D, stride_q, stride_k, stride_v, stride_o,
+                                                             items, n, scale, Hq / Hkv, gamma_q, eps, cos_sin, S,
+                                                             rot_dim, stream, sp);
+                    });
   } catch (...) {
     return fail_exception("h3a_varlen_attn_fwd_qnorm");
   }
@@ -803,14 +911,17 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
     if (ranges_hit(ro, byte_range(q_scale, qsb)) || ranges_hit(ro, byte_range(k_scale, ksb)))
       return fail(H3A_EINVAL, "o overlaps q_scale or k_scale");
     if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
-    Plan plan;
-    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_fp8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k, S * (D / 32),
-                                              S * (D / 32), stride_v, stride_o, plan.dev, plan.n, scale, Hq / Hkv,
-                                              causal != 0, stream);
-    if (e != hipSuccess) return fail_hip("varlen attention (fp8 qk) launch", e);
-    return H3A_OK;
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, true, stream, &plan, &plan_lock)) !=
+        H3A_OK)
+      return st;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention (fp8 qk) launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return h3a::launch_attn_fwd_fp8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k,
+                                                        S * (D / 32), S * (D / 32), stride_v, stride_o, items, n,
+                                                        scale, Hq / Hkv, causal != 0, stream, sp);
+                    });
   } catch (...) {
     return fail_exception("h3a_varlen_attn_fwd_fp8qk");
   }
@@ -905,14 +1016,17 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
     if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
     for (const Range& r : {byte_range(q_scale, qsb), byte_range(k_scale, ksb), byte_range(vt_scale, vsb)})
       if (ranges_hit(ro, r)) return fail(H3A_EINVAL, "o overlaps a scale array");
-    Plan plan;
-    std::unique_lock<std::mutex> plan_lock;  // held until the launch below is enqueued
-    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, stream, &plan, &plan_lock)) != H3A_OK) return st;
-    hipError_t e = h3a::launch_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, vt_scale, o, D, stride_q, stride_k,
-                                            S * (D / 32), S * (D / 32), vt_cols, stride_o, plan.dev, plan.n, scale,
-                                            Hq / Hkv, causal != 0, stream);
-    if (e != hipSuccess) return fail_hip("varlen attention (fp8) launch", e);
-    return H3A_OK;
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, true, stream, &plan, &plan_lock)) !=
+        H3A_OK)
+      return st;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention (fp8) launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return h3a::launch_attn_fwd_fp8(q8, k8, vt8, q_scale, k_scale, vt_scale, o, D, stride_q,
+                                                      stride_k, S * (D / 32), S * (D / 32), vt_cols, stride_o, items,
+                                                      n, scale, Hq / Hkv, causal != 0, stream, sp);
+                    });
   } catch (...) {
     return fail_exception("h3a_varlen_attn_fwd_fp8");
   }

@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o, int64_t sq,
                      int64_t sk, int64_t sv, int64_t so, const WorkItem* __restrict__ items,
-                     float c, int kv_group, QNormArgs qn, F8Scales fs) {
+                     float c, int kv_group, QNormArgs qn, F8Scales fs, SplitArgs sp) {
   // The body uses LDS address-space pointers and gfx950-only builtins, which
   // exist only in the device pass; the host pass needs just the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -491,6 +491,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Keys the item needs: the whole segment, or (causal) up to its last row.
   const int nkeys = CAUSAL ? min(it.seg_len, it.q_start + kBM) : it.seg_len;
   const int ntiles = (nkeys + kBN - 1) / kBN;
+  // This item's key tiles [tb, te): all of them, or one range of a split item
+  // (tb even, so every tile keeps the ring slot parity t & 1).
+  const int tb = it.kt1 > 0 ? it.kt0 : 0;
+  const int te = it.kt1 > 0 ? min(it.kt1, ntiles) : ntiles;
   // First key tile that crosses the causal diagonal of the item's rows.
   [[maybe_unused]] const int tdiag = it.q_start / kBN;
 
@@ -754,9 +758,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // while the VALU reduces tile t+1's max.
   f32x16 s[kBN / 32];
   bf16x8 pb[kBN / 16];
-  load_k(0, IC<0>{});
-  load_v(0, IC<0>{});
-  if (ntiles > 1) load_k(1, IC<1>{});
+  load_k(tb, IC<0>{});
+  load_v(tb, IC<0>{});
+  if (te > tb + 1) load_k(tb + 1, IC<1>{});
   if constexpr (QNORM) qnorm_apply();
   publish();
   // Every wave computes the first scores, also one whose rows all lie past
@@ -764,7 +768,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // where masked) and the steady loop below, which every wave runs, starts
   // from defined scores and a finite reference.
   qk(IC<0>{}, s);
-  if (needs_mask(0)) mask(s, 0);
+  if (needs_mask(tb)) mask(s, tb);
   update_max(s);
   // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
   __syncthreads();
@@ -799,21 +803,21 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
     publish();
   };
-  int t = 0;
+  int t = tb;
   constexpr int kTail = CAUSAL ? 4 : 3;
-  for (; t + kTail < ntiles; t += 2) {
+  for (; t + kTail < te; t += 2) {
     steady(t, IC<0>{});
     steady(t + 1, IC<1>{});
   }
   // Remaining iterations (at most kTail), with slot parity in a register.
-  for (; t < ntiles; ++t) {
+  for (; t < te; ++t) {
     const int par = t & 1;
-    if (t + 2 < ntiles) load_k(t + 2, par);
-    if (t + 1 < ntiles) load_v(t + 1, par ^ 1);
+    if (t + 2 < te) load_k(t + 2, par);
+    if (t + 1 < te) load_v(t + 1, par ^ 1);
     if (active) {
       if constexpr (F8 <= 1) probs_checked(s, pb, probs_part(s, pb));
       else probs(s, pb);
-      if (t + 1 < ntiles) {
+      if (t + 1 < te) {
         qk(par ^ 1, s);
         pv(par, pb);
         if (needs_mask(t + 1)) mask(s, t + 1);
@@ -828,8 +832,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (!active) return;
   const int qi = qrow0 + l32;
   const float l_tot = F8 == 2 ? lacc[0] : l_run + other_half(l_run, hi);
-  const float inv = 1.0f / l_tot;
   if (qi >= it.seg_len) return;
+  if (it.part > 0) {
+    // one key range of a split item: unnormalised rows, their reference max
+    // and row sum, for the merge pass
+    const int64_t row = int64_t(it.part - 1) * kBM + wave * 32 + l32;
+    float* po = sp.o + row * D + hi * 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + db * 32 + g * 8) =
+            make_float4(oacc[db][g * 4 + 0], oacc[db][g * 4 + 1], oacc[db][g * 4 + 2], oacc[db][g * 4 + 3]);
+    if (hi == 0) *reinterpret_cast<float2*>(sp.ml + 2 * row) = make_float2(m_run, l_tot);
+    return;
+  }
+  const float inv = 1.0f / l_tot;
   uint16_t* op = o + int64_t(it.seg_start + qi) * so + head_off + hi * 4;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -846,13 +864,55 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 template <int D, bool CAUSAL, bool QNORM = false, int RH = 0, int F8 = 0>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t sq, int64_t sk,
                   int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                  int kv_group, const QNormArgs& qn, hipStream_t stream, const F8Scales& fs = F8Scales{}) {
+                  int kv_group, const QNormArgs& qn, hipStream_t stream, const F8Scales& fs = F8Scales{},
+                  const SplitArgs& sp = SplitArgs{}) {
   const float c = scale * 1.4426950408889634f;  // scale * log2(e)
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QNORM, RH, F8>), dim3(unsigned(n_items)), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), sq, sk, sv, so, items, c,
-                     kv_group, qn, fs);
+                     kv_group, qn, fs, sp);
   return hipGetLastError();
+}
+
+// Merge of a split item's partial rows: with m_p, l_p, o_p the reference max,
+// row sum and unnormalised row of key range p (all relative to 2^m_p), the
+// row over all keys is sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M =
+// max_p m_p -- the streaming softmax's own rescale step, applied once per
+// range in key order (deterministic).  One workgroup per split item; each
+// thread produces 8 dims of a row at a time.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads)
+attn_merge_kernel(const MergeItem* __restrict__ merges, SplitArgs sp, uint16_t* __restrict__ o, int64_t so) {
+  const MergeItem g = merges[blockIdx.x];
+  const int rows = min(kBM, g.seg_len - g.q_start);
+  constexpr int CPR = D / 8;  // 8-dim chunks per row
+  for (int u = threadIdx.x; u < rows * CPR; u += kMergeThreads) {
+    const int r = u / CPR, ch = u % CPR;
+    float M = -INFINITY;
+    for (int p = 0; p < g.nparts; ++p) M = fmaxf(M, sp.ml[2 * (int64_t(g.part0 + p) * kBM + r)]);
+    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < g.nparts; ++p) {
+      const int64_t row = int64_t(g.part0 + p) * kBM + r;
+      const float2 ml = *reinterpret_cast<const float2*>(sp.ml + 2 * row);
+      const float w = exp2f(ml.x - M);
+      L = fmaf(w, ml.y, L);
+      const float4* src = reinterpret_cast<const float4*>(sp.o + row * D + ch * 8);
+      const float4 a = src[0], b = src[1];
+      acc[0] = fmaf(w, a.x, acc[0]); acc[1] = fmaf(w, a.y, acc[1]);
+      acc[2] = fmaf(w, a.z, acc[2]); acc[3] = fmaf(w, a.w, acc[3]);
+      acc[4] = fmaf(w, b.x, acc[4]); acc[5] = fmaf(w, b.y, acc[5]);
+      acc[6] = fmaf(w, b.z, acc[6]); acc[7] = fmaf(w, b.w, acc[7]);
+    }
+    const float inv = 1.0f / L;
+    uint4 pk;
+    pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<uint4*>(o + int64_t(g.seg_start + g.q_start + r) * so + g.head * D + ch * 8) = pk;
+  }
 }
 
 }  // namespace
@@ -860,23 +920,39 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, int64_t 
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int32_t D,
                                 int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                 const WorkItem* items, int64_t n_items, float scale,
-                                int32_t kv_group, bool causal, hipStream_t stream) {
+                                int32_t kv_group, bool causal, hipStream_t stream, const SplitArgs& sp) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
   const QNormArgs none{};
+  const F8Scales nofs{};
   if (D == 128)
-    return causal ? launch<128, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream)
-                  : launch<128, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream);
+    return causal ? launch<128, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream, nofs, sp)
+                  : launch<128, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream, nofs, sp);
   if (D == 64)
-    return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream)
-                  : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream);
+    return causal ? launch<64, true>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream, nofs, sp)
+                  : launch<64, false>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, none, stream, nofs, sp);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const MergeItem* merges, int64_t n_merges, const SplitArgs& sp, void* o, int32_t D,
+                             int64_t so, hipStream_t stream) {
+  if (n_merges <= 0) return hipSuccess;
+  if (n_merges > int64_t(INT32_MAX)) return hipErrorInvalidValue;
+  if (D == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(unsigned(n_merges)), dim3(kMergeThreads), 0, stream, merges, sp,
+                       static_cast<uint16_t*>(o), so);
+  else if (D == 64)
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(unsigned(n_merges)), dim3(kMergeThreads), 0, stream, merges, sp,
+                       static_cast<uint16_t*>(o), so);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
                                  void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks, int64_t sv,
                                  int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
-                                 bool causal, hipStream_t stream) {
+                                 bool causal, hipStream_t stream, const SplitArgs& sp) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
   const QNormArgs none{};
@@ -884,9 +960,9 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s
 #define H3A_F8_CASE(DD)                                                                                     \
   if (D == DD)                                                                                              \
     return causal ? launch<DD, true, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,        \
-                                                  kv_group, none, stream, fs)                              \
+                                                  kv_group, none, stream, fs, sp)                          \
                   : launch<DD, false, false, 0, 1>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,       \
-                                                   kv_group, none, stream, fs);
+                                                   kv_group, none, stream, fs, sp);
   H3A_F8_CASE(128) H3A_F8_CASE(64)
 #undef H3A_F8_CASE
   return hipErrorInvalidValue;
@@ -895,7 +971,7 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
                                const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
                                int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                               int32_t kv_group, bool causal, hipStream_t stream) {
+                               int32_t kv_group, bool causal, hipStream_t stream, const SplitArgs& sp) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1) return hipErrorInvalidValue;
   const QNormArgs none{};
@@ -904,9 +980,9 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, 
 #define H3A_F8PV_CASE(DD)                                                                                   \
   if (D == DD)                                                                                              \
     return causal ? launch<DD, true, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale, \
-                                                  kv_group, none, stream, fs)                              \
+                                                  kv_group, none, stream, fs, sp)                          \
                   : launch<DD, false, false, 0, 2>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale,\
-                                                   kv_group, none, stream, fs);
+                                                   kv_group, none, stream, fs, sp);
   H3A_F8PV_CASE(128) H3A_F8PV_CASE(64)
 #undef H3A_F8PV_CASE
   return hipErrorInvalidValue;
@@ -916,13 +992,15 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
                                       int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                       const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
                                       const float* gamma_q, float eps, const float* cos_sin, int64_t S,
-                                      int32_t rot_dim, hipStream_t stream) {
+                                      int32_t rot_dim, hipStream_t stream, const SplitArgs& sp) {
   if (n_items <= 0) return hipSuccess;
   if (kv_group < 1 || rot_dim % 32 != 0) return hipErrorInvalidValue;
   const QNormArgs qn{gamma_q, cos_sin, S, rot_dim / 2, eps};
+  const F8Scales nofs{};
 #define H3A_QNORM_CASE(DD, R)                                                                               \
   if (D == DD && rot_dim == 32 * R)                                                                         \
-    return launch<DD, false, true, R>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, qn, stream);
+    return launch<DD, false, true, R>(q, k, v, o, sq, sk, sv, so, items, n_items, scale, kv_group, qn, stream, \
+                                      nofs, sp);
   H3A_QNORM_CASE(128, 0) H3A_QNORM_CASE(128, 1) H3A_QNORM_CASE(128, 2) H3A_QNORM_CASE(128, 3)
   H3A_QNORM_CASE(128, 4) H3A_QNORM_CASE(64, 0) H3A_QNORM_CASE(64, 1) H3A_QNORM_CASE(64, 2)
 #undef H3A_QNORM_CASE

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(kPlanThreads) noalloc_plan_kernel(NoAllocPlanA
   if (b >= a.n_blocks) return;
   const int32_t xcd = b % a.n_xcd, pos = b / a.n_xcd;
   const int64_t i = (int64_t(pos / kChunk) * a.n_xcd + xcd) * kChunk + pos % kChunk;
-  WorkItem w{0, 0, 0, 0, 0, {0, 0, 0}};
+  WorkItem w{0, 0, 0, 0, 0, 0, 0, 0};
   if (i < a.n_items) {
     int32_t lo = 0, hi = a.nseg - 1;  // last segment whose first item is <= i
     while (lo < hi) {

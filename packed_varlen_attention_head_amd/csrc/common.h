@@ -10,19 +10,48 @@
 namespace h3a {
 
 // One attention work item: query rows [q_start, q_start + block_m) of one
-// segment and one head.  seg_len == 0 marks a padding item (the workgroup
+// segment and one head, against the segment's 64-key tiles [kt0, kt1)
+// (kt1 == 0: all of them).  seg_len == 0 marks a padding item (the workgroup
 // exits at once).  vt_col0 is the segment's first column in the transposed
 // E4M3 V layout, where every segment is padded to whole 64-key tiles (the sum
 // of the earlier segments' padded lengths); only the FP8-PV kernel reads it.
+// part == 0: the item covers all keys and stores its normalised rows; part
+// > 0: it covers one key range of a split item and stores its unnormalised
+// rows with their running max and row sum in partial slot part - 1, for the
+// merge pass (kt0 is then even, so tile parities match a full item's).
 struct WorkItem {
   int32_t seg_start;
   int32_t seg_len;
   int32_t q_start;  // relative to seg_start
   int32_t head;
   int32_t vt_col0;
-  int32_t reserved[3];
+  int32_t kt0;
+  int32_t kt1;
+  int32_t part;
 };
 static_assert(sizeof(WorkItem) == 32, "WorkItem is uploaded as 8 x int32");
+
+// One split item to merge: query rows [q_start, q_start + block_m) of one
+// segment and head, whose key ranges wrote partial slots part0 .. part0 +
+// nparts - 1 (in key order).
+struct MergeItem {
+  int32_t seg_start;
+  int32_t seg_len;
+  int32_t q_start;
+  int32_t head;
+  int32_t part0;
+  int32_t nparts;
+  int32_t pad[2];
+};
+static_assert(sizeof(MergeItem) == 32, "MergeItem is uploaded as 8 x int32");
+
+// Partial results of split items, in device memory: slot p holds block_m rows
+// of D fp32 unnormalised outputs at o + p * block_m * D, and per row the
+// running max (scale * log2(e) units) and row sum at ml + 2 * (p * block_m + r).
+struct SplitArgs {
+  float* o;
+  float* ml;
+};
 
 // Keys per tile of the transposed E4M3 V layout (and of the attention's K/V
 // tiles).
@@ -36,6 +65,20 @@ constexpr int32_t kVtTile = 64;
 // chunk's costliest (last) query tiles first.
 std::vector<WorkItem> plan_tiles(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
                                  int32_t n_xcd, bool causal = false);
+
+// Split policies of plan_tiles_split.
+constexpr int32_t kSplitAuto = 0, kSplitNever = 1, kSplitAlways = 2;
+
+// As plan_tiles, but (bidirectional plans) an item's keys may be cut into
+// even-tile ranges, each its own item writing a partial slot, so that the
+// longest items no longer set the time on `slots` concurrent workgroups:
+// kSplitAuto picks the largest part length that minimises a list-scheduling
+// estimate of the makespan plus the merge pass; kSplitAlways cuts every item
+// of four or more key tiles into parts of about a third (for tests).  Fills
+// merges (one per split item) and *n_parts (partial slots used).
+std::vector<WorkItem> plan_tiles_split(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
+                                       int32_t n_xcd, int32_t slots, bool causal, int32_t policy,
+                                       std::vector<MergeItem>* merges, int64_t* n_parts);
 
 // ---- kernel launchers (one per .hip file) ---------------------------------
 
@@ -71,7 +114,8 @@ constexpr int kAttnBlockM_F32 = 64;
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int32_t D,
                                 int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                 const WorkItem* items, int64_t n_items, float scale,
-                                int32_t kv_group, bool causal, hipStream_t stream);
+                                int32_t kv_group, bool causal, hipStream_t stream,
+                                const SplitArgs& sp = SplitArgs{});
 
 // Bidirectional bf16 attention that RMS-normalises and rotates the raw q rows
 // in its prologue (rot_dim a multiple of 32, at most D); q' is bit-identical
@@ -80,7 +124,8 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
                                       int64_t sq, int64_t sk, int64_t sv, int64_t so,
                                       const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
                                       const float* gamma_q, float eps, const float* cos_sin, int64_t S,
-                                      int32_t rot_dim, hipStream_t stream);
+                                      int32_t rot_dim, hipStream_t stream,
+                                      const SplitArgs& sp = SplitArgs{});
 
 // Attention whose q and k are FP8 E4M3 codes (token strides in bytes) with
 // one E8M0 scale per 32 head dims, head-major (q8s [Hq][S][D/32], k8s
@@ -89,7 +134,8 @@ hipError_t launch_attn_fwd_bf16_qnorm(const void* q, const void* k, const void* 
 hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s, const void* k8s, const void* v,
                                  void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks, int64_t sv,
                                  int64_t so, const WorkItem* items, int64_t n_items, float scale, int32_t kv_group,
-                                 bool causal, hipStream_t stream);
+                                 bool causal, hipStream_t stream,
+                                 const SplitArgs& sp = SplitArgs{});
 
 // The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
 // token strides sq8, sk8 in bytes) with one E8M0 scale per 32 head dims in
@@ -105,7 +151,14 @@ hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, v
 hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, const void* q8s, const void* k8s,
                                const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
                                int64_t vt_cols, int64_t so, const WorkItem* items, int64_t n_items, float scale,
-                               int32_t kv_group, bool causal, hipStream_t stream);
+                               int32_t kv_group, bool causal, hipStream_t stream,
+                               const SplitArgs& sp = SplitArgs{});
+
+// Merge pass of a split plan: for each of the n_merges split items, the
+// softmax-weighted combination of its key ranges' partial rows (sp), written
+// as bf16 rows of o [S, H, D] (token stride so elements).
+hipError_t launch_attn_merge(const MergeItem* merges, int64_t n_merges, const SplitArgs& sp, void* o, int32_t D,
+                             int64_t so, hipStream_t stream);
 
 // Columns of the transposed E4M3 V layout: every segment padded to whole
 // kVtTile-key tiles.

@@ -203,9 +203,14 @@ CAUSAL_GQA_16K = CAUSAL_GQA_TEXT.replace(
     note="one 16,384-token causal prompt, 32 q heads / 8 kv heads, interleaved M-RoPE",
 )
 
+# One GPU's share of the S = 20,423 request when its 24 heads are spread over
+# eight GPUs (head parallelism): 3 heads, the same packing.
+H3_S20423_3H = H3_S20423.replace(name="h3_s20423_3heads_bf16", heads=3,
+                                 note="S=20,423 packing, 3 of its 24 heads (one GPU of eight)")
+
 # Every bf16 workload, by name (the benchmark can run any of them).
 BF16 = {w.name: w for w in (TWO_SEG, H3_S20423, H3_S25103, RAGGED64, VIT3D_TILES, MROPE_PACKED, CAUSAL_GQA_TEXT,
-                            CAUSAL_GQA_16K, VISION_FRAMES)}
+                            CAUSAL_GQA_16K, VISION_FRAMES, H3_S20423_3H)}
 
 # The configuration the headline throughput is quoted on.
 HEADLINE = H3_S20423

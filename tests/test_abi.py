@@ -407,3 +407,10 @@ def test_noalloc_validates_like_the_cached_entry():
     assert attn_noalloc([0, 10], dtype=7) == h3a.H3A_EDTYPE
     assert attn_noalloc([0, 10, 9]) == h3a.H3A_EINVAL and "decreases" in h3a.last_error()
     assert attn_noalloc([0, 10], causal=2) == h3a.H3A_EINVAL
+
+
+def test_set_split_policy():
+    assert h3a.lib().h3a_set_split_policy(7) == h3a.H3A_EINVAL and "split policy" in h3a.last_error()
+    assert h3a.lib().h3a_set_split_policy(-1) == h3a.H3A_EINVAL
+    for p in (h3a.H3A_SPLIT_NEVER, h3a.H3A_SPLIT_ALWAYS, h3a.H3A_SPLIT_AUTO):
+        assert h3a.lib().h3a_set_split_policy(p) == h3a.H3A_OK

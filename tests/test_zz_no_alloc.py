@@ -5,7 +5,8 @@ on two calls in a row, the second with a smaller input, for bf16 and fp32,
 bidirectional and causal, grouped K/V; on two streams back to back (the
 second call waits for the first's kernel before rewriting the shared plan);
 and on the headline packing (S = 20,423, 24 heads), which is also compared
-with the oracle on sampled rows."""
+with the oracle on sampled rows.  The reference calls use the never-split
+policy: a split plan's items differ from the fixed-array plan's."""
 from __future__ import annotations
 
 import numpy as np
@@ -21,9 +22,12 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     require_gpu()
-    yield
     import packed_varlen_attention_head_amd as h3a
 
+    # the reference path on the same (unsplit) work items as the fixed-array plan
+    h3a.set_split_policy(h3a.H3A_SPLIT_NEVER)
+    yield
+    h3a.set_split_policy(h3a.H3A_SPLIT_AUTO)
     h3a.release_caches()
 
 

@@ -142,7 +142,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // it a branch-free scalar, so loads need no per-lane waterfall.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows, int max_rows,
                                                             int stride_bytes) {
-  const int r = __builtin_amdgcn_readfirstlane(rows < 0 ? 0 : (rows > max_rows ? max_rows : rows));
+  // clamp in two scalar steps: as one clamp the compiler picks the vector
+  // v_med3 and reads the result back, two instructions per descriptor per tile
+  int r = __builtin_amdgcn_readfirstlane(rows);
+  r = r < 0 ? 0 : r;
+  asm volatile("" : "+s"(r));
+  r = r > max_rows ? max_rows : r;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            __builtin_amdgcn_readfirstlane(r * stride_bytes), 0x00020000);
 }
@@ -288,7 +293,17 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 2, ln * 2, 0, 0, 0);
   };
 
-  const WorkItem it = items[blockIdx.x];
+  // The item is uniform over the workgroup: its fields in scalar registers,
+  // so per-tile descriptor arithmetic stays on the scalar unit.
+  WorkItem it = items[blockIdx.x];
+  it.seg_start = __builtin_amdgcn_readfirstlane(it.seg_start);
+  it.seg_len = __builtin_amdgcn_readfirstlane(it.seg_len);
+  it.q_start = __builtin_amdgcn_readfirstlane(it.q_start);
+  it.head = __builtin_amdgcn_readfirstlane(it.head);
+  it.vt_col0 = __builtin_amdgcn_readfirstlane(it.vt_col0);
+  it.kt0 = __builtin_amdgcn_readfirstlane(it.kt0);
+  it.kt1 = __builtin_amdgcn_readfirstlane(it.kt1);
+  it.part = __builtin_amdgcn_readfirstlane(it.part);
   if (it.seg_len <= 0) return;
 
   const int tid = threadIdx.x;
@@ -411,6 +426,11 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -1e30f;  // reference max of scale*log2(e)*score
+  // Kept with it (updated only where m_run moves, not per tile): the bound
+  // past which a tile max raises it, and F8 == 2's exponent offset.
+  constexpr float kSlack = F8 == 2 ? kRescaleSlackF8 : kRescaleSlack;
+  float m_thr = m_run + kSlack;
+  [[maybe_unused]] float m_off = kProbOffsetF8 - m_run;
   float l_run = 0.f;     // this lane's partial row sum (its 16-of-32 keys)
   // F8 == 2: the row sums come from the matrix core instead -- an all-ones
   // A operand against the E4M3 probabilities puts sum_k p[k][q] in every
@@ -611,7 +631,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = pair_max(mx) * c;
-    const bool grow = mx > m_run + (F8 == 2 ? kRescaleSlackF8 : kRescaleSlack);
+    const bool grow = mx > m_thr;
     if (__builtin_expect(__any(grow), 0)) {
       // Rare after the first tiles; the empty asm keeps the compiler from
       // speculating the accumulator rescale onto every tile.
@@ -619,6 +639,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const float m_new = grow ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;
+      m_thr = m_run + kSlack;
+      if constexpr (F8 == 2) m_off = kProbOffsetF8 - m_run;
       l_run *= alpha;
       if constexpr (F8 == 2) lacc *= alpha;
 #pragma unroll
@@ -668,6 +690,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const float m_new = mx > m_run ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;
+      m_thr = m_run + kSlack;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
@@ -679,7 +702,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if constexpr (F8 == 2) {
       // E4M3 weights 2^4 p (p <= 2^4 against the reference, so <= 256), dword
       // g = keys 8g + 4 hi + {0..3}.
-      const float moff = kProbOffsetF8 - m_run;
+      const float moff = m_off;
       int d[8];
 #pragma unroll
       for (int g = 0; g < 8; ++g) {

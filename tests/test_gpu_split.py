@@ -110,13 +110,14 @@ def test_split_fused_q_norm():
     compare(o, ref, "bf16", "o (split, fused q norm)")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", ["fp8qk", "fp8"])
-def test_split_fp8(mode):
+def test_split_fp8(mode, D):
     from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, gpu_fp8, gpu_fp8qk, mx_operands, weight_rounding_bound
 
-    cu, q, k, v = inputs(931, EDGE_LENS, 4, 2, 128)
-    log(f"[split {mode}] S={int(cu[-1])}")
-    scale = 1.0 / np.sqrt(128)
+    cu, q, k, v = inputs(931 + D, EDGE_LENS, 4, 2, D)
+    log(f"[split {mode}] D={D} S={int(cu[-1])}")
+    scale = 1.0 / np.sqrt(D)
     if mode == "fp8qk":
         o = to_f64(gpu_fp8qk(q, k, v, cu, scale))
         qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))

@@ -479,7 +479,8 @@ void h3a_release_caches(void);
  * the kernel time, charging the merge pass for reading every partial result
  * back, improves by more than 10%; H3A_SPLIT_NEVER never; H3A_SPLIT_ALWAYS
  * cuts every item of four or more key tiles into about three ranges (for
- * tests).  The policy applies to plans built afterwards; cached plans keep
+ * tests); a plan that would need more than 16,384 partial results (1.1 GB of
+ * workspace) stays unsplit.  The policy applies to plans built afterwards; cached plans keep
  * theirs (they are keyed by it).  Calls under stream capture always use the
  * unsplit items of a cached plan, so a graph never holds the shared partial
  * workspace; calls outside capture that use one plan's split items are

@@ -74,7 +74,8 @@ constexpr int32_t kSplitAuto = 0, kSplitNever = 1, kSplitAlways = 2;
 // longest items no longer set the time on `slots` concurrent workgroups:
 // kSplitAuto picks the largest part length that minimises a list-scheduling
 // estimate of the makespan plus the merge pass; kSplitAlways cuts every item
-// of four or more key tiles into parts of about a third (for tests).  Fills
+// of four or more key tiles into parts of about a third (for tests).  Plans
+// needing more than 16,384 partial slots stay unsplit.  Fills
 // merges (one per split item) and *n_parts (partial slots used).
 std::vector<WorkItem> plan_tiles_split(const int32_t* cu, int32_t nseg, int32_t heads, int32_t block_m,
                                        int32_t n_xcd, int32_t slots, bool causal, int32_t policy,

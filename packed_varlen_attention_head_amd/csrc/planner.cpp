@@ -67,6 +67,10 @@ constexpr double kMergeLaunchKeys = 192.0;
 constexpr double kSplitMinGain = 0.10;
 // Shortest key range of a split item in automatic plans (tiles).
 constexpr int32_t kMinPartTiles = 8;
+// Most partial slots a split plan may use: 16,384 slots of 128 rows x 128
+// fp32 dims (+ max and sum) are 1.1 GB of workspace.  Splits only pay where
+// items are few, far below this.
+constexpr int64_t kMaxSplitParts = 16384;
 
 int32_t key_tiles(int32_t len) { return (len + kVtTile - 1) / kVtTile; }
 
@@ -194,6 +198,11 @@ std::vector<WorkItem> plan_tiles_split(const int32_t* cu, int32_t nseg, int32_t 
 
   int32_t Lp = 0;  // 0: no split
   if (policy == kSplitAuto) {
+    // With many rounds of items per slot the ragged last round is a small
+    // share of the time: not worth estimating.
+    int64_t n_items = 0;
+    for (int32_t s : order) n_items += int64_t(heads) * ((cu[s + 1] - cu[s] + block_m - 1) / block_m);
+    if (n_items > 64 * int64_t(slots)) return plan_tiles(cu, nseg, heads, block_m, n_xcd, causal);
     const int32_t nk_max = key_tiles(cu[order[0] + 1] - cu[order[0]]);
     auto estimate = [&](int32_t L) {
       std::vector<double> costs;
@@ -210,6 +219,7 @@ std::vector<WorkItem> plan_tiles_split(const int32_t* cu, int32_t nseg, int32_t 
           if (k > 1) parts += int64_t(nq) * heads;
         }
       }
+      if (parts > kMaxSplitParts) return 1e300;
       return list_makespan(std::move(costs), slots) +
              (parts > 0 ? kMergeLaunchKeys + kMergeKeysPerPart * double(parts) : 0.0);
     };
@@ -225,6 +235,14 @@ std::vector<WorkItem> plan_tiles_split(const int32_t* cu, int32_t nseg, int32_t 
     }
     if (Lp == 0) return plan_tiles(cu, nseg, heads, block_m, n_xcd, causal);
   }
+
+  // Partial slots this choice needs: none at all when over the limit.
+  int64_t need = 0;
+  for (int32_t s : order) {
+    const int32_t k = parts_for(s, Lp);
+    if (k > 1) need += int64_t(k) * heads * ((cu[s + 1] - cu[s] + block_m - 1) / block_m);
+  }
+  if (need > kMaxSplitParts) return plan_tiles(cu, nseg, heads, block_m, n_xcd, causal);
 
   std::vector<Chunk> chunks;
   int32_t next_part = 0;

@@ -120,3 +120,12 @@ def test_auto_policy_choices(tool):
         assert bool(merges) == split, (h, len(lens), len(merges))
         if split:  # only the long segment's items are cut
             assert {m[1] for m in merges} == {16200}
+
+
+def test_split_partial_slots_are_capped(tool):
+    """A forced split that would need more than 16,384 partial slots stays unsplit."""
+    items, merges, parts = plan(tool, ALWAYS, 64, [16384] * 3)  # 3 x 128 x 64 items x 3 ranges
+    assert not merges and parts == 0
+    check_plan(items, merges, parts, 64, [16384] * 3)
+    items, merges, parts = plan(tool, ALWAYS, 8, [16384] * 3)  # 3,072 items x 3 ranges = 9,216
+    assert parts == 9216 and len(merges) == 3072

@@ -34,7 +34,9 @@ sqrt are the only library primitives used):
    The encoder text tower's causal grouped-query attention (query i of a
    segment sees keys 0..i; K/V heads broadcast over their query groups) is
    section 5b; the low-precision variant (Q and K rounded to FP8 E4M3 before
-   the score product) is section 5c, and its per-block-scaled form section 5d.
+   the score product) is section 5c, its per-block-scaled form section 5d,
+   and the INT8 score product with per-token Q and per-key-block K scales
+   section 5e.
 
 Readings where the pages are silent:
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]
@@ -541,6 +543,113 @@ def varlen_attention_mx(q, k, v, cu, scale: float, causal: bool = False) -> np.n
     block of each segment; exact softmax weights.  (A kernel that also rounds
     the weights to E4M3 for the PV product differs from this by that rounding.)"""
     return varlen_attention_gqa(mx_round(q), mx_round(k), mx_round_keys(v, cu), cu, scale, causal=causal)
+
+
+# ----------------------------------------------------------------------------
+# 5e. INT8 scores with per-token Q and per-key-block K scales
+#
+# The pages' GB10 image offers INT8 attention beside its FP8-class Sage
+# kernels: Comfy Kitchen's approximate INT8 Q/K/V kernel, a Sol-Attn switch
+# for INT8 QK, and a fused Q RMSNorm + rot96 RoPE -> "Sage Q-INT8" tail
+# (H3 Blackwell Runtime README, request-level attention backends; h3-spark
+# model card, "What this config does").  Reading where the pages stop short
+# (SageAttention's per-block smoothing-free form): every query row (token and
+# head) of q shares one scale, and every block of 64 consecutive keys of one
+# k head (aligned at the segment start; a segment's last block may be
+# shorter) shares one scale over its keys and head dims.  With amax the
+# block's largest magnitude, in fp32: scale = amax / 127 and code =
+# rint(x * (127 / amax)) (nearest, ties to even) clamped to [-127, 127]; each
+# element stands for code * scale.  An all-zero block has scale 0 and codes
+# 0.  A block holding a NaN has a NaN scale, one holding an infinity an
+# infinite scale, and codes 0 there: the non-finite value reaches the scores
+# as NaN.  v, the softmax and the PV product stay as in section 5.
+# Key blocks are numbered segment by segment: block j of segment s is
+# sum over earlier segments of ceil(L / 64), plus j.
+# ----------------------------------------------------------------------------
+
+I8_KEY_BLOCK = 64
+
+
+def _i8_quantize(x32, amax):
+    """(codes int8, scale float32) of fp32 values x32 whose block maxima amax
+    (fp32, broadcast against x32) are given."""
+    with np.errstate(all="ignore"):
+        inv = np.where(amax == 0, np.float32(0), np.float32(127) / amax).astype(np.float32)
+        r = np.rint((x32 * inv).astype(np.float32))
+        codes = np.where(np.isfinite(r), np.clip(r, -127, 127), 0).astype(np.int8)
+        scale = (amax / np.float32(127)).astype(np.float32)
+    return codes, scale
+
+
+def i8_quantize_rows(x):
+    """x [S, H, D] -> (codes int8 [S, H, D], scales float32 [H, S]): one scale
+    per token and head."""
+    x32 = np.asarray(x, dtype=np.float32)
+    with np.errstate(invalid="ignore"):
+        amax = np.abs(x32).max(axis=-1, keepdims=True)  # NaN propagates
+    codes, scale = _i8_quantize(x32, amax)
+    return codes, np.ascontiguousarray(scale[..., 0].T)
+
+
+def i8_key_blocks(cu) -> np.ndarray:
+    """Number of the first 64-key block of each segment, and the total: int64
+    [nseg + 1]."""
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    return np.concatenate([[0], np.cumsum(-(-lens // I8_KEY_BLOCK))]).astype(np.int64)
+
+
+def i8_quantize_key_blocks(x, cu):
+    """x [S, H, D] -> (codes int8 [S, H, D], scales float32 [H, n_blocks]): one
+    scale per block of 64 keys of a segment and head."""
+    x32 = np.asarray(x, dtype=np.float32)
+    first = i8_key_blocks(cu)
+    codes = np.zeros(x32.shape, dtype=np.int8)
+    scales = np.zeros((x32.shape[1], int(first[-1])), dtype=np.float32)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for j, r0 in enumerate(range(a, b, I8_KEY_BLOCK)):
+            r1 = min(r0 + I8_KEY_BLOCK, b)
+            blk = x32[r0:r1]  # [rows, H, D]
+            with np.errstate(invalid="ignore"):
+                amax = np.abs(blk).max(axis=(0, 2))  # [H]
+            c, sc = _i8_quantize(blk, amax[None, :, None])
+            codes[r0:r1] = c
+            scales[:, first[s] + j] = sc[0, :, 0]
+    return codes, scales
+
+
+def i8_dequantize_rows(codes, scales) -> np.ndarray:
+    """code * scale of its token and head, fp64."""
+    return codes.astype(np.float64) * np.asarray(scales, dtype=np.float64).T[..., None]
+
+
+def i8_dequantize_key_blocks(codes, scales, cu) -> np.ndarray:
+    """code * scale of its key block and head, fp64."""
+    first = i8_key_blocks(cu)
+    out = np.zeros(codes.shape, dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for j, r0 in enumerate(range(a, b, I8_KEY_BLOCK)):
+            r1 = min(r0 + I8_KEY_BLOCK, b)
+            out[r0:r1] = codes[r0:r1].astype(np.float64) * np.asarray(scales, dtype=np.float64)[:, first[s] + j][
+                None, :, None]
+    return out
+
+
+def i8_round_q(q) -> np.ndarray:
+    """q through its INT8 codes (per-token scales), fp64."""
+    return i8_dequantize_rows(*i8_quantize_rows(q))
+
+
+def i8_round_k(k, cu) -> np.ndarray:
+    """k through its INT8 codes (per-64-key-block scales), fp64."""
+    return i8_dequantize_key_blocks(*i8_quantize_key_blocks(k, cu), cu)
+
+
+def varlen_attention_i8qk(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """varlen_attention_gqa with q and k replaced by what their INT8 codes stand
+    for (section 5e); v and the softmax exact."""
+    return varlen_attention_gqa(i8_round_q(q), i8_round_k(k, cu), v, cu, scale, causal=causal)
 
 
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):

@@ -724,6 +724,91 @@ def check_mx_keys_and_attention(O):
         assert np.abs(unscaled - exact).sum() > 4 * np.abs(base - exact).sum(), e
 
 
+def check_i8_quantize(O):
+    """Hand-derived rows (an fp32 product that ties at 127; integer ties to even); on
+    wide-range random rows: codes within +-127, each row's largest magnitude at +-127,
+    error at most half a step, the same codes for the row times any power of two;
+    zero rows give zeros, a NaN or an infinity poisons only its own row's scale."""
+    g = golden()["i8"]
+    for row in (g["row_a"], g["row_b"]):
+        c, sc = O.i8_quantize_rows(np.array(row["x"])[None, None, :])
+        assert list(c[0, 0]) == row["codes"] and float(sc[0, 0]) == row["scale"], (row, c, sc)
+    r = _rng(41)
+    x = r.normal(size=(30, 3, 64)) * 2.0 ** r.integers(-20, 20, size=(30, 3, 1)).astype(np.float64)
+    x = x.astype(np.float32).astype(np.float64)
+    c, sc = O.i8_quantize_rows(x)
+    assert c.dtype == np.int8 and sc.shape == (3, 30) and sc.dtype == np.float32
+    assert np.all(np.abs(c.astype(np.int64)) <= 127)
+    top = np.abs(x).argmax(axis=-1)
+    assert np.all(np.abs(np.take_along_axis(c, top[..., None], -1)) == 127)
+    step = sc.T.astype(np.float64)[..., None]
+    err = np.abs(O.i8_dequantize_rows(c, sc) - x)
+    assert np.all(err <= 0.5 * step * (1 + 1e-6) + 1e-6 * np.abs(x))
+    for k in (-7, 3, 11):
+        c2, sc2 = O.i8_quantize_rows(x * 2.0 ** k)
+        assert np.array_equal(c2, c) and np.array_equal(sc2, (sc * np.float32(2.0 ** k)).astype(np.float32))
+    y = x.copy()
+    y[4, 1] = 0.0
+    y[5, 2, 7] = np.nan
+    y[6, 0, 3] = -np.inf
+    cy, sy = O.i8_quantize_rows(y)
+    assert np.all(cy[4, 1] == 0) and sy[1, 4] == 0
+    assert np.isnan(sy[2, 5]) and np.all(cy[5, 2] == 0)
+    assert np.isinf(sy[0, 6]) and np.all(cy[6, 0] == 0)
+    keep = np.ones((30, 3), bool)
+    keep[[4, 5, 6], [1, 2, 0]] = False
+    assert np.array_equal(cy[keep], c[keep]) and np.array_equal(sy.T[keep], sc.T[keep])
+
+
+def check_i8_key_blocks_and_attention(O):
+    """Key blocks: hand-derived numbering; blocks of 64 keys start at each segment's start (a
+    segment quantises the same alone as packed) and a scalar loop gives each block's scale;
+    attention on operands already on their INT8 grids is the exact attention, and otherwise
+    it is the exact attention of what the codes stand for, q and k both rounded."""
+    g = golden()["i8"]["key_blocks"]
+    cu = np.concatenate([[0], np.cumsum(g["lens"])])
+    assert list(O.i8_key_blocks(cu)) == g["first"]
+    r = _rng(42)
+    lens = [65, 0, 130, 1, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    k = (r.normal(size=(S, 2, 32)) * np.repeat(2.0 ** np.array([-5.0, 0, 3.0, 0, 8.0]), lens)[:, None, None])
+    k = k.astype(np.float32).astype(np.float64)
+    c, sc = O.i8_quantize_key_blocks(k, cu)
+    first = O.i8_key_blocks(cu)
+    assert sc.shape == (2, int(first[-1]))
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        a, b = int(a), int(b)
+        if b == a:
+            continue
+        cs, ss = O.i8_quantize_key_blocks(k[a:b], np.array([0, b - a]))
+        assert np.array_equal(cs, c[a:b]) and np.array_equal(ss, sc[:, first[s]:first[s + 1]])
+        for j, r0 in enumerate(range(a, b, 64)):
+            rows = range(r0, min(r0 + 64, b))
+            for h in range(2):
+                amax = max(abs(float(k[i, h, d])) for i in rows for d in range(32))
+                assert float(sc[h, first[s] + j]) == float(np.float32(amax) / np.float32(127))
+                assert max(abs(int(c[i, h, d])) for i in rows for d in range(32)) == 127
+    # operands on their grids pass through exactly
+    q = r.integers(-127, 128, size=(S, 4, 32)).astype(np.float64)
+    q[:, :, 0] = 127.0
+    kk = r.integers(-127, 128, size=(S, 2, 32)).astype(np.float64)
+    kk[:, :, 5] = -127.0
+    v = r.normal(size=(S, 2, 32))
+    for causal in (False, True):
+        assert np.array_equal(O.varlen_attention_i8qk(q, kk, v, cu, 1e-3, causal),
+                              O.varlen_attention_gqa(q, kk, v, cu, 1e-3, causal))
+    qn, kn = r.normal(size=(S, 4, 32)), r.normal(size=(S, 2, 32))
+    got = O.varlen_attention_i8qk(qn, kn, v, cu, 0.2)
+    qd = O.i8_dequantize_rows(*O.i8_quantize_rows(qn))
+    kd = O.i8_dequantize_key_blocks(*O.i8_quantize_key_blocks(kn, cu), cu)
+    assert np.array_equal(got, O.varlen_attention_gqa(qd, kd, v, cu, 0.2))
+    exact = O.varlen_attention_gqa(qn, kn, v, cu, 0.2)
+    only_q = O.varlen_attention_gqa(qd, kn, v, cu, 0.2)
+    assert not np.allclose(got, only_q, rtol=0, atol=1e-9) and not np.allclose(got, exact, rtol=0, atol=1e-6)
+    assert np.abs(got - exact).sum() / np.abs(exact).sum() < 0.05
+
+
 # ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
@@ -809,6 +894,8 @@ ALL_CHECKS = [
     check_mx_block_exponent,
     check_mx_quantize,
     check_mx_keys_and_attention,
+    check_i8_quantize,
+    check_i8_key_blocks_and_attention,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

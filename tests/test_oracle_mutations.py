@@ -258,6 +258,36 @@ def _mx_keys_global_blocks(v, cu):
     return oracle.mx_round(pad, axis=0)[: v.shape[0]]
 
 
+def _i8_rows_with(rounding=np.rint, levels=127):
+    def q(x):
+        x32 = np.asarray(x, dtype=np.float32)
+        amax = np.abs(x32).max(axis=-1, keepdims=True)
+        with np.errstate(all="ignore"):
+            inv = np.where(amax == 0, np.float32(0), np.float32(levels) / amax).astype(np.float32)
+            rr = rounding((x32 * inv).astype(np.float32))
+            codes = np.where(np.isfinite(rr), np.clip(rr, -127, 127), 0).astype(np.int8)
+            scale = (amax / np.float32(levels)).astype(np.float32)
+        return codes, np.ascontiguousarray(scale[..., 0].T)
+    return q
+
+
+def _i8_half_up(y):
+    return np.floor(y + np.float32(0.5))
+
+
+def _i8_keys_global_blocks(x, cu):
+    """Key blocks of 64 tokens counted from token 0 of the packing, not each segment's start."""
+    S = np.asarray(x).shape[0]
+    c, sc = oracle.i8_quantize_key_blocks(x, np.array([0, S]))
+    # spread the global blocks' scales over the per-segment numbering the dequantiser reads
+    first = oracle.i8_key_blocks(cu)
+    out = np.zeros((sc.shape[0], int(first[-1])), dtype=np.float32)
+    for s in range(len(cu) - 1):
+        for j, r0 in enumerate(range(int(cu[s]), int(cu[s + 1]), 64)):
+            out[:, first[s] + j] = sc[:, r0 // 64]
+    return c, out
+
+
 MUTANTS = {
     "bf16_round_7_bits": dict(bf16_round=_bf16_round_7_bits),
     "e4m3_decode_bias_8": dict(e4m3_decode=_decode_bias_8),
@@ -300,6 +330,12 @@ MUTANTS = {
     "attn_softmax_wrong_axis": dict(varlen_attention=_attn_softmax_wrong_axis),
     "attn_not_segmented": dict(varlen_attention=_attn_global_not_segmented),
     "weights_unnormalised": dict(attention_weights=_weights_unnormalised),
+    "i8_round_half_up": dict(i8_quantize_rows=_i8_rows_with(rounding=_i8_half_up)),
+    "i8_truncating": dict(i8_quantize_rows=_i8_rows_with(rounding=np.trunc)),
+    "i8_128_levels": dict(i8_quantize_rows=_i8_rows_with(levels=128)),
+    "i8_keys_not_segment_aligned": dict(i8_quantize_key_blocks=_i8_keys_global_blocks),
+    "i8qk_rounds_only_q": dict(varlen_attention_i8qk=lambda q, k, v, cu, scale, causal=False:
+                               oracle.varlen_attention_gqa(oracle.i8_round_q(q), k, v, cu, scale, causal)),
 }
 
 

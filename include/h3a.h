@@ -378,6 +378,51 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
 
 
 /*
+ * INT8 score product, after the pages' INT8 Q/K attention (Comfy Kitchen's
+ * INT8 Q/K/V kernel and a Sol-Attn INT8 QK switch among the request-level
+ * attention backends: H3 Blackwell Runtime README, "Hot Runtime Service";
+ * the "Sage Q-INT8" tail of the fused Q norm + rotary: h3-spark model card,
+ * "What this config does").  q has one fp32 scale per token and head, k one
+ * per block of 64 keys of a segment and head (blocks aligned at the segment
+ * start, a segment's last one possibly shorter, numbered segment by segment:
+ * block j of segment s is sum over earlier segments of ceil(L / 64), plus j).
+ * With amax a block's largest magnitude: scale = amax / 127 and code =
+ * rint(x * (127 / amax)) clamped to [-127, 127], in fp32 with correctly
+ * rounded divisions; a zero block has scale 0 and codes 0; a block holding a
+ * NaN or an infinity gets a NaN or infinite scale and codes 0, so its scores
+ * become NaN.
+ *
+ * h3a_quantize_i8_rows: bf16 x [S, H, D] (token stride stride_x elements) ->
+ *   codes y [S, H, D] (int8, token stride stride_y bytes, a multiple of 16)
+ *   and y_scale [H][S] fp32 (4-byte aligned).
+ * h3a_i8_key_blocks: the number of 64-key blocks of cu_seqlens (host only).
+ * h3a_quantize_i8_keys: as h3a_quantize_i8_rows with y_scale [H][n_blocks]
+ *   fp32, one scale per key block of each head; n_blocks must equal
+ *   h3a_i8_key_blocks (else ESHAPE).
+ * h3a_varlen_attn_fwd_i8qk: h3a_varlen_attn_fwd_ex with q8 / q_scale from
+ *   h3a_quantize_i8_rows (Hq heads) and k8 / k_scale from
+ *   h3a_quantize_i8_keys (Hkv heads) on the same cu_seqlens.  The score
+ *   product runs on the INT8 MFMA (int32 sums, exact), each score is the sum
+ *   times q scale * k scale * scale; the softmax, the bf16 probabilities, the
+ *   PV product with bf16 v and the bf16 output are those of the bf16 path.
+ *   The result equals attention on the values the codes stand for (code *
+ *   scale) up to the bf16 path's rounding.  Errors: as
+ *   h3a_varlen_attn_fwd_fp8qk, plus EUNSUPPORTED when the segments' padded
+ *   64-key blocks cover more than INT32_MAX keys.
+ */
+h3a_status h3a_quantize_i8_rows(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                                int64_t stride_x, int64_t stride_y, hipStream_t stream);
+h3a_status h3a_i8_key_blocks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_blocks);
+h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                                int64_t stride_x, int64_t stride_y, int64_t n_blocks, const int32_t* cu_seqlens,
+                                int32_t nseg, hipStream_t stream);
+h3a_status h3a_varlen_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                    const void* v, void* o, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                    const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal,
+                                    hipStream_t stream);
+
+/*
  * Varlen attention with grouped K/V heads and an optional causal mask: the
  * encoder text tower's causal GQA (vllm.cpp PR #26, encoder-tower commit,
  * "Causal GQA attention": K/V heads are broadcast across their query group).

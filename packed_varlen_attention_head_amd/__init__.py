@@ -47,6 +47,10 @@ EXPORTS = (
     "h3a_vt_e4m3_columns",
     "h3a_prepare_vt_e4m3",
     "h3a_varlen_attn_fwd_fp8",
+    "h3a_quantize_i8_rows",
+    "h3a_i8_key_blocks",
+    "h3a_quantize_i8_keys",
+    "h3a_varlen_attn_fwd_i8qk",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -111,6 +115,10 @@ def lib() -> ctypes.CDLL:
     L.h3a_varlen_attn_fwd_fp8qk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64,
                                             _i64, _i64,
                                             _c_i32p, _i32, _f32, _i32, _vp]
+    L.h3a_quantize_i8_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
+    L.h3a_i8_key_blocks.argtypes = [_c_i32p, _i32, _c_i64p]
+    L.h3a_quantize_i8_keys.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _c_i32p, _i32, _vp]
+    L.h3a_varlen_attn_fwd_i8qk.argtypes = L.h3a_varlen_attn_fwd_fp8qk.argtypes
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
@@ -122,6 +130,7 @@ def lib() -> ctypes.CDLL:
                  "h3a_rmsnorm_rope", "h3a_varlen_attn_fwd_qnorm", "h3a_varlen_attn_fwd",
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
+                 "h3a_quantize_i8_rows", "h3a_i8_key_blocks", "h3a_quantize_i8_keys", "h3a_varlen_attn_fwd_i8qk",
                  "h3a_varlen_attn_fwd_ex", "h3a_varlen_attn_fwd_noalloc", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -518,6 +527,93 @@ def varlen_attn_fwd_fp8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fa
     _check(lib().h3a_varlen_attn_fwd_fp8qk(q8.data_ptr(), k8.data_ptr(), qs.data_ptr(), ks.data_ptr(), v.data_ptr(),
                                            out.data_ptr(), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
                                            float(scale), int(bool(causal)), _stream_handle(stream)))
+    return out
+
+
+# INT8 operands are (codes, scales) pairs too: int8 codes and fp32 scales,
+# [H, S] per token for q and [H, n_blocks] per 64-key block of a segment for k.
+
+def _f32_scales(name, t, shape, device):
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _expect(name, t, shape, torch.float32)
+    return t
+
+
+def _i8_out(name, out, x, S, H, D):
+    import torch
+
+    if out is None:
+        out = torch.empty((S, H, D), dtype=torch.int8, device=x.device)
+    _, _, _, sy = _token_major(name, out)
+    if tuple(out.shape) != (S, H, D) or out.dtype != torch.int8:
+        raise H3AError(H3A_ESHAPE, f"{name} must be int8 {(S, H, D)}, got {out.dtype} {tuple(out.shape)}")
+    return out, sy
+
+
+def quantize_i8_rows(x, out=None, scale_out=None, stream=None):
+    """bf16 [S, H, D] -> (int8 [S, H, D] codes, fp32 [H, S] per-token scales)."""
+    import torch
+
+    S, H, D, sx = _token_major("x", x)
+    if x.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"x must be bfloat16, got {x.dtype}")
+    out, sy = _i8_out("out", out, x, S, H, D)
+    sc = _f32_scales("scale_out", scale_out, (H, S), x.device)
+    _check(lib().h3a_quantize_i8_rows(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy,
+                                      _stream_handle(stream)))
+    return out, sc
+
+
+def i8_key_blocks(cu_seqlens) -> int:
+    """Number of 64-key blocks of cu_seqlens (each segment's keys in blocks from its start)."""
+    cu = _i32_array(cu_seqlens)
+    n = ctypes.c_int64(0)
+    _check(lib().h3a_i8_key_blocks(_ptr_i32(cu), len(cu) - 1, ctypes.byref(n)))
+    return int(n.value)
+
+
+def quantize_i8_keys(x, cu_seqlens, out=None, scale_out=None, stream=None):
+    """bf16 [S, H, D] -> (int8 [S, H, D] codes, fp32 [H, n_blocks] scales, one per 64 keys of a segment)."""
+    import torch
+
+    S, H, D, sx = _token_major("x", x)
+    if x.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"x must be bfloat16, got {x.dtype}")
+    cu = _i32_array(cu_seqlens)
+    nb = i8_key_blocks(cu)
+    out, sy = _i8_out("out", out, x, S, H, D)
+    sc = _f32_scales("scale_out", scale_out, (H, max(nb, 1)), x.device)
+    _check(lib().h3a_quantize_i8_keys(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy, nb,
+                                      _ptr_i32(cu), len(cu) - 1, _stream_handle(stream)))
+    return out, sc
+
+
+def varlen_attn_fwd_i8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):
+    """Attention with q8 = quantize_i8_rows(q) and k8 = quantize_i8_keys(k, cu_seqlens) pairs, bf16 v."""
+    import torch
+
+    (q8, qs), (k8, ks) = _pair("q8", q8), _pair("k8", k8)
+    S, Hq, D, sq = _token_major("q8", q8)
+    _, Hkv, _, sk = _token_major("k8", k8)
+    _, _, _, sv = _token_major("v", v)
+    if q8.dtype != torch.int8 or k8.dtype != torch.int8:
+        raise H3AError(H3A_EDTYPE, f"q8/k8 must hold int8 codes, got {q8.dtype}/{k8.dtype}")
+    if tuple(k8.shape) != (S, Hkv, D) or tuple(v.shape) != (S, Hkv, D) or v.dtype != torch.bfloat16:
+        raise H3AError(H3A_ESHAPE, f"k8 {tuple(k8.shape)} / v {tuple(v.shape)} {v.dtype} do not match q8")
+    cu = _i32_array(cu_seqlens)
+    nb = i8_key_blocks(cu)
+    qs = _f32_scales("q_scale", qs, (Hq, S), q8.device)
+    ks = _f32_scales("k_scale", ks, (Hkv, max(nb, 1)), q8.device)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=v.device)
+    _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), torch.bfloat16)
+    _check(lib().h3a_varlen_attn_fwd_i8qk(q8.data_ptr(), k8.data_ptr(), qs.data_ptr(), ks.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
+                                          float(scale), int(bool(causal)), _stream_handle(stream)))
     return out
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh3a.so")
 
 SOURCES = ["api.cpp", "planner.cpp", "rope_table.hip", "qk_norm_rope.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
-           "quantize_fp8.hip", "attn_noalloc.hip"]
+           "quantize_fp8.hip", "quantize_i8.hip", "attn_noalloc.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -927,6 +927,130 @@ h3a_status h3a_varlen_attn_fwd_fp8qk(const void* q8, const void* k8, const void*
   }
 }
 
+h3a_status h3a_quantize_i8_rows(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                                int64_t stride_x, int64_t stride_y, hipStream_t stream) {
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    h3a_status st;
+    if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
+    if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+    const int64_t sbytes = S * H * 4;
+    if ((st = check_scales("y_scale", y_scale, sbytes, 4)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    const Range rx = tensor_range(x, S, H, D, stride_x, 2), ry = tensor_range(y, S, H, D, stride_y, 1);
+    if (ranges_hit(rx, ry)) return fail(H3A_EINVAL, "y overlaps x");
+    const Range rs = byte_range(y_scale, sbytes);
+    if (ranges_hit(rs, rx) || ranges_hit(rs, ry)) return fail(H3A_EINVAL, "y_scale overlaps x or y");
+    hipError_t e = h3a::launch_quantize_i8_rows(x, y, y_scale, S, H, D, stride_x, stride_y, stream);
+    if (e != hipSuccess) return fail_hip("quantize_i8_rows launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_quantize_i8_rows");
+  }
+}
+
+h3a_status h3a_i8_key_blocks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_blocks) {
+  try {
+    if (n_blocks == nullptr) return fail(H3A_EINVAL, "n_blocks is NULL");
+    if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+    if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+    *n_blocks = h3a::vt_e4m3_columns(cu_seqlens, nseg) / h3a::kVtTile;
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_i8_key_blocks");
+  }
+}
+
+h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
+                                int64_t stride_x, int64_t stride_y, int64_t n_blocks, const int32_t* cu_seqlens,
+                                int32_t nseg, hipStream_t stream) {
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg) / h3a::kVtTile;
+    if (n_blocks != need)
+      return fail(H3A_ESHAPE, "n_blocks = %lld but cu_seqlens has %lld blocks of 64 keys", (long long)n_blocks,
+                  (long long)need);
+    if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
+    if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+    const int64_t sbytes = int64_t(H) * n_blocks * 4;
+    if ((st = check_scales("y_scale", y_scale, sbytes, 4)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    const Range rx = tensor_range(x, S, H, D, stride_x, 2), ry = tensor_range(y, S, H, D, stride_y, 1);
+    if (ranges_hit(rx, ry)) return fail(H3A_EINVAL, "y overlaps x");
+    const Range rs = byte_range(y_scale, sbytes);
+    if (ranges_hit(rs, rx) || ranges_hit(rs, ry)) return fail(H3A_EINVAL, "y_scale overlaps x or y");
+    hipError_t e = h3a::launch_quantize_i8_keys(x, y, y_scale, cu_seqlens, nseg, H, D, stride_x, stride_y, n_blocks,
+                                                stream);
+    if (e != hipSuccess) return fail_hip("quantize_i8_keys launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_quantize_i8_keys");
+  }
+}
+
+h3a_status h3a_varlen_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                    const void* v, void* o, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                                    const int32_t* cu_seqlens, int32_t nseg, float scale, int32_t causal,
+                                    hipStream_t stream) {
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    // the kernel finds a segment's key blocks from its padded column (an int32)
+    const int64_t cols = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+    if (cols > int64_t(INT32_MAX))
+      return fail(H3A_EUNSUPPORTED, "the segments' 64-key blocks cover %lld keys, more than INT32_MAX", (long long)cols);
+    const int64_t n_blocks = cols / h3a::kVtTile;
+    if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+    if ((st = check_operand("v", v, S, Hkv, D, stride_v, 2)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+    const int64_t qsb = S * Hq * 4, ksb = int64_t(Hkv) * n_blocks * 4;
+    if ((st = check_scales("q_scale", q_scale, qsb, 4)) != H3A_OK) return st;
+    if ((st = check_scales("k_scale", k_scale, ksb, 4)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    // o (bf16) against the byte-coded q and k, their scales, and v (bf16)
+    const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+    const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+    if (ranges_hit(ro, rq)) return fail(H3A_EINVAL, "o overlaps q");
+    if (ranges_hit(ro, rk)) return fail(H3A_EINVAL, "o overlaps k");
+    if (ranges_hit(ro, byte_range(q_scale, qsb)) || ranges_hit(ro, byte_range(k_scale, ksb)))
+      return fail(H3A_EINVAL, "o overlaps q_scale or k_scale");
+    if (may_overlap(o, stride_o, Hq, v, stride_v, Hkv, S, D, 2)) return fail(H3A_EINVAL, "o overlaps v");
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, true, stream, &plan, &plan_lock)) !=
+        H3A_OK)
+      return st;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention (int8 qk) launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return h3a::launch_attn_fwd_i8qk(q8, k8, q_scale, k_scale, v, o, D, stride_q, stride_k, S * 4,
+                                                       n_blocks * 4, stride_v, stride_o, items, n, scale, Hq / Hkv,
+                                                       causal != 0, stream, sp);
+                    });
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_i8qk");
+  }
+}
+
 h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns) {
   try {
     if (columns == nullptr) return fail(H3A_EINVAL, "columns is NULL");

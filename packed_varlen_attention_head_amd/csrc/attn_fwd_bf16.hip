@@ -95,7 +95,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per work item
@@ -246,6 +248,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int NDMAK = kBN * KCH / (64 * kWaves);
   constexpr int KS8 = D / 64;                      // FP8 MFMA k-steps over the head dim
   constexpr int NDMAV8 = D * 4 / (64 * kWaves);    // FP8 V^T tile: D rows x 4 chunks
+  constexpr bool kF8K = F8 == 1 || F8 == 2;       // E4M3 q, k with per-32-dim scales
+  constexpr bool kI8 = F8 == 3;                   // INT8 q, k: per-row q, per-64-key-block k scales
+  constexpr bool kPbf = F8 != 2;                  // bf16 probabilities and V
+  constexpr int KS32 = D / 32;                    // INT8 MFMA k-steps over the head dim
   static_assert(NDMAK >= 1 && NDMAV8 >= 1 && !(F8 && QNORM), "tile layout / variant");
 
   // One object per ring slot, so alias analysis can tell a load into one slot
@@ -269,7 +275,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // V^T tile's (key block j, dim 32 b + r) words in lane order 32 j + r.  One
   // wave fetches each with one LDS-bound load, shared by the workgroup like
   // the tile itself.
-  constexpr int SCB = F8 ? kBN * 4 : 4;
+  constexpr int SCB = kF8K ? kBN * 4 : 4;
   __shared__ __align__(16) uint8_t ks_slot0[SCB], ks_slot1[SCB];
   __shared__ __align__(16) uint8_t vs_slot0[F8 == 2 ? SCB : 4], vs_slot1[F8 == 2 ? SCB : 4];
   auto kscl = [&](auto slot) -> uint8_t* {
@@ -321,8 +327,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // F8: lane holds query (qrow0 + l32), dims ks8*64 + hi*16 .. +16 and
   // ks8*64 + 32 + hi*16 .. +16; qsc: the row's scales, shifted so that byte
   // 2 ks8 is block 2 ks8 + hi.
-  [[maybe_unused]] i32x8 qb8[F8 ? KS8 : 1];
+  [[maybe_unused]] i32x8 qb8[kF8K ? KS8 : 1];
   [[maybe_unused]] uint32_t qsc = 0;
+  // kI8: lane holds query (qrow0 + l32), dims ks*32 + hi*16 .. +16, and the
+  // score multiplier c times the row's scale.
+  [[maybe_unused]] i32x4 qi8[kI8 ? KS32 : 1];
+  [[maybe_unused]] float cq = c;
   const int kv_head = __builtin_amdgcn_readfirstlane(it.head / kv_group);
   if constexpr (F8 == 0) {
     const auto rq = rows_rsrc(q + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq) * 2);
@@ -330,6 +340,17 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
+  } else if constexpr (kI8) {
+    const uint8_t* q8 = reinterpret_cast<const uint8_t*>(q);
+    const auto rq = rows_rsrc(q8 + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq));
+    const int off = l32 * int(sq) + hi * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS32; ++ks)
+      qi8[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + ks * 32, 0, 0));
+    // the row's fp32 scale ([head][token]); rows past the segment end read 0
+    const auto rqs = rows_rsrc(fs.q + it.head * fs.q_head + (int64_t(it.seg_start) + qrow0) * 4, it.seg_len - qrow0,
+                               32, 4);
+    cq = c * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rqs, l32 * 4, 0, 0));
   } else {
     const uint8_t* q8 = reinterpret_cast<const uint8_t*>(q);
     const auto rq = rows_rsrc(q8 + (int64_t(it.seg_start) + qrow0) * sq + head_off, it.seg_len - qrow0, 32, int(sq));
@@ -444,6 +465,28 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     ones8 = i32x8{one4, one4, one4, one4, one4, one4, one4, one4};
     asm volatile("" : "+v"(ones8));
   }
+  // kI8: the INT8 score product starts from the bits of the float 1.5 * 2^23,
+  // so an integer sum S (|S| < 2^22) reads as the float 1.5 * 2^23 + S: the
+  // probabilities then take it straight into their FMA, exp2(c_t * (1.5 *
+  // 2^23 + S) - (c_t * 1.5 * 2^23 + m)), with c_t = c * q_scale * k_scale of
+  // the tile; an exact integer-to-float conversion at no instruction cost.
+  // Kept in registers (opaque to the compiler), like ones8.
+  [[maybe_unused]] i32x16 magic;
+  if constexpr (kI8) {
+    constexpr int m = 0x4B400000;
+    magic = i32x16{m, m, m, m, m, m, m, m, m, m, m, m, m, m, m, m};
+    asm volatile("" : "+v"(magic));
+  }
+  // Score multiplier and offset of the tile whose probabilities are formed
+  // next: scores are sacc * cmul + cadd (c and 0 but for kI8), its k scale
+  // arriving in kscale with the tile's V load.
+  [[maybe_unused]] float cmul = c, cadd = 0.f, kscale = 0.f;
+  [[maybe_unused]] auto set_tile_scale = [&]() {
+    if constexpr (kI8) {
+      cmul = cq * kscale;
+      cadd = -cmul * 12582912.0f;
+    }
+  };
 
   // LDS-bound loads: slot s = (i * kWaves + wave) * 64 + lane holds physical
   // chunk s % CH of row s / CH; the lane fetches the logical chunk stored there.
@@ -454,7 +497,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int row = s / KCH, pc = s % KCH;
     koff[i] = row * int(sk) * KESZ + ((pc ^ (F8 ? k8_swz<D>(row) : k_swz<D>(row))) * 16);
   }
-  if constexpr (F8 < 2) {
+  if constexpr (kPbf) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int s = (i * kWaves + wave) * 64 + lane;
@@ -475,12 +518,17 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kaddr[ks] = l32 * ROWB + (((2 * ks + hi) ^ k_swz<D>(l32)) * 16);
   // F8 K operand reads: row l32 (+32 kb), chunks 4 ks8 + hi + {0, 2}.
-  [[maybe_unused]] int kaddr8[F8 ? KS8 : 1][2];
-  if constexpr (F8)
+  [[maybe_unused]] int kaddr8[kF8K ? KS8 : 1][2];
+  if constexpr (kF8K)
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
       for (int j = 0; j < 2; ++j) kaddr8[ks][j] = l32 * KROWB + (((4 * ks + hi + 2 * j) ^ k8_swz<D>(l32)) * 16);
+  // INT8 K operand reads: row l32 (+32 kb), chunk 2 ks + hi.
+  [[maybe_unused]] int kaddr_i8[kI8 ? KS32 : 1];
+  if constexpr (kI8)
+#pragma unroll
+    for (int ks = 0; ks < KS32; ++ks) kaddr_i8[ks] = l32 * KROWB + (((2 * ks + hi) ^ k8_swz<D>(l32)) * 16);
   // V^T operand reads (transposing): 16-lane group g reads keys
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
@@ -526,7 +574,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int i = 0; i < NDMAK; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)(kslot(slot) + (i * kWaves + wave) * 64 * 8), 16,
                                                koff[i], 0, 0, 0);
-    if constexpr (F8 >= 1) {
+    if constexpr (kF8K) {
       // the tile's 64 scale rows, contiguous (head-major scales): lane = key;
       // keys past the segment end read scale code 0 (their codes are 0 too)
       if (wave == 0) {
@@ -538,7 +586,14 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   auto load_v = [&](int t, auto slot) {
     const int key0 = t * kBN;
-    if constexpr (F8 < 2) {
+    if constexpr (kI8) {
+      // the tile's k scale ([kv head][key block], the segment's first block at
+      // vt_col0 / 64), one fp32 for every lane; past the segment: 0
+      const auto rs = rows_rsrc(fs.k + kv_head * fs.k_head + int64_t(it.vt_col0 / kVtTile) * 4,
+                                (it.seg_len + kBN - 1) / kBN, 1 << 20, 4);
+      kscale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, 0, 0));
+    }
+    if constexpr (kPbf) {
       const auto r = rows_rsrc(vbase + int64_t(key0) * sv * 2, it.seg_len - key0, kBN, int(sv) * 2);
 #pragma unroll
       for (int i = 0; i < NDMA; ++i)
@@ -587,6 +642,30 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       }
       return;
     }
+    if constexpr (kI8) {
+      // as the bf16 product: k-steps outer, 32-key blocks inner, each step's K
+      // operands read while the previous step's products issue
+      constexpr int NB = kBN / 32;
+      const LDS char* kp = (const LDS char*)kslot(slot);
+      i32x16 acc[NB];
+      i32x4 cur[NB], nxt[NB];
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) cur[kb] = *(const LDS i32x4*)(kp + kaddr_i8[0] + kb * 32 * KROWB);
+#pragma unroll
+      for (int ks = 0; ks < KS32; ++ks) {
+        if (ks + 1 < KS32)
+#pragma unroll
+          for (int kb = 0; kb < NB; ++kb) nxt[kb] = *(const LDS i32x4*)(kp + kaddr_i8[ks + 1] + kb * 32 * KROWB);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+          acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[kb], qi8[ks], ks == 0 ? magic : acc[kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) cur[kb] = nxt[kb];
+      }
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) sacc[kb] = __builtin_bit_cast(f32x16, acc[kb]);
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
       sacc[kb] = f32x16{};
@@ -630,7 +709,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = pair_max(mx) * c;
+    if constexpr (kI8) mx = fmaf(pair_max(mx), cmul, cadd);
+    else mx = pair_max(mx) * c;
     const bool grow = mx > m_thr;
     if (__builtin_expect(__any(grow), 0)) {
       // Rare after the first tiles; the empty asm keeps the compiler from
@@ -653,13 +733,18 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto probs_part = [&](const f32x16* sacc, bf16x8* pb) {
     const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
     float part = 0.f;
+    float mul = c, bias = -m_run;
+    if constexpr (kI8) {
+      mul = cmul;
+      bias = cadd - m_run;
+    }
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         bf16x8 v8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], c, -m_run)));
+        for (int i = 0; i < 8; ++i) v8[i] = __bf16(__builtin_amdgcn_exp2f(fmaf(sacc[kb][hh * 8 + i], mul, bias)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16x2 pr = {v8[2 * i], v8[2 * i + 1]};
@@ -686,7 +771,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = pair_max(mx) * c;
+      if constexpr (kI8) mx = fmaf(pair_max(mx), cmul, cadd);
+      else mx = pair_max(mx) * c;
       const float m_new = mx > m_run ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;
@@ -791,6 +877,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // where masked) and the steady loop below, which every wave runs, starts
   // from defined scores and a finite reference.
   qk(IC<0>{}, s);
+  set_tile_scale();
   if (needs_mask(tb)) mask(s, tb);
   update_max(s);
   // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
@@ -809,10 +896,10 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // Every wave computes here, also one whose rows all lie past the segment
     // end (rare: last query tile only; its rows are not stored), so the loads
     // and the MFMA/softmax work form one block the scheduler can interleave.
-    if constexpr (F8 <= 1) {
-      // bf16 probabilities (also behind FP8 scores): tile t's probabilities
-      // beside tile t+1's scores; the check (rarely taken) still sees tile
-      // t's scores in sold
+    if constexpr (kPbf) {
+      // bf16 probabilities (also behind FP8 or INT8 scores): tile t's
+      // probabilities beside tile t+1's scores; the check (rarely taken)
+      // still sees tile t's scores in sold
       const f32x16 sold[kBN / 32] = {s[0], s[1]};
       const float part = probs_part(sold, pb);
       qk(IC<P ^ 1>{}, s);
@@ -825,6 +912,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       update_max(s);
     }
     publish();
+    set_tile_scale();  // (kI8) tile t+1's, for the next iteration
   };
   int t = tb;
   constexpr int kTail = CAUSAL ? 4 : 3;
@@ -838,11 +926,12 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t + 2 < te) load_k(t + 2, par);
     if (t + 1 < te) load_v(t + 1, par ^ 1);
     if (active) {
-      if constexpr (F8 <= 1) probs_checked(s, pb, probs_part(s, pb));
+      if constexpr (kPbf) probs_checked(s, pb, probs_part(s, pb));
       else probs(s, pb);
       if (t + 1 < te) {
         qk(par ^ 1, s);
         pv(par, pb);
+        set_tile_scale();
         if (needs_mask(t + 1)) mask(s, t + 1);
         update_max(s);
       } else {
@@ -1008,6 +1097,25 @@ hipError_t launch_attn_fwd_fp8(const void* q8, const void* k8, const void* vt8, 
                                                    kv_group, none, stream, fs, sp);
   H3A_F8PV_CASE(128) H3A_F8PV_CASE(64)
 #undef H3A_F8PV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                 const void* v, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
+                                 int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
+                                 int32_t kv_group, bool causal, hipStream_t stream, const SplitArgs& sp) {
+  if (n_items <= 0) return hipSuccess;
+  if (kv_group < 1) return hipErrorInvalidValue;
+  const QNormArgs none{};
+  const F8Scales fs{static_cast<const uint8_t*>(q_scale), static_cast<const uint8_t*>(k_scale), nullptr, sqs, sks, 0};
+#define H3A_I8_CASE(DD)                                                                                     \
+  if (D == DD)                                                                                              \
+    return causal ? launch<DD, true, false, 0, 3>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,        \
+                                                  kv_group, none, stream, fs, sp)                          \
+                  : launch<DD, false, false, 0, 3>(q8, k8, v, o, sq, sk, sv, so, items, n_items, scale,       \
+                                                   kv_group, none, stream, fs, sp);
+  H3A_I8_CASE(128) H3A_I8_CASE(64)
+#undef H3A_I8_CASE
   return hipErrorInvalidValue;
 }
 

@@ -138,6 +138,26 @@ hipError_t launch_attn_fwd_fp8qk(const void* q8, const void* k8, const void* q8s
                                  bool causal, hipStream_t stream,
                                  const SplitArgs& sp = SplitArgs{});
 
+// Attention whose q and k are INT8 codes (token strides in bytes): q with one
+// fp32 scale per token (q_scale [Hq][S], head stride sqs bytes), k with one
+// per block of 64 keys of a segment (k_scale [Hkv][blocks], the segment's
+// first block at its padded column / 64, head stride sks bytes); the score
+// product runs on the INT8 MFMA, the rest as launch_attn_fwd_bf16.
+hipError_t launch_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
+                                const void* v, void* o, int32_t D, int64_t sq, int64_t sk, int64_t sqs, int64_t sks,
+                                int64_t sv, int64_t so, const WorkItem* items, int64_t n_items, float scale,
+                                int32_t kv_group, bool causal, hipStream_t stream,
+                                const SplitArgs& sp = SplitArgs{});
+
+// bf16 [S, H, D] rows (token stride sx elements) -> INT8 codes (token stride
+// sy bytes) with one fp32 scale per token and head (ys [H][S]); and, per
+// segment of cu (host array, nseg + 1 entries), with one fp32 scale per block
+// of 64 keys of a head (ys [H][blocks], blocks numbered segment by segment).
+hipError_t launch_quantize_i8_rows(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
+                                   int64_t sy, hipStream_t stream);
+hipError_t launch_quantize_i8_keys(const void* x, void* y, void* ys, const int32_t* cu, int32_t nseg, int32_t H,
+                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream);
+
 // The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
 // token strides sq8, sk8 in bytes) with one E8M0 scale per 32 head dims in
 // q8s [H][S][D/32], k8s [Hk][S][D/32].

@@ -1,0 +1,190 @@
+// bf16 -> INT8 codes with fp32 scales for the INT8 score product: q with one
+// scale per token and head, k with one per block of 64 keys of a segment and
+// head (the pages' GB10 image runs INT8 Q/K attention -- Comfy Kitchen's
+// kernel, a Sol-Attn INT8 QK switch, the fused "Sage Q-INT8" tail of the Q
+// norm + rotary pass; H3 Blackwell Runtime README, attention backends;
+// h3-spark model card, "What this config does").
+//
+// With amax a block's largest magnitude (fp32): scale = amax / 127 and code =
+// rint(x * (127 / amax)) clamped to [-127, 127], both divisions correctly
+// rounded, the product a plain fp32 multiply.  A zero block has scale 0 and
+// codes 0.  amax is NaN when the block holds a NaN and infinite when it holds
+// an infinity; then every code of the block is 0 and its scale NaN or
+// infinite, so the scores the block enters become NaN.
+//
+// HBM-bound elementwise passes: a token row is read once (16 bytes a lane)
+// and its codes written once (8 bytes a lane).
+#include <cstdint>
+
+#include "common.h"
+
+namespace h3a {
+namespace {
+
+constexpr int kThreads = 256;
+
+// max of two magnitudes that keeps a NaN (fmaxf would drop it)
+__device__ __forceinline__ float nan_max(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight codes of x * inv, as two dwords (byte i = element i).
+__device__ __forceinline__ uint2 i8_codes(const float (&f)[8], float inv) {
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float r = __builtin_rintf(f[e] * inv);
+    // a non-finite product (a NaN or infinite block maximum, or 127 / amax
+    // overflowing for a block of tiny values) gives code 0
+    const int c = __builtin_isfinite(r) ? min(127, max(-127, int(r))) : 0;
+    out[e / 4] |= (uint32_t(c) & 0xffu) << (8 * (e % 4));
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+__device__ __forceinline__ float inv_of(float amax) { return amax == 0.f ? 0.f : __fdiv_rn(127.0f, amax); }
+
+// One (token, head) row of D dims per D / 8 consecutive lanes (8 dims each).
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+quantize_i8_rows_kernel(const uint16_t* __restrict__ x, int8_t* __restrict__ y, float* __restrict__ ys, int64_t S,
+                        int32_t H, int64_t sx, int64_t sy) {
+  constexpr int G = D / 8;  // lanes per row (a power of two dividing 64)
+  const int64_t row = (int64_t(blockIdx.x) * kThreads + threadIdx.x) / G;
+  const int c = int(threadIdx.x % G);
+  const bool in = row < S * H;  // the group of a row exits together
+  const int64_t token = in ? row / H : 0;
+  const int h = in ? int(row % H) : 0;
+  float f[8];
+  float amax = 0.f;
+  if (in) {
+    const uint4 r = *reinterpret_cast<const uint4*>(x + token * sx + h * D + c * 8);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+      amax = nan_max(nan_max(amax, __builtin_fabsf(f[2 * i])), __builtin_fabsf(f[2 * i + 1]));
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < G; m <<= 1) amax = nan_max(amax, __shfl_xor(amax, m, 64));
+  if (!in) return;
+  *reinterpret_cast<uint2*>(y + token * sy + h * D + c * 8) = i8_codes(f, inv_of(amax));
+  if (c == 0) ys[int64_t(h) * S + token] = __fdiv_rn(amax, 127.0f);
+}
+
+// One block of 64 keys of one head per workgroup: the block's maximum meets in
+// LDS, then each thread writes the codes of its rows.  Segments of this
+// launch: key 0 at start[s], len[s] keys, first block blocks[s] (from block0).
+constexpr int kKeyMaxSegs = 64;
+
+struct KeyBlockArgs {
+  int32_t nseg;
+  int32_t block0;  // first block of this launch
+  int32_t start[kKeyMaxSegs];
+  int32_t len[kKeyMaxSegs];
+  int32_t blocks[kKeyMaxSegs + 1];  // prefix sums of the segments' block counts
+};
+
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* __restrict__ y,
+                        float* __restrict__ ys, int64_t n_blocks, int64_t sx, int64_t sy) {
+  constexpr int CH = D / 8;               // 8-dim chunks per key
+  constexpr int KPP = kThreads / CH;      // keys per pass
+  constexpr int NP = kVtTile / KPP;       // passes over the block's 64 keys
+  __shared__ float wave_max[kThreads / 64];
+  const int tau = blockIdx.x;
+  const int h = blockIdx.y;
+  int s = 0;
+  while (s + 1 < a.nseg && tau >= a.blocks[s + 1]) ++s;
+  const int key0 = (tau - a.blocks[s]) * kVtTile;
+  const int c = int(threadIdx.x % CH), kr = int(threadIdx.x / CH);
+  float f[NP][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int key = key0 + p * KPP + kr;
+    uint4 r = make_uint4(0, 0, 0, 0);  // keys past the segment: zeros, not stored
+    if (key < a.len[s]) r = *reinterpret_cast<const uint4*>(x + int64_t(a.start[s] + key) * sx + h * D + c * 8);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[p][2 * i] = bf16_lo(w[i]);
+      f[p][2 * i + 1] = bf16_hi(w[i]);
+      amax = nan_max(nan_max(amax, __builtin_fabsf(f[p][2 * i])), __builtin_fabsf(f[p][2 * i + 1]));
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = nan_max(amax, __shfl_xor(amax, m, 64));
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x / 64] = amax;
+  __syncthreads();
+  amax = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) amax = nan_max(amax, wave_max[w]);
+  const float inv = inv_of(amax);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int key = key0 + p * KPP + kr;
+    if (key < a.len[s]) *reinterpret_cast<uint2*>(y + int64_t(a.start[s] + key) * sy + h * D + c * 8) = i8_codes(f[p], inv);
+  }
+  if (threadIdx.x == 0) ys[int64_t(h) * n_blocks + a.block0 + tau] = __fdiv_rn(amax, 127.0f);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_i8_rows(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
+                                   int64_t sy, hipStream_t stream) {
+  if (S <= 0) return hipSuccess;
+  if (H < 1) return hipErrorInvalidValue;
+  const int64_t lanes = S * H * (D / 8);
+  const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
+  if (D == 128)
+    hipLaunchKernelGGL(quantize_i8_rows_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), S, H, sx, sy);
+  else if (D == 64)
+    hipLaunchKernelGGL(quantize_i8_rows_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), S, H, sx, sy);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_i8_keys(const void* x, void* y, void* ys, const int32_t* cu, int32_t nseg, int32_t H,
+                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream) {
+  if (D != 128 && D != 64) return hipErrorInvalidValue;
+  int32_t block0 = 0;
+  for (int32_t s0 = 0; s0 < nseg; s0 += kKeyMaxSegs) {
+    const int32_t n = nseg - s0 < kKeyMaxSegs ? nseg - s0 : kKeyMaxSegs;
+    KeyBlockArgs a{};
+    a.nseg = n;
+    a.block0 = block0;
+    a.blocks[0] = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      a.start[i] = cu[s0 + i];
+      a.len[i] = cu[s0 + i + 1] - cu[s0 + i];
+      a.blocks[i + 1] = a.blocks[i] + (a.len[i] + kVtTile - 1) / kVtTile;
+    }
+    const int32_t nb = a.blocks[n];
+    if (nb > 0) {
+      if (int64_t(block0) + nb > n_blocks) return hipErrorInvalidValue;
+      const dim3 grid{unsigned(nb), unsigned(H), 1u};
+      if (D == 128)
+        hipLaunchKernelGGL(quantize_i8_keys_kernel<128>, grid, dim3(kThreads), 0, stream, a,
+                           static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), n_blocks,
+                           sx, sy);
+      else
+        hipLaunchKernelGGL(quantize_i8_keys_kernel<64>, grid, dim3(kThreads), 0, stream, a,
+                           static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), n_blocks,
+                           sx, sy);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    block0 += nb;
+  }
+  return hipSuccess;
+}
+
+}  // namespace h3a

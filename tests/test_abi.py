@@ -354,6 +354,69 @@ def test_varlen_attn_fwd_fp8_rejects(kw, status, word):
     assert word in h3a.last_error(), h3a.last_error()
 
 
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(H=0), h3a.H3A_EINVAL, "H ="),
+    (dict(D=96), h3a.H3A_EUNSUPPORTED, "head_dim"),
+    (dict(sy=120), h3a.H3A_ESHAPE, "y: token stride"),
+    (dict(y=P + 256), h3a.H3A_EINVAL, "y overlaps x"),
+    (dict(ys=None), h3a.H3A_EINVAL, "y_scale is NULL"),
+    (dict(ys=P + (2 << 24) + 2), h3a.H3A_EUNSUPPORTED, "y_scale is not 4-byte aligned"),
+    (dict(ys=P + (1 << 24) + 4000), h3a.H3A_EINVAL, "y_scale overlaps"),
+])
+def test_quantize_i8_rows_rejects(kw, status, word):
+    H, D = kw.get("H", 2), kw.get("D", 128)
+    st = h3a.lib().h3a_quantize_i8_rows(P, kw.get("y", P + (1 << 24)), kw.get("ys", P + (2 << 24)), 16, H, D,
+                                        max(H, 1) * D, kw.get("sy", max(H, 1) * D), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(nb=5), h3a.H3A_ESHAPE, "n_blocks = 5"),
+    (dict(cu=(0, 100, 90)), h3a.H3A_EINVAL, "decreases"),
+    (dict(ys=None), h3a.H3A_EINVAL, "y_scale is NULL"),
+    (dict(y=P + 256), h3a.H3A_EINVAL, "y overlaps x"),
+    (dict(ys=P + (1 << 24) + 256), h3a.H3A_EINVAL, "y_scale overlaps"),
+])
+def test_quantize_i8_keys_rejects(kw, status, word):
+    H, D = 2, 128
+    c, cp = i32(kw.get("cu", (0, 100, 300)))  # 2 + 4 key blocks
+    S = 300 if c[-1] == 300 else int(c[-1])
+    st = h3a.lib().h3a_quantize_i8_keys(P, kw.get("y", P + (1 << 24)), kw.get("ys", P + (2 << 24)), S, H, D, H * D,
+                                        H * D, kw.get("nb", 6), cp, 2, None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+def test_i8_key_blocks_counts_each_segment_from_its_start():
+    n = ctypes.c_int64(-1)
+    c, cp = i32((0, 65, 65, 66, 194))
+    assert h3a.lib().h3a_i8_key_blocks(cp, 4, ctypes.byref(n)) == h3a.H3A_OK and n.value == 2 + 0 + 1 + 2
+    assert h3a.i8_key_blocks([0, 64, 128, 129]) == 3
+    assert h3a.lib().h3a_i8_key_blocks(cp, 4, None) == h3a.H3A_EINVAL
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(Hkv=3), h3a.H3A_ESHAPE, "does not divide"),
+    (dict(causal=2), h3a.H3A_EINVAL, "causal"),
+    (dict(sk=64), h3a.H3A_ESHAPE, "k: token stride"),
+    (dict(o=P + 512), h3a.H3A_EINVAL, "o overlaps q"),
+    (dict(qs=None), h3a.H3A_EINVAL, "q_scale is NULL"),
+    (dict(ks=P + (5 << 24) + 2), h3a.H3A_EUNSUPPORTED, "k_scale is not 4-byte aligned"),
+    (dict(qs=P + (3 << 24) + 64), h3a.H3A_EINVAL, "o overlaps q_scale"),
+    (dict(scale=0.0), h3a.H3A_EINVAL, "scale"),
+])
+def test_varlen_attn_fwd_i8qk_rejects(kw, status, word):
+    Hq, Hkv, D = 8, kw.get("Hkv", 2), 128
+    c, cp = i32((0, 100, 300))
+    st = h3a.lib().h3a_varlen_attn_fwd_i8qk(P, P + (1 << 24), kw.get("qs", P + (4 << 24)), kw.get("ks", P + (5 << 24)),
+                                            P + (2 << 24), kw.get("o", P + (3 << 24)), 300, Hq, Hkv, D, Hq * D,
+                                            kw.get("sk", Hkv * D), Hkv * D, Hq * D, cp, 2, kw.get("scale", 0.088),
+                                            kw.get("causal", 0), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
 def qk_ex(Hq=8, Hk=0, **kw):
     D, hd, hk = 128, Hq * 128, max(Hk, 1) * 128
     return h3a.lib().h3a_qk_rmsnorm_rope_ex(P, P + (1 << 24), P, P + (1 << 24), h3a.H3A_BF16, 16, Hq, Hk, D, hd, hk,

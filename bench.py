@@ -483,13 +483,15 @@ def main():
         if fp8:  # one pass: norm + rotary writing E4M3 codes
             return h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8[0], k8=k8[0], q_scale=q8[1],
                                             k_scale=k8[1], stream=stream)
+        if i8:  # one pass: norm + rotary writing INT8 q codes with per-token scales, bf16 k
+            return h3a.qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8[0], q_scale=q8[1], k_out=kn,
+                                           stream=stream)
         return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
 
     def vprep(cu):
         if fp8pv:  # V as transposed E4M3 tiles (changes every step, like q and k)
             h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
-        if i8:  # INT8 codes of the normalised, rotated q and k
-            h3a.quantize_i8_rows(qn, out=q8[0], scale_out=q8[1], stream=stream)
+        if i8:  # INT8 codes of the normalised, rotated k, one scale per 64 keys of a segment
             h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], stream=stream)
 
     def attention(cu):
@@ -587,6 +589,8 @@ def main():
     norm_bytes = 2 * (S * normed_heads * D * 2) + 2 * S * (w.rot_dim // 2) * 4 + (1 if fused else 2) * D * 4
     if fp8:  # the norm + rotary pass writes one byte per element (and a scale per 32) instead of two
         norm_bytes -= S * (H + Hkv) * D - S * (H + Hkv) * (D // 32)
+    if i8:  # q written as one byte per element and an fp32 scale per row
+        norm_bytes -= S * H * D - S * H * 4
     copy_src = torch.empty(norm_bytes // 2, dtype=torch.uint8, device=dev)
     copy_dst = torch.empty_like(copy_src)
     copy_gbps = 2 * copy_src.numel() / timed(lambda: copy_dst.copy_(copy_src), n_ev) / 1e9
@@ -619,7 +623,7 @@ def main():
                      else "rope table + q/k norm/rotary to E4M3 codes + transposed E4M3 V + attention with both "
                           "products in FP8" if fp8pv
                      else "rope table + q/k norm/rotary to E4M3 codes + attention with FP8 QK^T" if fp8
-                     else "rope table + q/k norm/rotary + INT8 codes of q and k + attention with INT8 QK^T" if i8
+                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k + attention with INT8 QK^T" if i8
                      else "rope table + q/k norm/rotary + attention"),
         },
         "pct_bf16_peak_step": 100.0 * F / step_s / 1e12 / PEAK_BF16_TFLOPS,
@@ -636,7 +640,7 @@ def main():
         "norm_rope_GBps": norm_bytes / norm_s / 1e9,
         "rope_table_ms": table_s * 1e3,
         "v_e4m3_ms": vprep_s * 1e3 if fp8pv else 0.0,
-        "i8_quant_ms": vprep_s * 1e3 if i8 else 0.0,
+        "i8_k_quant_ms": vprep_s * 1e3 if i8 else 0.0,
         "checksum_o": checksum,
         "roofline": {
             "bound": "mfma",

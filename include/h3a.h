@@ -413,6 +413,24 @@ h3a_status h3a_varlen_attn_fwd_fp8(const void* q8, const void* k8, const void* v
 h3a_status h3a_quantize_i8_rows(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
                                 int64_t stride_x, int64_t stride_y, hipStream_t stream);
 h3a_status h3a_i8_key_blocks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_blocks);
+
+/*
+ * Norm + rotary and the q quantisation in one HBM pass (the fused "Sage
+ * Q-INT8" tail of the GB10 build's Q RMSNorm + rot96 RoPE: h3-spark model
+ * card, "What this config does"): h3a_qk_rmsnorm_rope_ex on bf16 q [S, Hq, D]
+ * and k [S, Hk, D], writing q as INT8 codes q8 [S, Hq, D] (token stride
+ * stride_q8 bytes, a multiple of 16) with q_scale [Hq][S] fp32, and k as bf16
+ * k_out [S, Hk, D] (token stride stride_ko elements; k_out may be k itself)
+ * for h3a_quantize_i8_keys.  Each q result is rounded to bf16 first, so codes
+ * and scales equal h3a_qk_rmsnorm_rope_ex followed by h3a_quantize_i8_rows,
+ * and k_out equals its k result.  q is not modified.  Errors: as
+ * h3a_qk_rmsnorm_rope_ex (bf16 only), plus EINVAL when q8 or q_scale overlaps
+ * another tensor.
+ */
+h3a_status h3a_qk_rmsnorm_rope_i8q(const void* q, const void* k, void* q8, void* k_out, void* q_scale,
+                                   int64_t S, int32_t Hq, int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k,
+                                   int64_t stride_q8, int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                                   float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
                                 int64_t stride_x, int64_t stride_y, int64_t n_blocks, const int32_t* cu_seqlens,
                                 int32_t nseg, hipStream_t stream);

@@ -49,6 +49,7 @@ EXPORTS = (
     "h3a_varlen_attn_fwd_fp8",
     "h3a_quantize_i8_rows",
     "h3a_i8_key_blocks",
+    "h3a_qk_rmsnorm_rope_i8q",
     "h3a_quantize_i8_keys",
     "h3a_varlen_attn_fwd_i8qk",
     "h3a_plan_tiles",
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
                                             _c_i32p, _i32, _f32, _i32, _vp]
     L.h3a_quantize_i8_rows.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp]
     L.h3a_i8_key_blocks.argtypes = [_c_i32p, _i32, _c_i64p]
+    L.h3a_qk_rmsnorm_rope_i8q.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
+                                          _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_quantize_i8_keys.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _c_i32p, _i32, _vp]
     L.h3a_varlen_attn_fwd_i8qk.argtypes = L.h3a_varlen_attn_fwd_fp8qk.argtypes
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
@@ -131,6 +134,7 @@ def lib() -> ctypes.CDLL:
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
                  "h3a_quantize_i8_rows", "h3a_i8_key_blocks", "h3a_quantize_i8_keys", "h3a_varlen_attn_fwd_i8qk",
+                 "h3a_qk_rmsnorm_rope_i8q",
                  "h3a_varlen_attn_fwd_ex", "h3a_varlen_attn_fwd_noalloc", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -565,6 +569,31 @@ def quantize_i8_rows(x, out=None, scale_out=None, stream=None):
     _check(lib().h3a_quantize_i8_rows(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy,
                                       _stream_handle(stream)))
     return out, sc
+
+
+def qk_rmsnorm_rope_i8q(q, k, gamma_q, gamma_k, eps: float, cos_sin, rot_dim: int, q8=None, q_scale=None,
+                        k_out=None, stream=None):
+    """Norm + rotary of bf16 q [S, Hq, D], k [S, Hk, D] with q written as INT8 codes and per-token
+    scales, k as bf16 (k_out may be k); returns ((q8, q_scale), k_out)."""
+    import torch
+
+    S, Hq, D, sq = _token_major("q", q)
+    _, Hk, _, sk = _token_major("k", k)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"q/k must be bfloat16, got {q.dtype}/{k.dtype}")
+    if tuple(k.shape) != (S, Hk, D):
+        raise H3AError(H3A_ESHAPE, f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    q8, sq8 = _i8_out("q8", q8, q, S, Hq, D)
+    qs = _f32_scales("q_scale", q_scale, (Hq, S), q.device)
+    k_out = torch.empty_like(k, memory_format=torch.contiguous_format) if k_out is None else k_out
+    _, _, _, sko = _token_major("k_out", k_out)
+    _same("k_out", k_out, (S, Hk, D), torch.bfloat16)
+    cs = _table(cos_sin, S, int(rot_dim))
+    _check(lib().h3a_qk_rmsnorm_rope_i8q(q.data_ptr(), k.data_ptr(), q8.data_ptr(), k_out.data_ptr(), qs.data_ptr(),
+                                         S, Hq, Hk, D, sq, sk, sq8, sko, _gain("gamma_q", gamma_q, D),
+                                         _gain("gamma_k", gamma_k, D), float(eps), cs, int(rot_dim),
+                                         _stream_handle(stream)))
+    return (q8, qs), k_out
 
 
 def i8_key_blocks(cu_seqlens) -> int:

@@ -952,6 +952,60 @@ h3a_status h3a_quantize_i8_rows(const void* x, void* y, void* y_scale, int64_t S
   }
 }
 
+h3a_status h3a_qk_rmsnorm_rope_i8q(const void* q, const void* k, void* q8, void* k_out, void* q_scale,
+                                   int64_t S, int32_t Hq, int32_t Hk, int32_t D, int64_t stride_q, int64_t stride_k,
+                                   int64_t stride_q8, int64_t stride_ko, const float* gamma_q, const float* gamma_k,
+                                   float eps, const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hk < 1) return fail(H3A_EINVAL, "Hk = %d must be >= 1", Hk);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (rot_dim < 0 || rot_dim > D || rot_dim % 2 != 0)
+      return fail(H3A_EINVAL, "rot_dim = %d must be even and in [0, D = %d]", rot_dim, D);
+    if ((rot_dim / 2) % 8 != 0)
+      return fail(H3A_EUNSUPPORTED, "rot_dim / 2 = %d must be a multiple of 8 for this dtype", rot_dim / 2);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(H3A_EINVAL, "eps = %g must be finite and >= 0", double(eps));
+    h3a_status st;
+    if ((st = check_operand("q", q, S, Hq, D, stride_q, 2)) != H3A_OK) return st;
+    if ((st = check_operand("k", k, S, Hk, D, stride_k, 2)) != H3A_OK) return st;
+    if ((st = check_operand("q8", q8, S, Hq, D, stride_q8, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k_out", k_out, S, Hk, D, stride_ko, 2)) != H3A_OK) return st;
+    const int64_t qsb = S * Hq * 4;
+    if ((st = check_scales("q_scale", q_scale, qsb, 4)) != H3A_OK) return st;
+    if (gamma_q == nullptr) return fail(H3A_EINVAL, "gamma_q is NULL");
+    if (gamma_k == nullptr) return fail(H3A_EINVAL, "gamma_k is NULL");
+    if (!aligned(gamma_q, 4) || !aligned(gamma_k, 4)) return fail(H3A_EUNSUPPORTED, "gamma is not 4-byte aligned");
+    if (rot_dim > 0 && S > 0) {
+      if (cos_sin == nullptr) return fail(H3A_EINVAL, "cos_sin is NULL with rot_dim = %d", rot_dim);
+      if (!aligned(cos_sin, 16)) return fail(H3A_EUNSUPPORTED, "cos_sin is not 16-byte aligned");
+    }
+    if (S == 0) return H3A_OK;
+    // k_out may be k itself (each token is read before it is written); q8 and
+    // q_scale are byte ranges that may touch nothing else
+    const bool k_inplace = k_out == k && stride_ko == stride_k;
+    if (!k_inplace && may_overlap(k_out, stride_ko, Hk, k, stride_k, Hk, S, D, 2))
+      return fail(H3A_EINVAL, "k_out overlaps k without being k itself");
+    if (may_overlap(k_out, stride_ko, Hk, q, stride_q, Hq, S, D, 2)) return fail(H3A_EINVAL, "k_out overlaps q");
+    const Range rq = tensor_range(q, S, Hq, D, stride_q, 2), rk = tensor_range(k, S, Hk, D, stride_k, 2);
+    const Range rko = tensor_range(k_out, S, Hk, D, stride_ko, 2);
+    const Range rq8 = tensor_range(q8, S, Hq, D, stride_q8, 1), rqs = byte_range(q_scale, qsb);
+    for (const Range& r : {rq, rk, rko}) {
+      if (ranges_hit(rq8, r)) return fail(H3A_EINVAL, "q8 overlaps q, k or k_out");
+      if (ranges_hit(rqs, r)) return fail(H3A_EINVAL, "q_scale overlaps q, k or k_out");
+    }
+    if (ranges_hit(rqs, rq8)) return fail(H3A_EINVAL, "q_scale overlaps q8");
+    hipError_t e = h3a::launch_qk_rmsnorm_rope_i8q(q, k, q8, k_out, q_scale, S, Hq, Hk, D, stride_q, stride_k,
+                                                   stride_q8, stride_ko, gamma_q, gamma_k, eps, cos_sin, rot_dim,
+                                                   stream);
+    if (e != hipSuccess) return fail_hip("qk_rmsnorm_rope_i8q launch", e);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_qk_rmsnorm_rope_i8q");
+  }
+}
+
 h3a_status h3a_i8_key_blocks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_blocks) {
   try {
     if (n_blocks == nullptr) return fail(H3A_EINVAL, "n_blocks is NULL");

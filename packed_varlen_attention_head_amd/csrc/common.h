@@ -166,6 +166,14 @@ hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, v
                                        int64_t sq8, int64_t sk8, const float* gq, const float* gk, float eps,
                                        const float* cos_sin, int32_t rot_dim, hipStream_t stream);
 
+// The bf16 norm + rotary pass writing q as INT8 codes of its bf16 results
+// (token stride sq8 in bytes) with one fp32 scale per token and head in
+// q8s [H][S], and k as bf16 (token stride sko elements).
+hipError_t launch_qk_rmsnorm_rope_i8q(const void* q, const void* k, void* q8, void* k_out, void* q8s, int64_t S,
+                                      int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8,
+                                      int64_t sko, const float* gq, const float* gk, float eps,
+                                      const float* cos_sin, int32_t rot_dim, hipStream_t stream);
+
 // Attention with q, k as scaled E4M3 codes (as launch_attn_fwd_fp8qk) and V
 // as the transposed E4M3 layout of launch_prepare_vt_e4m3 (row length vt_cols
 // bytes, scales vt8s); both products on the scaled FP8 MFMA.

@@ -27,7 +27,12 @@
 //     first and every block of 32 head dims shares one power-of-two scale
 //     (mx_scale.h; the four lanes of a block exchange their maxima), so the
 //     codes and scales equal those of the bf16 pass followed by the separate
-//     quantiser.
+//     quantiser;
+//   * or (I8) the q results are written as INT8 codes with one fp32 scale per
+//     token and head (the fused "Sage Q-INT8" tail of the same model card
+//     section), k as plain bf16 for the key-block quantiser: rounded to bf16
+//     first, the row maximum met over the row's lanes, so codes and scales
+//     equal the bf16 pass followed by the row quantiser.
 #include <cstdint>
 
 #include "common.h"
@@ -35,6 +40,9 @@
 
 namespace h3a {
 namespace {
+
+// max of two magnitudes that keeps a NaN (fmaxf would drop it)
+__device__ __forceinline__ float nan_max(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
 
 template <typename T>
 struct Elem;
@@ -98,6 +106,32 @@ struct Elem<Bf16Tag> {
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(b[6], b[7], w1, true);
     return make_uint2(uint32_t(w0), uint32_t(w1));
   }
+  // bf16 rounding, then INT8 codes rint(b * 127 / amax) of a row whose LPV
+  // lanes (consecutive, an aligned group) share amax; a NaN maximum is kept,
+  // so a row holding a NaN or an infinity has a non-finite scale and codes 0.
+  // Returns the codes and leaves the row's scale amax / 127 in *scale.
+  template <int LPV>
+  __device__ static uint2 pack_i8(const float* y, float* scale) {
+    float b[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      b[e] = float(__bf16(y[e]));
+      amax = nan_max(amax, __builtin_fabsf(b[e]));
+    }
+#pragma unroll
+    for (int off = LPV / 2; off >= 1; off >>= 1) amax = nan_max(amax, __shfl_xor(amax, off, 64));
+    const float inv = amax == 0.f ? 0.f : __fdiv_rn(127.0f, amax);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = __builtin_rintf(b[e] * inv);
+      const int c = __builtin_isfinite(r) ? min(127, max(-127, int(r))) : 0;
+      w[e / 4] |= (uint32_t(c) & 0xffu) << (8 * (e % 4));
+    }
+    *scale = __fdiv_rn(amax, 127.0f);
+    return make_uint2(w[0], w[1]);
+  }
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -106,10 +140,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWavesPerBlock = 4;
 constexpr int kBatch = 8;  // head vectors a lane keeps in flight
 
-// F8OUT: dst_scale [H][S][D / 32] E8M0 codes (head-major: a head's tokens are
-// contiguous, the order the attention reads a tile's keys in).
-template <typename T, int D, bool F8OUT>
-__device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, uint8_t* dst_scale,
+// Output forms of one tensor: plain (the input type), E4M3 codes with
+// dst_scale [H][S][D / 32] E8M0 codes (head-major: a head's tokens are
+// contiguous, the order the attention reads a tile's keys in), or INT8 codes
+// with dst_scale [H][S] fp32.
+constexpr int kOutPlain = 0, kOutE4M3 = 1, kOutI8 = 2;
+
+template <typename T, int D, int OUT>
+__device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char* dst, void* dst_scale,
                                               int64_t stride_b, int64_t stride_ob, int32_t token, int32_t S,
                                               int32_t H,
                                               const float* g, const float* c, const float* s, int role,
@@ -121,7 +159,7 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
   const int sub = lane % LPV;
   const int grp = lane / LPV;
   const char* row = src + int64_t(token) * stride_b + sub * 16;
-  char* orow = dst + int64_t(token) * stride_ob + sub * (F8OUT ? V : 16);
+  char* orow = dst + int64_t(token) * stride_ob + sub * (OUT != kOutPlain ? V : 16);
   for (int h0 = 0; h0 < H; h0 += G * kBatch) {
     uint4 raw[kBatch];
 #pragma unroll
@@ -152,11 +190,17 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
       if (h < H) {
         // Streaming (non-temporal) stores: the outputs are not re-read by
         // this pass; measured 14% faster than ordinary stores at S = 20,423.
-        if constexpr (F8OUT) {
+        if constexpr (OUT == kOutE4M3) {
           int X = 0;
           const uint2 pk = Elem<T>::pack_e4m3(out, &X);
           __builtin_nontemporal_store(u32x2{pk.x, pk.y}, reinterpret_cast<u32x2*>(orow + int64_t(h) * D));
-          if ((sub & 3) == 0) dst_scale[(int64_t(h) * S + token) * (D / 32) + sub / 4] = uint8_t(X + 127);
+          if ((sub & 3) == 0)
+            static_cast<uint8_t*>(dst_scale)[(int64_t(h) * S + token) * (D / 32) + sub / 4] = uint8_t(X + 127);
+        } else if constexpr (OUT == kOutI8) {
+          float sc = 0.f;
+          const uint2 pk = Elem<T>::template pack_i8<LPV>(out, &sc);
+          __builtin_nontemporal_store(u32x2{pk.x, pk.y}, reinterpret_cast<u32x2*>(orow + int64_t(h) * D));
+          if (sub == 0) static_cast<float*>(dst_scale)[int64_t(h) * S + token] = sc;
         } else {
           const uint4 pk = Elem<T>::pack(out);
           __builtin_nontemporal_store(u32x4{pk.x, pk.y, pk.z, pk.w},
@@ -167,9 +211,9 @@ __device__ __forceinline__ void norm_rope_one(const char* __restrict__ src, char
   }
 }
 
-template <typename T, int D, bool F8OUT = false>
+template <typename T, int D, int QOUT = kOutPlain, int KOUT = QOUT>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, uint8_t* qos, uint8_t* kos, int64_t sq_b,
+qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, void* qos, void* kos, int64_t sq_b,
                     int64_t sk_b, int64_t sqo_b, int64_t sko_b, int32_t S, int32_t H, int32_t Hk,
                     const float* __restrict__ gq, const float* __restrict__ gk, float eps,
                     const float* __restrict__ cos_sin, int32_t rot_dim) {
@@ -206,25 +250,24 @@ qk_norm_rope_kernel(const char* q, const char* k, char* qo, char* ko, uint8_t* q
     g_q[e] = gq[d0 + e];
     g_k[e] = gk[d0 + e];
   }
-  norm_rope_one<T, D, F8OUT>(q, qo, qos, sq_b, sqo_b, token, S, H, g_q, c, s, role, partner, eps, lane);
-  norm_rope_one<T, D, F8OUT>(k, ko, kos, sk_b, sko_b, token, S, Hk, g_k, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, QOUT>(q, qo, qos, sq_b, sqo_b, token, S, H, g_q, c, s, role, partner, eps, lane);
+  norm_rope_one<T, D, KOUT>(k, ko, kos, sk_b, sko_b, token, S, Hk, g_k, c, s, role, partner, eps, lane);
 }
 
-// Strides in elements of the input type; with F8OUT the output strides are
-// in bytes (one per code).
-template <typename T, int D, bool F8OUT = false>
+// Strides in elements of the input type; for code outputs the output strides
+// are in bytes (one per code).
+template <typename T, int D, int QOUT = kOutPlain, int KOUT = QOUT>
 hipError_t launch(const void* q, const void* k, void* qo, void* ko, int64_t S, int32_t H, int32_t Hk, int64_t sq,
                   int64_t sk, int64_t sqo, int64_t sko, const float* gq, const float* gk, float eps,
                   const float* cos_sin, int32_t rot_dim, hipStream_t stream, void* qos = nullptr,
                   void* kos = nullptr) {
   constexpr int esz = 16 / Elem<T>::V;
-  constexpr int oesz = F8OUT ? 1 : esz;
+  constexpr int qoesz = QOUT != kOutPlain ? 1 : esz, koesz = KOUT != kOutPlain ? 1 : esz;
   const unsigned blocks = unsigned((S + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, F8OUT>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D, QOUT, KOUT>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream,
                      static_cast<const char*>(q), static_cast<const char*>(k), static_cast<char*>(qo),
-                     static_cast<char*>(ko), static_cast<uint8_t*>(qos), static_cast<uint8_t*>(kos), sq * esz,
-                     sk * esz, sqo * oesz, sko * oesz, int32_t(S), H, Hk, gq,
-                     gk, eps, cos_sin, rot_dim);
+                     static_cast<char*>(ko), qos, kos, sq * esz, sk * esz, sqo * qoesz, sko * koesz, int32_t(S), H,
+                     Hk, gq, gk, eps, cos_sin, rot_dim);
   return hipGetLastError();
 }
 
@@ -254,11 +297,24 @@ hipError_t launch_qk_rmsnorm_rope_e4m3(const void* q, const void* k, void* q8, v
                                        int64_t sq8, int64_t sk8, const float* gq, const float* gk, float eps,
                                        const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
   if (D == 128)
-    return launch<Bf16Tag, 128, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream,
-                                      q8s, k8s);
+    return launch<Bf16Tag, 128, kOutE4M3>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim,
+                                          stream, q8s, k8s);
   if (D == 64)
-    return launch<Bf16Tag, 64, true>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim, stream,
-                                     q8s, k8s);
+    return launch<Bf16Tag, 64, kOutE4M3>(q, k, q8, k8, S, H, Hk, sq, sk, sq8, sk8, gq, gk, eps, cos_sin, rot_dim,
+                                         stream, q8s, k8s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_qk_rmsnorm_rope_i8q(const void* q, const void* k, void* q8, void* k_out, void* q8s, int64_t S,
+                                      int32_t H, int32_t Hk, int32_t D, int64_t sq, int64_t sk, int64_t sq8,
+                                      int64_t sko, const float* gq, const float* gk, float eps,
+                                      const float* cos_sin, int32_t rot_dim, hipStream_t stream) {
+  if (D == 128)
+    return launch<Bf16Tag, 128, kOutI8, kOutPlain>(q, k, q8, k_out, S, H, Hk, sq, sk, sq8, sko, gq, gk, eps, cos_sin,
+                                                   rot_dim, stream, q8s, nullptr);
+  if (D == 64)
+    return launch<Bf16Tag, 64, kOutI8, kOutPlain>(q, k, q8, k_out, S, H, Hk, sq, sk, sq8, sko, gq, gk, eps, cos_sin,
+                                                  rot_dim, stream, q8s, nullptr);
   return hipErrorInvalidValue;
 }
 

@@ -322,6 +322,38 @@ def test_qk_rmsnorm_rope_e4m3_rejects(kw, status, word):
 
 
 @pytest.mark.parametrize("kw,status,word", [
+    (dict(Hk=0), h3a.H3A_EINVAL, "Hk ="),
+    (dict(rot=40), h3a.H3A_EUNSUPPORTED, "rot_dim / 2"),
+    (dict(sq8=100), h3a.H3A_ESHAPE, "q8: token stride"),
+    (dict(q8=P + 512), h3a.H3A_EINVAL, "q8 overlaps"),
+    (dict(q8=P + (3 << 24) + 256), h3a.H3A_EINVAL, "q8 overlaps"),
+    (dict(cs=None), h3a.H3A_EINVAL, "cos_sin"),
+    (dict(qs=None), h3a.H3A_EINVAL, "q_scale is NULL"),
+    (dict(qs=P + (7 << 24) + 2), h3a.H3A_EUNSUPPORTED, "q_scale is not 4-byte aligned"),
+    (dict(qs=P + (1 << 24) + 64), h3a.H3A_EINVAL, "q_scale overlaps"),
+    (dict(qs=P + (2 << 24) + 64), h3a.H3A_EINVAL, "q_scale overlaps q8"),
+    (dict(ko=P + (1 << 24) + 256), h3a.H3A_EINVAL, "k_out overlaps k without"),
+    (dict(ko=P + 256), h3a.H3A_EINVAL, "k_out overlaps q"),
+])
+def test_qk_rmsnorm_rope_i8q_rejects(kw, status, word):
+    Hq, Hk, D = 8, kw.get("Hk", 2), 128
+    st = h3a.lib().h3a_qk_rmsnorm_rope_i8q(P, P + (1 << 24), kw.get("q8", P + (2 << 24)), kw.get("ko", P + (3 << 24)),
+                                           kw.get("qs", P + (7 << 24)), 16, Hq, Hk, D, Hq * D, max(Hk, 1) * D,
+                                           kw.get("sq8", Hq * D), max(Hk, 1) * D, P + (4 << 24), P + (5 << 24), 1e-6,
+                                           kw.get("cs", P + (6 << 24)), kw.get("rot", 96), None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+def test_qk_rmsnorm_rope_i8q_accepts_k_in_place_and_empty():
+    """k_out = k with the same stride is accepted (validation only: S = 0 launches nothing)."""
+    st = h3a.lib().h3a_qk_rmsnorm_rope_i8q(P, P + (1 << 24), P + (2 << 24), P + (1 << 24), P + (7 << 24), 0, 8, 2,
+                                           128, 8 * 128, 2 * 128, 8 * 128, 2 * 128, P + (4 << 24), P + (5 << 24),
+                                           1e-6, P + (6 << 24), 96, None)
+    assert st == h3a.H3A_OK, h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
     (dict(cols=320), h3a.H3A_ESHAPE, "vt_cols = 320"),
     (dict(vt=P + (1 << 24) + 8), h3a.H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned"),
     (dict(vs=None), h3a.H3A_EINVAL, "vt_scale is NULL"),

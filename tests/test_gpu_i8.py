@@ -220,6 +220,45 @@ def test_i8qk_nan_propagation():
     compare(to_f64(o[near]), to_f64(base[near]), "bf16", "the NaN row's wave mates")
 
 
+@pytest.mark.parametrize("name,kv", [("h3_s20423_bf16", 24), ("two_seg_bf16", 8), ("vit3d_tiles_bf16", 8)])
+def test_fused_norm_rope_i8q_equals_two_passes(name, kv):
+    """The norm + rotary pass writing q as INT8 codes and per-token scales gives the same
+    bytes as the bf16 pass followed by the row quantiser (and k_out the same bf16 values,
+    also in place), on q holding a zero row, a NaN and an infinity; q is left untouched."""
+    import torch
+
+    w = configs.BF16[name].replace(kv_heads=kv)
+    T = configs.make_tensors(w)
+    log(f"[fused i8q] {name} Hq={w.heads} Hk={w.kv} D={w.head_dim}")
+    qb = T.q.copy()
+    qb[5, 0] = 0
+    qb[17, 1, 9] = _f32_bits_to_bf16(np.array([np.nan], np.float32))[0]
+    qb[w.tokens - 1, w.heads - 1, 0] = _f32_bits_to_bf16(np.array([np.inf], np.float32))[0]
+    q, k = to_device(qb, "bf16"), to_device(T.k, "bf16")
+    q0, k0 = q.clone(), k.clone()
+    gq, gk = torch.from_numpy(T.gamma_q).cuda(), torch.from_numpy(T.gamma_k).cuda()
+    tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    h3a().build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start, stop=w.lin_stop)
+    (q8, qs), kn_f = h3a().qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    h3a().qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn)
+    q8b, qsb = h3a().quantize_i8_rows(qn)
+    torch.cuda.synchronize()
+    # bit patterns: q holds a NaN
+    assert torch.equal(q.view(torch.int16), q0.view(torch.int16)) and torch.equal(k, k0)
+    assert torch.equal(kn_f, kn)
+    _codes_and_scales_equal(q8, qs, q8b.cpu().numpy(), qsb.cpu().numpy(), "fused q rows")
+    assert qs[0, 5] == 0 and torch.isnan(qs[1, 17]) and not torch.isfinite(qs[w.heads - 1, w.tokens - 1])
+    # k in place, q8 written into a wider token stride
+    wide = torch.zeros((w.tokens, w.heads + 1, w.head_dim), dtype=torch.int8, device="cuda")
+    (q8w, qsw), kk = h3a().qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=wide[:, :w.heads],
+                                                k_out=k)
+    torch.cuda.synchronize()
+    assert kk is k and torch.equal(k, kn)
+    assert torch.equal(q8w, q8) and torch.equal(wide[:, w.heads], torch.zeros_like(wide[:, w.heads]))
+    _codes_and_scales_equal(q8w, qsw, q8.cpu().numpy(), qs.cpu().numpy(), "fused q rows, strided")
+
+
 @pytest.mark.parametrize("name", ["two_seg_bf16", "h3_s20423_bf16"])
 def test_i8qk_chain(name):
     """table -> norm + rotary -> INT8 q', k' -> INT8-score attention, against the oracle's
@@ -235,9 +274,14 @@ def test_i8qk_chain(name):
     gq, gk = torch.from_numpy(T.gamma_q).cuda(), torch.from_numpy(T.gamma_k).cuda()
     tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
     cu = h3a().build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    # the fused q path (norm + rotary writing INT8 q), then the bf16 pass (in place) and the
+    # row quantiser: the same output bit for bit
+    q8f, kn_f = h3a().qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim)
+    o_f = h3a().varlen_attn_fwd_i8qk(q8f, h3a().quantize_i8_keys(kn_f, cu), v, cu, w.scale)
     qn_d, kn_d = h3a().qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim)
-    o = to_f64(h3a().varlen_attn_fwd_i8qk(h3a().quantize_i8_rows(qn_d), h3a().quantize_i8_keys(kn_d, cu), v, cu,
-                                          w.scale))
+    o_d = h3a().varlen_attn_fwd_i8qk(h3a().quantize_i8_rows(qn_d), h3a().quantize_i8_keys(kn_d, cu), v, cu, w.scale)
+    assert torch.equal(o_f, o_d)
+    o = to_f64(o_d)
     qf, kf, vf = (rng.as_f64(x, w.dtype) for x in (T.q, T.k, T.v))
     ocu, cos, sin = oracle.rope_table(w.segments, w.rot_dims, w.base)
     qn, kn = oracle.qk_rmsnorm_rope(qf, kf, T.gamma_q, T.gamma_k, w.eps, cos, sin, w.rot_dim)

@@ -652,6 +652,16 @@ def varlen_attention_i8qk(q, k, v, cu, scale: float, causal: bool = False) -> np
     return varlen_attention_gqa(i8_round_q(q), i8_round_k(k, cu), v, cu, scale, causal=causal)
 
 
+def varlen_attention_i8qk_mxv(q, k, v, cu, scale: float, causal: bool = False) -> np.ndarray:
+    """INT8 scores with the PV product on block-scaled E4M3 values (SageAttention
+    2's split between the two products, among the pages' INT8/FP8 Sage backends):
+    varlen_attention_gqa with q and k replaced by what their INT8 codes stand for
+    (section 5e) and v rounded per 32-key block of each segment (section 5d);
+    exact softmax weights.  (A kernel that also rounds the weights to E4M3 for
+    the PV product differs from this by that rounding.)"""
+    return varlen_attention_gqa(i8_round_q(q), i8_round_k(k, cu), mx_round_keys(v, cu), cu, scale, causal=causal)
+
+
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):
     """The whole chain: table, norm + rotary on q and k, then varlen attention."""
     cu, cos, sin = rope_table(segments, rot_dims, base)

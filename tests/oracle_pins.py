@@ -809,6 +809,53 @@ def check_i8_key_blocks_and_attention(O):
     assert np.abs(got - exact).sum() / np.abs(exact).sum() < 0.05
 
 
+def check_i8qk_mxv_attention(O):
+    """INT8 scores with E4M3 V: operands already on their grids (q, k integers with a 127 in
+    every block, v on every segment's 32-key E4M3 block grid) pass through to the exact
+    attention; v off its grid changes the result, by less than E4M3's half step allows; q and
+    k off their grids change it too (both products rounded, not one)."""
+    r = _rng(43)
+    lens = [65, 0, 33, 1, 96]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    q = r.integers(-127, 128, size=(S, 4, 32)).astype(np.float64)
+    q[:, :, 0] = 127.0
+    kk = r.integers(-127, 128, size=(S, 2, 32)).astype(np.float64)
+    kk[:, :, 5] = -127.0
+    # v on the grid: small integers times a power of two per segment are E4M3 values whose
+    # block maxima map onto themselves
+    v = r.integers(-15, 16, size=(S, 2, 32)).astype(np.float64) * np.repeat(2.0 ** np.array([-3.0, 0, 2.0, 0, 5.0]),
+                                                                           lens)[:, None, None]
+    assert np.array_equal(O.mx_round_keys(v, cu), v)
+    for causal in (False, True):
+        assert np.array_equal(O.varlen_attention_i8qk_mxv(q, kk, v, cu, 1e-3, causal),
+                              O.varlen_attention_gqa(q, kk, v, cu, 1e-3, causal))
+    vn = r.normal(size=(S, 2, 32))
+    got = O.varlen_attention_i8qk_mxv(q, kk, vn, cu, 1e-3)
+    exact = O.varlen_attention_gqa(q, kk, vn, cu, 1e-3)
+    assert not np.allclose(got, exact, rtol=0, atol=1e-9)
+    # each output is a convex combination of v rows, each moved by at most 2^-4 of its block max
+    bound = np.zeros((S, 2, 32))
+    for a, b in zip(cu[:-1], cu[1:]):
+        a, b = int(a), int(b)
+        for j in range(a, b, 32):
+            blk = np.abs(vn[j:min(j + 32, b)]).max(axis=0)
+            bound[j:min(j + 32, b)] = 2.0 ** -4 * blk
+    for s_, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        a, b = int(a), int(b)
+        if b > a:
+            lim = bound[a:b].max(axis=0)  # [2, 32]
+            assert np.all(np.abs(got[a:b] - exact[a:b]) <= np.repeat(lim, 2, axis=0)[None] + 1e-12)
+    # tokens at magnitudes 2^0 .. 2^-23: a 32-key block's scale follows its largest token, so
+    # the smaller tokens of the block lose precision (a per-token block would keep it)
+    vm = vn * 2.0 ** -(np.arange(S) % 24)[:, None, None]
+    qn, kn = r.normal(size=(S, 4, 32)), r.normal(size=(S, 2, 32))
+    g2 = O.varlen_attention_i8qk_mxv(qn, kn, vm, cu, 0.2)
+    assert np.array_equal(g2, O.varlen_attention_gqa(O.i8_round_q(qn), O.i8_round_k(kn, cu), O.mx_round_keys(vm, cu),
+                                                     cu, 0.2))
+    assert not np.allclose(g2, O.varlen_attention_gqa(qn, kn, O.mx_round_keys(vm, cu), cu, 0.2), rtol=0, atol=1e-9)
+
+
 # ---------------------------------------------------------------------------
 # the chain
 # ---------------------------------------------------------------------------
@@ -895,7 +942,7 @@ ALL_CHECKS = [
     check_mx_quantize,
     check_mx_keys_and_attention,
     check_i8_quantize,
-    check_i8_key_blocks_and_attention,
+    check_i8_key_blocks_and_attention, check_i8qk_mxv_attention,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

@@ -336,6 +336,12 @@ MUTANTS = {
     "i8_keys_not_segment_aligned": dict(i8_quantize_key_blocks=_i8_keys_global_blocks),
     "i8qk_rounds_only_q": dict(varlen_attention_i8qk=lambda q, k, v, cu, scale, causal=False:
                                oracle.varlen_attention_gqa(oracle.i8_round_q(q), k, v, cu, scale, causal)),
+    "i8qk_mxv_v_exact": dict(varlen_attention_i8qk_mxv=lambda q, k, v, cu, scale, causal=False:
+                             oracle.varlen_attention_i8qk(q, k, v, cu, scale, causal)),
+    "i8qk_mxv_v_per_dim_block": dict(varlen_attention_i8qk_mxv=lambda q, k, v, cu, scale, causal=False:
+                                     oracle.varlen_attention_i8qk(q, k, oracle.mx_round(v), cu, scale, causal)),
+    "i8qk_mxv_scores_exact": dict(varlen_attention_i8qk_mxv=lambda q, k, v, cu, scale, causal=False:
+                                  oracle.varlen_attention_gqa(q, k, oracle.mx_round_keys(v, cu), cu, scale, causal)),
 }
 
 

@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--i8-qk", action="store_true",
                     help="step = table + q/k norm/rotary + INT8 codes of q (one scale per token) and k (one per 64 "
                          "keys of a segment) + INT8-score attention")
+    ap.add_argument("--i8-fp8pv", action="store_true",
+                    help="step = table + q/k norm/rotary writing INT8 q + INT8 codes of k + transposed E4M3 V + "
+                         "attention with INT8 QK^T and FP8 PV")
     ap.add_argument("--fused-q", action="store_true",
                     help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
     ap.add_argument("--split", choices=("auto", "never", "always"), default="auto",
@@ -115,6 +118,8 @@ def _short_kernel(name):
             tags.append("fp8")
         if len(a) > 4 and a[4] == "3":
             tags.append("i8qk")
+        if len(a) > 4 and a[4] == "4":
+            tags.append("i8qk fp8pv")
         return f"{m.group(1)}<{', '.join(tags)}>"
     m = re.search(r"(qk_norm_rope_kernel<[^>]*>|rope_table_kernel|"
                   r"__amd_rocclr_\w+|elementwise_kernel|vectorized_elementwise_kernel|reduce_kernel)", name)
@@ -453,13 +458,14 @@ def main():
         return h3a.build_rope_table_ex(w.segments, w.rope_mode, w.rot_dims, w.base, tab, start=w.lin_start,
                                        stop=w.lin_stop, stream=stream)
 
-    fused, fp8, fp8pv, i8 = args.fused_q, args.fp8_qk or args.fp8, args.fp8, args.i8_qk
+    fused, fp8, fp8pv, i8pv = args.fused_q, args.fp8_qk or args.fp8, args.fp8, args.i8_fp8pv
+    i8 = args.i8_qk or i8pv
     if fused and (w.causal or w.rot_dim % 32 != 0 or fp8):
         print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32, without --fp8-qk "
               f"({w.name})", file=sys.stderr)
         return 2
     if i8 and (fused or fp8):
-        print("--i8-qk excludes --fused-q, --fp8 and --fp8-qk", file=sys.stderr)
+        print("--i8-qk and --i8-fp8pv exclude --fused-q, --fp8 and --fp8-qk", file=sys.stderr)
         return 2
     if i8:  # int8 codes: q with an fp32 scale per token, k with one per 64 keys of a segment
         nb = h3a.i8_key_blocks(np.concatenate([[0], np.cumsum(w.lengths)]))
@@ -472,7 +478,7 @@ def main():
               torch.empty((q.shape[1], q.shape[0], q.shape[2] // 32), dtype=torch.uint8, device=dev))
         k8 = (torch.empty(k.shape, dtype=torch.uint8, device=dev),
               torch.empty((k.shape[1], k.shape[0], k.shape[2] // 32), dtype=torch.uint8, device=dev))
-    if fp8pv:  # transposed codes and one scale per 32 keys of each head dim
+    if fp8pv or i8pv:  # transposed codes and one scale per 32 keys of each head dim
         cols = h3a.vt_e4m3_columns(np.concatenate([[0], np.cumsum(w.lengths)]))
         vt8 = (torch.empty((w.kv, w.head_dim, cols), dtype=torch.uint8, device=dev),
                torch.empty((w.kv, cols // 64, 2, 32, w.head_dim // 32), dtype=torch.uint8, device=dev))
@@ -488,13 +494,21 @@ def main():
                                            stream=stream)
         return h3a.qk_rmsnorm_rope(q, k, gq, gk, w.eps, tab, w.rot_dim, q_out=qn, k_out=kn, stream=stream)
 
+    def vt_prep(cu):  # V as transposed E4M3 tiles (changes every step, like q and k)
+        h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
+
+    def k_quant(cu):  # INT8 codes of the normalised, rotated k, one scale per 64 keys of a segment
+        h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], stream=stream)
+
     def vprep(cu):
-        if fp8pv:  # V as transposed E4M3 tiles (changes every step, like q and k)
-            h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
-        if i8:  # INT8 codes of the normalised, rotated k, one scale per 64 keys of a segment
-            h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], stream=stream)
+        if fp8pv or i8pv:
+            vt_prep(cu)
+        if i8:
+            k_quant(cu)
 
     def attention(cu):
+        if i8pv:
+            return h3a.varlen_attn_fwd_i8qk_fp8pv(q8, k8, vt8, cu, w.scale, causal=w.causal, out=o, stream=stream)
         if i8:
             return h3a.varlen_attn_fwd_i8qk(q8, k8, v, cu, w.scale, causal=w.causal, out=o, stream=stream)
         if fp8pv:
@@ -574,14 +588,15 @@ def main():
     sclk = clock.stop()
     norm_s = timed(norm, n_ev)
     table_s = timed(table, n_ev)
-    vprep_s = timed(lambda: vprep(cu), n_ev) if (fp8pv or i8) else 0.0
+    vt_s = timed(lambda: vt_prep(cu), n_ev) if (fp8pv or i8pv) else 0.0
+    kq_s = timed(lambda: k_quant(cu), n_ev) if i8 else 0.0
 
     F = w.attention_flops()
     attn_tflops = F / attn_s / 1e12
     # FP8 QK^T (half of F) at the FP8 dense peak and bf16 PV at the bf16 one:
     # F / (F/2 / 5000 + F/2 / 2500) = 3333 TFLOP/s for the kernel as a whole.
     # (INT8 QK^T at the INT8 dense peak, the same figure, with bf16 PV: 3333 too)
-    peak = (PEAK_FP8_TFLOPS if fp8pv else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS) if (fp8 or i8)
+    peak = (PEAK_FP8_TFLOPS if (fp8pv or i8pv) else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS) if (fp8 or i8)
             else PEAK_BF16_TFLOPS)
     S, H, Hkv, D = w.tokens, w.heads, w.kv, w.head_dim
     # q and k (H + Hkv heads; k only when fused) read and written, the table and gains read
@@ -609,7 +624,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("fp8 e4m3 QK^T and PV" if fp8pv else "fp8 e4m3 QK^T, bf16 PV" if fp8
-                  else "int8 QK^T, bf16 PV" if i8 else "bf16"),
+                  else "int8 QK^T, fp8 e4m3 PV" if i8pv else "int8 QK^T, bf16 PV" if i8 else "bf16"),
         "data": f"synthetic: Q,K,V ~ N(0,1) bf16, gains ~ {w.gamma_mean:g}+N(0,{w.gamma_std:g}) fp32, "
                 f"SplitMix64 seed {w.seed}",
         "config": {
@@ -623,6 +638,8 @@ def main():
                      else "rope table + q/k norm/rotary to E4M3 codes + transposed E4M3 V + attention with both "
                           "products in FP8" if fp8pv
                      else "rope table + q/k norm/rotary to E4M3 codes + attention with FP8 QK^T" if fp8
+                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k + transposed E4M3 V + "
+                          "attention with INT8 QK^T and FP8 PV" if i8pv
                      else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k + attention with INT8 QK^T" if i8
                      else "rope table + q/k norm/rotary + attention"),
         },
@@ -639,8 +656,8 @@ def main():
         "norm_rope_ms": norm_s * 1e3,
         "norm_rope_GBps": norm_bytes / norm_s / 1e9,
         "rope_table_ms": table_s * 1e3,
-        "v_e4m3_ms": vprep_s * 1e3 if fp8pv else 0.0,
-        "i8_k_quant_ms": vprep_s * 1e3 if i8 else 0.0,
+        "v_e4m3_ms": vt_s * 1e3,
+        "i8_k_quant_ms": kq_s * 1e3,
         "checksum_o": checksum,
         "roofline": {
             "bound": "mfma",
@@ -650,7 +667,7 @@ def main():
             "frac": attn_tflops / peak,
             "traffic": (measured_traffic(ATTN_KERNEL, ATTN_SRC) if (w.name == HEADLINE and not (fp8 or fused or i8))
                         else None),
-            "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8' if fp8pv else ', fp8qk' if fp8 else ', i8qk' if i8 else ''}"
+            "kernel": f"attn_fwd_bf16_kernel<{D}{', fp8' if fp8pv else ', fp8qk' if fp8 else ', i8qk fp8pv' if i8pv else ', i8qk' if i8 else ''}"
                       f"{', qnorm' if fused else ''}>",
             "algorithmic_flop_per_launch": F,
             "algorithmic_bytes_per_launch": attn_alg_bytes,

@@ -441,6 +441,23 @@ h3a_status h3a_varlen_attn_fwd_i8qk(const void* q8, const void* k8, const void* 
                                     hipStream_t stream);
 
 /*
+ * INT8 scores with the PV product in FP8 (SageAttention 2's split of the two
+ * products, named by the pages among the GB10 build's attention backends:
+ * H3 Blackwell Runtime README, attention backends): q8 / q_scale and k8 /
+ * k_scale as for h3a_varlen_attn_fwd_i8qk, v as the transposed E4M3 layout
+ * vt8 / vt_scale of h3a_prepare_vt_e4m3 (vt_cols from h3a_vt_e4m3_columns,
+ * whose 64-key column blocks are also k_scale's key blocks).  The weights are
+ * formed and rounded as for h3a_varlen_attn_fwd_fp8.  The result equals
+ * attention on the values the codes stand for up to the rounding of the
+ * weights to E4M3 and the bf16 output.  Errors: as h3a_varlen_attn_fwd_fp8.
+ */
+h3a_status h3a_varlen_attn_fwd_i8qk_fp8pv(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                          const void* k_scale, const void* vt_scale, void* o, int64_t S, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
+                                          int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                          int32_t causal, hipStream_t stream);
+
+/*
  * Varlen attention with grouped K/V heads and an optional causal mask: the
  * encoder text tower's causal GQA (vllm.cpp PR #26, encoder-tower commit,
  * "Causal GQA attention": K/V heads are broadcast across their query group).

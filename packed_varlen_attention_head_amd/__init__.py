@@ -52,6 +52,7 @@ EXPORTS = (
     "h3a_qk_rmsnorm_rope_i8q",
     "h3a_quantize_i8_keys",
     "h3a_varlen_attn_fwd_i8qk",
+    "h3a_varlen_attn_fwd_i8qk_fp8pv",
     "h3a_plan_tiles",
     "h3a_plan_tiles_ex",
     "h3a_last_error",
@@ -122,6 +123,7 @@ def lib() -> ctypes.CDLL:
                                           _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_quantize_i8_keys.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _c_i32p, _i32, _vp]
     L.h3a_varlen_attn_fwd_i8qk.argtypes = L.h3a_varlen_attn_fwd_fp8qk.argtypes
+    L.h3a_varlen_attn_fwd_i8qk_fp8pv.argtypes = L.h3a_varlen_attn_fwd_fp8.argtypes
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
                                       _c_i32p, _i32, _f32, _vp]
     L.h3a_varlen_attn_fwd_ex.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i64, _i64, _i64,
@@ -134,7 +136,7 @@ def lib() -> ctypes.CDLL:
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
                  "h3a_quantize_i8_rows", "h3a_i8_key_blocks", "h3a_quantize_i8_keys", "h3a_varlen_attn_fwd_i8qk",
-                 "h3a_qk_rmsnorm_rope_i8q",
+                 "h3a_qk_rmsnorm_rope_i8q", "h3a_varlen_attn_fwd_i8qk_fp8pv",
                  "h3a_varlen_attn_fwd_ex", "h3a_varlen_attn_fwd_noalloc", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -643,6 +645,37 @@ def varlen_attn_fwd_i8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = Fal
     _check(lib().h3a_varlen_attn_fwd_i8qk(q8.data_ptr(), k8.data_ptr(), qs.data_ptr(), ks.data_ptr(), v.data_ptr(),
                                           out.data_ptr(), S, Hq, Hkv, D, sq, sk, sv, so, _ptr_i32(cu), len(cu) - 1,
                                           float(scale), int(bool(causal)), _stream_handle(stream)))
+    return out
+
+
+def varlen_attn_fwd_i8qk_fp8pv(q8, k8, vt8, cu_seqlens, scale: float, causal: bool = False, out=None,
+                              stream=None):
+    """Attention with INT8 q8 = quantize_i8_rows(q), k8 = quantize_i8_keys(k, cu_seqlens) pairs and
+    vt8 = prepare_vt_e4m3(v, cu_seqlens) (E4M3 V^T codes, scales); bf16 output."""
+    import torch
+
+    (q8, qs), (k8, ks), (vt8, vs) = _pair("q8", q8), _pair("k8", k8), _pair("vt8", vt8)
+    S, Hq, D, sq = _token_major("q8", q8)
+    _, Hkv, _, sk = _token_major("k8", k8)
+    if q8.dtype != torch.int8 or k8.dtype != torch.int8:
+        raise H3AError(H3A_EDTYPE, f"q8/k8 must hold int8 codes, got {q8.dtype}/{k8.dtype}")
+    if tuple(k8.shape) != (S, Hkv, D):
+        raise H3AError(H3A_ESHAPE, f"k8 shape {tuple(k8.shape)} does not match q8 {tuple(q8.shape)}")
+    cu = _i32_array(cu_seqlens)
+    cols = vt_e4m3_columns(cu)
+    nb = cols // 64
+    _expect("vt8", vt8, (Hkv, D, max(cols, 1)), torch.uint8)
+    qs = _f32_scales("q_scale", qs, (Hq, S), q8.device)
+    ks = _f32_scales("k_scale", ks, (Hkv, max(nb, 1)), q8.device)
+    vs = _scales("vt_scale", vs, (Hkv, max(cols, 64) // 64, 2, 32, D // 32), q8.device)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=q8.device)
+    _, _, _, so = _token_major("out", out)
+    _same("out", out, (S, Hq, D), torch.bfloat16)
+    _check(lib().h3a_varlen_attn_fwd_i8qk_fp8pv(q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), qs.data_ptr(),
+                                                ks.data_ptr(), vs.data_ptr(), out.data_ptr(), S, Hq, Hkv, D, sq, sk,
+                                                cols, so, _ptr_i32(cu), len(cu) - 1, float(scale),
+                                                int(bool(causal)), _stream_handle(stream)))
     return out
 
 

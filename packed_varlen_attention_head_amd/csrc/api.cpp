@@ -1105,6 +1105,64 @@ h3a_status h3a_varlen_attn_fwd_i8qk(const void* q8, const void* k8, const void* 
   }
 }
 
+h3a_status h3a_varlen_attn_fwd_i8qk_fp8pv(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                          const void* k_scale, const void* vt_scale, void* o, int64_t S, int32_t Hq,
+                                          int32_t Hkv, int32_t D, int64_t stride_q, int64_t stride_k, int64_t vt_cols,
+                                          int64_t stride_o, const int32_t* cu_seqlens, int32_t nseg, float scale,
+                                          int32_t causal, hipStream_t stream) {
+  try {
+    if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+    if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+    if (Hq < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", Hq);
+    if (Hkv < 1) return fail(H3A_EINVAL, "Hkv = %d must be >= 1", Hkv);
+    if (Hq % Hkv != 0) return fail(H3A_ESHAPE, "Hkv = %d does not divide H = %d", Hkv, Hq);
+    if (causal != 0 && causal != 1) return fail(H3A_EINVAL, "causal = %d must be 0 or 1", causal);
+    if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+    if (!(scale > 0.f) || !std::isfinite(scale)) return fail(H3A_EINVAL, "scale = %g must be finite and > 0", double(scale));
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+    if ((st = check_operand("q", q8, S, Hq, D, stride_q, 1)) != H3A_OK) return st;
+    if ((st = check_operand("k", k8, S, Hkv, D, stride_k, 1)) != H3A_OK) return st;
+    if ((st = check_operand("o", o, S, Hq, D, stride_o, 2)) != H3A_OK) return st;
+    // the padded columns of the V^T layout are also the k scales' key blocks
+    const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg);
+    if (vt_cols != need)
+      return fail(H3A_ESHAPE, "vt_cols = %lld but the padded layout of cu_seqlens has %lld columns", (long long)vt_cols,
+                  (long long)need);
+    if (int64_t(D) * vt_cols > int64_t(INT32_MAX))
+      return fail(H3A_EUNSUPPORTED, "D * vt_cols = %lld exceeds INT32_MAX", (long long)(int64_t(D) * vt_cols));
+    const int64_t n_blocks = vt_cols / h3a::kVtTile;
+    const int64_t qsb = S * Hq * 4, ksb = int64_t(Hkv) * n_blocks * 4, vsb = int64_t(Hkv) * vt_cols * (D / 32);
+    if ((st = check_scales("q_scale", q_scale, qsb, 4)) != H3A_OK) return st;
+    if ((st = check_scales("k_scale", k_scale, ksb, 4)) != H3A_OK) return st;
+    if ((st = check_scales("vt_scale", vt_scale, vsb, D / 32)) != H3A_OK) return st;
+    if (S == 0) return H3A_OK;
+    if (vt8 == nullptr) return fail(H3A_EINVAL, "vt8 is NULL");
+    if (!aligned(vt8, 16)) return fail(H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned");
+    const Range ro = tensor_range(o, S, Hq, D, stride_o, 2);
+    const Range rq = tensor_range(q8, S, Hq, D, stride_q, 1), rk = tensor_range(k8, S, Hkv, D, stride_k, 1);
+    const uintptr_t t0 = reinterpret_cast<uintptr_t>(vt8), t1 = t0 + uintptr_t(int64_t(Hkv) * D * vt_cols);
+    if (ranges_hit(ro, rq)) return fail(H3A_EINVAL, "o overlaps q");
+    if (ranges_hit(ro, rk)) return fail(H3A_EINVAL, "o overlaps k");
+    if (ro.lo < t1 && t0 < ro.hi) return fail(H3A_EINVAL, "o overlaps vt8");
+    for (const Range& r : {byte_range(q_scale, qsb), byte_range(k_scale, ksb), byte_range(vt_scale, vsb)})
+      if (ranges_hit(ro, r)) return fail(H3A_EINVAL, "o overlaps a scale array");
+    PlanUse plan;
+    std::unique_lock<std::mutex> plan_lock;  // held until the launches below are enqueued
+    if ((st = get_plan(cu_seqlens, nseg, Hq, h3a::kAttnBlockM_BF16, causal != 0, true, stream, &plan, &plan_lock)) !=
+        H3A_OK)
+      return st;
+    return run_plan(plan, stream, o, D, stride_o, "varlen attention (int8 qk, fp8 pv) launch",
+                    [&](const h3a::WorkItem* items, int64_t n, const h3a::SplitArgs& sp) {
+                      return h3a::launch_attn_fwd_i8qk_fp8pv(q8, k8, vt8, q_scale, k_scale, vt_scale, o, D, stride_q,
+                                                             stride_k, S * 4, n_blocks * 4, vt_cols, stride_o, items,
+                                                             n, scale, Hq / Hkv, causal != 0, stream, sp);
+                    });
+  } catch (...) {
+    return fail_exception("h3a_varlen_attn_fwd_i8qk_fp8pv");
+  }
+}
+
 h3a_status h3a_vt_e4m3_columns(const int32_t* cu_seqlens, int32_t nseg, int64_t* columns) {
   try {
     if (columns == nullptr) return fail(H3A_EINVAL, "columns is NULL");

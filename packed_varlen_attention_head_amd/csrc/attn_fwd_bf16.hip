@@ -76,6 +76,13 @@
 //     B operand after four lane-half swaps that give each lane the same keys.
 //     The row sums are one more FP8 MFMA per tile with an all-ones A operand,
 //     so they add exactly the E4M3 weights PV applies; the 2^4 cancels.
+//     F8 == 3 takes Q and K as INT8 codes (one fp32 scale per query row, one
+//     per 64-key block of a segment) and runs the score product on
+//     v_mfma_i32_32x32x32_i8: the accumulator starts from the bits of the
+//     float 1.5 * 2^23, so the exact int32 sum reads as a float offset by that
+//     constant and the probabilities' existing FMA applies both scales and
+//     removes the offset.  F8 == 4 combines those scores with F8 == 2's FP8 PV
+//     product (INT8 QK^T, FP8 PV).
 //   * Variants: K/V heads shared by groups of query heads (query head h reads
 //     K/V head h / kv_group), and a causal mask aligned at the segment start
 //     (the encoder text tower's causal GQA; encoder-tower commit).  Causal
@@ -210,8 +217,9 @@ struct QNormArgs {
 
 // Per-block E8M0 scales of the FP8 operands (F8 >= 1), head-major so a
 // tile's rows are contiguous: q [Hq][S][D/32] and k [Hkv][S][D/32] (head
-// strides q_head, k_head bytes); F8 == 2 also v [Hkv][v_tiles][2][32][D/32]
-// (dim 32 b + r of 32-key block j of a tile at [j][r][b]).
+// strides q_head, k_head bytes); F8 == 2 and 4 also v [Hkv][v_tiles][2][32][D/32]
+// (dim 32 b + r of 32-key block j of a tile at [j][r][b]).  INT8 (F8 == 3, 4):
+// q holds fp32 [Hq][S] and k fp32 [Hkv][key blocks] instead.
 struct F8Scales {
   const uint8_t* q;
   const uint8_t* k;
@@ -224,9 +232,10 @@ struct F8Scales {
 namespace {
 
 // RH: 16-dim blocks per rotary half when QNORM (rot_dim = 32 RH), else 0.
-// F8 >= 1: q and k hold E4M3 codes (token strides sq, sk in bytes).  F8 == 2:
-// v is the transposed E4M3 layout [head][dim][column], sv its row length in
-// bytes, each item's segment starting at column it.vt_col0.
+// F8 >= 1: q and k hold E4M3 (F8 1, 2) or INT8 (F8 3, 4) codes (token strides
+// sq, sk in bytes).  F8 == 2, 4: v is the transposed E4M3 layout
+// [head][dim][column], sv its row length in bytes, each item's segment
+// starting at column it.vt_col0.
 template <int D, bool CAUSAL, bool QNORM, int RH, int F8>
 __global__ void __launch_bounds__(64 * kWaves, 2)
 attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -249,15 +258,16 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int KS8 = D / 64;                      // FP8 MFMA k-steps over the head dim
   constexpr int NDMAV8 = D * 4 / (64 * kWaves);    // FP8 V^T tile: D rows x 4 chunks
   constexpr bool kF8K = F8 == 1 || F8 == 2;       // E4M3 q, k with per-32-dim scales
-  constexpr bool kI8 = F8 == 3;                   // INT8 q, k: per-row q, per-64-key-block k scales
-  constexpr bool kPbf = F8 != 2;                  // bf16 probabilities and V
+  constexpr bool kI8 = F8 == 3 || F8 == 4;       // INT8 q, k: per-row q, per-64-key-block k scales
+  constexpr bool kPV8 = F8 == 2 || F8 == 4;       // E4M3 probabilities and V^T, FP8 PV product
+  constexpr bool kPbf = !kPV8;                    // bf16 probabilities and V
   constexpr int KS32 = D / 32;                    // INT8 MFMA k-steps over the head dim
   static_assert(NDMAK >= 1 && NDMAV8 >= 1 && !(F8 && QNORM), "tile layout / variant");
 
   // One object per ring slot, so alias analysis can tell a load into one slot
   // from reads of another (otherwise every LDS read waits for all loads).
   __shared__ uint16_t k_slot0[kBN * KROWB / 2], k_slot1[kBN * KROWB / 2];
-  __shared__ uint16_t v_slot0[F8 == 2 ? kBN * D / 2 : kBN * D], v_slot1[F8 == 2 ? kBN * D / 2 : kBN * D];
+  __shared__ uint16_t v_slot0[kPV8 ? kBN * D / 2 : kBN * D], v_slot1[kPV8 ? kBN * D / 2 : kBN * D];
   // Slot pointers: compile-time choice for IC<> slots, a select otherwise.
   auto kslot = [&](auto slot) -> uint16_t* {
     if constexpr (std::is_integral_v<decltype(slot)>) return slot ? k_slot1 : k_slot0;
@@ -271,13 +281,13 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // F8: the block scales of a ring slot's tile, one dword per row (the row's
   // D / 32 bytes, zero-extended: an LDS-bound load narrower than a dword
-  // still fills one dword per lane): the K tile's 64 keys; F8 == 2 also the
-  // V^T tile's (key block j, dim 32 b + r) words in lane order 32 j + r.  One
-  // wave fetches each with one LDS-bound load, shared by the workgroup like
-  // the tile itself.
-  constexpr int SCB = kF8K ? kBN * 4 : 4;
-  __shared__ __align__(16) uint8_t ks_slot0[SCB], ks_slot1[SCB];
-  __shared__ __align__(16) uint8_t vs_slot0[F8 == 2 ? SCB : 4], vs_slot1[F8 == 2 ? SCB : 4];
+  // still fills one dword per lane): the K tile's 64 keys (E4M3 scores); with
+  // FP8 PV the V^T tile's (key block j, dim 32 b + r) words in lane order
+  // 32 j + r.  One wave fetches each with one LDS-bound load, shared by the
+  // workgroup like the tile itself.
+  constexpr int SCBK = kF8K ? kBN * 4 : 4, SCBV = kPV8 ? kBN * 4 : 4;
+  __shared__ __align__(16) uint8_t ks_slot0[SCBK], ks_slot1[SCBK];
+  __shared__ __align__(16) uint8_t vs_slot0[SCBV], vs_slot1[SCBV];
   auto kscl = [&](auto slot) -> uint8_t* {
     if constexpr (std::is_integral_v<decltype(slot)>) return slot ? ks_slot1 : ks_slot0;
     else if constexpr (decltype(slot)::value == 0) return ks_slot0;
@@ -448,19 +458,19 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   float m_run = -1e30f;  // reference max of scale*log2(e)*score
   // Kept with it (updated only where m_run moves, not per tile): the bound
-  // past which a tile max raises it, and F8 == 2's exponent offset.
-  constexpr float kSlack = F8 == 2 ? kRescaleSlackF8 : kRescaleSlack;
+  // past which a tile max raises it, and the FP8 PV exponent offset.
+  constexpr float kSlack = kPV8 ? kRescaleSlackF8 : kRescaleSlack;
   float m_thr = m_run + kSlack;
   [[maybe_unused]] float m_off = kProbOffsetF8 - m_run;
   float l_run = 0.f;     // this lane's partial row sum (its 16-of-32 keys)
-  // F8 == 2: the row sums come from the matrix core instead -- an all-ones
+  // FP8 PV: the row sums come from the matrix core instead -- an all-ones
   // A operand against the E4M3 probabilities puts sum_k p[k][q] in every
   // register of lane q (both halves), the same weights PV applies.
   [[maybe_unused]] f32x16 lacc = f32x16{};
   // The all-ones A operand (four E4M3 ones per dword), built once: opaque to
   // the compiler so it stays in registers instead of being rebuilt per tile.
   [[maybe_unused]] i32x8 ones8;
-  if constexpr (F8 == 2) {
+  if constexpr (kPV8) {
     const int one4 = 0x38383838;
     ones8 = i32x8{one4, one4, one4, one4, one4, one4, one4, one4};
     asm volatile("" : "+v"(ones8));
@@ -475,15 +485,26 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if constexpr (kI8) {
     constexpr int m = 0x4B400000;
     magic = i32x16{m, m, m, m, m, m, m, m, m, m, m, m, m, m, m, m};
-    asm volatile("" : "+v"(magic));
+    if constexpr (!kPV8) asm volatile("" : "+v"(magic));
   }
   // Score multiplier and offset of the tile whose probabilities are formed
-  // next: scores are sacc * cmul + cadd (c and 0 but for kI8), its k scale
-  // arriving in kscale with the tile's V load.
-  [[maybe_unused]] float cmul = c, cadd = 0.f, kscale = 0.f;
-  [[maybe_unused]] auto set_tile_scale = [&]() {
+  // next: scores are sacc * cmul + cadd (c and 0 but for kI8).  kI8: the k
+  // scale of the tile in K ring slot j arrives in kscale[j] with the tile's
+  // K load, two tiles before its scores are formed.
+  [[maybe_unused]] float cmul = c, cadd = 0.f;
+  [[maybe_unused]] float kscale[2] = {0.f, 0.f};
+  [[maybe_unused]] auto set_tile_scale = [&](auto slot) {
     if constexpr (kI8) {
-      cmul = cq * kscale;
+      float ks;
+      if constexpr (std::is_integral_v<decltype(slot)>) ks = slot ? kscale[1] : kscale[0];
+      else ks = kscale[decltype(slot)::value];
+      // A zero scale (an all-zero q row or k block, or rows past the segment
+      // end) would turn a masked key's -inf into -inf * 0 = NaN: use the
+      // smallest normal instead (every such score is 0 exactly, or at most
+      // 2^22 * 2^-126 from it, either way a probability of 1 against the
+      // reference).  A NaN scale stays NaN.
+      cmul = cq * ks;
+      cmul = cmul < 1.17549435e-38f ? 1.17549435e-38f : cmul;
       cadd = -cmul * 12582912.0f;
     }
   };
@@ -533,9 +554,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // kk*16 + 4 (g / 2) + {0..3} (and +8) at dims db*32 + 16 (g % 2) + 0..15;
   // lane m of the group addresses row m / 4, columns 4 (m % 4) .. +3.
   int vaddr[DB];
-  // F8 == 2 V^T operand reads: row db*32 + l32, chunks hi + {0, 2}.
-  [[maybe_unused]] int vaddr8[F8 == 2 ? DB : 1][2];
-  if constexpr (F8 == 2)
+  // FP8 V^T operand reads: row db*32 + l32, chunks hi + {0, 2}.
+  [[maybe_unused]] int vaddr8[kPV8 ? DB : 1][2];
+  if constexpr (kPV8)
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -554,7 +575,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
 
   const char* kbase = reinterpret_cast<const char*>(k) + (int64_t(it.seg_start) * sk + kv_off) * KESZ;
-  const char* vbase = F8 == 2 ? reinterpret_cast<const char*>(v) + int64_t(kv_off) * sv + it.vt_col0
+  const char* vbase = kPV8 ? reinterpret_cast<const char*>(v) + int64_t(kv_off) * sv + it.vt_col0
                               : reinterpret_cast<const char*>(v + int64_t(it.seg_start) * sv + kv_off);
   // Keys the item needs: the whole segment, or (causal) up to its last row.
   const int nkeys = CAUSAL ? min(it.seg_len, it.q_start + kBM) : it.seg_len;
@@ -583,16 +604,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         load_scales(rs, kscl(slot));
       }
     }
-  };
-  auto load_v = [&](int t, auto slot) {
-    const int key0 = t * kBN;
     if constexpr (kI8) {
       // the tile's k scale ([kv head][key block], the segment's first block at
       // vt_col0 / 64), one fp32 for every lane; past the segment: 0
       const auto rs = rows_rsrc(fs.k + kv_head * fs.k_head + int64_t(it.vt_col0 / kVtTile) * 4,
                                 (it.seg_len + kBN - 1) / kBN, 1 << 20, 4);
-      kscale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, 0, 0));
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, 0, 0));
+      if constexpr (std::is_integral_v<decltype(slot)>) {
+        if (slot) kscale[1] = x;
+        else kscale[0] = x;
+      } else {
+        kscale[decltype(slot)::value] = x;
+      }
     }
+  };
+  auto load_v = [&](int t, auto slot) {
+    const int key0 = t * kBN;
     if constexpr (kPbf) {
       const auto r = rows_rsrc(vbase + int64_t(key0) * sv * 2, it.seg_len - key0, kBN, int(sv) * 2);
 #pragma unroll
@@ -720,9 +747,9 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where unchanged
       m_run = m_new;
       m_thr = m_run + kSlack;
-      if constexpr (F8 == 2) m_off = kProbOffsetF8 - m_run;
+      if constexpr (kPV8) m_off = kProbOffsetF8 - m_run;
       l_run *= alpha;
-      if constexpr (F8 == 2) lacc *= alpha;
+      if constexpr (kPV8) lacc *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
@@ -785,16 +812,17 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     l_run += part;
   };
   auto probs = [&](const f32x16* sacc, bf16x8* pb) {
-    if constexpr (F8 == 2) {
+    if constexpr (kPV8) {
       // E4M3 weights 2^4 p (p <= 2^4 against the reference, so <= 256), dword
-      // g = keys 8g + 4 hi + {0..3}.
-      const float moff = m_off;
+      // g = keys 8g + 4 hi + {0..3}; INT8 scores: s * cmul + cadd
+      const float mul = kI8 ? cmul : c;
+      const float moff = kI8 ? cadd + m_off : m_off;
       int d[8];
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         float p4[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], c, moff));
+        for (int w = 0; w < 4; ++w) p4[w] = __builtin_amdgcn_exp2f(fmaf(sacc[g / 4][4 * (g % 4) + w], mul, moff));
         // bytes 2-3 of the first conversion's destination are overwritten by
         // the second, so any value serves as its prior contents
         int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], __builtin_bit_cast(int, p4[0]), false);
@@ -819,7 +847,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // O^T += V^T P^T for the V tile in `slot`.
   auto pv = [&](auto slot, const bf16x8* pb) {
-    if constexpr (F8 == 2) {
+    if constexpr (kPV8) {
       const int4 b0 = __builtin_bit_cast(int4, pb[0]), b1 = __builtin_bit_cast(int4, pb[1]);
       const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       const uint32_t vs_w = scale_word(vscl(slot), lane);  // byte db: dim block db, key block hi
@@ -877,7 +905,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // where masked) and the steady loop below, which every wave runs, starts
   // from defined scores and a finite reference.
   qk(IC<0>{}, s);
-  set_tile_scale();
+  set_tile_scale(IC<0>{});
   if (needs_mask(tb)) mask(s, tb);
   update_max(s);
   // Iteration 0 reloads K slot 0: every wave must be done reading K_0 first.
@@ -909,10 +937,11 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       probs(s, pb);
       qk(IC<P ^ 1>{}, s);
       pv(IC<P>{}, pb);
+      set_tile_scale(IC<P ^ 1>{});  // (kI8) tile t+1's, for its max
       update_max(s);
     }
     publish();
-    set_tile_scale();  // (kI8) tile t+1's, for the next iteration
+    if constexpr (kPbf) set_tile_scale(IC<P ^ 1>{});  // (kI8) tile t+1's, for the next iteration
   };
   int t = tb;
   constexpr int kTail = CAUSAL ? 4 : 3;
@@ -931,7 +960,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       if (t + 1 < te) {
         qk(par ^ 1, s);
         pv(par, pb);
-        set_tile_scale();
+        set_tile_scale(par ^ 1);
         if (needs_mask(t + 1)) mask(s, t + 1);
         update_max(s);
       } else {
@@ -943,7 +972,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   if (!active) return;
   const int qi = qrow0 + l32;
-  const float l_tot = F8 == 2 ? lacc[0] : l_run + other_half(l_run, hi);
+  const float l_tot = kPV8 ? lacc[0] : l_run + other_half(l_run, hi);
   if (qi >= it.seg_len) return;
   if (it.part > 0) {
     // one key range of a split item: unnormalised rows, their reference max
@@ -1116,6 +1145,27 @@ hipError_t launch_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_sc
                                                    kv_group, none, stream, fs, sp);
   H3A_I8_CASE(128) H3A_I8_CASE(64)
 #undef H3A_I8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_i8qk_fp8pv(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                     const void* k_scale, const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk,
+                                     int64_t sqs, int64_t sks, int64_t vt_cols, int64_t so, const WorkItem* items,
+                                     int64_t n_items, float scale, int32_t kv_group, bool causal, hipStream_t stream,
+                                     const SplitArgs& sp) {
+  if (n_items <= 0) return hipSuccess;
+  if (kv_group < 1) return hipErrorInvalidValue;
+  const QNormArgs none{};
+  const F8Scales fs{static_cast<const uint8_t*>(q_scale), static_cast<const uint8_t*>(k_scale),
+                    static_cast<const uint8_t*>(vt8s), sqs, sks, int32_t(vt_cols / kVtTile)};
+#define H3A_I8PV_CASE(DD)                                                                                   \
+  if (D == DD)                                                                                              \
+    return causal ? launch<DD, true, false, 0, 4>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale, \
+                                                  kv_group, none, stream, fs, sp)                          \
+                  : launch<DD, false, false, 0, 4>(q8, k8, vt8, o, sq, sk, vt_cols, so, items, n_items, scale,\
+                                                   kv_group, none, stream, fs, sp);
+  H3A_I8PV_CASE(128) H3A_I8PV_CASE(64)
+#undef H3A_I8PV_CASE
   return hipErrorInvalidValue;
 }
 

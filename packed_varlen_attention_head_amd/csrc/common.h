@@ -149,6 +149,14 @@ hipError_t launch_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_sc
                                 int32_t kv_group, bool causal, hipStream_t stream,
                                 const SplitArgs& sp = SplitArgs{});
 
+// INT8 scores (as launch_attn_fwd_i8qk) with FP8 PV on the transposed E4M3
+// V layout (as launch_attn_fwd_fp8).
+hipError_t launch_attn_fwd_i8qk_fp8pv(const void* q8, const void* k8, const void* vt8, const void* q_scale,
+                                     const void* k_scale, const void* vt8s, void* o, int32_t D, int64_t sq, int64_t sk,
+                                     int64_t sqs, int64_t sks, int64_t vt_cols, int64_t so, const WorkItem* items,
+                                     int64_t n_items, float scale, int32_t kv_group, bool causal, hipStream_t stream,
+                                     const SplitArgs& sp);
+
 // bf16 [S, H, D] rows (token stride sx elements) -> INT8 codes (token stride
 // sy bytes) with one fp32 scale per token and head (ys [H][S]); and, per
 // segment of cu (host array, nseg + 1 entries), with one fp32 scale per block

@@ -509,3 +509,25 @@ def test_set_split_policy():
     assert h3a.lib().h3a_set_split_policy(-1) == h3a.H3A_EINVAL
     for p in (h3a.H3A_SPLIT_NEVER, h3a.H3A_SPLIT_ALWAYS, h3a.H3A_SPLIT_AUTO):
         assert h3a.lib().h3a_set_split_policy(p) == h3a.H3A_OK
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(cols=448), h3a.H3A_ESHAPE, "vt_cols = 448"),
+    (dict(vs=None), h3a.H3A_EINVAL, "vt_scale is NULL"),
+    (dict(qs=P + (4 << 24) + 2), h3a.H3A_EUNSUPPORTED, "q_scale is not 4-byte aligned"),
+    (dict(ks=None), h3a.H3A_EINVAL, "k_scale is NULL"),
+    (dict(vs=P + (3 << 24) + 256), h3a.H3A_EINVAL, "o overlaps a scale array"),
+    (dict(ks=P + (3 << 24) + 64), h3a.H3A_EINVAL, "o overlaps a scale array"),
+    (dict(vt=None), h3a.H3A_EINVAL, "vt8 is NULL"),
+    (dict(vt=P + (2 << 24) + 8), h3a.H3A_EUNSUPPORTED, "vt8 is not 16-byte aligned"),
+    (dict(Hkv=3), h3a.H3A_ESHAPE, "does not divide"),
+])
+def test_varlen_attn_fwd_i8qk_fp8pv_rejects(kw, status, word):
+    Hq, Hkv, D = 8, kw.get("Hkv", 2), 128
+    c, cp = i32((0, 100, 300))  # 2 + 4 key blocks, 384 padded columns
+    st = h3a.lib().h3a_varlen_attn_fwd_i8qk_fp8pv(P, P + (1 << 24), kw.get("vt", P + (2 << 24)),
+                                                  kw.get("qs", P + (4 << 24)), kw.get("ks", P + (5 << 24)),
+                                                  kw.get("vs", P + (6 << 24)), P + (3 << 24), 300, Hq, Hkv, D, Hq * D,
+                                                  Hkv * D, kw.get("cols", 384), Hq * D, cp, 2, 0.088, 0, None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()

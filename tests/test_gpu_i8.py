@@ -19,6 +19,8 @@ import pytest
 import oracle
 from synth import configs, rng
 from tests.gpu_util import TOL_BF16_MEANREL, compare, log, require_gpu, sample_rows, to_device, to_f64
+from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, weight_rounding_bound
+from tests.test_gpu_fp8 import check as check_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -295,3 +297,140 @@ def test_i8qk_chain(name):
     log(f"  mean-rel vs exact attention: {got:.3e} (oracle's INT8 rounding alone: {own:.3e})")
     assert got <= own + TOL_BF16_MEANREL, (got, own)
     assert own < 0.02, own  # per-token / per-block INT8: several times below E4M3 scores
+
+
+# ---------------------------------------------------------------------------
+# INT8 scores with the PV product in FP8 (E4M3 weights, transposed E4M3 V)
+
+
+def gpu_i8qk_fp8pv(qb, kb, vb, cu, scale, causal=False):
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    return h3a().varlen_attn_fwd_i8qk_fp8pv(h3a().quantize_i8_rows(q), h3a().quantize_i8_keys(k, cu),
+                                           h3a().prepare_vt_e4m3(v, cu), cu, scale, causal=causal)
+
+
+def i8_mx_operands(qb, kb, vb, cu):
+    """The oracle's INT8-rounded q (per token), k (per 64-key block) and E4M3-rounded v (per
+    32-key block of each segment)."""
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    return oracle.i8_round_q(qf), oracle.i8_round_k(kf, cu), oracle.mx_round_keys(vf, cu)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2)])
+def test_i8qk_fp8pv_vs_oracle(D, Hq, Hkv, causal):
+    """Against attention on the oracle's rounded operands (varlen_attention_i8qk_mxv), within
+    the per-element bound of the weights' E4M3 rounding."""
+    cu, qb, kb, vb = _inputs(900 + D + Hq + (1 if causal else 0), EDGE_LENS, Hq, Hkv, D)
+    log(f"[i8qk fp8pv] D={D} Hq={Hq} Hkv={Hkv} causal={causal} S={int(cu[-1])}")
+    o = to_f64(gpu_i8qk_fp8pv(qb, kb, vb, cu, 1.0 / np.sqrt(D), causal))
+    bound, ref = weight_rounding_bound(*i8_mx_operands(qb, kb, vb, cu), cu, 1.0 / np.sqrt(D), causal)
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    assert np.allclose(ref, oracle.varlen_attention_i8qk_mxv(qf, kf, vf, cu, 1.0 / np.sqrt(D), causal),
+                       rtol=0, atol=1e-12)
+    check_bound(o, ref, "o vs INT8 + E4M3 oracle", bound, TOL_FP8PV_MEANREL)
+
+
+@pytest.mark.parametrize("vmag", [1e-3, 1e3])
+def test_i8qk_fp8pv_magnitudes_far_from_one(vmag):
+    """v at 1e-3 and 1e3, q at 1e-3 and k at 1e3: the scales keep every operand's relative
+    precision, so the outputs divided by vmag meet the magnitude-one bounds."""
+    cu = np.concatenate([[0], np.cumsum([300, 129, 64, 1, 700])]).astype(np.int64)
+    S, Hq, Hkv, D = int(cu[-1]), 4, 2, 128
+    seed = 950 + (1 if vmag > 1 else 0)
+    log(f"[i8qk fp8pv magnitudes] v*{vmag:g} q*1e-3 k*1e3 S={S}")
+
+    def scaled(tag, shape, m):
+        return rng.f32_to_bf16_bits(rng.bf16_bits_to_f32(rng.normal_tensor(seed, tag, shape, "bf16")) * np.float32(m))
+
+    qb, kb = scaled(rng.TAG_Q, (S, Hq, D), 1e-3), scaled(rng.TAG_K, (S, Hkv, D), 1e3)
+    vb = scaled(rng.TAG_V, (S, Hkv, D), vmag)
+    o = to_f64(gpu_i8qk_fp8pv(qb, kb, vb, cu, 1.0 / np.sqrt(D)))
+    bound, ref = weight_rounding_bound(*i8_mx_operands(qb, kb, vb, cu), cu, 1.0 / np.sqrt(D))
+    check_bound(o / vmag, ref / vmag, "o / vmag vs INT8 + E4M3 oracle", bound / vmag, TOL_FP8PV_MEANREL)
+
+
+@pytest.mark.parametrize("pv8", [False, True])
+def test_i8qk_zero_rows_and_key_blocks(pv8):
+    """All-zero query rows and an all-zero last (partial) key block have scale 0: their
+    scores are 0, and the masked keys of that partial tile stay excluded (no 0 * -inf)."""
+    lens = [100, 70, 129]
+    cu, qb, kb, vb = _inputs(1401 + pv8, lens, 2, 2, 128)
+    qb[100 + 5:100 + 10, 1] = 0      # segment 1, rows 5..9, head 1
+    qb[200 + 3, 0] = 0               # segment 2, row 3, head 0
+    kb[64:100, 0] = 0                # segment 0's last block (keys 64..99; tile 1 is partial), head 0
+    kb[100 + 64:170, 1] = 0          # segment 1's last block (keys 64..69), head 1
+    log(f"[i8 zero scales] pv8={pv8}")
+    scale = 0.088
+    if not pv8:
+        o = to_f64(gpu_i8qk(qb, kb, vb, cu, scale))
+        qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+        ref = oracle.varlen_attention_i8qk(qf, kf, vf, cu, scale)
+        assert np.all(np.isfinite(o))
+        compare(o, ref, "bf16", "o vs INT8 oracle, zero rows and blocks")
+        return
+    o = to_f64(gpu_i8qk_fp8pv(qb, kb, vb, cu, scale))
+    assert np.all(np.isfinite(o))
+    bound, ref = weight_rounding_bound(*i8_mx_operands(qb, kb, vb, cu), cu, scale)
+    check_bound(o, ref, "o vs INT8 + E4M3 oracle, zero rows and blocks", bound, TOL_FP8PV_MEANREL)
+
+
+def test_i8qk_fp8pv_split_plans_nan_and_determinism():
+    """Forced key-range splits against the unsplit result (at the weights' bound: a range
+    item's reference max differs), bitwise equal across runs; a NaN query element makes its
+    row NaN and a NaN key element its segment's rows of that head, nothing else."""
+    import torch
+
+    lens = [3000, 700, 257]
+    cu, qb, kb, vb = _inputs(1501, lens, 4, 2, 128)
+    log("[i8qk fp8pv split / nan]")
+    bound, ref = weight_rounding_bound(*i8_mx_operands(qb, kb, vb, cu), cu, 0.088)
+    try:
+        h3a().set_split_policy(h3a().H3A_SPLIT_ALWAYS)
+        a = gpu_i8qk_fp8pv(qb, kb, vb, cu, 0.088)
+        b = gpu_i8qk_fp8pv(qb, kb, vb, cu, 0.088)
+    finally:
+        h3a().set_split_policy(h3a().H3A_SPLIT_AUTO)
+    assert torch.equal(a, b)
+    check_bound(to_f64(a), ref, "split o vs INT8 + E4M3 oracle", bound, TOL_FP8PV_MEANREL)
+    nan = _f32_bits_to_bf16(np.array([np.nan], np.float32))[0]
+    q2, k2 = qb.copy(), kb.copy()
+    q2[10, 1, 7] = nan
+    k2[3000 + 70, 0, 3] = nan  # segment 1, kv head 0 (query heads 0, 1)
+    o = gpu_i8qk_fp8pv(q2, k2, vb, cu, 0.088)
+    bad = torch.zeros(o.shape, dtype=torch.bool, device=o.device)
+    bad[10, 1] = True
+    bad[3000:3700, 0:2] = True
+    assert torch.isnan(o[bad]).all() and not torch.isnan(o[~bad]).any()
+
+
+@pytest.mark.parametrize("name", ["two_seg_bf16", "h3_s20423_bf16"])
+def test_i8qk_fp8pv_chain(name):
+    """table -> norm + rotary writing INT8 q -> INT8 k codes, E4M3 V^T -> attention: against
+    the oracle's rounded operands within the weights' bound, and against exact attention
+    within the oracle's own rounding error plus 3e-2 for the E4M3 weights."""
+    import torch
+
+    w = configs.ALL[name]
+    T = configs.make_tensors(w)
+    log(f"[i8qk fp8pv chain] {name} S={w.tokens}")
+    q, k, v = (to_device(x, w.dtype) for x in (T.q, T.k, T.v))
+    gq, gk = torch.from_numpy(T.gamma_q).cuda(), torch.from_numpy(T.gamma_k).cuda()
+    tab = torch.empty((2, w.tokens, w.rot_dim // 2), dtype=torch.float32, device="cuda")
+    cu = h3a().build_rope_table(w.segments, w.rot_dims, w.base, tab)
+    q8, kn_d = h3a().qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim)
+    o = to_f64(h3a().varlen_attn_fwd_i8qk_fp8pv(q8, h3a().quantize_i8_keys(kn_d, cu), h3a().prepare_vt_e4m3(v, cu),
+                                                cu, w.scale))
+    qf, kf, vf = (rng.as_f64(x, w.dtype) for x in (T.q, T.k, T.v))
+    ocu, cos, sin = oracle.rope_table(w.segments, w.rot_dims, w.base)
+    qn, kn = oracle.qk_rmsnorm_rope(qf, kf, T.gamma_q, T.gamma_k, w.eps, cos, sin, w.rot_dim)
+    rows = sample_rows(ocu, every=97)
+    qi, ki = oracle.i8_round_q(oracle.bf16_round(qn)), oracle.i8_round_k(oracle.bf16_round(kn), ocu)
+    bound, ref8 = weight_rounding_bound(qi, ki, oracle.mx_round_keys(vf, ocu), ocu, w.scale, rows=rows)
+    check_bound(o[rows], ref8, f"o vs INT8 + E4M3 oracle ({len(rows)} rows)", bound, TOL_FP8PV_MEANREL)
+    exact = oracle.varlen_attention_rows(qn, kn, vf, ocu, w.scale, rows)
+    own = float(np.abs(ref8 - exact).sum() / np.abs(exact).sum())
+    got = float(np.abs(o[rows] - exact).sum() / np.abs(exact).sum())
+    log(f"  mean-rel vs exact attention: {got:.3e} (oracle's INT8 + E4M3 operand rounding alone: {own:.3e})")
+    assert got <= own + 3e-2, (got, own)

@@ -41,8 +41,39 @@
 namespace h3a {
 namespace {
 
-// max of two magnitudes that keeps a NaN (fmaxf would drop it)
-__device__ __forceinline__ float nan_max(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
+// The larger magnitude of a and b, a NaN kept (fmaxf would drop it):
+// magnitudes compare as their bit patterns with the sign cleared, every NaN
+// above +inf, with no branch.
+__device__ __forceinline__ float nan_max(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a) & 0x7fffffffu, __float_as_uint(b) & 0x7fffffffu));
+}
+
+// INT8 codes rint(b[e] * inv) of eight values, byte e of the pair = code e.
+// With |b| <= amax and inv = 127 / amax correctly rounded, every product is
+// at most 127 * (1 + 2^-24)^2 < 127.5 in magnitude: no clamp.  Adding
+// 1.5 * 2^23 rounds the product to the nearest integer (ties to even) in the
+// low mantissa bits, whose low byte is the code in two's complement; three
+// byte permutes gather four codes.  `ok` false (a NaN or infinite maximum,
+// or 127 / amax overflowing): every product is NaN, infinite or 0, so every
+// code is 0.
+__device__ __forceinline__ uint2 i8_pack8(const float* b, float inv, bool ok) {
+  uint32_t t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // the product rounded on its own (kept out of an FMA with the add)
+    float r = b[e] * inv;
+    asm volatile("" : "+v"(r));
+    t[e] = __float_as_uint(r + 12582912.0f);
+  }
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[4 * h + 1], t[4 * h], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[4 * h + 3], t[4 * h + 2], 0x0c0c0400u);
+    w[h] = ok ? __builtin_amdgcn_perm(hi, lo, 0x05040100u) : 0u;
+  }
+  return make_uint2(w[0], w[1]);
+}
 
 template <typename T>
 struct Elem;
@@ -122,15 +153,8 @@ struct Elem<Bf16Tag> {
 #pragma unroll
     for (int off = LPV / 2; off >= 1; off >>= 1) amax = nan_max(amax, __shfl_xor(amax, off, 64));
     const float inv = amax == 0.f ? 0.f : __fdiv_rn(127.0f, amax);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float r = __builtin_rintf(b[e] * inv);
-      const int c = __builtin_isfinite(r) ? min(127, max(-127, int(r))) : 0;
-      w[e / 4] |= (uint32_t(c) & 0xffu) << (8 * (e % 4));
-    }
     *scale = __fdiv_rn(amax, 127.0f);
-    return make_uint2(w[0], w[1]);
+    return i8_pack8(b, inv, __builtin_isfinite(amax) && __builtin_isfinite(inv));
   }
 };
 

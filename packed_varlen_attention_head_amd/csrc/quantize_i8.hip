@@ -23,24 +23,42 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// max of two magnitudes that keeps a NaN (fmaxf would drop it)
-__device__ __forceinline__ float nan_max(float a, float b) { return a != a ? a : (b != b ? b : fmaxf(a, b)); }
+// The larger magnitude of a and b, a NaN kept (fmaxf would drop it):
+// magnitudes compare as their bit patterns with the sign cleared, every NaN
+// above +inf, with no branch.
+__device__ __forceinline__ float nan_max(float a, float b) {
+  return __uint_as_float(max(__float_as_uint(a) & 0x7fffffffu, __float_as_uint(b) & 0x7fffffffu));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Eight codes of x * inv, as two dwords (byte i = element i).
-__device__ __forceinline__ uint2 i8_codes(const float (&f)[8], float inv) {
-  uint32_t out[2] = {0u, 0u};
+// Eight codes rint(f[e] * inv), as two dwords (byte e = element e).  With
+// |f| <= amax and inv = 127 / amax correctly rounded, every product is at
+// most 127 * (1 + 2^-24)^2 < 127.5 in magnitude: no clamp.  Adding
+// 1.5 * 2^23 rounds the product to the nearest integer (ties to even) in the
+// low mantissa bits, whose low byte is the code in two's complement; three
+// byte permutes gather four codes.  When the block maximum is NaN or
+// infinite, or 127 / amax overflows, every product is NaN, infinite or 0,
+// and every code is 0.
+__device__ __forceinline__ uint2 i8_codes(const float (&f)[8], float inv, float amax) {
+  uint32_t t[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float r = __builtin_rintf(f[e] * inv);
-    // a non-finite product (a NaN or infinite block maximum, or 127 / amax
-    // overflowing for a block of tiny values) gives code 0
-    const int c = __builtin_isfinite(r) ? min(127, max(-127, int(r))) : 0;
-    out[e / 4] |= (uint32_t(c) & 0xffu) << (8 * (e % 4));
+    // the product rounded on its own (kept out of an FMA with the add)
+    float r = f[e] * inv;
+    asm volatile("" : "+v"(r));
+    t[e] = __float_as_uint(r + 12582912.0f);
   }
-  return make_uint2(out[0], out[1]);
+  const bool ok = __builtin_isfinite(amax) && __builtin_isfinite(inv);
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[4 * h + 1], t[4 * h], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[4 * h + 3], t[4 * h + 2], 0x0c0c0400u);
+    w[h] = ok ? __builtin_amdgcn_perm(hi, lo, 0x05040100u) : 0u;
+  }
+  return make_uint2(w[0], w[1]);
 }
 
 __device__ __forceinline__ float inv_of(float amax) { return amax == 0.f ? 0.f : __fdiv_rn(127.0f, amax); }
@@ -71,7 +89,7 @@ quantize_i8_rows_kernel(const uint16_t* __restrict__ x, int8_t* __restrict__ y, 
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) amax = nan_max(amax, __shfl_xor(amax, m, 64));
   if (!in) return;
-  *reinterpret_cast<uint2*>(y + token * sy + h * D + c * 8) = i8_codes(f, inv_of(amax));
+  *reinterpret_cast<uint2*>(y + token * sy + h * D + c * 8) = i8_codes(f, inv_of(amax), amax);
   if (c == 0) ys[int64_t(h) * S + token] = __fdiv_rn(amax, 127.0f);
 }
 
@@ -128,7 +146,8 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int key = key0 + p * KPP + kr;
-    if (key < a.len[s]) *reinterpret_cast<uint2*>(y + int64_t(a.start[s] + key) * sy + h * D + c * 8) = i8_codes(f[p], inv);
+    if (key < a.len[s])
+      *reinterpret_cast<uint2*>(y + int64_t(a.start[s] + key) * sy + h * D + c * 8) = i8_codes(f[p], inv, amax);
   }
   if (threadIdx.x == 0) ys[int64_t(h) * n_blocks + a.block0 + tau] = __fdiv_rn(amax, 127.0f);
 }

@@ -46,7 +46,7 @@ ATTN_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "attn_
 NORM_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "qk_norm_rope.hip")
 TABLE_SRC = os.path.join(ROOT, "packed_varlen_attention_head_amd", "csrc", "rope_table.hip")
 ATTN_KERNEL = "attn_fwd_bf16_kernel<128>"
-NORM_KERNEL = "qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, false>"
+NORM_KERNEL = "qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, 0, 0>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_h3_s20423_traffic.json")
 
 
@@ -678,7 +678,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": norm_bytes / norm_s / 1e9 / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(NORM_KERNEL, NORM_SRC) if (w.name == HEADLINE and not (fp8 or fused)) else None,
+            "traffic": measured_traffic(NORM_KERNEL, NORM_SRC) if (w.name == HEADLINE and not (fp8 or fused or i8)) else None,
             "kernel": "qk_norm_rope_kernel<bf16, 128>",
             "algorithmic_bytes_per_launch": norm_bytes,
             # a plain device-to-device copy moving the same bytes (half read,

@@ -16,7 +16,7 @@ import bench
 ATTN = ("void h3a::(anonymous namespace)::attn_fwd_bf16_kernel<128, false, false, 0, 0>(unsigned short const*, "
         "unsigned short const*, unsigned short const*, unsigned short*, long, long, long, long, h3a::WorkItem const*, "
         "float, int, h3a::QNormArgs)")
-NORM = ("void h3a::(anonymous namespace)::qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, false>"
+NORM = ("void h3a::(anonymous namespace)::qk_norm_rope_kernel<h3a::(anonymous namespace)::Bf16Tag, 128, 0, 0>"
         "(char const*, char const*, char*, char*, long, long, long, long, int, int, int, float const*, "
         "float const*, float, float const*, int)")
 TABLE = "h3a::(anonymous namespace)::rope_table_kernel(h3a::(anonymous namespace)::RopeArgs, float*, int, int)"
@@ -29,6 +29,8 @@ COPY = "__amd_rocclr_copyBuffer"
     (ATTN.replace("<128, false, false, 0, 0>", "<128, false, false, 0, 2>"), "attn_fwd_bf16_kernel<128, fp8>"),
     (ATTN.replace("<128, false, false, 0, 0>", "<128, false, false, 0, 1>"), "attn_fwd_bf16_kernel<128, fp8qk>"),
     (ATTN.replace("<128, false, false, 0, 0>", "<128, false, true, 3, 0>"), "attn_fwd_bf16_kernel<128, qnorm r96>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, false, false, 0, 3>"), "attn_fwd_bf16_kernel<128, i8qk>"),
+    (ATTN.replace("<128, false, false, 0, 0>", "<128, true, false, 0, 4>"), "attn_fwd_bf16_kernel<128, causal, i8qk fp8pv>"),
     (NORM, bench.NORM_KERNEL),
     (TABLE, "rope_table_kernel"),
     (COPY, COPY),

@@ -24,15 +24,15 @@ def _gpu():
     h3a.release_caches()
 
 
-@pytest.mark.parametrize("fp8", [False, True])
-def test_capture_and_replay(fp8):
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "i8", "i8pv"])
+def test_capture_and_replay(mode):
     import torch
 
     import packed_varlen_attention_head_amd as h3a
 
     w = configs.BF16["two_seg_bf16"]
     S, H, D = w.tokens, w.heads, w.head_dim
-    log(f"[graph] {w.name} fp8={fp8}")
+    log(f"[graph] {w.name} {mode}")
     tab = torch.empty((2, S, w.rot_dim // 2), dtype=torch.float32, device="cuda")
     cu = h3a.build_rope_table(w.segments, w.rot_dims, w.base, tab)
     gq = torch.from_numpy((1.0 + 0.1 * rng.normal(71, rng.TAG_GAMMA_Q, D)).astype(np.float32)).cuda()
@@ -47,10 +47,22 @@ def test_capture_and_replay(fp8):
     k8 = tuple(torch.empty_like(x) for x in q8)
     vt8 = (torch.empty((H, D, cols), dtype=torch.uint8, device="cuda"),
            torch.empty((H, cols // 64, 2, 32, D // 32), dtype=torch.uint8, device="cuda"))
+    nb = h3a.i8_key_blocks(cu)
+    qi8 = (torch.empty(q.shape, dtype=torch.int8, device="cuda"), torch.empty((H, S), dtype=torch.float32, device="cuda"))
+    ki8 = (torch.empty(k.shape, dtype=torch.int8, device="cuda"), torch.empty((H, nb), dtype=torch.float32, device="cuda"))
     scale = w.scale
 
     def step(stream=None):
-        if fp8:
+        if mode in ("i8", "i8pv"):
+            h3a.qk_rmsnorm_rope_i8q(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=qi8[0], q_scale=qi8[1], k_out=ko,
+                                    stream=stream)
+            h3a.quantize_i8_keys(ko, cu, out=ki8[0], scale_out=ki8[1], stream=stream)
+            if mode == "i8":
+                h3a.varlen_attn_fwd_i8qk(qi8, ki8, v, cu, scale, out=o, stream=stream)
+            else:
+                h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
+                h3a.varlen_attn_fwd_i8qk_fp8pv(qi8, ki8, vt8, cu, scale, out=o, stream=stream)
+        elif mode == "fp8":
             h3a.qk_rmsnorm_rope_e4m3(q, k, gq, gk, w.eps, tab, w.rot_dim, q8=q8[0], k8=k8[0], q_scale=q8[1],
                                      k_scale=k8[1], stream=stream)
             h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)

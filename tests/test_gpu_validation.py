@@ -127,6 +127,41 @@ def test_fp8_operands():
     assert np.isfinite(o.float().cpu().numpy()).all()
 
 
+def test_int8_operands():
+    import torch
+
+    h3a, q, k, v, tab, cu, gam = setup()
+    S = q.shape[0]
+    nb = h3a.i8_key_blocks(cu)
+    assert nb == sum(-(-L // 64) for L in LENS)
+    qi8, ki8 = h3a.quantize_i8_rows(q), h3a.quantize_i8_keys(k, cu)
+    out = torch.zeros((S, H, D), dtype=torch.bfloat16, device="cuda")
+    refused(lambda: h3a.quantize_i8_rows(q.float()), h3a.H3A_EDTYPE)
+    refused(lambda: h3a.quantize_i8_rows(q, scale_out=torch.zeros((H, S - 1), device="cuda")), h3a.H3A_ESHAPE)
+    refused(lambda: h3a.quantize_i8_keys(k, cu, scale_out=torch.zeros((H, nb + 1), device="cuda")), h3a.H3A_ESHAPE)
+    u8 = torch.zeros((S, H, D), dtype=torch.uint8, device="cuda")
+    refused(lambda: h3a.quantize_i8_rows(q, out=u8), h3a.H3A_ESHAPE, u8)
+    # E4M3 codes are not INT8 codes, and scale arrays must be fp32 of the exact shape
+    q8, k8 = h3a.quantize_e4m3(q), h3a.quantize_e4m3(k)
+    refused(lambda: h3a.varlen_attn_fwd_i8qk(q8, ki8, v, cu, 0.1, out=out), h3a.H3A_EDTYPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_i8qk(qi8, (ki8[0], ki8[1][:, :-1].contiguous()), v, cu, 0.1, out=out),
+            h3a.H3A_ESHAPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_i8qk((qi8[0], qi8[1].half()), ki8, v, cu, 0.1, out=out), h3a.H3A_EDTYPE, out)
+    vt8 = h3a.prepare_vt_e4m3(v, cu)
+    refused(lambda: h3a.varlen_attn_fwd_i8qk_fp8pv(qi8, ki8, (vt8[0][:, :, :-64].contiguous(), vt8[1]), cu, 0.1,
+                                                   out=out), h3a.H3A_ESHAPE, out)
+    refused(lambda: h3a.varlen_attn_fwd_i8qk_fp8pv(q8, k8, vt8, cu, 0.1, out=out), h3a.H3A_EDTYPE, out)
+    qi8o = torch.zeros((S - 1, H, D), dtype=torch.int8, device="cuda")
+    refused(lambda: h3a.qk_rmsnorm_rope_i8q(q, k, gam, gam, 1e-6, tab, R, q8=qi8o), h3a.H3A_ESHAPE, qi8o)
+    refused(lambda: h3a.qk_rmsnorm_rope_i8q(q.float(), k.float(), gam, gam, 1e-6, tab, R), h3a.H3A_EDTYPE)
+    o = h3a.varlen_attn_fwd_i8qk(qi8, ki8, v, cu, 0.1, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    o = h3a.varlen_attn_fwd_i8qk_fp8pv(qi8, ki8, vt8, cu, 0.1, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+
+
 def test_all_empty_packing_is_a_no_op():
     """Every call accepts a packing whose segments are all empty (S = 0, zero-size
     tensors whose data pointers may be null) and returns empty results."""
@@ -149,4 +184,10 @@ def test_all_empty_packing_is_a_no_op():
     vt8 = h3a.prepare_vt_e4m3(v, cu)
     assert h3a.varlen_attn_fwd_fp8qk(q8, k8, v, cu, 0.1).shape == (0, H, D)
     assert h3a.varlen_attn_fwd_fp8(q8, k8, vt8, cu, 0.1).shape == (0, H, D)
+    assert h3a.i8_key_blocks(cu) == 0
+    qi8, kn = h3a.qk_rmsnorm_rope_i8q(q, k, gam, gam, 1e-6, tab, R)
+    ki8 = h3a.quantize_i8_keys(kn, cu)
+    assert h3a.quantize_i8_rows(q)[0].shape == (0, H, D)
+    assert h3a.varlen_attn_fwd_i8qk(qi8, ki8, v, cu, 0.1).shape == (0, H, D)
+    assert h3a.varlen_attn_fwd_i8qk_fp8pv(qi8, ki8, vt8, cu, 0.1).shape == (0, H, D)
     torch.cuda.synchronize()

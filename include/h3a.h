@@ -10,7 +10,9 @@
  * table modes (fp64 linspace grid, the ViT3D's length-normalised ids,
  * interleaved M-RoPE), grouped K/V heads and a causal mask (the encoder text
  * tower), the Q norm + rotary folded into the attention, and low-precision
- * attention on FP8 E4M3 operands.
+ * attention: FP8 E4M3 operands with per-block power-of-two scales, INT8
+ * scores with per-token q and per-64-key-block k scales (with a bf16 or FP8
+ * PV product), and norm + rotary passes writing the quantised operands.
  *
  * Sources (the pages this library was built from):
  *   - vllm.cpp PR #26 "feat(minimax-h3): port the MiniMax-H3 omni-modal

@@ -434,3 +434,19 @@ def test_i8qk_fp8pv_chain(name):
     got = float(np.abs(o[rows] - exact).sum() / np.abs(exact).sum())
     log(f"  mean-rel vs exact attention: {got:.3e} (oracle's INT8 + E4M3 operand rounding alone: {own:.3e})")
     assert got <= own + 3e-2, (got, own)
+
+
+def test_many_segments_key_blocks_and_attention():
+    """150 ragged segments (three launches of the key-block quantiser, 64 segments each),
+    one of them empty, grouped K/V: codes and scales bit-exact, attention against the
+    oracle at the bf16 tolerance."""
+    lens = [int(x) for x in 1 + (rng.uniform(79, rng.TAG_LENS, 150) * 300).astype(np.int64)]
+    lens[7] = 0
+    cu, qb, kb, vb = _inputs(80, lens, 4, 2, 64)
+    log(f"[i8 many segments] S={int(cu[-1])} nseg={len(lens)} blocks={h3a().i8_key_blocks(cu)}")
+    k8 = h3a().quantize_i8_keys(to_device(kb, "bf16"), cu)
+    wc, ws = oracle.i8_quantize_key_blocks(rng.as_f64(kb, "bf16"), cu)
+    _codes_and_scales_equal(k8[0], k8[1], wc, ws, "k blocks, 150 segments")
+    o = to_f64(gpu_i8qk(qb, kb, vb, cu, 0.125))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    compare(o, oracle.varlen_attention_i8qk(qf, kf, vf, cu, 0.125), "bf16", "o vs INT8 oracle, 150 segments")

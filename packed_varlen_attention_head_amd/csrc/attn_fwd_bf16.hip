@@ -973,8 +973,8 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (!active) return;
   const int qi = qrow0 + l32;
   const float l_tot = kPV8 ? lacc[0] : l_run + other_half(l_run, hi);
-  if (qi >= it.seg_len) return;
   if (it.part > 0) {
+    if (qi >= it.seg_len) return;
     // one key range of a split item: unnormalised rows, their reference max
     // and row sum, for the merge pass
     const int64_t row = int64_t(it.part - 1) * kBM + wave * 32 + l32;
@@ -988,8 +988,16 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (hi == 0) *reinterpret_cast<float2*>(sp.ml + 2 * row) = make_float2(m_run, l_tot);
     return;
   }
+  // The normalised rows go through LDS so that every global store writes
+  // whole 16-byte pieces of rows (64 / NCH rows per instruction) instead of
+  // 8 bytes in each of 32 rows.  Each wave stages its 32 rows (32 x D bf16)
+  // in one ring slot of its own: every wave has passed the last barrier after
+  // its last operand read and its K/V loads have landed, so the ring is free.
+  // 16-byte chunks are swizzled by row so both phases spread over the banks.
+  constexpr int NCH = D / 8;  // 16-byte chunks per output row
+  static_assert(32 * D * 2 <= kBN * KROWB && 32 * D * 2 <= (kPV8 ? kBN * D : kBN * D * 2), "staging fits a slot");
+  LDS char* stage = (LDS char*)(wave == 0 ? k_slot0 : wave == 1 ? k_slot1 : wave == 2 ? v_slot0 : v_slot1);
   const float inv = 1.0f / l_tot;
-  uint16_t* op = o + int64_t(it.seg_start + qi) * so + head_off + hi * 4;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -997,8 +1005,22 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       uint2 pk;
       pk.x = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
       pk.y = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(op + db * 32 + g * 8) = pk;
+      const int ch = (db * 4 + g) ^ (l32 & (NCH - 1));
+      *(LDS uint2*)(stage + l32 * (D * 2) + ch * 16 + hi * 8) = pk;
     }
+  // the wave's LDS writes complete before its reads (one wave, in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int RPI = 64 / NCH;  // rows per store instruction
+  const int oc = lane % NCH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / NCH;
+    const uint4 v4 = *(const LDS uint4*)(stage + r * (D * 2) + ((oc ^ (r & (NCH - 1))) * 16));
+    if (qrow0 + r < it.seg_len)
+      *reinterpret_cast<uint4*>(o + int64_t(it.seg_start + qrow0 + r) * so + head_off + oc * 8) = v4;
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

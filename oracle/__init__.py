@@ -662,6 +662,64 @@ def varlen_attention_i8qk_mxv(q, k, v, cu, scale: float, causal: bool = False) -
     return varlen_attention_gqa(i8_round_q(q), i8_round_k(k, cu), mx_round_keys(v, cu), cu, scale, causal=causal)
 
 
+# ----------------------------------------------------------------------------
+# 5f. Centred keys for the INT8 scores (SageAttention's K smoothing)
+#
+# SageAttention, among the pages' attention backends (H3 Blackwell Runtime
+# README, request-level attention backends; h3-spark model card, "What this
+# config does"), subtracts the mean key from K before quantising it.  Within
+# one softmax every score then moves by the same q . mean, which the softmax
+# cancels, so attention is unchanged while K's per-channel offsets no longer
+# set the INT8 block scales.  Reading for packed segments: the mean is taken
+# per segment (every key a query sees belongs to its own segment), per head
+# and head dim, over the segment's keys; an empty segment has mean 0.  The
+# quantised value of a key is the fp32 difference x - mean (x the bf16 key,
+# mean given in fp32), quantised as in section 5e.
+# ----------------------------------------------------------------------------
+
+def segment_key_means(k, cu) -> np.ndarray:
+    """[nseg, H, D] fp64: the mean of k over each segment's keys (0 if empty)."""
+    k = np.asarray(k, dtype=np.float64)
+    mu = np.zeros((len(cu) - 1,) + k.shape[1:])
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            mu[s] = k[a:b].mean(axis=0)
+    return mu
+
+
+def i8_center_keys(k, cu, mu32) -> np.ndarray:
+    """[S, H, D] fp32: each key minus its segment's mean (mu32 [nseg, H, D]
+    fp32), the difference rounded once to fp32."""
+    k32 = np.asarray(k, dtype=np.float32)
+    mu32 = np.asarray(mu32, dtype=np.float32)
+    out = np.empty_like(k32)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        out[a:b] = k32[a:b] - mu32[s][None]
+    return out
+
+
+def i8_quantize_key_blocks_centered(k, cu, mu32):
+    """(codes, scales) of the centred keys, blocks as i8_quantize_key_blocks."""
+    return i8_quantize_key_blocks(i8_center_keys(k, cu, mu32), cu)
+
+
+def i8_round_k_centered(k, cu, mu32) -> np.ndarray:
+    """What the centred keys' INT8 codes stand for, fp64 (the mean not added back)."""
+    return i8_dequantize_key_blocks(*i8_quantize_key_blocks_centered(k, cu, mu32), cu)
+
+
+def varlen_attention_i8qk_centered(q, k, v, cu, scale: float, causal: bool = False, mu32=None) -> np.ndarray:
+    """INT8 scores with centred keys: varlen_attention_gqa on what q's codes and
+    the centred keys' codes stand for; mu32 defaults to the segment means
+    rounded to fp32.  Exact attention is unchanged by the centring; only the
+    rounding differs from varlen_attention_i8qk."""
+    if mu32 is None:
+        mu32 = segment_key_means(k, cu).astype(np.float32)
+    return varlen_attention_gqa(i8_round_q(q), i8_round_k_centered(k, cu, mu32), v, cu, scale, causal=causal)
+
+
 def hot_path(q, k, v, gamma_q, gamma_k, segments, rot_dims, base, eps, scale):
     """The whole chain: table, norm + rotary on q and k, then varlen attention."""
     cu, cos, sin = rope_table(segments, rot_dims, base)

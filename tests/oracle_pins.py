@@ -809,6 +809,64 @@ def check_i8_key_blocks_and_attention(O):
     assert np.abs(got - exact).sum() / np.abs(exact).sum() < 0.05
 
 
+def check_i8_centered_keys(O):
+    """Centred keys: segment means against a scalar loop (an empty segment's is 0; a segment
+    alone gives the same means as packed); a hand-derived case (keys 1 and 3 of one dim centre
+    to -1 and 1, codes -127 and 127, scale 1/127); the centred value is the fp32 difference;
+    zero means give the plain codes; any per-segment constant subtracted from k leaves exact
+    attention unchanged; with per-channel key offsets of 30 sigma the centred INT8 scores are
+    far closer to exact attention than the plain ones."""
+    r = _rng(44)
+    lens = [70, 0, 5, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S = int(cu[-1])
+    k = r.normal(size=(S, 2, 16)) + 3.0 * r.normal(size=(1, 2, 16))
+    mu = O.segment_key_means(k, cu)
+    assert mu.shape == (4, 2, 16) and np.all(mu[1] == 0)
+    for si, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        a, b = int(a), int(b)
+        if b == a:
+            continue
+        for h in range(2):
+            for d in range(16):
+                tot = 0.0
+                for i in range(a, b):
+                    tot += float(k[i, h, d])
+                assert abs(float(mu[si, h, d]) - tot / (b - a)) <= 1e-12 * max(1.0, abs(tot))
+        assert np.array_equal(O.segment_key_means(k[a:b], np.array([0, b - a]))[0], mu[si])
+    # hand-derived: one segment of two keys, one head, one dim
+    kk = np.array([[[1.0]], [[3.0]]])
+    c2 = np.array([0, 2])
+    mu2 = O.segment_key_means(kk, c2).astype(np.float32)
+    assert float(mu2[0, 0, 0]) == 2.0
+    codes, sc = O.i8_quantize_key_blocks_centered(kk, c2, mu2)
+    assert codes[:, 0, 0].tolist() == [-127, 127] and float(sc[0, 0]) == float(np.float32(1) / np.float32(127))
+    # the centred value is the fp32 difference (here 1 - 2^-30 rounds to 1 in fp32)
+    kf = np.array([[[1.0]]])
+    tiny = np.array([[[2.0 ** -30]]], dtype=np.float32)
+    assert float(O.i8_center_keys(kf, np.array([0, 1]), tiny)[0, 0, 0]) == 1.0
+    z = np.zeros((4, 2, 16), dtype=np.float32)
+    k32 = k.astype(np.float32).astype(np.float64)
+    pc, ps = O.i8_quantize_key_blocks(k32, cu)
+    zc, zs = O.i8_quantize_key_blocks_centered(k32, cu, z)
+    assert np.array_equal(pc, zc) and np.array_equal(ps, zs)
+    # exact attention does not see a per-segment constant subtracted from k
+    q, v = r.normal(size=(S, 4, 16)), r.normal(size=(S, 2, 16))
+    shift = np.concatenate([np.repeat(r.normal(size=(1, 2, 16)) * 5, L, axis=0) for L in lens])
+    for causal in (False, True):
+        assert np.allclose(O.varlen_attention_gqa(q, k - shift, v, cu, 0.3, causal),
+                           O.varlen_attention_gqa(q, k, v, cu, 0.3, causal), rtol=0, atol=1e-12)
+    # accuracy with per-channel offsets
+    ko = r.normal(size=(S, 2, 16)) + 30.0 * r.normal(size=(1, 2, 16))
+    exact = O.varlen_attention_gqa(q, ko, v, cu, 0.3)
+    plain = O.varlen_attention_i8qk(q, ko, v, cu, 0.3)
+    cent = O.varlen_attention_i8qk_centered(q, ko, v, cu, 0.3)
+    err = lambda x: float(np.abs(x - exact).sum() / np.abs(exact).sum())  # noqa: E731
+    assert err(cent) < 0.02 and err(cent) < 0.2 * err(plain), (err(cent), err(plain))
+    m32 = O.segment_key_means(ko, cu).astype(np.float32)
+    assert np.array_equal(cent, O.varlen_attention_i8qk_centered(q, ko, v, cu, 0.3, mu32=m32))
+
+
 def check_i8qk_mxv_attention(O):
     """INT8 scores with E4M3 V: operands already on their grids (q, k integers with a 127 in
     every block, v on every segment's 32-key E4M3 block grid) pass through to the exact
@@ -942,7 +1000,7 @@ ALL_CHECKS = [
     check_mx_quantize,
     check_mx_keys_and_attention,
     check_i8_quantize,
-    check_i8_key_blocks_and_attention, check_i8qk_mxv_attention,
+    check_i8_key_blocks_and_attention, check_i8qk_mxv_attention, check_i8_centered_keys,
     check_chain_shift_invariance,
     check_chain_composition,
 ]

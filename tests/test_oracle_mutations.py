@@ -340,6 +340,16 @@ MUTANTS = {
                              oracle.varlen_attention_i8qk(q, k, v, cu, scale, causal)),
     "i8qk_mxv_v_per_dim_block": dict(varlen_attention_i8qk_mxv=lambda q, k, v, cu, scale, causal=False:
                                      oracle.varlen_attention_i8qk(q, k, oracle.mx_round(v), cu, scale, causal)),
+    "i8_means_global": dict(segment_key_means=lambda k, cu: np.repeat(
+        np.asarray(k, dtype=np.float64).mean(axis=0)[None], len(cu) - 1, axis=0)),
+    "i8_means_over_heads": dict(segment_key_means=lambda k, cu: np.repeat(
+        oracle.segment_key_means(k, cu).mean(axis=1, keepdims=True), np.asarray(k).shape[1], axis=1)),
+    "i8_center_in_fp64": dict(i8_center_keys=lambda k, cu, mu32: np.asarray(k, dtype=np.float64) - np.concatenate(
+        [np.repeat(np.asarray(mu32, dtype=np.float64)[i][None], int(cu[i + 1] - cu[i]), axis=0)
+         for i in range(len(cu) - 1)])),
+    "i8_centering_skipped": dict(i8_quantize_key_blocks_centered=lambda k, cu, mu32: oracle.i8_quantize_key_blocks(k, cu)),
+    "i8qk_centered_uses_plain_keys": dict(varlen_attention_i8qk_centered=lambda q, k, v, cu, scale, causal=False, mu32=None:
+                                          oracle.varlen_attention_i8qk(q, k, v, cu, scale, causal)),
     "i8qk_mxv_scores_exact": dict(varlen_attention_i8qk_mxv=lambda q, k, v, cu, scale, causal=False:
                                   oracle.varlen_attention_gqa(q, k, oracle.mx_round_keys(v, cu), cu, scale, causal)),
 }

@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--i8-fp8pv", action="store_true",
                     help="step = table + q/k norm/rotary writing INT8 q + INT8 codes of k + transposed E4M3 V + "
                          "attention with INT8 QK^T and FP8 PV")
+    ap.add_argument("--i8-smooth", action="store_true",
+                    help="with --i8-qk or --i8-fp8pv: subtract each segment's mean key before the key codes "
+                         "(two mean passes added to the step)")
     ap.add_argument("--fused-q", action="store_true",
                     help="step = table + K-only norm/rotary + attention that normalises and rotates Q itself")
     ap.add_argument("--split", choices=("auto", "never", "always"), default="auto",
@@ -464,6 +467,9 @@ def main():
         print(f"--fused-q needs a bidirectional workload with rot_dim a multiple of 32, without --fp8-qk "
               f"({w.name})", file=sys.stderr)
         return 2
+    if args.i8_smooth and not i8:
+        print("--i8-smooth needs --i8-qk or --i8-fp8pv", file=sys.stderr)
+        return 2
     if i8 and (fused or fp8):
         print("--i8-qk and --i8-fp8pv exclude --fused-q, --fp8 and --fp8-qk", file=sys.stderr)
         return 2
@@ -473,6 +479,11 @@ def main():
               torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=dev))
         k8 = (torch.empty(k.shape, dtype=torch.int8, device=dev),
               torch.empty((k.shape[1], max(nb, 1)), dtype=torch.float32, device=dev))
+        if args.i8_smooth:  # segment means of k and their chunk-sum workspace
+            nseg = len(w.lengths)
+            kmu = torch.empty((nseg, k.shape[1], k.shape[2]), dtype=torch.float32, device=dev)
+            kws = torch.empty((max(h3a.i8_key_mean_chunks(np.concatenate([[0], np.cumsum(w.lengths)])), 1),
+                               k.shape[1], k.shape[2]), dtype=torch.float32, device=dev)
     if fp8:  # E4M3 codes and one E8M0 scale per 32 head dims
         q8 = (torch.empty(q.shape, dtype=torch.uint8, device=dev),
               torch.empty((q.shape[1], q.shape[0], q.shape[2] // 32), dtype=torch.uint8, device=dev))
@@ -498,7 +509,11 @@ def main():
         h3a.prepare_vt_e4m3(v, cu, out=vt8[0], scale_out=vt8[1], stream=stream)
 
     def k_quant(cu):  # INT8 codes of the normalised, rotated k, one scale per 64 keys of a segment
-        h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], stream=stream)
+        if args.i8_smooth:  # of the centred keys
+            h3a.segment_key_means(kn, cu, out=kmu, workspace=kws, stream=stream)
+            h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], mu=kmu, stream=stream)
+        else:
+            h3a.quantize_i8_keys(kn, cu, out=k8[0], scale_out=k8[1], stream=stream)
 
     def vprep(cu):
         if fp8pv or i8pv:
@@ -638,9 +653,11 @@ def main():
                      else "rope table + q/k norm/rotary to E4M3 codes + transposed E4M3 V + attention with both "
                           "products in FP8" if fp8pv
                      else "rope table + q/k norm/rotary to E4M3 codes + attention with FP8 QK^T" if fp8
-                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k + transposed E4M3 V + "
+                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k" +
+                          (" (centred on segment means)" if args.i8_smooth else "") + " + transposed E4M3 V + "
                           "attention with INT8 QK^T and FP8 PV" if i8pv
-                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k + attention with INT8 QK^T" if i8
+                     else "rope table + q/k norm/rotary writing INT8 q + INT8 codes of k" +
+                          (" (centred on segment means)" if args.i8_smooth else "") + " + attention with INT8 QK^T" if i8
                      else "rope table + q/k norm/rotary + attention"),
         },
         "pct_bf16_peak_step": 100.0 * F / step_s / 1e12 / PEAK_BF16_TFLOPS,

@@ -436,6 +436,35 @@ h3a_status h3a_qk_rmsnorm_rope_i8q(const void* q, const void* k, void* q8, void*
 h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
                                 int64_t stride_x, int64_t stride_y, int64_t n_blocks, const int32_t* cu_seqlens,
                                 int32_t nseg, hipStream_t stream);
+
+/*
+ * Centred keys for the INT8 scores (SageAttention's K smoothing, SageAttention
+ * being among the GB10 build's attention backends: H3 Blackwell Runtime
+ * README, attention backends).  Within one segment every query's scores move
+ * by the same q . mean when the segment's mean key is subtracted from k, which
+ * the softmax cancels; K's per-channel offsets then no longer set the INT8
+ * block scales.
+ *
+ * h3a_i8_key_mean_chunks: the number of 256-key chunks of cu_seqlens (each
+ *   segment's counted from its start; host only).
+ * h3a_segment_key_means: mu [nseg][H][D] fp32 = the mean of bf16 k [S, H, D]
+ *   (token stride stride_k elements) over each segment's keys, 0 for an empty
+ *   segment, through the caller's workspace partial [n_chunks][H][D] fp32
+ *   (n_chunks from h3a_i8_key_mean_chunks, else ESHAPE).  Sums are taken in
+ *   fp32 in a fixed order (bitwise deterministic), then divided by the
+ *   segment length.  mu and partial are 4-byte aligned and overlap nothing.
+ * h3a_quantize_i8_keys_centered: h3a_quantize_i8_keys on the fp32
+ *   differences x - mu[segment] (mu 16-byte aligned, not overlapping y or
+ *   y_scale); the codes and scales stand for the centred keys, and
+ *   h3a_varlen_attn_fwd_i8qk / _i8qk_fp8pv take them unchanged.
+ */
+h3a_status h3a_i8_key_mean_chunks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_chunks);
+h3a_status h3a_segment_key_means(const void* k, void* partial, void* mu, int64_t S, int32_t H, int32_t D,
+                                 int64_t stride_k, int64_t n_chunks, const int32_t* cu_seqlens, int32_t nseg,
+                                 hipStream_t stream);
+h3a_status h3a_quantize_i8_keys_centered(const void* x, const void* mu, void* y, void* y_scale, int64_t S, int32_t H,
+                                         int32_t D, int64_t stride_x, int64_t stride_y, int64_t n_blocks,
+                                         const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream);
 h3a_status h3a_varlen_attn_fwd_i8qk(const void* q8, const void* k8, const void* q_scale, const void* k_scale,
                                     const void* v, void* o, int64_t S, int32_t Hq, int32_t Hkv, int32_t D,
                                     int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,

@@ -50,6 +50,9 @@ EXPORTS = (
     "h3a_quantize_i8_rows",
     "h3a_i8_key_blocks",
     "h3a_qk_rmsnorm_rope_i8q",
+    "h3a_i8_key_mean_chunks",
+    "h3a_segment_key_means",
+    "h3a_quantize_i8_keys_centered",
     "h3a_quantize_i8_keys",
     "h3a_varlen_attn_fwd_i8qk",
     "h3a_varlen_attn_fwd_i8qk_fp8pv",
@@ -122,6 +125,10 @@ def lib() -> ctypes.CDLL:
     L.h3a_qk_rmsnorm_rope_i8q.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i64,
                                           _vp, _vp, _f32, _vp, _i32, _vp]
     L.h3a_quantize_i8_keys.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _c_i32p, _i32, _vp]
+    L.h3a_quantize_i8_keys_centered.argtypes = [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _i64, _c_i32p, _i32,
+                                                _vp]
+    L.h3a_i8_key_mean_chunks.argtypes = [_c_i32p, _i32, _c_i64p]
+    L.h3a_segment_key_means.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _i64, _c_i32p, _i32, _vp]
     L.h3a_varlen_attn_fwd_i8qk.argtypes = L.h3a_varlen_attn_fwd_fp8qk.argtypes
     L.h3a_varlen_attn_fwd_i8qk_fp8pv.argtypes = L.h3a_varlen_attn_fwd_fp8.argtypes
     L.h3a_varlen_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i64, _i64,
@@ -136,7 +143,8 @@ def lib() -> ctypes.CDLL:
                  "h3a_quantize_e4m3", "h3a_varlen_attn_fwd_fp8qk", "h3a_qk_rmsnorm_rope_e4m3",
                  "h3a_vt_e4m3_columns", "h3a_prepare_vt_e4m3", "h3a_varlen_attn_fwd_fp8",
                  "h3a_quantize_i8_rows", "h3a_i8_key_blocks", "h3a_quantize_i8_keys", "h3a_varlen_attn_fwd_i8qk",
-                 "h3a_qk_rmsnorm_rope_i8q", "h3a_varlen_attn_fwd_i8qk_fp8pv",
+                 "h3a_qk_rmsnorm_rope_i8q", "h3a_varlen_attn_fwd_i8qk_fp8pv", "h3a_i8_key_mean_chunks",
+                 "h3a_segment_key_means", "h3a_quantize_i8_keys_centered",
                  "h3a_varlen_attn_fwd_ex", "h3a_varlen_attn_fwd_noalloc", "h3a_plan_tiles", "h3a_plan_tiles_ex"):
         getattr(L, name).restype = ctypes.c_int
     L.h3a_last_error.restype = ctypes.c_char_p
@@ -606,8 +614,9 @@ def i8_key_blocks(cu_seqlens) -> int:
     return int(n.value)
 
 
-def quantize_i8_keys(x, cu_seqlens, out=None, scale_out=None, stream=None):
-    """bf16 [S, H, D] -> (int8 [S, H, D] codes, fp32 [H, n_blocks] scales, one per 64 keys of a segment)."""
+def quantize_i8_keys(x, cu_seqlens, out=None, scale_out=None, mu=None, stream=None):
+    """bf16 [S, H, D] -> (int8 [S, H, D] codes, fp32 [H, n_blocks] scales, one per 64 keys of a segment);
+    with mu (fp32 [nseg, H, D], e.g. segment_key_means) the codes of the centred keys x - mu[segment]."""
     import torch
 
     S, H, D, sx = _token_major("x", x)
@@ -617,9 +626,38 @@ def quantize_i8_keys(x, cu_seqlens, out=None, scale_out=None, stream=None):
     nb = i8_key_blocks(cu)
     out, sy = _i8_out("out", out, x, S, H, D)
     sc = _f32_scales("scale_out", scale_out, (H, max(nb, 1)), x.device)
-    _check(lib().h3a_quantize_i8_keys(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy, nb,
-                                      _ptr_i32(cu), len(cu) - 1, _stream_handle(stream)))
+    if mu is None:
+        _check(lib().h3a_quantize_i8_keys(x.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H, D, sx, sy, nb,
+                                          _ptr_i32(cu), len(cu) - 1, _stream_handle(stream)))
+    else:
+        _expect("mu", mu, (len(cu) - 1, H, D), torch.float32)
+        _check(lib().h3a_quantize_i8_keys_centered(x.data_ptr(), mu.data_ptr(), out.data_ptr(), sc.data_ptr(), S, H,
+                                                   D, sx, sy, nb, _ptr_i32(cu), len(cu) - 1, _stream_handle(stream)))
     return out, sc
+
+
+def i8_key_mean_chunks(cu_seqlens) -> int:
+    """Number of 256-key chunks of cu_seqlens (the workspace rows of segment_key_means)."""
+    cu = _i32_array(cu_seqlens)
+    n = ctypes.c_int64(0)
+    _check(lib().h3a_i8_key_mean_chunks(_ptr_i32(cu), len(cu) - 1, ctypes.byref(n)))
+    return int(n.value)
+
+
+def segment_key_means(k, cu_seqlens, out=None, workspace=None, stream=None):
+    """bf16 k [S, H, D] -> fp32 [nseg, H, D]: each segment's mean key (0 for an empty segment)."""
+    import torch
+
+    S, H, D, sk = _token_major("k", k)
+    if k.dtype != torch.bfloat16:
+        raise H3AError(H3A_EDTYPE, f"k must be bfloat16, got {k.dtype}")
+    cu = _i32_array(cu_seqlens)
+    nc = i8_key_mean_chunks(cu)
+    out = _f32_scales("out", out, (len(cu) - 1, H, D), k.device)
+    ws = _f32_scales("workspace", workspace, (max(nc, 1), H, D), k.device)
+    _check(lib().h3a_segment_key_means(k.data_ptr(), ws.data_ptr(), out.data_ptr(), S, H, D, sk, nc, _ptr_i32(cu),
+                                       len(cu) - 1, _stream_handle(stream)))
+    return out
 
 
 def varlen_attn_fwd_i8qk(q8, k8, v, cu_seqlens, scale: float, causal: bool = False, out=None, stream=None):

@@ -1020,9 +1020,84 @@ h3a_status h3a_i8_key_blocks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n
   }
 }
 
+namespace {
+
+// The key quantiser, plain or on centred keys (mu: fp32 [nseg][H][D]).
+h3a_status quantize_i8_keys_impl(bool centered, const void* x, const float* mu, void* y, void* y_scale, int64_t S,
+                                 int32_t H, int32_t D, int64_t stride_x, int64_t stride_y, int64_t n_blocks,
+                                 const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream) {
+  if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
+  if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
+  if (H < 1) return fail(H3A_EINVAL, "H = %d must be >= 1", H);
+  if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
+  h3a_status st;
+  if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
+  const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg) / h3a::kVtTile;
+  if (n_blocks != need)
+    return fail(H3A_ESHAPE, "n_blocks = %lld but cu_seqlens has %lld blocks of 64 keys", (long long)n_blocks,
+                (long long)need);
+  if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
+  if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
+  const int64_t sbytes = int64_t(H) * n_blocks * 4;
+  if ((st = check_scales("y_scale", y_scale, sbytes, 4)) != H3A_OK) return st;
+  const int64_t mbytes = int64_t(nseg) * H * D * 4;
+  if (centered && (st = check_scales("mu", mu, mbytes, 16)) != H3A_OK) return st;
+  if (S == 0) return H3A_OK;
+  const Range rx = tensor_range(x, S, H, D, stride_x, 2), ry = tensor_range(y, S, H, D, stride_y, 1);
+  if (ranges_hit(rx, ry)) return fail(H3A_EINVAL, "y overlaps x");
+  const Range rs = byte_range(y_scale, sbytes);
+  if (ranges_hit(rs, rx) || ranges_hit(rs, ry)) return fail(H3A_EINVAL, "y_scale overlaps x or y");
+  if (centered) {
+    const Range rm = byte_range(mu, mbytes);
+    if (ranges_hit(rm, ry) || ranges_hit(rm, rs)) return fail(H3A_EINVAL, "mu overlaps y or y_scale");
+  }
+  hipError_t e = h3a::launch_quantize_i8_keys(x, y, y_scale, cu_seqlens, nseg, H, D, stride_x, stride_y, n_blocks,
+                                              stream, mu);
+  if (e != hipSuccess) return fail_hip("quantize_i8_keys launch", e);
+  return H3A_OK;
+}
+
+}  // namespace
+
 h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S, int32_t H, int32_t D,
                                 int64_t stride_x, int64_t stride_y, int64_t n_blocks, const int32_t* cu_seqlens,
                                 int32_t nseg, hipStream_t stream) {
+  try {
+    return quantize_i8_keys_impl(false, x, nullptr, y, y_scale, S, H, D, stride_x, stride_y, n_blocks,
+                                 cu_seqlens, nseg, stream);
+  } catch (...) {
+    return fail_exception("h3a_quantize_i8_keys");
+  }
+}
+
+h3a_status h3a_quantize_i8_keys_centered(const void* x, const void* mu, void* y, void* y_scale, int64_t S, int32_t H,
+                                         int32_t D, int64_t stride_x, int64_t stride_y, int64_t n_blocks,
+                                         const int32_t* cu_seqlens, int32_t nseg, hipStream_t stream) {
+  try {
+    return quantize_i8_keys_impl(true, x, static_cast<const float*>(mu), y, y_scale, S, H,
+                                 D, stride_x, stride_y, n_blocks, cu_seqlens, nseg, stream);
+  } catch (...) {
+    return fail_exception("h3a_quantize_i8_keys_centered");
+  }
+}
+
+h3a_status h3a_i8_key_mean_chunks(const int32_t* cu_seqlens, int32_t nseg, int64_t* n_chunks) {
+  try {
+    if (n_chunks == nullptr) return fail(H3A_EINVAL, "n_chunks is NULL");
+    if (cu_seqlens == nullptr) return fail(H3A_EINVAL, "cu_seqlens is NULL");
+    if (nseg < 1) return fail(H3A_EINVAL, "nseg = %d must be >= 1", nseg);
+    h3a_status st;
+    if ((st = check_cu_seqlens(cu_seqlens, nseg, cu_seqlens[nseg])) != H3A_OK) return st;
+    *n_chunks = h3a::key_mean_chunks(cu_seqlens, nseg);
+    return H3A_OK;
+  } catch (...) {
+    return fail_exception("h3a_i8_key_mean_chunks");
+  }
+}
+
+h3a_status h3a_segment_key_means(const void* k, void* partial, void* mu, int64_t S, int32_t H, int32_t D,
+                                 int64_t stride_k, int64_t n_chunks, const int32_t* cu_seqlens, int32_t nseg,
+                                 hipStream_t stream) {
   try {
     if (S < 0) return fail(H3A_EINVAL, "S = %lld must be >= 0", (long long)S);
     if (S > int64_t(INT32_MAX)) return fail(H3A_EUNSUPPORTED, "S = %lld exceeds INT32_MAX", (long long)S);
@@ -1030,25 +1105,25 @@ h3a_status h3a_quantize_i8_keys(const void* x, void* y, void* y_scale, int64_t S
     if (D != 64 && D != 128) return fail(H3A_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", D);
     h3a_status st;
     if ((st = check_cu_seqlens(cu_seqlens, nseg, S)) != H3A_OK) return st;
-    const int64_t need = h3a::vt_e4m3_columns(cu_seqlens, nseg) / h3a::kVtTile;
-    if (n_blocks != need)
-      return fail(H3A_ESHAPE, "n_blocks = %lld but cu_seqlens has %lld blocks of 64 keys", (long long)n_blocks,
+    const int64_t need = h3a::key_mean_chunks(cu_seqlens, nseg);
+    if (n_chunks != need)
+      return fail(H3A_ESHAPE, "n_chunks = %lld but cu_seqlens has %lld chunks of 256 keys", (long long)n_chunks,
                   (long long)need);
-    if ((st = check_operand("x", x, S, H, D, stride_x, 2)) != H3A_OK) return st;
-    if ((st = check_operand("y", y, S, H, D, stride_y, 1)) != H3A_OK) return st;
-    const int64_t sbytes = int64_t(H) * n_blocks * 4;
-    if ((st = check_scales("y_scale", y_scale, sbytes, 4)) != H3A_OK) return st;
-    if (S == 0) return H3A_OK;
-    const Range rx = tensor_range(x, S, H, D, stride_x, 2), ry = tensor_range(y, S, H, D, stride_y, 1);
-    if (ranges_hit(rx, ry)) return fail(H3A_EINVAL, "y overlaps x");
-    const Range rs = byte_range(y_scale, sbytes);
-    if (ranges_hit(rs, rx) || ranges_hit(rs, ry)) return fail(H3A_EINVAL, "y_scale overlaps x or y");
-    hipError_t e = h3a::launch_quantize_i8_keys(x, y, y_scale, cu_seqlens, nseg, H, D, stride_x, stride_y, n_blocks,
-                                                stream);
-    if (e != hipSuccess) return fail_hip("quantize_i8_keys launch", e);
+    if ((st = check_operand("k", k, S, H, D, stride_k, 2)) != H3A_OK) return st;
+    const int64_t pbytes = n_chunks * H * D * 4, mbytes = int64_t(nseg) * H * D * 4;
+    if ((st = check_scales("partial", partial, pbytes, 4)) != H3A_OK) return st;
+    if ((st = check_scales("mu", mu, mbytes, 4)) != H3A_OK) return st;
+    const Range rp = byte_range(partial, pbytes), rm = byte_range(mu, mbytes);
+    if (ranges_hit(rp, rm)) return fail(H3A_EINVAL, "partial overlaps mu");
+    if (S > 0) {
+      const Range rk = tensor_range(k, S, H, D, stride_k, 2);
+      if (ranges_hit(rp, rk) || ranges_hit(rm, rk)) return fail(H3A_EINVAL, "partial or mu overlaps k");
+    }
+    hipError_t e = h3a::launch_segment_key_means(k, partial, mu, cu_seqlens, nseg, H, D, stride_k, n_chunks, stream);
+    if (e != hipSuccess) return fail_hip("segment_key_means launch", e);
     return H3A_OK;
   } catch (...) {
-    return fail_exception("h3a_quantize_i8_keys");
+    return fail_exception("h3a_segment_key_means");
   }
 }
 

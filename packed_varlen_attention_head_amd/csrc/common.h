@@ -164,7 +164,16 @@ hipError_t launch_attn_fwd_i8qk_fp8pv(const void* q8, const void* k8, const void
 hipError_t launch_quantize_i8_rows(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
                                    int64_t sy, hipStream_t stream);
 hipError_t launch_quantize_i8_keys(const void* x, void* y, void* ys, const int32_t* cu, int32_t nseg, int32_t H,
-                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream);
+                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream,
+                                   const float* mu = nullptr);
+
+// Centred keys: the number of 256-key chunks of cu_seqlens (each segment's
+// from its start), and the segment means of x [S, H, D] (bf16, token stride
+// sx elements) into mu [nseg][H][D] fp32 through the chunk sums part
+// [n_chunks][H][D] fp32.
+int64_t key_mean_chunks(const int32_t* cu, int32_t nseg);
+hipError_t launch_segment_key_means(const void* x, void* part, void* mu, const int32_t* cu, int32_t nseg, int32_t H,
+                                    int32_t D, int64_t sx, int64_t n_chunks, hipStream_t stream);
 
 // The bf16 norm + rotary pass writing E4M3 codes of its bf16 results (output
 // token strides sq8, sk8 in bytes) with one E8M0 scale per 32 head dims in

@@ -14,6 +14,13 @@
 //
 // HBM-bound elementwise passes: a token row is read once (16 bytes a lane)
 // and its codes written once (8 bytes a lane).
+//
+// Centred keys (SageAttention's K smoothing, among the same backends): the
+// key quantiser can subtract each segment's mean key (per head and dim, fp32)
+// first; within a softmax every score then moves by the same q . mean, which
+// the softmax cancels.  The means come from two deterministic passes: sums of
+// 256-key chunks (aligned at each segment's start) in a fixed order, then each
+// segment's chunk sums in chunk order, divided by its length.
 #include <cstdint>
 
 #include "common.h"
@@ -100,6 +107,7 @@ constexpr int kKeyMaxSegs = 64;
 
 struct KeyBlockArgs {
   int32_t nseg;
+  int32_t seg0;    // first segment of this launch
   int32_t block0;  // first block of this launch
   int32_t start[kKeyMaxSegs];
   int32_t len[kKeyMaxSegs];
@@ -109,7 +117,8 @@ struct KeyBlockArgs {
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* __restrict__ y,
-                        float* __restrict__ ys, int64_t n_blocks, int64_t sx, int64_t sy) {
+                        float* __restrict__ ys, int64_t n_blocks, int64_t sx, int64_t sy,
+                        const float* __restrict__ mu) {
   constexpr int CH = D / 8;               // 8-dim chunks per key
   constexpr int KPP = kThreads / CH;      // keys per pass
   constexpr int NP = kVtTile / KPP;       // passes over the block's 64 keys
@@ -120,6 +129,13 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
   while (s + 1 < a.nseg && tau >= a.blocks[s + 1]) ++s;
   const int key0 = (tau - a.blocks[s]) * kVtTile;
   const int c = int(threadIdx.x % CH), kr = int(threadIdx.x / CH);
+  // centred keys: the segment's mean for this lane's 8 dims (0 without)
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (mu != nullptr) {
+    const float4* mp = reinterpret_cast<const float4*>(mu + (int64_t(a.seg0 + s) * gridDim.y + h) * D + c * 8);
+    const float4 m0 = mp[0], m1 = mp[1];
+    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+  }
   float f[NP][8];
   float amax = 0.f;
 #pragma unroll
@@ -130,9 +146,10 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[p][2 * i] = bf16_lo(w[i]);
-      f[p][2 * i + 1] = bf16_hi(w[i]);
-      amax = nan_max(nan_max(amax, __builtin_fabsf(f[p][2 * i])), __builtin_fabsf(f[p][2 * i + 1]));
+      f[p][2 * i] = bf16_lo(w[i]) - m[2 * i];
+      f[p][2 * i + 1] = bf16_hi(w[i]) - m[2 * i + 1];
+      if (key < a.len[s])  // keys past the segment take no part in the maximum
+        amax = nan_max(nan_max(amax, __builtin_fabsf(f[p][2 * i])), __builtin_fabsf(f[p][2 * i + 1]));
     }
   }
 #pragma unroll
@@ -152,7 +169,121 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
   if (threadIdx.x == 0) ys[int64_t(h) * n_blocks + a.block0 + tau] = __fdiv_rn(amax, 127.0f);
 }
 
+// Segment means of the keys.  Segments of one launch: key 0 at start[s],
+// len[s] keys, chunks[s] .. chunks[s + 1] its 256-key chunks (from chunk0).
+constexpr int kMeanChunk = 256;
+
+struct KeyChunkArgs {
+  int32_t nseg;
+  int32_t seg0;    // first segment of this launch
+  int32_t chunk0;  // first chunk of this launch
+  int32_t start[kKeyMaxSegs];
+  int32_t len[kKeyMaxSegs];
+  int32_t chunks[kKeyMaxSegs + 1];
+};
+
+// One 256-key chunk of one head per workgroup: each thread sums 8 dims of
+// every (kThreads / (D / 8))-th key, then the rows of partial sums meet in LDS
+// in row order; part [chunks][H][D].
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+key_chunk_sums_kernel(KeyChunkArgs a, const uint16_t* __restrict__ x, float* __restrict__ part, int64_t sx) {
+  constexpr int CH = D / 8;           // 8-dim pieces per key
+  constexpr int RPP = kThreads / CH;  // keys per pass
+  __shared__ float rows[RPP][D];
+  const int tau = blockIdx.x;
+  const int h = blockIdx.y;
+  int s = 0;
+  while (s + 1 < a.nseg && tau >= a.chunks[s + 1]) ++s;
+  const int key0 = (tau - a.chunks[s]) * kMeanChunk;
+  const int c = int(threadIdx.x % CH), kr = int(threadIdx.x / CH);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p = 0; p < kMeanChunk / RPP; ++p) {
+    const int key = key0 + p * RPP + kr;
+    if (key < a.len[s]) {
+      const uint4 r = *reinterpret_cast<const uint4*>(x + int64_t(a.start[s] + key) * sx + h * D + c * 8);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += bf16_lo(w[i]);
+        acc[2 * i + 1] += bf16_hi(w[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rows[kr][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (int(threadIdx.x) < D) {
+    float t = 0.f;
+    for (int r = 0; r < RPP; ++r) t += rows[r][threadIdx.x];
+    part[(int64_t(a.chunk0 + tau) * gridDim.y + h) * D + threadIdx.x] = t;
+  }
+}
+
+// One segment and head per workgroup, one dim per thread: the segment's chunk
+// sums in chunk order, divided by its length (0 for an empty segment).
+template <int D>
+__global__ void __launch_bounds__(D)
+key_means_kernel(KeyChunkArgs a, const float* __restrict__ part, float* __restrict__ mu) {
+  const int s = blockIdx.x;
+  const int h = blockIdx.y;
+  const int d = threadIdx.x;
+  float t = 0.f;
+  for (int ci = a.chunks[s]; ci < a.chunks[s + 1]; ++ci) t += part[(int64_t(a.chunk0 + ci) * gridDim.y + h) * D + d];
+  mu[(int64_t(a.seg0 + s) * gridDim.y + h) * D + d] = a.len[s] > 0 ? __fdiv_rn(t, float(a.len[s])) : 0.f;
+}
+
 }  // namespace
+
+int64_t key_mean_chunks(const int32_t* cu, int32_t nseg) {
+  int64_t n = 0;
+  for (int32_t s = 0; s < nseg; ++s) n += (int64_t(cu[s + 1]) - cu[s] + kMeanChunk - 1) / kMeanChunk;
+  return n;
+}
+
+hipError_t launch_segment_key_means(const void* x, void* part, void* mu, const int32_t* cu, int32_t nseg, int32_t H,
+                                    int32_t D, int64_t sx, int64_t n_chunks, hipStream_t stream) {
+  if (D != 128 && D != 64) return hipErrorInvalidValue;
+  int32_t chunk0 = 0;
+  for (int32_t s0 = 0; s0 < nseg; s0 += kKeyMaxSegs) {
+    const int32_t n = nseg - s0 < kKeyMaxSegs ? nseg - s0 : kKeyMaxSegs;
+    KeyChunkArgs a{};
+    a.nseg = n;
+    a.seg0 = s0;
+    a.chunk0 = chunk0;
+    a.chunks[0] = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      a.start[i] = cu[s0 + i];
+      a.len[i] = cu[s0 + i + 1] - cu[s0 + i];
+      a.chunks[i + 1] = a.chunks[i] + (a.len[i] + kMeanChunk - 1) / kMeanChunk;
+    }
+    const int32_t nc = a.chunks[n];
+    if (int64_t(chunk0) + nc > n_chunks) return hipErrorInvalidValue;
+    if (nc > 0) {
+      const dim3 grid{unsigned(nc), unsigned(H), 1u};
+      if (D == 128)
+        hipLaunchKernelGGL(key_chunk_sums_kernel<128>, grid, dim3(kThreads), 0, stream, a,
+                           static_cast<const uint16_t*>(x), static_cast<float*>(part), sx);
+      else
+        hipLaunchKernelGGL(key_chunk_sums_kernel<64>, grid, dim3(kThreads), 0, stream, a,
+                           static_cast<const uint16_t*>(x), static_cast<float*>(part), sx);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const dim3 grid{unsigned(n), unsigned(H), 1u};
+    if (D == 128)
+      hipLaunchKernelGGL(key_means_kernel<128>, grid, dim3(128), 0, stream, a, static_cast<const float*>(part),
+                         static_cast<float*>(mu));
+    else
+      hipLaunchKernelGGL(key_means_kernel<64>, grid, dim3(64), 0, stream, a, static_cast<const float*>(part),
+                         static_cast<float*>(mu));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    chunk0 += nc;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_quantize_i8_rows(const void* x, void* y, void* ys, int64_t S, int32_t H, int32_t D, int64_t sx,
                                    int64_t sy, hipStream_t stream) {
@@ -172,13 +303,15 @@ hipError_t launch_quantize_i8_rows(const void* x, void* y, void* ys, int64_t S, 
 }
 
 hipError_t launch_quantize_i8_keys(const void* x, void* y, void* ys, const int32_t* cu, int32_t nseg, int32_t H,
-                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream) {
+                                   int32_t D, int64_t sx, int64_t sy, int64_t n_blocks, hipStream_t stream,
+                                   const float* mu) {
   if (D != 128 && D != 64) return hipErrorInvalidValue;
   int32_t block0 = 0;
   for (int32_t s0 = 0; s0 < nseg; s0 += kKeyMaxSegs) {
     const int32_t n = nseg - s0 < kKeyMaxSegs ? nseg - s0 : kKeyMaxSegs;
     KeyBlockArgs a{};
     a.nseg = n;
+    a.seg0 = s0;
     a.block0 = block0;
     a.blocks[0] = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -193,11 +326,11 @@ hipError_t launch_quantize_i8_keys(const void* x, void* y, void* ys, const int32
       if (D == 128)
         hipLaunchKernelGGL(quantize_i8_keys_kernel<128>, grid, dim3(kThreads), 0, stream, a,
                            static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), n_blocks,
-                           sx, sy);
+                           sx, sy, mu);
       else
         hipLaunchKernelGGL(quantize_i8_keys_kernel<64>, grid, dim3(kThreads), 0, stream, a,
                            static_cast<const uint16_t*>(x), static_cast<int8_t*>(y), static_cast<float*>(ys), n_blocks,
-                           sx, sy);
+                           sx, sy, mu);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -531,3 +531,43 @@ def test_varlen_attn_fwd_i8qk_fp8pv_rejects(kw, status, word):
                                                   Hkv * D, kw.get("cols", 384), Hq * D, cp, 2, 0.088, 0, None)
     assert st == status
     assert word in h3a.last_error(), h3a.last_error()
+
+
+def test_i8_key_mean_chunks_counts_each_segment_from_its_start():
+    n = ctypes.c_int64(-1)
+    c, cp = i32((0, 257, 257, 258, 770))
+    assert h3a.lib().h3a_i8_key_mean_chunks(cp, 4, ctypes.byref(n)) == h3a.H3A_OK and n.value == 2 + 0 + 1 + 2
+    assert h3a.i8_key_mean_chunks([0, 256, 512, 513]) == 3
+    assert h3a.lib().h3a_i8_key_mean_chunks(cp, 4, None) == h3a.H3A_EINVAL
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(nc=3), h3a.H3A_ESHAPE, "n_chunks = 3"),
+    (dict(part=None), h3a.H3A_EINVAL, "partial is NULL"),
+    (dict(mu=None), h3a.H3A_EINVAL, "mu is NULL"),
+    (dict(mu=P + (2 << 24) + 2), h3a.H3A_EUNSUPPORTED, "mu is not 4-byte aligned"),
+    (dict(mu=P + (1 << 24) + 64), h3a.H3A_EINVAL, "partial overlaps mu"),
+    (dict(part=P + 4096), h3a.H3A_EINVAL, "partial or mu overlaps k"),
+])
+def test_segment_key_means_rejects(kw, status, word):
+    H, D = 2, 128
+    c, cp = i32((0, 100, 300))  # 1 + 1 chunks of 256 keys
+    st = h3a.lib().h3a_segment_key_means(P, kw.get("part", P + (1 << 24)), kw.get("mu", P + (2 << 24)), 300, H, D,
+                                         H * D, kw.get("nc", 2), cp, 2, None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(mu=None), h3a.H3A_EINVAL, "mu is NULL"),
+    (dict(mu=P + (3 << 24) + 4), h3a.H3A_EUNSUPPORTED, "mu is not 16-byte aligned"),
+    (dict(mu=P + (1 << 24) + 256), h3a.H3A_EINVAL, "mu overlaps y or y_scale"),
+    (dict(nb=5), h3a.H3A_ESHAPE, "n_blocks = 5"),
+])
+def test_quantize_i8_keys_centered_rejects(kw, status, word):
+    H, D = 2, 128
+    c, cp = i32((0, 100, 300))  # 2 + 4 key blocks
+    st = h3a.lib().h3a_quantize_i8_keys_centered(P, kw.get("mu", P + (3 << 24)), P + (1 << 24), P + (2 << 24), 300, H,
+                                                 D, H * D, H * D, kw.get("nb", 6), cp, 2, None)
+    assert st == status
+    assert word in h3a.last_error(), h3a.last_error()

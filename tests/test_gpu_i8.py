@@ -450,3 +450,131 @@ def test_many_segments_key_blocks_and_attention():
     o = to_f64(gpu_i8qk(qb, kb, vb, cu, 0.125))
     qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
     compare(o, oracle.varlen_attention_i8qk(qf, kf, vf, cu, 0.125), "bf16", "o vs INT8 oracle, 150 segments")
+
+
+# ---------------------------------------------------------------------------
+# centred keys (segment means subtracted before the key codes)
+
+
+def _offset_keys(seed, lens, H, D, offset=20.0):
+    """bf16 keys N(0,1) plus a per-(head, dim) offset of `offset` sigma, as real key
+    activations carry per-channel offsets."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S = int(cu[-1])
+    base = rng.bf16_bits_to_f32(rng.normal_tensor(seed, rng.TAG_K, (S, H, D), "bf16"))
+    off = rng.bf16_bits_to_f32(rng.normal_tensor(seed + 1, rng.TAG_K, (1, H, D), "bf16")) * np.float32(offset)
+    return cu, rng.f32_to_bf16_bits(base + off)
+
+
+def _mean_bound(kf, cu, mu):
+    """Per (segment, head, dim) bound on the fp32 mean's error: every key enters at most
+    40 + chunks partial sums (a thread's 16 or 8 keys, 16 or 32 rows of thread sums, the
+    chunk sums), each rounded to within 2^-24 of itself, then one division."""
+    b = np.zeros_like(mu)
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e > a:
+            nc = -(-(e - a) // 256)
+            b[s] = (40 + nc) * 2.0 ** -24 * np.abs(kf[a:e]).mean(axis=0) + 1e-30
+    return b
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_segment_key_means(D):
+    import torch
+
+    lens = EDGE_LENS + [1000, 3000]
+    cu, kb = _offset_keys(1601 + D, lens, 3, D)
+    k = to_device(kb, "bf16")
+    log(f"[key means] D={D} S={int(cu[-1])} chunks={h3a().i8_key_mean_chunks(cu)}")
+    mu = h3a().segment_key_means(k, cu)
+    mu2 = h3a().segment_key_means(k, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(mu, mu2)  # fixed summation order
+    kf = rng.as_f64(kb, "bf16")
+    want = oracle.segment_key_means(kf, cu)
+    got = mu.cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    bound = _mean_bound(kf, cu, want)
+    log(f"  max |mu - oracle| = {err.max():.3e}, max err / bound = {(err / np.maximum(bound, 1e-300)).max():.3f}")
+    assert np.all(err <= bound)
+    assert np.all(got[EDGE_LENS.index(0)] == 0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantize_keys_centered_bit_exact(D):
+    """Given the same fp32 means, the centred key codes and scales equal the oracle's bit for bit."""
+    import torch
+
+    lens = EDGE_LENS + [1000]
+    cu, kb = _offset_keys(1701 + D, lens, 2, D)
+    kb[5, 1, 3] = _f32_bits_to_bf16(np.array([np.nan], np.float32))[0]
+    kf = rng.as_f64(kb, "bf16")
+    mu32 = oracle.segment_key_means(kf, cu).astype(np.float32)
+    log(f"[centred key codes] D={D} S={int(cu[-1])}")
+    c, s = h3a().quantize_i8_keys(to_device(kb, "bf16"), cu, mu=torch.from_numpy(mu32).cuda())
+    wc, ws = oracle.i8_quantize_key_blocks_centered(kf, cu, mu32)
+    _codes_and_scales_equal(c, s, wc, ws, "centred k blocks")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("pv8", [False, True])
+def test_i8qk_centered_vs_oracle(D, causal, pv8):
+    """Keys with per-channel offsets of 20 sigma, grouped K/V: INT8 attention on centred keys
+    (the oracle's fp32 means) against the oracle at the bf16 tolerance (FP8 PV: within the
+    weights' rounding bound); on the GPU's own means, far closer to exact attention than
+    INT8 attention on the plain keys (beyond the E4M3 floor with FP8 PV)."""
+    import torch
+
+    lens = EDGE_LENS + [1000]
+    cu, kb = _offset_keys(1801 + D + 2 * causal + 4 * pv8, lens, 2, D)
+    S = int(cu[-1])
+    qb = rng.normal_tensor(1802 + D, rng.TAG_Q, (S, 4, D), "bf16")
+    vb = rng.normal_tensor(1803 + D, rng.TAG_V, (S, 2, D), "bf16")
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (qb, kb, vb))
+    scale = 1.0 / np.sqrt(D)
+    mu32 = oracle.segment_key_means(kf, cu).astype(np.float32)
+    q, k, v = (to_device(x, "bf16") for x in (qb, kb, vb))
+    log(f"[i8 centred] D={D} causal={causal} pv8={pv8} S={S}")
+
+    def run(mu):
+        q8, k8 = h3a().quantize_i8_rows(q), h3a().quantize_i8_keys(k, cu, mu=mu)
+        if pv8:
+            return to_f64(h3a().varlen_attn_fwd_i8qk_fp8pv(q8, k8, h3a().prepare_vt_e4m3(v, cu), cu, scale, causal))
+        return to_f64(h3a().varlen_attn_fwd_i8qk(q8, k8, v, cu, scale, causal))
+
+    o = run(torch.from_numpy(mu32).cuda())
+    if pv8:
+        bound, ref = weight_rounding_bound(oracle.i8_round_q(qf), oracle.i8_round_k_centered(kf, cu, mu32),
+                                           oracle.mx_round_keys(vf, cu), cu, scale, causal)
+        check_bound(o, ref, "o vs centred INT8 + E4M3 oracle", bound, TOL_FP8PV_MEANREL)
+    else:
+        compare(o, oracle.varlen_attention_i8qk_centered(qf, kf, vf, cu, scale, causal, mu32=mu32), "bf16",
+                "o vs centred INT8 oracle")
+    exact = oracle.varlen_attention_gqa(qf, kf, vf, cu, scale, causal)
+    own = run(h3a().segment_key_means(k, cu))
+    plain = run(None)
+    err = lambda x: float(np.abs(x - exact).sum() / np.abs(exact).sum())  # noqa: E731
+    log(f"  mean-rel vs exact: centred (GPU means) {err(own):.3e}, plain keys {err(plain):.3e}")
+    # with FP8 PV the E4M3 V and weights add their own ~3e-2 (the chain tests) to both
+    assert err(own) < 0.3 * err(plain) + (0.03 if pv8 else 0.0)
+
+
+def test_centered_keys_many_segments():
+    """150 ragged segments (three launches of both mean passes and of the quantiser)."""
+    import torch
+
+    lens = [int(x) for x in 1 + (rng.uniform(81, rng.TAG_LENS, 150) * 700).astype(np.int64)]
+    lens[9] = 0
+    cu, kb = _offset_keys(82, lens, 2, 64)
+    kf = rng.as_f64(kb, "bf16")
+    k = to_device(kb, "bf16")
+    log(f"[centred many segments] S={int(cu[-1])} nseg={len(lens)} chunks={h3a().i8_key_mean_chunks(cu)}")
+    mu = h3a().segment_key_means(k, cu).cpu().numpy().astype(np.float64)
+    want = oracle.segment_key_means(kf, cu)
+    assert np.all(np.abs(mu - want) <= _mean_bound(kf, cu, want))
+    mu32 = want.astype(np.float32)
+    c, s = h3a().quantize_i8_keys(k, cu, mu=torch.from_numpy(mu32).cuda())
+    wc, ws = oracle.i8_quantize_key_blocks_centered(kf, cu, mu32)
+    _codes_and_scales_equal(c, s, wc, ws, "centred k blocks, 150 segments")

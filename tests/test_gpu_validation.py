@@ -154,6 +154,16 @@ def test_int8_operands():
     qi8o = torch.zeros((S - 1, H, D), dtype=torch.int8, device="cuda")
     refused(lambda: h3a.qk_rmsnorm_rope_i8q(q, k, gam, gam, 1e-6, tab, R, q8=qi8o), h3a.H3A_ESHAPE, qi8o)
     refused(lambda: h3a.qk_rmsnorm_rope_i8q(q.float(), k.float(), gam, gam, 1e-6, tab, R), h3a.H3A_EDTYPE)
+    # centred keys: means and their workspace fp32 of the exact shapes
+    nseg = len(LENS)
+    refused(lambda: h3a.segment_key_means(k.float(), cu), h3a.H3A_EDTYPE)
+    refused(lambda: h3a.segment_key_means(k, cu, workspace=torch.zeros((1, H, D), device="cuda")), h3a.H3A_ESHAPE)
+    mu_bad = torch.zeros((nseg, H, D - 1), device="cuda")
+    refused(lambda: h3a.segment_key_means(k, cu, out=mu_bad), h3a.H3A_ESHAPE, mu_bad)
+    refused(lambda: h3a.quantize_i8_keys(k, cu, mu=mu_bad), h3a.H3A_ESHAPE)
+    refused(lambda: h3a.quantize_i8_keys(k, cu, mu=torch.zeros((nseg, H, D), device="cuda").half()), h3a.H3A_EDTYPE)
+    mu = h3a.segment_key_means(k, cu)
+    ki8 = h3a.quantize_i8_keys(k, cu, mu=mu)
     o = h3a.varlen_attn_fwd_i8qk(qi8, ki8, v, cu, 0.1, out=out)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
@@ -190,4 +200,9 @@ def test_all_empty_packing_is_a_no_op():
     assert h3a.quantize_i8_rows(q)[0].shape == (0, H, D)
     assert h3a.varlen_attn_fwd_i8qk(qi8, ki8, v, cu, 0.1).shape == (0, H, D)
     assert h3a.varlen_attn_fwd_i8qk_fp8pv(qi8, ki8, vt8, cu, 0.1).shape == (0, H, D)
+    assert h3a.i8_key_mean_chunks(cu) == 0
+    mu = h3a.segment_key_means(k, cu)
+    torch.cuda.synchronize()
+    assert mu.shape == (2, H, D) and not mu.any()  # every segment empty: mean 0
+    assert h3a.quantize_i8_keys(kn, cu, mu=mu)[0].shape == (0, H, D)
     torch.cuda.synchronize()

@@ -112,3 +112,37 @@ def test_random_packing_fp8(case, _gpu):
     assert np.all(np.isfinite(o))
     bound, ref = weight_rounding_bound(*mx_operands(q, k, v, cu), cu, scale, causal)
     check(o, ref, "o, both products FP8", bound, TOL_FP8PV_MEANREL)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_packing_int8(case, _gpu):
+    """The same packings through the INT8 score kernels (q and k quantised on the GPU,
+    per token and per 64-key block of each segment): bf16 PV against attention on what
+    the codes stand for at the bf16 tolerance; FP8 PV (transposed E4M3 V) within the
+    weight-rounding bound of attention on those q, k and block-rounded v."""
+    import packed_varlen_attention_head_amd as h3a
+    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, weight_rounding_bound
+
+    lens, Hq, Hkv, D, causal, _ = layout(case)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    S = int(cu[-1])
+    seed = 4000 + case
+    log(f"[random packing int8] case={case} nseg={len(lens)} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    if S == 0:
+        pytest.skip("empty packing (covered by test_gpu_validation.py)")
+    q = rng.normal_tensor(seed, rng.TAG_Q, (S, Hq, D), "bf16")
+    k = rng.normal_tensor(seed, rng.TAG_K, (S, Hkv, D), "bf16")
+    v = rng.normal_tensor(seed, rng.TAG_V, (S, Hkv, D), "bf16")
+    scale = 1.0 / np.sqrt(D)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    q8, k8 = h3a.quantize_i8_rows(qd), h3a.quantize_i8_keys(kd, cu)
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
+    o = to_f64(h3a.varlen_attn_fwd_i8qk(q8, k8, vd, cu, scale, causal=causal))
+    assert np.all(np.isfinite(o))
+    compare(o, oracle.varlen_attention_i8qk(qf, kf, vf, cu, scale, causal=causal), "bf16", "o, INT8 scores")
+    o = to_f64(h3a.varlen_attn_fwd_i8qk_fp8pv(q8, k8, h3a.prepare_vt_e4m3(vd, cu), cu, scale, causal=causal))
+    assert np.all(np.isfinite(o))
+    bound, ref = weight_rounding_bound(oracle.i8_round_q(qf), oracle.i8_round_k(kf, cu), oracle.mx_round_keys(vf, cu),
+                                       cu, scale, causal)
+    check(o, ref, "o, INT8 scores and FP8 PV", bound, TOL_FP8PV_MEANREL)

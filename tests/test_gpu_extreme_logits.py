@@ -124,6 +124,38 @@ def test_rising_logits_fp8_both():
     check(o, ref, "o vs block-scaled oracle", bound, TOL_FP8PV_MEANREL)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_logits_int8_scores(causal):
+    """INT8 score product (per-tile score multiplier in the probabilities' FMA), bf16
+    probabilities: against attention on what the codes stand for.  The gain-40 tile sets
+    its own key-block scale, so its scores jump as in the bf16 case."""
+    D, Hq, Hkv = 128, 4, 2
+    cu, q, k, v = rising_inputs(61 + causal, Hq, Hkv, D)
+    log(f"[rising] int8 scores causal={causal}")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o = to_f64(h3a().varlen_attn_fwd_i8qk(h3a().quantize_i8_rows(qd), h3a().quantize_i8_keys(kd, cu), vd, cu,
+                                          1.0 / np.sqrt(D), causal=causal))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
+    compare(o, oracle.varlen_attention_i8qk(qf, kf, vf, cu, 1.0 / np.sqrt(D), causal), "bf16", "o vs INT8 oracle")
+
+
+def test_rising_logits_int8_scores_fp8_output():
+    """INT8 scores with FP8 PV: within the weight-rounding bound of attention on the INT8
+    q, k and block-rounded v."""
+    from tests.test_gpu_fp8 import TOL_FP8PV_MEANREL, check, weight_rounding_bound
+
+    D, H = 128, 2
+    cu, q, k, v = rising_inputs(71, H, H, D)
+    log("[rising] int8 scores, fp8 output")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o = to_f64(h3a().varlen_attn_fwd_i8qk_fp8pv(h3a().quantize_i8_rows(qd), h3a().quantize_i8_keys(kd, cu),
+                                                h3a().prepare_vt_e4m3(vd, cu), cu, 1.0 / np.sqrt(D)))
+    qf, kf, vf = (rng.as_f64(x, "bf16") for x in (q, k, v))
+    bound, ref = weight_rounding_bound(oracle.i8_round_q(qf), oracle.i8_round_k(kf, cu), oracle.mx_round_keys(vf, cu),
+                                       cu, 1.0 / np.sqrt(D))
+    check(o, ref, "o vs INT8 + E4M3 oracle", bound, TOL_FP8PV_MEANREL)
+
+
 def test_rising_logits_fused_q_bitwise():
     """Q norm + rotary inside the attention prologue gives the same bytes as the norm
     pass followed by the attention, on rising keys."""

@@ -498,13 +498,7 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       float ks;
       if constexpr (std::is_integral_v<decltype(slot)>) ks = slot ? kscale[1] : kscale[0];
       else ks = kscale[decltype(slot)::value];
-      // A zero scale (an all-zero q row or k block, or rows past the segment
-      // end) would turn a masked key's -inf into -inf * 0 = NaN: use the
-      // smallest normal instead (every such score is 0 exactly, or at most
-      // 2^22 * 2^-126 from it, either way a probability of 1 against the
-      // reference).  A NaN scale stays NaN.
       cmul = cq * ks;
-      cmul = cmul < 1.17549435e-38f ? 1.17549435e-38f : cmul;
       cadd = -cmul * 12582912.0f;
     }
   };
@@ -712,6 +706,18 @@ attn_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // query row, get -inf.  The lane's key offset hi*4 is folded into one
   // bound, so every compare is against a constant.
   auto mask = [&](f32x16* sacc, int tt) {
+    if constexpr (kI8) {
+      // A zero score multiplier (an all-zero q row or k block, or rows past
+      // the segment end) would turn a masked key's -inf into -inf * 0 = NaN:
+      // in a masked tile it takes the smallest normal instead (every such
+      // score is 0 exactly, or at most 2^22 * 2^-126 from it, a probability of
+      // 1 against the reference either way).  A NaN multiplier stays NaN.
+      // Only the tiles that hold masked keys pay for this check.
+      if (cmul < 1.17549435e-38f) {
+        cmul = 1.17549435e-38f;
+        cadd = -cmul * 12582912.0f;
+      }
+    }
     int lim = it.seg_len - tt * kBN - 1;  // last key of the tile inside the segment
     if constexpr (CAUSAL) lim = min(lim, qrow0 + l32 - tt * kBN);
     lim -= hi * 4;

@@ -130,11 +130,11 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
   const int key0 = (tau - a.blocks[s]) * kVtTile;
   const int c = int(threadIdx.x % CH), kr = int(threadIdx.x / CH);
   // centred keys: the segment's mean for this lane's 8 dims (0 without)
-  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float mk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (mu != nullptr) {
     const float4* mp = reinterpret_cast<const float4*>(mu + (int64_t(a.seg0 + s) * gridDim.y + h) * D + c * 8);
     const float4 m0 = mp[0], m1 = mp[1];
-    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+    mk[0] = m0.x; mk[1] = m0.y; mk[2] = m0.z; mk[3] = m0.w; mk[4] = m1.x; mk[5] = m1.y; mk[6] = m1.z; mk[7] = m1.w;
   }
   float f[NP][8];
   float amax = 0.f;
@@ -146,8 +146,8 @@ quantize_i8_keys_kernel(KeyBlockArgs a, const uint16_t* __restrict__ x, int8_t* 
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[p][2 * i] = bf16_lo(w[i]) - m[2 * i];
-      f[p][2 * i + 1] = bf16_hi(w[i]) - m[2 * i + 1];
+      f[p][2 * i] = bf16_lo(w[i]) - mk[2 * i];
+      f[p][2 * i + 1] = bf16_hi(w[i]) - mk[2 * i + 1];
       if (key < a.len[s])  // keys past the segment take no part in the maximum
         amax = nan_max(nan_max(amax, __builtin_fabsf(f[p][2 * i])), __builtin_fabsf(f[p][2 * i + 1]));
     }

@@ -36,7 +36,8 @@ sqrt are the only library primitives used):
    section 5b; the low-precision variant (Q and K rounded to FP8 E4M3 before
    the score product) is section 5c, its per-block-scaled form section 5d,
    and the INT8 score product with per-token Q and per-key-block K scales
-   section 5e.
+   section 5e (with the PV product on block-scaled E4M3 V as well); keys
+   centred on their segment's mean before their INT8 codes are section 5f.
 
 Readings where the pages are silent:
 integer per-segment positions starting at 0; base 10000; gains are fp32 [D]

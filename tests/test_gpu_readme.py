@@ -1,5 +1,7 @@
-"""The usage example in README.md runs as written and its output matches the
-oracle on sampled rows."""
+"""The usage examples in README.md run as written: the bf16 chain's output
+matches the oracle on sampled rows, and the low-precision block, run on the
+inputs from before the in-place norm, stays within the INT8 + FP8 PV chain's
+error of the bf16 output."""
 from __future__ import annotations
 
 import os
@@ -22,7 +24,7 @@ def test_readme_example():
 
     text = open(os.path.join(ROOT, "README.md")).read()
     blocks = re.findall(r"```python\n(.*?)```", text, re.S)
-    assert len(blocks) == 1
+    assert len(blocks) == 2
     torch.manual_seed(0)
     env = {}
     # keep a copy of q, k, v before the in-place norm: run the block up to the norm first
@@ -42,3 +44,13 @@ def test_readme_example():
     qn, kn = oracle.qk_rmsnorm_rope(qf, kf, ones, ones, 1e-6, cos, sin, 96)
     ref = oracle.varlen_attention_rows(qn, kn, vf, cu, 1.0 / np.sqrt(qf.shape[2]), rows)
     compare(to_f64(o)[rows], ref, "bf16", f"o ({len(rows)} rows)")
+
+    # the low-precision block, on the inputs before the in-place norm
+    env["q"], env["k"] = q0.clone(), k0.clone()
+    exec(blocks[1], env)
+    torch.cuda.synchronize()
+    o8 = env["o"]
+    assert o8.dtype == torch.bfloat16 and o8.shape == o.shape and torch.isfinite(o8.float()).all()
+    d = (o8.float() - o.float()).abs().mean().item() / o.float().abs().mean().item()
+    log(f"[readme] INT8 scores + FP8 PV vs bf16: mean rel {d:.2e}")
+    assert d < 8e-2  # the chain measures 3.9e-2 against exact attention
